@@ -1,0 +1,167 @@
+/*
+ * ie.h - C ABI of the integer-only (C, e) layer-step library for MI355X (gfx950).
+ *
+ * Every tensor is a pair (C, e): signed INT8 mantissas C and signed INT8
+ * power-of-two exponents e, value C * 2^e ("Memory-Efficient Integer-Only
+ * Training of Deep Neural Networks", Abstract and Figure 1).  An exponent is
+ * shared by a group: the whole tensor (IE_GROUP_TENSOR) or one leading-index
+ * row (IE_GROUP_ROW: a token / pixel row of an activation, an output channel of
+ * a weight [N x K]; Table 5 gives one exponent byte per output channel).
+ *
+ * Arithmetic contract (identical for every entry point):
+ *   - products are exact int8 x int8 sums, exponent e_a + e_b (Table 6,
+ *     "Product"); every stored result is rounded exactly once from the exact
+ *     value, right shifts rounding half to even;
+ *   - a result group's exponent is the smallest e with all |C| <= 127, or
+ *     -128 if the group is all zero or smaller; mantissas -128 are accepted on
+ *     input and never produced;
+ *   - an operand whose exponent varies along a contraction axis is first
+ *     re-expressed at the largest exponent on that axis (same rounding);
+ *   - an exponent above 127 sets IE_FLAG_EXP_RANGE in the workspace's sticky
+ *     flags (read with ie_device_status); that output's values are undefined.
+ *
+ * Memory and execution:
+ *   - every mantissa/exponent/workspace pointer is a DEVICE pointer owned by
+ *     the caller; the library allocates nothing and keeps no global state;
+ *   - matrices are row-major and contiguous; activations of convolutions are
+ *     NHWC, viewed as a matrix [N*H*W x C]; weights are [K x R*S*C] (KRSC);
+ *   - outputs are fully overwritten, mantissas and exponents; outputs must not
+ *     alias inputs (ie_sgd_update works in place on W and V);
+ *   - `ws` is a workspace of at least the size the matching *_workspace_bytes
+ *     call returns; its first 256 bytes hold sticky flags and must be zeroed
+ *     once (ie_workspace_init) before first use;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     runs asynchronously; calls sharing one workspace must be ordered on one
+ *     stream;
+ *   - argument errors are detected on the host and returned before anything
+ *     is enqueued; launch failures return IE_ERR_HIP.
+ */
+#ifndef IE_H
+#define IE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IE_OK = 0,
+    IE_ERR_NULL = 1,        /* a required pointer is NULL */
+    IE_ERR_SHAPE = 2,       /* shapes do not agree or are negative */
+    IE_ERR_GROUP = 3,       /* unknown group kind */
+    IE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+    IE_ERR_EXP_RANGE = 5,   /* reported by ie_device_status callers */
+    IE_ERR_UNSUPPORTED = 6, /* valid but outside what this build supports */
+    IE_ERR_HIP = 7          /* a HIP runtime call failed */
+} ie_status;
+
+typedef enum { IE_GROUP_TENSOR = 0, IE_GROUP_ROW = 1 } ie_group;
+
+#define IE_FLAG_EXP_RANGE 1u
+
+/* A (C, e) matrix.  mant: rows*cols bytes, row-major.  exp: 1 byte (TENSOR)
+ * or `rows` bytes (ROW). */
+typedef struct {
+    int8_t *mant;
+    int8_t *exp;
+    int64_t rows;
+    int64_t cols;
+    int32_t group;
+} ie_mat;
+
+/* Convolution shape: input NHWC [n, h, w, c], weight [k, r, s, c], zero
+ * padding `pad` on every side, equal strides; output [n, p, q, k] with
+ * p = (h + 2 pad - r) / stride + 1, q = (w + 2 pad - s) / stride + 1. */
+typedef struct {
+    int32_t n, h, w, c, k, r, s, stride, pad;
+} ie_conv_desc;
+
+/* A (C, e) scalar (learning rate, momentum, weight decay): value mant * 2^exp. */
+typedef struct {
+    int8_t mant;
+    int8_t exp;
+} ie_scalar;
+
+/* Workspace sizes (bytes) for one call of the matching entry point. */
+size_t ie_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
+size_t ie_linear_bwd_dx_workspace(int64_t M, int64_t N, int64_t K);
+size_t ie_linear_bwd_dw_workspace(int64_t M, int64_t N, int64_t K);
+size_t ie_conv_fwd_workspace(const ie_conv_desc *d);
+size_t ie_conv_bwd_workspace(const ie_conv_desc *d);
+size_t ie_sgd_update_workspace(int64_t rows, int64_t cols);
+
+/* Zero the workspace's sticky flags (enqueued on `stream`). */
+ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Forward product of a linear layer, Y = X . W^T (Table 6 "Linear /
+ * fully-connected -> Product"; Figure 1a).
+ *   X [M x K], W [N x K], Y [M x N]; groups: X, W, Y each TENSOR or ROW.
+ *   Contraction limit: K <= 65536.
+ */
+ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Input gradient of a linear layer, dX = dY . W (Figure 1a, backward).
+ *   dY [M x N], W [N x K], dX [M x K].  A ROW-grouped W is aligned over its
+ *   rows (the contraction axis) first.  N <= 65536.
+ */
+ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Weight gradient of a linear layer, dW = dY^T . X (Figure 1a, backward;
+ * Table 5 groups: ROW = per output channel).
+ *   dY [M x N], X [M x K], dW [N x K].  ROW-grouped dY or X are aligned over
+ *   their rows (the contraction axis) first.  Any M (exact int32 partial sums
+ *   over chunks of at most 65536 rows, merged in int64).
+ */
+ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Forward convolution (Table 6 "Convolution -> Product"), implicit GEMM:
+ *   Y[n,p,q,k] = sum_{r,s,c} X[n, p*st+r-pad, q*st+s-pad, c] * W[k,r,s,c].
+ *   X: rows n*h*w, cols c, TENSOR.  W: rows k, cols r*s*c, TENSOR or ROW.
+ *   Y: rows n*p*q, cols k, TENSOR.  r*s*c <= 65536.
+ */
+ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
+                      const ie_mat *Y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward convolution: input gradient dX (the exact adjoint of ie_conv_fwd
+ * in X, W aligned over output channels when ROW-grouped) and weight gradient
+ * dW (its adjoint in W, per output channel groups when ROW).  dX or dW may be
+ * NULL to skip that output.  dX: TENSOR; dW: TENSOR or ROW.
+ */
+ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
+                      const ie_mat *dY, const ie_mat *dX, const ie_mat *dW,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Integer SGD with momentum and per-group velocity (Figure 1b; Table 5),
+ * in place on W and V:
+ *   V <- R_V(momentum * V + G),  W <- R_W(W - lr * V)
+ * where R_x requantises into x's groups and the weight step uses the stored,
+ * rounded V.  W, V, G: [rows x cols], each TENSOR or ROW.
+ * weight_decay must have mant == 0 in this build.
+ */
+ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G,
+                        ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Wait for `stream`, then copy the workspace's sticky flags to *flags and,
+ * if clear != 0, zero them. */
+ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
+
+/* Human-readable name of a status code. */
+const char *ie_status_str(ie_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IE_H */

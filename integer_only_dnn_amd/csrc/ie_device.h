@@ -1,0 +1,88 @@
+// Device-side integer helpers of the (C, e) arithmetic, for gfx950.
+//
+// Number format ("Memory-Efficient Integer-Only Training of Deep Neural
+// Networks", Abstract, Figure 1): value = C * 2^e, C an int8 mantissa, e an
+// int8 exponent.  Every right shift rounds half to even; a group's exponent is
+// the smallest one that brings every |C| to 127 or less.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ie {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+constexpr int E_MIN = -128;
+constexpr int E_MAX = 127;
+// "No nonzero value": below every reachable exponent, above int overflow.
+constexpr int NEED_NONE = -(1 << 28);
+// Sentinel provisional exponent of an all-zero row tile (fits int16).
+constexpr int P_NONE = -30000;
+
+// Smallest s with |rne(m / 2^s)| <= 127, for m = |a| > 0 (32-bit).
+// With b the bit length of m and t the top 8 bits of m (m normalised), the
+// answer is b - 7, plus one when t == 255 (m / 2^(b-7) >= 127.5 rounds to 128).
+__device__ __forceinline__ int mant_shift32(uint32_t m) {
+    int z = __clz(m);
+    uint32_t top = (m << z) >> 24;
+    return 25 - z + (top == 255u ? 1 : 0);
+}
+
+__device__ __forceinline__ int mant_shift64(uint64_t m) {
+    int z = __clzll(m);
+    uint32_t top = (uint32_t)((m << z) >> 56);
+    return 57 - z + (top == 255u ? 1 : 0);
+}
+
+// Smallest exponent for the exact value a * 2^eps; NEED_NONE when a == 0.
+__device__ __forceinline__ int need32(int a, int eps) {
+    uint32_t m = (uint32_t)(a < 0 ? -a : a);
+    return m ? eps + mant_shift32(m) : NEED_NONE;
+}
+
+__device__ __forceinline__ int need64(long long a, int eps) {
+    uint64_t m = (uint64_t)(a < 0 ? -a : a);
+    return m ? eps + mant_shift64(m) : NEED_NONE;
+}
+
+// a * 2^-s rounded half to even, |a| < 2^30.  s <= 0 is an exact left shift
+// (callers guarantee the result fits); s >= 31 gives 0.
+__device__ __forceinline__ int rne_shift32(int a, int s) {
+    s = s > 31 ? 31 : (s < -31 ? -31 : s);
+    if (s <= 0) return a << (-s);
+    int bit = (a >> s) & 1;
+    return (a + (1 << (s - 1)) - 1 + bit) >> s;
+}
+
+// 64-bit version, |a| < 2^62; s >= 63 gives 0.
+__device__ __forceinline__ long long rne_shift64(long long a, int s) {
+    s = s > 63 ? 63 : (s < -63 ? -63 : s);
+    if (s <= 0) return a << (-s);
+    long long bit = (a >> s) & 1;
+    return (a + (1ll << (s - 1)) - 1 + bit) >> s;
+}
+
+// Round to odd at 2^t: floor(a / 2^t) with the lowest bit forced to 1 when
+// any discarded bit is nonzero.  Followed by a half-to-even rounding at least
+// two bits higher, this gives the same result as rounding a directly.
+__device__ __forceinline__ int rto_shift32(int a, int t) {
+    t = t > 31 ? 31 : (t < -31 ? -31 : t);
+    if (t <= 0) return a << (-t);
+    int q = a >> t;
+    int sticky = (a & (int)((1u << t) - 1u)) != 0;
+    return q | sticky;
+}
+
+__device__ __forceinline__ int clamp_exp_flag(int e, uint32_t *flags) {
+    if (e < E_MIN) e = E_MIN;
+    if (e > E_MAX) {
+        atomicOr(flags, 1u);
+        e = E_MAX;
+    }
+    return e;
+}
+
+}  // namespace ie

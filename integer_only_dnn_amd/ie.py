@@ -1,0 +1,196 @@
+"""ctypes binding of libie.so: argument marshalling only.
+
+Every function here forwards to the C entry point of the same name declared
+in include/ie.h; all arithmetic runs in the library's HIP kernels.  PyTorch
+supplies device memory (int8 CUDA tensors) and the current stream.  The
+library must be built (integer_only_dnn_amd/build.py); nothing here falls
+back to another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_int, c_int8, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+import torch
+
+TENSOR = 0
+ROW = 1
+FLAG_EXP_RANGE = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libie.so")
+
+STATUS = {0: "IE_OK", 1: "IE_ERR_NULL", 2: "IE_ERR_SHAPE", 3: "IE_ERR_GROUP", 4: "IE_ERR_WORKSPACE",
+          5: "IE_ERR_EXP_RANGE", 6: "IE_ERR_UNSUPPORTED", 7: "IE_ERR_HIP"}
+
+
+class IeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class ie_mat(ctypes.Structure):
+    _fields_ = [("mant", c_void_p), ("exp", c_void_p), ("rows", c_int64), ("cols", c_int64),
+                ("group", c_int32)]
+
+
+class ie_conv_desc(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("n", "h", "w", "c", "k", "r", "s", "stride", "pad")]
+
+
+class ie_scalar(ctypes.Structure):
+    _fields_ = [("mant", c_int8), ("exp", c_int8)]
+
+
+EXPORTS = [
+    ("ie_linear_fwd_workspace", c_size_t, [c_int64, c_int64, c_int64]),
+    ("ie_linear_bwd_dx_workspace", c_size_t, [c_int64, c_int64, c_int64]),
+    ("ie_linear_bwd_dw_workspace", c_size_t, [c_int64, c_int64, c_int64]),
+    ("ie_conv_fwd_workspace", c_size_t, [POINTER(ie_conv_desc)]),
+    ("ie_conv_bwd_workspace", c_size_t, [POINTER(ie_conv_desc)]),
+    ("ie_sgd_update_workspace", c_size_t, [c_int64, c_int64]),
+    ("ie_workspace_init", c_int, [c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_fwd", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_bwd_dx", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_bwd_dw", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_conv_fwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_device_status", c_int, [c_void_p, c_void_p, POINTER(c_uint32), c_int]),
+    ("ie_status_str", c_char_p, [c_int]),
+]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libie.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with integer_only_dnn_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in EXPORTS:
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise IeError(code, where)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+class Mat:
+    """A (C, e) matrix in device memory: int8 mantissas [rows, cols],
+    int8 exponents (1 entry for TENSOR, `rows` for ROW)."""
+
+    def __init__(self, mant: torch.Tensor, exp: torch.Tensor, group: int):
+        assert mant.dtype == torch.int8 and exp.dtype == torch.int8
+        assert mant.is_contiguous() and exp.is_contiguous()
+        self.mant = mant
+        self.exp = exp
+        self.group = int(group)
+
+    @staticmethod
+    def empty(rows: int, cols: int, group: int, device="cuda") -> "Mat":
+        m = torch.empty((rows, cols), dtype=torch.int8, device=device)
+        e = torch.empty((rows if group == ROW else 1,), dtype=torch.int8, device=device)
+        return Mat(m, e, group)
+
+    def c(self, rows=None, cols=None) -> ie_mat:
+        """The C descriptor; `rows`/`cols` view an NHWC tensor as [N*H*W x C]."""
+        if rows is None:
+            assert self.mant.dim() == 2
+            rows, cols = self.mant.shape
+        return ie_mat(self.mant.data_ptr(), self.exp.data_ptr(), rows, cols, self.group)
+
+
+class Workspace:
+    """Device scratch for the library, grown on demand; its first 256 bytes
+    hold the sticky status flags (zeroed when the buffer is created)."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if self.buf is None or self.buf.numel() < nbytes:
+            flags = self.status(clear=False) if self.buf is not None else 0
+            self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            _check(lib().ie_workspace_init(self.buf.data_ptr(), self.buf.numel(), _stream(self.device)),
+                   "ie_workspace_init")
+            if flags:
+                raise IeError(5, "workspace flags were set before it grew")
+        return self.buf.data_ptr(), self.buf.numel()
+
+    def status(self, clear: bool = True) -> int:
+        if self.buf is None:
+            return 0
+        f = c_uint32(0)
+        _check(lib().ie_device_status(self.buf.data_ptr(), _stream(self.device), byref(f), int(clear)),
+               "ie_device_status")
+        return f.value
+
+
+def conv_desc(n, h, w, c, k, r, s, stride, pad) -> ie_conv_desc:
+    return ie_conv_desc(n, h, w, c, k, r, s, stride, pad)
+
+
+def ie_linear_fwd(X: Mat, W: Mat, Y: Mat, ws: Workspace) -> None:
+    x, w, y = X.c(), W.c(), Y.c()
+    p, b = ws.get(lib().ie_linear_fwd_workspace(x.rows, w.rows, x.cols))
+    _check(lib().ie_linear_fwd(byref(x), byref(w), byref(y), p, b, _stream(ws.device)), "ie_linear_fwd")
+
+
+def ie_linear_bwd_dx(dY: Mat, W: Mat, dX: Mat, ws: Workspace) -> None:
+    dy, w, dx = dY.c(), W.c(), dX.c()
+    p, b = ws.get(lib().ie_linear_bwd_dx_workspace(dy.rows, dy.cols, w.cols))
+    _check(lib().ie_linear_bwd_dx(byref(dy), byref(w), byref(dx), p, b, _stream(ws.device)), "ie_linear_bwd_dx")
+
+
+def ie_linear_bwd_dw(dY: Mat, X: Mat, dW: Mat, ws: Workspace) -> None:
+    dy, x, dw = dY.c(), X.c(), dW.c()
+    p, b = ws.get(lib().ie_linear_bwd_dw_workspace(dy.rows, dy.cols, x.cols))
+    _check(lib().ie_linear_bwd_dw(byref(dy), byref(x), byref(dw), p, b, _stream(ws.device)), "ie_linear_bwd_dw")
+
+
+def ie_conv_fwd(d: ie_conv_desc, X: Mat, W: Mat, Y: Mat, ws: Workspace) -> None:
+    x = X.c(d.n * d.h * d.w, d.c)
+    w = W.c(d.k, d.r * d.s * d.c)
+    P = (d.h + 2 * d.pad - d.r) // d.stride + 1
+    Q = (d.w + 2 * d.pad - d.s) // d.stride + 1
+    y = Y.c(d.n * P * Q, d.k)
+    p, b = ws.get(lib().ie_conv_fwd_workspace(byref(d)))
+    _check(lib().ie_conv_fwd(byref(d), byref(x), byref(w), byref(y), p, b, _stream(ws.device)), "ie_conv_fwd")
+
+
+def ie_conv_bwd(d: ie_conv_desc, X: Mat, W: Mat, dY: Mat, dX: Mat | None, dW: Mat | None,
+                ws: Workspace) -> None:
+    P = (d.h + 2 * d.pad - d.r) // d.stride + 1
+    Q = (d.w + 2 * d.pad - d.s) // d.stride + 1
+    x = X.c(d.n * d.h * d.w, d.c)
+    w = W.c(d.k, d.r * d.s * d.c)
+    dy = dY.c(d.n * P * Q, d.k)
+    dx = dX.c(d.n * d.h * d.w, d.c) if dX is not None else None
+    dw = dW.c(d.k, d.r * d.s * d.c) if dW is not None else None
+    p, b = ws.get(lib().ie_conv_bwd_workspace(byref(d)))
+    _check(lib().ie_conv_bwd(byref(d), byref(x), byref(w), byref(dy),
+                             byref(dx) if dx is not None else None,
+                             byref(dw) if dw is not None else None, p, b, _stream(ws.device)), "ie_conv_bwd")
+
+
+def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws: Workspace = None) -> None:
+    w, v, g = W.c(), V.c(), G.c()
+    p, b = ws.get(lib().ie_sgd_update_workspace(w.rows, w.cols))
+    _check(lib().ie_sgd_update(byref(w), byref(v), byref(g), ie_scalar(*lr), ie_scalar(*momentum),
+                               ie_scalar(*weight_decay), p, b, _stream(ws.device)), "ie_sgd_update")

@@ -1,0 +1,76 @@
+"""The C ABI library loads, exports every entry point include/ie.h declares,
+and rejects bad arguments on the host before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from integer_only_dnn_amd import ie
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ie.h")).read()
+    return sorted(set(re.findall(r"\b(ie_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    L = ie.lib()
+    names = _declared()
+    assert "ie_linear_fwd" in names and "ie_sgd_update" in names and "ie_conv_bwd" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in ie.EXPORTS) == names
+
+
+def test_status_strings():
+    L = ie.lib()
+    for code, name in ie.STATUS.items():
+        assert L.ie_status_str(code).decode() == name
+
+
+def _mat(rows, cols, group=0, mant=1, exp=1):
+    return ie.ie_mat(mant, exp, rows, cols, group)
+
+
+def test_linear_argument_errors():
+    L = ie.lib()
+    by = ctypes.byref
+    X, W, Y = _mat(4, 8), _mat(3, 8), _mat(4, 3)
+    assert L.ie_linear_fwd(None, by(W), by(Y), 1, 1 << 20, None) == 1
+    assert L.ie_linear_fwd(by(X), by(_mat(3, 9)), by(Y), 1, 1 << 20, None) == 2
+    assert L.ie_linear_fwd(by(X), by(W), by(_mat(4, 3, group=7)), 1, 1 << 20, None) == 3
+    assert L.ie_linear_fwd(by(X), by(W), by(Y), None, 1 << 20, None) == 4
+    assert L.ie_linear_fwd(by(X), by(W), by(Y), 1, 16, None) == 4
+    assert L.ie_linear_fwd(by(_mat(4, 8, mant=0)), by(W), by(Y), 1, 1 << 20, None) == 1
+    assert L.ie_linear_fwd(by(_mat(4, 70000)), by(_mat(3, 70000)), by(Y), 1, 1 << 30, None) == 6
+    assert L.ie_linear_bwd_dx(by(Y), by(W), by(_mat(4, 9)), 1, 1 << 20, None) == 2
+    assert L.ie_linear_bwd_dw(by(Y), by(X), by(_mat(3, 9)), 1, 1 << 20, None) == 2
+
+
+def test_conv_and_update_argument_errors():
+    L = ie.lib()
+    by = ctypes.byref
+    d = ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 1, 1)
+    X, W, Y = _mat(2 * 64, 16), _mat(32, 144), _mat(2 * 64, 32)
+    assert L.ie_conv_fwd(by(d), by(X), by(_mat(32, 145)), by(Y), 1, 1 << 30, None) == 2
+    assert L.ie_conv_fwd(by(ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 0, 1)), by(X), by(W), by(Y), 1, 1 << 30, None) == 2
+    assert L.ie_conv_fwd(by(d), by(_mat(2 * 64, 16, group=1)), by(W), by(Y), 1, 1 << 30, None) == 6
+    assert L.ie_conv_bwd(by(d), by(X), by(W), by(Y), by(_mat(5, 16)), None, 1, 1 << 30, None) == 2
+    S = ie.ie_scalar
+    assert L.ie_sgd_update(by(W), by(_mat(32, 144)), by(_mat(31, 144)), S(1, -7), S(7, -3), S(0, 0),
+                           1, 4096, None) == 2
+    assert L.ie_sgd_update(by(W), by(W), by(W), S(1, -7), S(7, -3), S(1, -13), 1, 4096, None) == 6
+
+
+def test_workspace_sizes_grow_with_shape():
+    L = ie.lib()
+    a = L.ie_linear_fwd_workspace(64, 128, 256)
+    b = L.ie_linear_fwd_workspace(6400, 1280, 256)
+    assert 256 <= a < b
+    assert L.ie_linear_fwd_workspace(-1, 1, 1) == 0
+    d = ie.conv_desc(128, 32, 32, 64, 64, 3, 3, 1, 1)
+    assert L.ie_conv_bwd_workspace(ctypes.byref(d)) > L.ie_conv_fwd_workspace(ctypes.byref(d)) > 0
