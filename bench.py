@@ -1,0 +1,378 @@
+"""Benchmark of the integer-only (C, e) layer step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for every layer, the forward product, the input gradient, the weight
+gradient and the integer SGD-momentum update of that layer's weights.
+
+Default workload: the 3x3 convolutions of a ResNet-18 on 32x32x3 inputs at
+batch 128 (NHWC, per-tensor activation exponents, per-output-channel weight
+gradient / velocity groups).  Other workloads (--workload) are the ViT-B and
+ViT-Ti block linears, the ResNet-50 bottleneck convolutions and the single
+small linear layer.
+
+Output: one JSON line (rank 0).  `value` is the step's algorithmic int8 ops
+(2*M*N*K per product; the input gradient counted at the forward MAC count)
+divided by the measured step time.  `roofline` describes the kernel that
+takes the most time, from HIP events the library records around every
+kernel launch in the timed region; `cpu_baseline` times the oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+METRIC = "int8 layer fwd+bwd TOPS & % INT8 MFMA peak; SGD-update GB/s & % HBM"
+
+KIND_NAMES = {
+    1000: "gemm_K_K_direct", 1100: "gemm_K_K_rto", 1020: "gemm_im2col_direct", 1120: "gemm_im2col_rto",
+    1030: "gemm_dgrad_direct", 1130: "gemm_dgrad_rto", 1211: "gemm_T_T_partial", 1214: "gemm_T_im2colT_partial",
+    2000: "sgd_pass0", 2001: "sgd_pass1", 2002: "sgd_pass2", 3000: "rto_finalize", 3100: "dw_finalize",
+    3200: "align",
+}
+# Kernel symbols as rocprofv3 reports them (template <loader A, loader B, epilogue>).
+KIND_SYMBOL = {
+    1000: "gemm_i8_kernel<0, 0, 0>", 1100: "gemm_i8_kernel<0, 0, 1>", 1020: "gemm_i8_kernel<2, 0, 0>",
+    1120: "gemm_i8_kernel<2, 0, 1>", 1030: "gemm_i8_kernel<3, 0, 0>", 1130: "gemm_i8_kernel<3, 0, 1>",
+    1211: "gemm_i8_kernel<1, 1, 2>", 1214: "gemm_i8_kernel<1, 4, 2>", 2001: "sgd_rows_kernel",
+    3000: "rto_finalize_kernel", 3100: "dw_finalize_kernel", 3200: "align_*_kernel",
+}
+
+
+def is_gemm(kind: int) -> bool:
+    return 1000 <= kind < 2000
+
+
+# ---------------------------------------------------------------------------
+# Workload construction (device side)
+# ---------------------------------------------------------------------------
+
+class Call:
+    """One library call of the step: a closure plus what it computes."""
+
+    def __init__(self, label, fn, ops=0.0, bytes_=0.0):
+        self.label = label
+        self.fn = fn
+        self.ops = ops          # algorithmic int8 ops of its contraction
+        self.bytes = bytes_     # algorithmic HBM bytes (update)
+        self.kinds = None
+
+
+def _dev(torch, ie, code, rows=None):
+    m = np.ascontiguousarray(code.mant)
+    if m.ndim != 2:
+        m = m.reshape(rows if rows is not None else m.shape[0], -1)
+    return ie.Mat(torch.from_numpy(m).cuda(), torch.from_numpy(np.ascontiguousarray(code.exp)).cuda(), code.group)
+
+
+def build_resnet18(torch, ie, ws, batch):
+    calls, meta = [], {"layers": [], "params": 0}
+    layers = wl.resnet18_cifar_layers(batch)
+    seed = 2000
+    for L in layers:
+        for inst in range(L.count):
+            seed += 1
+            inp = wl.resnet18_conv_inputs(L, seed)
+            d = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+            M, N, K = L.gemm_mnk()
+            X = _dev(torch, ie, inp.X, rows=L.n * L.h * L.w)
+            W = _dev(torch, ie, inp.W)
+            dY = _dev(torch, ie, inp.dY, rows=M)
+            Y = ie.Mat.empty(M, N, wl.TENSOR)
+            dX = None if L.first else ie.Mat.empty(L.n * L.h * L.w, L.c, wl.TENSOR)
+            dW = ie.Mat.empty(N, K, wl.ROW)
+            upd = wl.update_inputs(N, K, seed + 50000, w_group=wl.TENSOR)
+            V = _dev(torch, ie, upd.V)
+            ops = 2.0 * M * N * K
+            name = f"{L.name}#{inst}"
+            calls.append(Call(f"{name}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops))
+            bwd_ops = ops * (1 if L.first else 2)
+            calls.append(Call(f"{name}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
+                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), bwd_ops))
+            params = N * K
+            # read W, V, G and write W, V (1 byte each) + group exponents
+            ubytes = 5.0 * params + 3.0 * N + 2.0
+            calls.append(Call(f"{name}:update", lambda W=W, V=V, dW=dW:
+                              ie.ie_sgd_update(W, V, dW, wl.LR, wl.MOMENTUM, ws=ws), 0.0, ubytes))
+            meta["params"] += params
+        meta["layers"].append({"name": L.name, "count": L.count, "gemm_mnk": list(L.gemm_mnk())})
+    return calls, meta
+
+
+def build_resnet50(torch, ie, ws, batch):
+    calls, meta = [], {"layers": [], "params": 0}
+    seed = 4000
+    for L in wl.resnet50_layers(batch):
+        seed += 1
+        inp = wl.resnet50_conv_inputs(L, seed)
+        d = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+        M, N, K = L.gemm_mnk()
+        X = _dev(torch, ie, inp.X, rows=L.n * L.h * L.w)
+        W = _dev(torch, ie, inp.W)
+        dY = _dev(torch, ie, inp.dY, rows=M)
+        Y = ie.Mat.empty(M, N, wl.TENSOR)
+        dX = ie.Mat.empty(L.n * L.h * L.w, L.c, wl.TENSOR)
+        dW = ie.Mat.empty(N, K, wl.ROW)
+        ops = 2.0 * M * N * K
+        for inst in range(L.count):   # identical shapes: reuse the tensors
+            calls.append(Call(f"{L.name}#{inst}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops))
+            calls.append(Call(f"{L.name}#{inst}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
+                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), 2 * ops))
+        meta["layers"].append({"name": L.name, "count": L.count, "gemm_mnk": [M, N, K]})
+    return calls, meta
+
+
+def build_vit(torch, ie, ws, layers, with_update):
+    calls, meta = [], {"layers": [], "params": 0}
+    seed = 5000
+    for L in layers:
+        seed += 1
+        inp = wl.vit_linear_inputs(L, seed)
+        X, W, dY = _dev(torch, ie, inp.X), _dev(torch, ie, inp.W), _dev(torch, ie, inp.dY)
+        Y = ie.Mat.empty(L.m, L.n, inp.y_group)
+        dX = ie.Mat.empty(L.m, L.k, inp.dx_group)
+        dW = ie.Mat.empty(L.n, L.k, inp.dw_group)
+        ops = 2.0 * L.m * L.n * L.k
+        calls.append(Call(f"{L.name}:fwd", lambda X=X, W=W, Y=Y: ie.ie_linear_fwd(X, W, Y, ws), ops))
+        calls.append(Call(f"{L.name}:dx", lambda dY=dY, W=W, dX=dX: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops))
+        calls.append(Call(f"{L.name}:dw", lambda dY=dY, X=X, dW=dW: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops))
+        meta["layers"].append({"name": L.name, "gemm_mnk": [L.m, L.n, L.k]})
+    if with_update:
+        for i, (rows, cols) in enumerate(wl.vit_b_param_arenas()):
+            upd = wl.update_inputs(rows, cols, 6000 + i)
+            W, V, G = _dev(torch, ie, upd.W), _dev(torch, ie, upd.V), _dev(torch, ie, upd.G)
+            ubytes = 5.0 * rows * cols + 5.0 * rows
+            calls.append(Call(f"update_{cols}", lambda W=W, V=V, G=G:
+                              ie.ie_sgd_update(W, V, G, wl.LR, wl.MOMENTUM, ws=ws), 0.0, ubytes))
+            meta["params"] += rows * cols
+    return calls, meta
+
+
+def build_linear_small(torch, ie, ws):
+    inp = wl.linear_small_inputs(seed=1)
+    X, W, dY = _dev(torch, ie, inp.X), _dev(torch, ie, inp.W), _dev(torch, ie, inp.dY)
+    Y, dX, dW = ie.Mat.empty(64, 128, 0), ie.Mat.empty(64, 256, 0), ie.Mat.empty(128, 256, 1)
+    import torch as t
+    V = ie.Mat(t.zeros((128, 256), dtype=t.int8, device="cuda"), t.full((128,), -128, dtype=t.int8, device="cuda"), 1)
+    ops = 2.0 * 64 * 128 * 256
+    calls = [Call("fwd", lambda: ie.ie_linear_fwd(X, W, Y, ws), ops),
+             Call("dx", lambda: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops),
+             Call("dw", lambda: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops),
+             Call("update", lambda: ie.ie_sgd_update(W, V, dW, wl.LR, wl.MOMENTUM, ws=ws), 0.0,
+                  5.0 * 128 * 256 + 3 * 128 + 2)]
+    return calls, {"layers": [{"name": "linear", "gemm_mnk": [64, 128, 256]}], "params": 128 * 256}
+
+
+WORKLOADS = {
+    "resnet18": ("resnet18_cifar_conv3x3_batch128", "ResNet-18 3x3 convolutions on 32x32x3 inputs, batch 128"),
+    "vitb": ("vit_b_block_linears_128x197_plus_update_85M", "ViT-B block linears (128 x 197 tokens) + update of 84.9M params"),
+    "vitti": ("vit_ti_block_linears_256x197", "ViT-Ti block linears (256 x 197 tokens)"),
+    "resnet50": ("resnet50_bottleneck_convs_batch128", "ResNet-50 bottleneck convolutions on 224x224x3 inputs, batch 128"),
+    "linear_small": ("linear_64x256x128", "single linear layer 64x256 -> 128"),
+}
+
+
+def build_workload(name, torch, ie, ws):
+    if name == "resnet18":
+        return build_resnet18(torch, ie, ws, 128)
+    if name == "resnet50":
+        return build_resnet50(torch, ie, ws, 128)
+    if name == "vitb":
+        return build_vit(torch, ie, ws, wl.vit_b_linears(128), True)
+    if name == "vitti":
+        return build_vit(torch, ie, ws, wl.vit_ti_linears(256), False)
+    if name == "linear_small":
+        return build_linear_small(torch, ie, ws)
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(name: str):
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    ops = 0.0
+    if name in ("resnet18", "resnet50"):
+        batch = 8
+        layers = wl.resnet18_cifar_layers(batch) if name == "resnet18" else wl.resnet50_layers(2)
+        sample = (f"every layer once at batch {batch if name == 'resnet18' else 2} "
+                  f"(fwd, input and weight gradients, update)")
+        for i, L in enumerate(layers):
+            inp = (wl.resnet18_conv_inputs if name == "resnet18" else wl.resnet50_conv_inputs)(L, 9000 + i)
+            d = o.ConvShape(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+            X = o.QT(inp.X.mant, inp.X.exp, inp.X.group)
+            W = o.QT(inp.W.mant, inp.W.exp, inp.W.group)
+            dY = o.QT(inp.dY.mant, inp.dY.exp, inp.dY.group)
+            M, N, K = L.gemm_mnk()
+            o.conv_fwd(d, X, W, o.TENSOR)
+            if not L.first:
+                o.conv_dgrad(d, dY, W, o.TENSOR)
+            dW = o.conv_wgrad(d, dY, X, o.ROW)
+            upd = wl.update_inputs(N, K, 9500 + i, w_group=W.group)
+            o.sgd_update(W, o.QT(upd.V.mant, upd.V.exp, upd.V.group), dW, o.Scalar(*wl.LR), o.Scalar(*wl.MOMENTUM))
+            ops += 2.0 * M * N * K * (2 if L.first else 3)
+    else:
+        layers = (wl.vit_b_linears(128) if name == "vitb" else wl.vit_ti_linears(256)) \
+            if name in ("vitb", "vitti") else [wl.LinearLayer("linear", 64, 128, 256)]
+        rows = 1024 if name in ("vitb", "vitti") else 64
+        sample = f"every linear at {rows} tokens (fwd, dX, dW)"
+        for i, L in enumerate(layers):
+            inp = wl.vit_linear_inputs(L, 9000 + i, m_rows=rows)
+            X = o.QT(inp.X.mant, inp.X.exp, inp.X.group)
+            W = o.QT(inp.W.mant, inp.W.exp, inp.W.group)
+            dY = o.QT(inp.dY.mant, inp.dY.exp, inp.dY.group)
+            o.linear_fwd(X, W, o.ROW)
+            o.linear_bwd_dx(dY, W, o.ROW)
+            o.linear_bwd_dw(dY, X, o.ROW)
+            ops += 3 * 2.0 * rows * L.n * L.k
+    dt = time.perf_counter() - t0
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "sample_gop": round(ops / 1e9, 3)}
+
+
+# ---------------------------------------------------------------------------
+# Main
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="resnet18", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true", help="also print the per-kernel breakdown")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from integer_only_dnn_amd import ie
+    ie.lib()
+    torch.cuda.set_device(0)
+    ws = ie.Workspace("cuda")
+    wl_id, wl_desc = WORKLOADS[args.workload]
+    calls, meta = build_workload(args.workload, torch, ie, ws)
+    torch.cuda.synchronize()
+
+    # Calibration step (untimed): learn each call's kernel sequence.
+    ie.ie_profile_enable(True)
+    for c in calls:
+        c.fn()
+        torch.cuda.synchronize()
+        c.kinds = [k for _, k in ie.ie_profile_read()]
+    ie.ie_profile_enable(False)
+    for _ in range(args.warmup):
+        for c in calls:
+            c.fn()
+    torch.cuda.synchronize()
+    if ws.status() != 0:
+        raise SystemExit("exponent range flag raised during warmup")
+
+    # Timed region: K steps, library events around every kernel.
+    ie.ie_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in calls:
+            c.fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = ie.ie_profile_read()
+    ie.ie_profile_enable(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_step = sum(len(c.kinds) for c in calls)
+    assert len(recs) == per_step * args.steps, (len(recs), per_step, args.steps)
+    agg = {}
+    pos = 0
+    for _ in range(args.steps):
+        for c in calls:
+            n_gemm = sum(1 for k in c.kinds if is_gemm(k))
+            for k in c.kinds:
+                ms, kind = recs[pos]
+                assert kind == k
+                pos += 1
+                a = agg.setdefault(kind, {"ms": 0.0, "launches": 0, "ops": 0.0, "bytes": 0.0})
+                a["ms"] += ms
+                a["launches"] += 1
+                if is_gemm(kind):
+                    a["ops"] += c.ops / n_gemm
+                elif 2000 <= kind < 3000 and c.bytes:
+                    n_upd = sum(1 for kk in c.kinds if 2000 <= kk < 3000)
+                    a["bytes"] += c.bytes / n_upd
+
+    step_ops = sum(c.ops for c in calls)
+    value = step_ops / (ms_per_step * 1e-3) / 1e12
+    dom = max(agg, key=lambda k: agg[k]["ms"])
+    A = agg[dom]
+    if is_gemm(dom):
+        achieved = A["ops"] / (A["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": None}
+    else:
+        achieved = A["bytes"] / (A["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = KIND_SYMBOL.get(dom, str(dom))
+    roof["avg_launch_us"] = round(A["ms"] * 1e3 / A["launches"], 2)
+
+    upd_ms = sum(v["ms"] for k, v in agg.items() if 2000 <= k < 3000) / args.steps
+    upd_bytes = sum(c.bytes for c in calls)
+    gemm_ms = sum(v["ms"] for k, v in agg.items() if is_gemm(k)) / args.steps
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl_id, "description": wl_desc, "step_gop": round(step_ops / 1e9, 3),
+                   "params_updated": meta["params"]},
+        "frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "contraction_tops": round(step_ops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
+        "update": ({"gbps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(upd_bytes / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "ms_per_step": round(upd_ms, 4), "algorithmic_bytes": upd_bytes} if upd_ms else None),
+        "roofline": roof,
+    }
+    if args.kernels:
+        out["kernels"] = {KIND_NAMES.get(k, str(k)): {"ms_per_step": round(v["ms"] / args.steps, 4),
+                                                      "launches_per_step": v["launches"] // args.steps,
+                                                      "avg_us": round(v["ms"] * 1e3 / v["launches"], 2)}
+                          for k, v in sorted(agg.items())}
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

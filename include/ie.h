@@ -22,7 +22,8 @@
  *
  * Memory and execution:
  *   - every mantissa/exponent/workspace pointer is a DEVICE pointer owned by
- *     the caller; the library allocates nothing and keeps no global state;
+ *     the caller; the library allocates no device memory and keeps no global
+ *     state apart from the optional kernel timing below;
  *   - matrices are row-major and contiguous; activations of convolutions are
  *     NHWC, viewed as a matrix [N*H*W x C]; weights are [K x R*S*C] (KRSC);
  *   - outputs are fully overwritten, mantissas and exponents; outputs must not
@@ -156,6 +157,20 @@ ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G,
 /* Wait for `stream`, then copy the workspace's sticky flags to *flags and,
  * if clear != 0, zero them. */
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
+
+/*
+ * Kernel timing, for diagnostics and benchmarks.  While enabled, the launch
+ * of every contraction, finalize and update kernel is bracketed by two HIP
+ * events recorded on the launch's stream.  ie_profile_read waits for the
+ * recorded events, writes up to `max` records in launch order (elapsed
+ * milliseconds and a kernel-kind code: 1000 + 100*epilogue + 10*loader_A +
+ * loader_B for contractions, 2000 + pass for the update, 3000 round-to-odd
+ * finalize, 3100 weight-gradient finalize, 3200 alignment) and returns how
+ * many were recorded since the last read; the records are then cleared.
+ * This is the library's only process-wide state; it is not thread-safe.
+ */
+ie_status ie_profile_enable(int on);
+int ie_profile_read(float *ms, int *kind, int max);
 
 /* Human-readable name of a status code. */
 const char *ie_status_str(ie_status st);

@@ -472,6 +472,13 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {
     return IE_OK;
 }
 
+ie_status ie_profile_enable(int on) {
+    prof_enable(on);
+    return IE_OK;
+}
+
+int ie_profile_read(float *ms, int *kind, int max) { return prof_read(ms, kind, max); }
+
 const char *ie_status_str(ie_status s) {
     switch (s) {
         case IE_OK: return "IE_OK";

@@ -6,10 +6,79 @@
 // Networks", Table 6: products over operands whose exponents vary along the
 // summed axis) re-expresses every row at the largest row exponent e*:
 // C' = C / 2^(e* - e_row), rounded half to even.
+#include <vector>
+
 #include "ie_device.h"
 #include "ie_internal.h"
 
 namespace ie {
+
+// ---------------------------------------------------------------------------
+// Optional kernel timing
+// ---------------------------------------------------------------------------
+
+namespace {
+struct ProfRec {
+    hipEvent_t start, stop;
+    int kind;
+};
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_pool;
+std::vector<ProfRec> g_recs;
+hipEvent_t g_pending = nullptr;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+void prof_begin(hipStream_t st) {
+    if (!g_prof_on) return;
+    g_pending = take_event();
+    if (g_pending) (void)hipEventRecord(g_pending, st);
+}
+
+void prof_end(hipStream_t st, int kind) {
+    if (!g_prof_on || !g_pending) return;
+    hipEvent_t e = take_event();
+    if (!e) return;
+    (void)hipEventRecord(e, st);
+    g_recs.push_back({g_pending, e, kind});
+    g_pending = nullptr;
+}
+
+void prof_enable(int on) {
+    g_prof_on = on != 0;
+    for (auto &r : g_recs) {
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
+    }
+    g_recs.clear();
+}
+
+int prof_read(float *ms, int *kind, int max) {
+    int n = (int)g_recs.size();
+    for (int i = 0; i < n; ++i) {
+        ProfRec &r = g_recs[i];
+        float t = 0.f;
+        if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&t, r.start, r.stop);
+        if (i < max) {
+            if (ms) ms[i] = t;
+            if (kind) kind[i] = r.kind;
+        }
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
+    }
+    g_recs.clear();
+    return n;
+}
 
 __global__ void fill_i32_kernel(int *p, long long n, int v) {
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
@@ -85,8 +154,10 @@ hipError_t launch_align_rows(const int8_t *in, const int8_t *e, const int *estar
                              long long cols, int8_t *out, hipStream_t st) {
     long long n = rows * cols;
     if (n <= 0) return hipSuccess;
+    prof_begin(st);
     hipLaunchKernelGGL(align_rows_kernel, dim3(blocks_for(n, 256, 16384)), dim3(256), 0, st, in, e,
                        estar, rows, cols, out);
+    prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
 
@@ -119,7 +190,9 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, c
                                   int B, int C, int8_t *out, hipStream_t st) {
     if (A <= 0 || B <= 0 || C <= 0) return hipSuccess;
     dim3 grid((C + 63) / 64, (A + 63) / 64, B);
+    prof_begin(st);
     hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, estar, A, B, C, out);
+    prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
 
@@ -146,8 +219,10 @@ hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int
                                hipStream_t st) {
     if (M <= 0) return hipSuccess;
     int blocks = M < 16384 ? M : 16384;
+    prof_begin(st);
     hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, gneed, M, N, n_ct,
                        row_group, out, out_exp, flags);
+    prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
 
@@ -195,8 +270,10 @@ hipError_t launch_dw_finalize(const int *partial, int splits, long long split_st
     if (N <= 0) return hipSuccess;
     int blocks = N < 8192 ? N : 8192;
     if (row_group) {
+        prof_begin(st);
         hipLaunchKernelGGL(dw_finalize_kernel, dim3(blocks), dim3(256), 0, st, partial, splits, split_stride,
                            N, K, eps_a, eps_b, 0, gneed, out, out_exp, flags);
+        prof_end(st, PROF_DW_FINALIZE);
         return hipGetLastError();
     }
     hipError_t err = launch_fill_i32(gneed, 1, NEED_NONE, st);

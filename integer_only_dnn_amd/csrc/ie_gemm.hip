@@ -556,8 +556,10 @@ static hipError_t launch_t(const Operand &A, const Operand &B, int M, int N, int
                            int k_chunk, const Epi &ep, hipStream_t st) {
     int TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
     dim3 grid(TM * TN, 1, splits);
+    prof_begin(st);
     hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, EPI>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
                        k_chunk, TM, ep);
+    prof_end(st, 1000 + 100 * EPI + 10 * KA + KB);
     return hipGetLastError();
 }
 

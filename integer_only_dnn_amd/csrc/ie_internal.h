@@ -63,6 +63,15 @@ struct Operand {
 hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K,
                        int splits, int k_chunk, int epi, const Epi &ep, hipStream_t st);
 
+// Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
+void prof_begin(hipStream_t st);
+void prof_end(hipStream_t st, int kind);
+void prof_enable(int on);
+int prof_read(float *ms, int *kind, int max);
+constexpr int PROF_RTO_FINALIZE = 3000;
+constexpr int PROF_DW_FINALIZE = 3100;
+constexpr int PROF_ALIGN = 3200;
+
 // Auxiliary kernels (ie_aux.hip).
 hipError_t launch_fill_i32(int *p, long long n, int v, hipStream_t st);
 hipError_t launch_fill_i8(int8_t *p, long long n, int v, hipStream_t st);

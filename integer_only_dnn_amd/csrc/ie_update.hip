@@ -204,13 +204,19 @@ static hipError_t run_passes(const UpdateArgs &a, int vec, const int *old_ev, co
     if (blocks < 1) blocks = 1;
     hipError_t err;
     if (a.v_row == 0) {
+        prof_begin(st);
         hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 0, vec, old_ev, old_ew);
+        prof_end(st, 2000 + 0);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    prof_begin(st);
     hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 1, vec, old_ev, old_ew);
+    prof_end(st, 2000 + 1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.w_row == 0) {
+        prof_begin(st);
         hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 2, vec, old_ev, old_ew);
+        prof_end(st, 2000 + 2);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;

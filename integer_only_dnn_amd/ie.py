@@ -60,6 +60,8 @@ EXPORTS = [
     ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_device_status", c_int, [c_void_p, c_void_p, POINTER(c_uint32), c_int]),
+    ("ie_profile_enable", c_int, [c_int]),
+    ("ie_profile_read", c_int, [POINTER(ctypes.c_float), POINTER(c_int), c_int]),
     ("ie_status_str", c_char_p, [c_int]),
 ]
 
@@ -194,3 +196,15 @@ def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws:
     p, b = ws.get(lib().ie_sgd_update_workspace(w.rows, w.cols))
     _check(lib().ie_sgd_update(byref(w), byref(v), byref(g), ie_scalar(*lr), ie_scalar(*momentum),
                                ie_scalar(*weight_decay), p, b, _stream(ws.device)), "ie_sgd_update")
+
+
+def ie_profile_enable(on: bool = True) -> None:
+    _check(lib().ie_profile_enable(int(on)), "ie_profile_enable")
+
+
+def ie_profile_read(max_records: int = 1 << 16):
+    """[(milliseconds, kind)] of the kernels launched since the last read."""
+    ms = (ctypes.c_float * max_records)()
+    kind = (c_int * max_records)()
+    n = lib().ie_profile_read(ms, kind, max_records)
+    return [(ms[i], kind[i]) for i in range(min(n, max_records))]
