@@ -38,23 +38,33 @@ PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 METRIC = "int8 layer fwd+bwd TOPS & % INT8 MFMA peak; SGD-update GB/s & % HBM"
 
-KIND_NAMES = {
-    1000: "gemm_K_K_direct", 1100: "gemm_K_K_rto", 1020: "gemm_im2col_direct", 1120: "gemm_im2col_rto",
-    1030: "gemm_dgrad_direct", 1130: "gemm_dgrad_rto", 1211: "gemm_T_T_partial", 1214: "gemm_T_im2colT_partial",
-    2000: "sgd_pass0", 2001: "sgd_pass1", 2002: "sgd_pass2", 3000: "rto_finalize", 3100: "dw_finalize",
-    3200: "align",
-}
-# Kernel symbols as rocprofv3 reports them (template <loader A, loader B, epilogue>).
-KIND_SYMBOL = {
-    1000: "gemm_i8_kernel<0, 0, 0>", 1100: "gemm_i8_kernel<0, 0, 1>", 1020: "gemm_i8_kernel<2, 0, 0>",
-    1120: "gemm_i8_kernel<2, 0, 1>", 1030: "gemm_i8_kernel<3, 0, 0>", 1130: "gemm_i8_kernel<3, 0, 1>",
-    1211: "gemm_i8_kernel<1, 1, 2>", 1214: "gemm_i8_kernel<1, 4, 2>", 2001: "sgd_rows_kernel",
-    3000: "rto_finalize_kernel", 3100: "dw_finalize_kernel", 3200: "align_*_kernel",
-}
+LOADER = {0: "K", 1: "T", 2: "im2col", 3: "dgrad", 4: "im2colT"}
+EPI = {0: "direct", 1: "rto", 2: "partial"}
+OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_kernel"),
+         2002: ("sgd_pass2", "sgd_rows_kernel"), 3000: ("rto_finalize", "rto_finalize_kernel"),
+         3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
+         3200: ("pad_align", "pad_rows_kernel / align_transpose_kernel")}
 
 
 def is_gemm(kind: int) -> bool:
-    return 1000 <= kind < 2000
+    return kind >= 10000 and 1000 <= kind % 10000 < 2000
+
+
+def kind_name(kind: int) -> str:
+    if not is_gemm(kind):
+        return OTHER.get(kind, (str(kind), ""))[0]
+    mi, ni = (kind // 10000) // 10, (kind // 10000) % 10
+    k = kind % 10000 - 1000
+    return f"gemm_{LOADER[(k % 100) // 10]}_{LOADER[k % 10]}_{EPI[k // 100]}_{64 * mi}x{64 * ni}"
+
+
+def kind_symbol(kind: int) -> str:
+    """The kernel's name as rocprofv3 reports it."""
+    if not is_gemm(kind):
+        return OTHER.get(kind, ("", str(kind)))[1]
+    mi, ni = (kind // 10000) // 10, (kind // 10000) % 10
+    k = kind % 10000 - 1000
+    return f"gemm_i8_kernel<{(k % 100) // 10}, {k % 10}, {mi}, {ni}, {'true' if k // 100 == 2 else 'false'}>"
 
 
 # ---------------------------------------------------------------------------
@@ -337,7 +347,7 @@ def main():
         achieved = A["bytes"] / (A["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = KIND_SYMBOL.get(dom, str(dom))
+    roof["kernel"] = kind_symbol(dom)
     roof["avg_launch_us"] = round(A["ms"] * 1e3 / A["launches"], 2)
 
     upd_ms = sum(v["ms"] for k, v in agg.items() if 2000 <= k < 3000) / args.steps
@@ -366,7 +376,7 @@ def main():
         "roofline": roof,
     }
     if args.kernels:
-        out["kernels"] = {KIND_NAMES.get(k, str(k)): {"ms_per_step": round(v["ms"] / args.steps, 4),
+        out["kernels"] = {kind_name(k): {"ms_per_step": round(v["ms"] / args.steps, 4),
                                                       "launches_per_step": v["launches"] // args.steps,
                                                       "avg_us": round(v["ms"] * 1e3 / v["launches"], 2)}
                           for k, v in sorted(agg.items())}

@@ -163,9 +163,11 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * of every contraction, finalize and update kernel is bracketed by two HIP
  * events recorded on the launch's stream.  ie_profile_read waits for the
  * recorded events, writes up to `max` records in launch order (elapsed
- * milliseconds and a kernel-kind code: 1000 + 100*epilogue + 10*loader_A +
- * loader_B for contractions, 2000 + pass for the update, 3000 round-to-odd
- * finalize, 3100 weight-gradient finalize, 3200 alignment) and returns how
+ * milliseconds and a kernel-kind code: 10000*(10*mi + ni) + 1000 +
+ * 100*epilogue + 10*loader_A + loader_B for contractions with a
+ * (64 mi) x (64 ni) tile, 2000 + pass for the update, 3000 round-to-odd
+ * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
+ * alignment copies) and returns how
  * many were recorded since the last read; the records are then cleared.
  * This is the library's only process-wide state; it is not thread-safe.
  */

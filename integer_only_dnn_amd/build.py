@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libie.so")
-SOURCES = ["ie_api.hip", "ie_gemm.hip", "ie_aux.hip", "ie_update.hip"]
+SOURCES = ["ie_api.hip", "ie_aux.hip", "ie_update.hip", "ie_gemm_kk.hip", "ie_gemm_im2col.hip",
+           "ie_gemm_dgrad.hip", "ie_gemm_wgrad.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -1,5 +1,7 @@
 // C ABI of the (C, e) layer-step library: argument checks, workspace layout
 // and the launch sequence of every entry point.  See include/ie.h.
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/ie.h"
@@ -59,110 +61,253 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Workspace of a product whose int8 output [M x N] may need the two-pass
-// (round-to-odd) epilogue.
+// ---------------------------------------------------------------------------
+// Planning: tile shape, epilogue and contraction split of a product.
+// ---------------------------------------------------------------------------
+
+// Tiles instantiated per loader family (must match the ie_gemm_*.hip lists).
+const Tile FUSED_KK[] = {{2, 2}, {4, 1}, {1, 4}, {2, 1}, {1, 2}, {1, 1}};
+const Tile PARTIAL_KK[] = {{2, 2}, {4, 1}, {1, 4}, {2, 1}, {1, 2}, {1, 1}};
+const Tile FUSED_CONV[] = {{2, 2}, {4, 1}, {2, 1}, {1, 1}};
+const Tile PARTIAL_CONV[] = {{2, 2}, {4, 1}, {2, 1}, {1, 1}};
+const Tile WGRAD_TILES[] = {{2, 2}, {1, 4}, {4, 1}, {1, 1}};
+
+constexpr double CU_OPS = 1.9e15 / NCU;   // sustained int8 MFMA ops/s per CU (staged loop)
+constexpr double HBM_BPS = 4.0e12;         // sustained HBM bytes/s
+constexpr double LAUNCH_S = 4e-6;          // cost of one extra kernel launch
+
+// Relative MFMA efficiency of a wave tile (LDS bytes per MFMA grow as it shrinks).
+double tile_eff(Tile t) {
+    const int a = t.mi * t.ni;
+    return a >= 4 ? (t.mi == t.ni ? 1.0 : 0.85) : a >= 2 ? 0.6 : 0.4;
+}
+
+double tile_time(Tile t, long long M, long long N, long long Kc, int splits) {
+    long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn()) * splits;
+    long long rounds = (tiles + NCU - 1) / NCU;
+    return rounds * (2.0 * t.bm() * t.bn() * (double)(Kc > 0 ? Kc : 1) / tile_eff(t)) / CU_OPS;
+}
+
+enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2 };
+
+struct Plan {
+    Tile t;
+    int mode;
+    int splits;
+    int k_chunk;
+};
+
+int chunk_for(long long K, int splits) {
+    long long c = (K + splits - 1) / splits;
+    c = (c + BK - 1) / BK * BK;
+    return (int)(c > 0 ? c : BK);
+}
+
+// Tuning override: IE_TILE="mi,ni[,mode[,splits]]" forces the plan of every
+// product (mode 0 direct, 1 round-to-odd, 2 split).  Unset in normal use.
+bool forced_plan(long long K, Plan &pl) {
+    const char *v = getenv("IE_TILE");
+    if (!v || !*v) return false;
+    int mi = 0, ni = 0, mode = -1, sp = 1;
+    if (sscanf(v, "%d,%d,%d,%d", &mi, &ni, &mode, &sp) < 2) return false;
+    pl.t = Tile{mi, ni};
+    pl.mode = mode < 0 ? PLAN_RTO : mode;
+    pl.splits = sp < 1 ? 1 : sp;
+    pl.k_chunk = chunk_for(K, pl.splits);
+    pl.splits = (int)((K + pl.k_chunk - 1) / pl.k_chunk);
+    if (pl.splits < 1) pl.splits = 1;
+    return true;
+}
+
+// family: 0 = dense K-major, 1 = convolution (im2col / dgrad)
+Plan plan_product(long long M, long long N, long long K, int row_group, int family) {
+    {
+        Plan f;
+        if (forced_plan(K, f)) return f;
+    }
+    const Tile *fused = family == 0 ? FUSED_KK : FUSED_CONV;
+    const int nf = family == 0 ? (int)(sizeof FUSED_KK / sizeof(Tile)) : (int)(sizeof FUSED_CONV / sizeof(Tile));
+    const Tile *part = family == 0 ? PARTIAL_KK : PARTIAL_CONV;
+    const int np = family == 0 ? (int)(sizeof PARTIAL_KK / sizeof(Tile)) : (int)(sizeof PARTIAL_CONV / sizeof(Tile));
+    Plan best{fused[0], PLAN_RTO, 1, chunk_for(K, 1)};
+    double bt = 1e30;
+    for (int i = 0; i < nf; ++i) {
+        Tile t = fused[i];
+        long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+        bool direct = row_group ? N <= t.bn() : tiles == 1;
+        double tt = tile_time(t, M, N, K, 1);
+        if (!direct) tt += (double)M * N * 5 / HBM_BPS + 2 * LAUNCH_S;
+        if (tt < bt) {
+            bt = tt;
+            best = Plan{t, direct ? PLAN_DIRECT : PLAN_RTO, 1, chunk_for(K, 1)};
+        }
+    }
+    // split contraction for small outputs with long contractions
+    if (K >= 4 * BK && M * N <= (4ll << 20)) {
+        for (int i = 0; i < np; ++i) {
+            Tile t = part[i];
+            long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+            for (int sp = 2; sp <= 32; sp *= 2) {
+                if (tiles * sp > 4 * NCU || K / sp < 2 * BK) break;
+                int kc = chunk_for(K, sp);
+                int sreal = (int)((K + kc - 1) / kc);
+                double tt = tile_time(t, M, N, kc, sreal) + (double)M * N * (8.0 * sreal + 17) / HBM_BPS +
+                            3 * LAUNCH_S;
+                if (tt < bt) {
+                    bt = tt;
+                    best = Plan{t, PLAN_SPLIT, sreal, kc};
+                }
+            }
+        }
+    }
+    return best;
+}
+
+// Weight gradients: always split over the contraction in chunks of at most
+// 65536 rows (exact int32 partial sums).
+Plan plan_wgrad(long long M, long long N, long long L) {
+    Plan best{WGRAD_TILES[0], PLAN_SPLIT, 1, chunk_for(L, 1)};
+    double bt = 1e30;
+    int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
+    if (smin < 1) smin = 1;
+    for (const Tile &t : WGRAD_TILES) {
+        long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+        for (int sp = smin; sp <= 1024; sp = sp < 4 ? sp + 1 : sp * 2) {
+            int kc = chunk_for(L, sp);
+            if (kc > SPLIT_MAX_ROWS) continue;
+            int sreal = (int)((L + kc - 1) / kc);
+            double tt = tile_time(t, M, N, kc, sreal) + (double)M * N * (8.0 * sreal + 17) / HBM_BPS;
+            if (tt < bt) {
+                bt = tt;
+                best = Plan{t, PLAN_SPLIT, sreal, kc};
+            }
+            if (tiles * sp > 4 * NCU || kc <= 4 * BK) break;
+        }
+    }
+    return best;
+}
+
+// Workspace of a product's epilogue.
 struct ProductWs {
     int *gneed;
     int16_t *p16;
     int16_t *v16;
+    int *partial;
+    long long *sums;
 };
 
-ProductWs carve_product(Carve &c, long long M, long long N) {
-    ProductWs w;
-    long long n_ct = N > 0 ? cdiv(N, BN) : 1;
+ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family) {
+    ProductWs w{};
+    size_t p16 = 0, v16 = 0, part = 0, sums = 0;
+    for (int rg = 0; rg < 2; ++rg) {
+        Plan pl = plan_product(M, N, K, rg, family);
+        if (pl.mode == PLAN_RTO) {
+            size_t n_p = rg ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)cdiv(M, pl.t.bm()) * cdiv(N, pl.t.bn());
+            p16 = p16 > n_p ? p16 : n_p;
+            v16 = (size_t)M * N;
+        } else if (pl.mode == PLAN_SPLIT) {
+            size_t n_part = (size_t)pl.splits * M * N;
+            part = part > n_part ? part : n_part;
+            sums = (size_t)M * N;
+        }
+    }
     w.gneed = c.take<int>(M > 0 ? M : 1);
-    w.p16 = c.take<int16_t>(M * n_ct);
-    w.v16 = c.take<int16_t>(M * N);
+    w.p16 = c.take<int16_t>(p16);
+    w.v16 = c.take<int16_t>(v16);
+    w.partial = c.take<int>(part);
+    w.sums = c.take<long long>(sums);
     return w;
 }
 
-// Run A(m,k) . B(n,k) over K into an int8 output, choosing the one-pass
-// epilogue when every output group lies inside one tile.
-ie_status run_product(const Operand &A, const Operand &B, long long M, long long N, long long K,
-                      ExpSrc ea, ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags,
+// A(m,k) . B(n,k) over K into an int8 output with the planned epilogue.
+ie_status run_product(const Operand &A, const Operand &B, long long M, long long N, long long K, ExpSrc ea,
+                      ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, int family,
                       hipStream_t st) {
     if (M == 0 || N == 0) {
         return hip_status(launch_fill_i8(out->exp, out->group == IE_GROUP_ROW ? M : 1, E_MIN, st));
     }
+    const int rg = out->group == IE_GROUP_ROW;
+    Plan pl = plan_product(M, N, K, rg, family);
     Epi ep;
     memset(&ep, 0, sizeof ep);
     ep.ea = ea;
     ep.eb = eb;
-    ep.row_group = out->group == IE_GROUP_ROW;
+    ep.row_group = rg;
     ep.out = out->mant;
     ep.out_exp = out->exp;
     ep.flags = flags;
-    ep.n_ct = cdiv(N, BN);
-    bool direct = ep.row_group ? (N <= BN) : (M <= BM && N <= BN);
-    if (direct) {
-        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, 1, (int)(K > 0 ? cdiv(K, BK) * BK : BK),
-                           EPI_DIRECT, ep, st));
+    if (pl.mode == PLAN_DIRECT) {
+        ep.mode = EPI_DIRECT;
+        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
         return IE_OK;
     }
-    ep.v16 = pw.v16;
-    ep.p16 = pw.p16;
-    ep.gneed = pw.gneed;
-    IE_TRY(launch_fill_i32(pw.gneed, ep.row_group ? M : 1, NEED_NONE, st));
-    IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, 1, (int)(K > 0 ? cdiv(K, BK) * BK : BK), EPI_RTO, ep,
-                       st));
-    IE_TRY(launch_rto_finalize(pw.v16, pw.p16, pw.gneed, (int)M, (int)N, ep.n_ct, ep.row_group, out->mant,
-                               out->exp, flags, st));
+    if (pl.mode == PLAN_RTO) {
+        ep.mode = EPI_RTO;
+        ep.v16 = pw.v16;
+        ep.p16 = pw.p16;
+        ep.gneed = pw.gneed;
+        IE_TRY(launch_fill_i32(pw.gneed, rg ? M : 1, NEED_NONE, st));
+        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
+        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, pw.gneed, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags,
+                                   st));
+        return IE_OK;
+    }
+    ep.partial = pw.partial;
+    ep.split_stride = M * N;
+    IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
+    IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed, st));
+    IE_TRY(launch_round_sums(pw.sums, (int)M, (int)N, (int)N, 1, 1, ea, eb, rg, pw.gneed, out->mant, out->exp, flags,
+                             st));
     return IE_OK;
-}
-
-// Split of a long contraction (weight gradients) into exact int32 chunks.
-struct Split {
-    int splits;
-    int chunk;
-};
-
-Split choose_split(long long M, long long N, long long L) {
-    long long tiles = (long long)cdiv(M, BM) * cdiv(N, BN);
-    long long want = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
-    long long s = want < 1 ? 1 : want;
-    long long chunk = L > 0 ? (L + s - 1) / s : BK;
-    if (chunk < 512) chunk = 512;
-    chunk = (chunk + BK - 1) / BK * BK;
-    if (chunk > SPLIT_MAX_ROWS) chunk = SPLIT_MAX_ROWS;
-    long long splits = L > 0 ? (L + chunk - 1) / chunk : 1;
-    return {(int)splits, (int)chunk};
 }
 
 struct WgradWs {
     int *partial;
+    long long *sums;
     int *gneed;
     int *eps;  // [2]
 };
 
-WgradWs carve_wgrad(Carve &c, long long N, long long K, long long L) {
+// Weight gradient [N x Kg] contracted over L rows; the stored output is
+// [N x Kout] with column j taken from (j / mc) * mcp + j % mc of the GEMM
+// columns (mc == mcp: identity).
+WgradWs carve_wgrad(Carve &c, long long N, long long Kg, long long L) {
     WgradWs w;
-    Split sp = choose_split(N, K, L);
+    Plan pl = plan_wgrad(N, Kg, L);
     w.eps = c.take<int>(2);
-    w.gneed = c.take<int>(1);
-    w.partial = c.take<int>((size_t)sp.splits * N * K);
+    w.gneed = c.take<int>(N > 0 ? N : 1);
+    w.partial = c.take<int>((size_t)pl.splits * N * Kg);
+    w.sums = c.take<long long>((size_t)N * Kg);
     return w;
 }
 
-ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K, long long L,
-                    const ie_mat *dW, const WgradWs &w, uint32_t *flags, hipStream_t st) {
-    if (N == 0 || K == 0) {
+ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long Kg, long long Kout, int mc, int mcp,
+                    long long L, const ie_mat *dW, const WgradWs &w, uint32_t *flags, hipStream_t st) {
+    if (N == 0 || Kout == 0) {
         return hip_status(launch_fill_i8(dW->exp, dW->group == IE_GROUP_ROW ? N : 1, E_MIN, st));
     }
-    Split sp = choose_split(N, K, L);
+    Plan pl = plan_wgrad(N, Kg, L);
     Epi ep;
     memset(&ep, 0, sizeof ep);
     ep.partial = w.partial;
-    ep.split_stride = N * K;
+    ep.split_stride = N * Kg;
     ep.flags = flags;
+    int splits = pl.splits;
     if (L == 0) {
-        IE_TRY(launch_fill_i32(w.partial, N * K, 0, st));
+        IE_TRY(launch_fill_i32(w.partial, N * Kg, 0, st));
+        splits = 1;
     } else {
-        IE_TRY(launch_gemm(A, B, (int)N, (int)K, (int)L, sp.splits, sp.chunk, EPI_PARTIAL, ep, st));
+        IE_TRY(launch_gemm(A, B, (int)N, (int)Kg, (int)L, pl.t, pl.splits, pl.k_chunk, true, ep, st));
     }
-    IE_TRY(launch_dw_finalize(w.partial, L == 0 ? 1 : sp.splits, N * K, (int)N, (int)K, w.eps, w.eps + 1,
-                              dW->group == IE_GROUP_ROW, w.gneed, dW->mant, dW->exp, flags, st));
+    const int rg = dW->group == IE_GROUP_ROW;
+    ExpSrc ea{nullptr, w.eps, 0}, eb{nullptr, w.eps + 1, 0};
+    IE_TRY(launch_partial_reduce(w.partial, splits, N * Kg, (int)N, (int)Kg, ea, eb, rg, w.sums, w.gneed, st));
+    IE_TRY(launch_round_sums(w.sums, (int)N, (int)Kout, (int)Kg, mc, mcp, ea, eb, rg, w.gneed, dW->mant, dW->exp,
+                             flags, st));
     return IE_OK;
 }
+
+long long r16(long long x) { return (x + 15) / 16 * 16; }
 
 ConvGeom geom(const ie_conv_desc *d) {
     ConvGeom g;
@@ -177,6 +322,15 @@ ConvGeom geom(const ie_conv_desc *d) {
     g.pad = d->pad;
     g.p = (d->h + 2 * d->pad - d->r) / d->stride + 1;
     g.q = (d->w + 2 * d->pad - d->s) / d->stride + 1;
+    g.dpq = make_fastdiv((uint32_t)(g.p * g.q));
+    g.dq = make_fastdiv((uint32_t)g.q);
+    g.dhw = make_fastdiv((uint32_t)(g.h * g.w));
+    g.dw = make_fastdiv((uint32_t)g.w);
+    g.cp = (int)r16(g.c);
+    g.kp = (int)r16(g.k);
+    g.dc = make_fastdiv((uint32_t)g.cp);
+    g.ds = make_fastdiv((uint32_t)g.s);
+    g.dk = make_fastdiv((uint32_t)g.kp);
     return g;
 }
 
@@ -192,24 +346,28 @@ ie_status check_conv(const ie_conv_desc *d) {
 }
 
 size_t linear_fwd_ws(long long M, long long N, long long K) {
-    (void)K;
     Carve c{nullptr, HEADER};
-    carve_product(c, M, N);
+    if (K != r16(K)) {
+        c.take<int8_t>((size_t)M * r16(K));
+        c.take<int8_t>((size_t)N * r16(K));
+    }
+    carve_product(c, M, N, r16(K), 0);
     return align256(c.off);
 }
 
 size_t linear_dx_ws(long long M, long long N, long long K) {
     Carve c{nullptr, HEADER};
     c.take<int>(1);
-    c.take<int8_t>((size_t)N * K);
-    carve_product(c, M, K);
+    c.take<int8_t>((size_t)K * r16(N));
+    if (N != r16(N)) c.take<int8_t>((size_t)M * r16(N));
+    carve_product(c, M, K, r16(N), 0);
     return align256(c.off);
 }
 
 size_t linear_dw_ws(long long M, long long N, long long K) {
     Carve c{nullptr, HEADER};
-    c.take<int8_t>((size_t)M * N);
-    c.take<int8_t>((size_t)M * K);
+    c.take<int8_t>((size_t)M * r16(N));
+    c.take<int8_t>((size_t)M * r16(K));
     carve_wgrad(c, N, K, M);
     return align256(c.off);
 }
@@ -217,18 +375,23 @@ size_t linear_dw_ws(long long M, long long N, long long K) {
 size_t conv_fwd_ws(const ie_conv_desc *d) {
     ConvGeom g = geom(d);
     Carve c{nullptr, HEADER};
-    carve_product(c, (long long)g.n * g.p * g.q, g.k);
+    if (g.cp != g.c) {
+        c.take<int8_t>((size_t)g.n * g.h * g.w * g.cp);
+        c.take<int8_t>((size_t)g.k * g.r * g.s * g.cp);
+    }
+    carve_product(c, (long long)g.n * g.p * g.q, g.k, (long long)g.r * g.s * g.cp, 1);
     return align256(c.off);
 }
 
 size_t conv_bwd_ws(const ie_conv_desc *d) {
     ConvGeom g = geom(d);
-    long long rsc = (long long)g.r * g.s * g.c;
     Carve c{nullptr, HEADER};
     c.take<int>(1);
-    c.take<int8_t>((size_t)rsc * g.k);
-    carve_product(c, (long long)g.n * g.h * g.w, g.c);
-    carve_wgrad(c, g.k, rsc, (long long)g.n * g.p * g.q);
+    c.take<int8_t>((size_t)g.c * g.r * g.s * g.kp);
+    if (g.kp != g.k) c.take<int8_t>((size_t)g.n * g.p * g.q * g.kp);
+    if (g.cp != g.c) c.take<int8_t>((size_t)g.n * g.h * g.w * g.cp);
+    carve_product(c, (long long)g.n * g.h * g.w, g.c, (long long)g.r * g.s * g.kp, 1);
+    carve_wgrad(c, g.k, (long long)g.r * g.s * g.cp, (long long)g.n * g.p * g.q);
     return align256(c.off);
 }
 
@@ -276,17 +439,27 @@ ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void 
     long long M = X->rows, K = X->cols, N = W->rows;
     if (W->cols != K || Y->rows != M || Y->cols != N) return IE_ERR_SHAPE;
     if (K > MAX_CONTRACT) return IE_ERR_UNSUPPORTED;
+    if (!aligned(X->mant, 16) || !aligned(W->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < linear_fwd_ws(M, N, K)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
-    ProductWs pw = carve_product(c, M, N);
-    Operand A{LD_K, X->mant, K, (int)M, (K % 16 == 0) && aligned(X->mant, 16), {}};
-    Operand B{LD_K, W->mant, K, (int)N, (K % 16 == 0) && aligned(W->mant, 16), {}};
+    const long long Kp = r16(K);
+    const int8_t *xs = X->mant, *wsrc = W->mant;
+    if (Kp != K) {
+        int8_t *xp = c.take<int8_t>((size_t)M * Kp), *wp = c.take<int8_t>((size_t)N * Kp);
+        IE_TRY(launch_pad_rows(X->mant, M, K, nullptr, 0, nullptr, Kp, xp, st));
+        IE_TRY(launch_pad_rows(W->mant, N, K, nullptr, 0, nullptr, Kp, wp, st));
+        xs = xp;
+        wsrc = wp;
+    }
+    ProductWs pw = carve_product(c, M, N, Kp, 0);
+    Operand A{LD_K, xs, Kp, (int)M, {}};
+    Operand B{LD_K, wsrc, Kp, (int)N, {}};
     ExpSrc ea{X->exp, nullptr, X->group == IE_GROUP_ROW};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, M, N, K, ea, eb, Y, pw, flags, st);
+    return run_product(A, B, M, N, Kp, ea, eb, Y, pw, flags, 0, st);
 }
 
 ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
@@ -297,22 +470,31 @@ ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, 
     long long M = dY->rows, N = dY->cols, K = W->cols;
     if (W->rows != N || dX->rows != M || dX->cols != K) return IE_ERR_SHAPE;
     if (N > MAX_CONTRACT) return IE_ERR_UNSUPPORTED;
+    if (!aligned(dY->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < linear_dx_ws(M, N, K)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
+    const long long Np = r16(N);
     int *estar = c.take<int>(1);
-    int8_t *wt = c.take<int8_t>((size_t)N * K);
-    ProductWs pw = carve_product(c, M, K);
-    if (M == 0 || K == 0) return run_product(Operand{}, Operand{}, M, K, N, ExpSrc{}, ExpSrc{}, dX, pw, flags, st);
+    int8_t *wt = c.take<int8_t>((size_t)K * Np);
+    int8_t *dyp = Np != N ? c.take<int8_t>((size_t)M * Np) : nullptr;
+    ProductWs pw = carve_product(c, M, K, Np, 0);
+    if (M == 0 || K == 0) return run_product(Operand{}, Operand{}, M, K, Np, ExpSrc{}, ExpSrc{}, dX, pw, flags, 0, st);
     IE_TRY(launch_exp_max(W->exp, n_exps(W), estar, st));
-    IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, (int)N, 1, (int)K, wt, st));
-    Operand A{LD_K, dY->mant, N, (int)M, (N % 16 == 0) && aligned(dY->mant, 16), {}};
-    Operand B{LD_K, wt, N, (int)K, (N % 16 == 0), {}};
+    IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, (int)N, 1, (int)K, (int)Np, wt,
+                                  st));
+    const int8_t *dys = dY->mant;
+    if (dyp) {
+        IE_TRY(launch_pad_rows(dY->mant, M, N, nullptr, 0, nullptr, Np, dyp, st));
+        dys = dyp;
+    }
+    Operand A{LD_K, dys, Np, (int)M, {}};
+    Operand B{LD_K, wt, Np, (int)K, {}};
     ExpSrc ea{dY->exp, nullptr, dY->group == IE_GROUP_ROW};
     ExpSrc eb{nullptr, estar, 0};
-    return run_product(A, B, M, K, N, ea, eb, dX, pw, flags, st);
+    return run_product(A, B, M, K, Np, ea, eb, dX, pw, flags, 0, st);
 }
 
 ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, void *ws, size_t ws_bytes,
@@ -322,30 +504,34 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, 
     IE_CHECK(check_mat(dW));
     long long M = dY->rows, N = dY->cols, K = X->cols;
     if (X->rows != M || dW->rows != N || dW->cols != K) return IE_ERR_SHAPE;
+    if (!aligned(dY->mant, 16) || !aligned(X->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < linear_dw_ws(M, N, K)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
-    int8_t *dya = c.take<int8_t>((size_t)M * N);
-    int8_t *xa = c.take<int8_t>((size_t)M * K);
+    const long long Np = r16(N), Kp = r16(K);
+    int8_t *dya = c.take<int8_t>((size_t)M * Np);
+    int8_t *xa = c.take<int8_t>((size_t)M * Kp);
     WgradWs w = carve_wgrad(c, N, K, M);
-    if (N == 0 || K == 0) return run_wgrad(Operand{}, Operand{}, N, K, M, dW, w, flags, st);
-    // common exponents over the contraction axis (rows); align ROW operands
+    if (N == 0 || K == 0) return run_wgrad(Operand{}, Operand{}, N, K, K, 1, 1, M, dW, w, flags, st);
+    // common exponents over the contraction axis (rows); align ROW operands,
+    // pad rows to multiples of 16
     IE_TRY(launch_exp_max(dY->exp, n_exps(dY), w.eps, st));
     IE_TRY(launch_exp_max(X->exp, n_exps(X), w.eps + 1, st));
     const int8_t *dys = dY->mant, *xs = X->mant;
-    if (dY->group == IE_GROUP_ROW && M > 0) {
-        IE_TRY(launch_align_rows(dY->mant, dY->exp, w.eps, M, N, dya, st));
+    const bool dy_row = dY->group == IE_GROUP_ROW, x_row = X->group == IE_GROUP_ROW;
+    if ((dy_row || Np != N) && M > 0) {
+        IE_TRY(launch_pad_rows(dY->mant, M, N, dY->exp, dy_row, dy_row ? w.eps : nullptr, Np, dya, st));
         dys = dya;
     }
-    if (X->group == IE_GROUP_ROW && M > 0) {
-        IE_TRY(launch_align_rows(X->mant, X->exp, w.eps + 1, M, K, xa, st));
+    if ((x_row || Kp != K) && M > 0) {
+        IE_TRY(launch_pad_rows(X->mant, M, K, X->exp, x_row, x_row ? w.eps + 1 : nullptr, Kp, xa, st));
         xs = xa;
     }
-    Operand A{LD_T, dys, N, (int)N, (N % 8 == 0) && aligned(dys, 8), {}};
-    Operand B{LD_T, xs, K, (int)K, (K % 8 == 0) && aligned(xs, 8), {}};
-    return run_wgrad(A, B, N, K, M, dW, w, flags, st);
+    Operand A{LD_T, dys, Np, (int)N, {}};
+    Operand B{LD_T, xs, Kp, (int)K, {}};
+    return run_wgrad(A, B, N, K, K, 1, 1, M, dW, w, flags, st);
 }
 
 ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
@@ -357,22 +543,33 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     ConvGeom g = geom(d);
     long long rsc = (long long)g.r * g.s * g.c;
     long long npq = (long long)g.n * g.p * g.q;
-    if (X->rows != (long long)g.n * g.h * g.w || X->cols != g.c) return IE_ERR_SHAPE;
+    long long nhw = (long long)g.n * g.h * g.w;
+    if (X->rows != nhw || X->cols != g.c) return IE_ERR_SHAPE;
     if (W->rows != g.k || W->cols != rsc) return IE_ERR_SHAPE;
     if (Y->rows != npq || Y->cols != g.k) return IE_ERR_SHAPE;
     if (X->group != IE_GROUP_TENSOR) return IE_ERR_UNSUPPORTED;
     if (rsc > MAX_CONTRACT || npq > DIM_MAX) return IE_ERR_UNSUPPORTED;
+    if (!aligned(X->mant, 16) || !aligned(W->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < conv_fwd_ws(d)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
-    ProductWs pw = carve_product(c, npq, g.k);
-    Operand A{LD_IM2COL, X->mant, g.c, (int)npq, (g.c % 16 == 0) && aligned(X->mant, 16), g};
-    Operand B{LD_K, W->mant, rsc, g.k, (rsc % 16 == 0) && aligned(W->mant, 16), {}};
+    const int8_t *xs = X->mant, *wsrc = W->mant;
+    if (g.cp != g.c) {
+        int8_t *xp = c.take<int8_t>((size_t)nhw * g.cp), *wp = c.take<int8_t>((size_t)g.k * g.r * g.s * g.cp);
+        IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
+        IE_TRY(launch_pad_rows(W->mant, (long long)g.k * g.r * g.s, g.c, nullptr, 0, nullptr, g.cp, wp, st));
+        xs = xp;
+        wsrc = wp;
+    }
+    const long long kg = (long long)g.r * g.s * g.cp;
+    ProductWs pw = carve_product(c, npq, g.k, kg, 1);
+    Operand A{LD_IM2COL, xs, g.cp, (int)npq, g};
+    Operand B{LD_K, wsrc, kg, g.k, {}};
     ExpSrc ea{X->exp, nullptr, 0};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, npq, g.k, rsc, ea, eb, Y, pw, flags, st);
+    return run_product(A, B, npq, g.k, kg, ea, eb, Y, pw, flags, 1, st);
 }
 
 ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
@@ -394,32 +591,45 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     if (dW && (dW->rows != g.k || dW->cols != rsc)) return IE_ERR_SHAPE;
     if (X->group != IE_GROUP_TENSOR || dY->group != IE_GROUP_TENSOR) return IE_ERR_UNSUPPORTED;
     if ((long long)g.k * g.r * g.s > MAX_CONTRACT || nhw > DIM_MAX) return IE_ERR_UNSUPPORTED;
+    if (!aligned(X->mant, 16) || !aligned(dY->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < conv_bwd_ws(d)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
     int *estar = c.take<int>(1);
-    int8_t *wt = c.take<int8_t>((size_t)rsc * g.k);
-    ProductWs pw = carve_product(c, nhw, g.c);
-    WgradWs w = carve_wgrad(c, g.k, rsc, npq);
+    int8_t *wt = c.take<int8_t>((size_t)g.c * g.r * g.s * g.kp);
+    int8_t *dyp = g.kp != g.k ? c.take<int8_t>((size_t)npq * g.kp) : nullptr;
+    int8_t *xp = g.cp != g.c ? c.take<int8_t>((size_t)nhw * g.cp) : nullptr;
+    const long long rskp = (long long)g.r * g.s * g.kp, rscp = (long long)g.r * g.s * g.cp;
+    ProductWs pw = carve_product(c, nhw, g.c, rskp, 1);
+    WgradWs w = carve_wgrad(c, g.k, rscp, npq);
+    const int8_t *dys = dY->mant;
+    if (dyp && (dX || dW)) {
+        IE_TRY(launch_pad_rows(dY->mant, npq, g.k, nullptr, 0, nullptr, g.kp, dyp, st));
+        dys = dyp;
+    }
     if (dX) {
-        long long rsk = (long long)g.r * g.s * g.k;
         IE_TRY(launch_exp_max(W->exp, n_exps(W), estar, st));
-        IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, g.k, g.r * g.s, g.c,
+        IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, g.k, g.r * g.s, g.c, g.kp,
                                       wt, st));
-        Operand A{LD_DGRAD, dY->mant, g.k, (int)nhw, (g.k % 16 == 0) && aligned(dY->mant, 16), g};
-        Operand B{LD_K, wt, rsk, g.c, (rsk % 16 == 0), {}};
+        Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
+        Operand B{LD_K, wt, rskp, g.c, {}};
         ExpSrc ea{dY->exp, nullptr, 0};
         ExpSrc eb{nullptr, estar, 0};
-        IE_CHECK(run_product(A, B, nhw, g.c, rsk, ea, eb, dX, pw, flags, st));
+        IE_CHECK(run_product(A, B, nhw, g.c, rskp, ea, eb, dX, pw, flags, 1, st));
     }
     if (dW) {
+        const int8_t *xs = X->mant;
+        if (xp) {
+            IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
+            xs = xp;
+        }
         IE_TRY(launch_exp_max(dY->exp, 1, w.eps, st));
         IE_TRY(launch_exp_max(X->exp, 1, w.eps + 1, st));
-        Operand A{LD_T, dY->mant, g.k, g.k, (g.k % 8 == 0) && aligned(dY->mant, 8), {}};
-        Operand B{LD_IM2COL_T, X->mant, g.c, (int)rsc, (g.c % 8 == 0) && aligned(X->mant, 8), g};
-        IE_CHECK(run_wgrad(A, B, g.k, rsc, npq, dW, w, flags, st));
+        Operand A{LD_T, dys, g.kp, g.k, {}};
+        Operand B{LD_IM2COL_T, xs, g.cp, (int)rscp, g};
+        IE_CHECK(run_wgrad(A, B, g.k, rscp, rsc, g.c, g.cp, npq, dW, w, flags, st));
     }
     return IE_OK;
 }

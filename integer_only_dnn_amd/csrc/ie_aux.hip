@@ -115,6 +115,16 @@ hipError_t launch_zero_flags(void *ws, hipStream_t st) {
     return launch_fill_i32((int *)ws, 64, 0, st);
 }
 
+__device__ __forceinline__ void raise_max_aux(int *p, int v) {
+    if (v > __atomic_load_n(p, __ATOMIC_RELAXED)) atomicMax(p, v);
+}
+
+__device__ __forceinline__ int block_wave_max(int v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
+
 __device__ __forceinline__ int block_max256(int v, int *sh) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
@@ -138,32 +148,39 @@ hipError_t launch_exp_max(const int8_t *e, long long n, int *out, hipStream_t st
     return hipGetLastError();
 }
 
-// out[i][k] = in[i][k] re-expressed at *estar (row exponents e[i]).
-__global__ void align_rows_kernel(const int8_t *in, const int8_t *e, const int *estar, long long rows,
-                                  long long cols, int8_t *out) {
-    int es = *estar;
-    long long n = rows * cols;
+// out[i][k] = in[i][k] re-expressed at *estar (row exponents e[i]; no shift
+// when estar is null), for k < cols; zeros for cols <= k < cols_p.
+__global__ void pad_rows_kernel(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
+                                const int *estar, long long cols_p, int8_t *out) {
+    const int es = estar ? *estar : 0;
+    const long long n = rows * cols_p;
     for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
          i += (long long)gridDim.x * blockDim.x) {
-        long long r = i / cols;
-        out[i] = (int8_t)rne_shift32(in[i], es - (int)e[r]);
+        const long long r = i / cols_p, c = i - r * cols_p;
+        int v = 0;
+        if (c < cols) {
+            v = in[r * cols + c];
+            if (estar) v = rne_shift32(v, es - (e_row ? (int)e[r] : (int)e[0]));
+        }
+        out[i] = (int8_t)v;
     }
 }
 
-hipError_t launch_align_rows(const int8_t *in, const int8_t *e, const int *estar, long long rows,
-                             long long cols, int8_t *out, hipStream_t st) {
-    long long n = rows * cols;
+hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
+                           const int *estar, long long cols_p, int8_t *out, hipStream_t st) {
+    const long long n = rows * cols_p;
     if (n <= 0) return hipSuccess;
     prof_begin(st);
-    hipLaunchKernelGGL(align_rows_kernel, dim3(blocks_for(n, 256, 16384)), dim3(256), 0, st, in, e,
-                       estar, rows, cols, out);
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks_for(n, 256, 16384)), dim3(256), 0, st, in, rows, cols, e,
+                       e_row, estar, cols_p, out);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
 
-// w viewed as [A][B][C] (row exponent e[a]): out[c][b][a] = w[a][b][c] at *estar.
+// w viewed as [A][B][C] (row exponent e[a]): out[c][b][a] = w[a][b][c] at
+// *estar for a < A, zero for A <= a < Ap (output pitch Ap).
 __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, const int8_t *e, int e_row,
-                                                              const int *estar, int A, int B, int C,
+                                                              const int *estar, int A, int B, int C, int Ap,
                                                               int8_t *out) {
     __shared__ int8_t tile[64][65];
     int es = *estar;
@@ -182,107 +199,254 @@ __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, c
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
         int lc = i >> 6, la = i & 63;
         int a = a0 + la, c = c0 + lc;
-        if (a < A && c < C) out[((long long)c * B + b) * A + a] = tile[la][lc];
+        if (a < Ap && c < C) out[((long long)c * B + b) * Ap + a] = tile[la][lc];
     }
 }
 
-hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, const int *estar, int A,
-                                  int B, int C, int8_t *out, hipStream_t st) {
-    if (A <= 0 || B <= 0 || C <= 0) return hipSuccess;
-    dim3 grid((C + 63) / 64, (A + 63) / 64, B);
+hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, const int *estar, int A, int B,
+                                  int C, int Ap, int8_t *out, hipStream_t st) {
+    if (Ap <= 0 || B <= 0 || C <= 0) return hipSuccess;
+    dim3 grid((C + 63) / 64, (Ap + 63) / 64, B);
     prof_begin(st);
-    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, estar, A, B, C, out);
+    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, estar, A, B, C, Ap, out);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
 
-// Second pass of the round-to-odd epilogue: C = rne(v, e_group - p).
-__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16,
-                                                           const int *gneed, int M, int N, int n_ct,
-                                                           int row_group, int8_t *out, int8_t *out_exp,
-                                                           uint32_t *flags) {
-    for (int row = blockIdx.x; row < M; row += gridDim.x) {
-        int e = clamp_exp_flag(max(E_MIN, gneed[row_group ? row : 0]), flags);
-        const int16_t *v = v16 + (long long)row * N;
-        int8_t *o = out + (long long)row * N;
-        const int16_t *pr = p16 + (long long)row * n_ct;
-        for (int col = threadIdx.x; col < N; col += 256) {
-            int p = pr[col / BN];
-            o[col] = (int8_t)rne_shift32(v[col], e - p);
-        }
-        if (threadIdx.x == 0 && (row_group || row == 0)) out_exp[row_group ? row : 0] = (int8_t)e;
-    }
+// ---------------------------------------------------------------------------
+// Host helpers
+// ---------------------------------------------------------------------------
+
+FastDiv make_fastdiv(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
+    int s = 31 + l;
+    uint64_t m = ((1ull << s) + d - 1) / d;
+    return FastDiv{(uint32_t)m, s};
 }
 
-hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed, int M, int N,
-                               int n_ct, int row_group, int8_t *out, int8_t *out_exp, uint32_t *flags,
-                               hipStream_t st) {
-    if (M <= 0) return hipSuccess;
-    int blocks = M < 16384 ? M : 16384;
+hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                       int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (A.kind == LD_K && B.kind == LD_K) return launch_gemm_kk(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
+    if (A.kind == LD_IM2COL && B.kind == LD_K)
+        return launch_gemm_im2col(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
+    if (A.kind == LD_DGRAD && B.kind == LD_K)
+        return launch_gemm_dgrad(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
+    if (A.kind == LD_T) return launch_gemm_wgrad(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Second pass of the round-to-odd epilogue: C = rne(v, e_group - p).
+// Each thread rounds 8 consecutive elements of a row (or 1 when the row
+// length is not a multiple of 8).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.s); }
+
+__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16,
+                                                           const int *gneed, int M, int N, int bm, int bn,
+                                                           int TM, int n_ct, int row_group, int8_t *out,
+                                                           int8_t *out_exp, uint32_t *flags, int vw,
+                                                           FastDiv dper) {
+    const uint32_t per_row = N / vw;
+    const uint32_t total = (uint32_t)M * per_row;
+    const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
+    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+        const uint32_t row = fdiv32(i, dper);
+        const int c0 = (int)(i - row * per_row) * vw;
+        const int e = row_group ? clamp_exp_flag(max(E_MIN, gneed[row]), flags) : eT;
+        const int p = row_group ? p16[(long long)row * n_ct + c0 / bn] : p16[row / bm + TM * (c0 / bn)];
+        const int sh = e - p;
+        const long long o = (long long)row * N + c0;
+        if (vw == 8) {
+            v4i v = *(const v4i *)(v16 + o);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int x = (int)(int16_t)((uint32_t)v[j] & 0xffff), y = (int)(int16_t)((uint32_t)v[j] >> 16);
+                uint32_t b = ((uint32_t)(uint8_t)rne_shift32(x, sh)) | ((uint32_t)(uint8_t)rne_shift32(y, sh) << 8);
+                if (j < 2) lo |= b << (16 * j);
+                else hi |= b << (16 * (j - 2));
+            }
+            *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
+        } else {
+            out[o] = (int8_t)rne_shift32(v16[o], sh);
+        }
+        if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
+    }
+    if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
+}
+
+hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed, int M, int N, Tile t,
+                               int row_group, int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const int vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0) ? 8 : 1;
+    const long long total = (long long)M * (N / vw);
+    const int TM = (M + t.bm() - 1) / t.bm();
+    const int n_ct = (N + t.bn() - 1) / t.bn();
     prof_begin(st);
-    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, gneed, M, N, n_ct,
-                       row_group, out, out_exp, flags);
+    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, v16, p16,
+                       gneed, M, N, t.bm(), t.bn(), TM, n_ct, row_group, out, out_exp, flags, vw,
+                       make_fastdiv((uint32_t)(N / vw)));
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
 
-// Weight-gradient finalize: merge exact int32 partial sums in int64, then
-// requantise per output channel (row) or over the whole tensor.
-//   mode 0: row groups, one pass.  mode 1: whole tensor, raise gneed[0].
-//   mode 2: whole tensor, round with gneed[0].
-__global__ __launch_bounds__(256) void dw_finalize_kernel(const int *partial, int splits, long long stride,
-                                                          int N, int K, const int *eps_a, const int *eps_b,
-                                                          int mode, int *gneed, int8_t *out, int8_t *out_exp,
-                                                          uint32_t *flags) {
-    __shared__ int sh[4];
-    int eps = *eps_a + *eps_b;
-    for (int row = blockIdx.x; row < N; row += gridDim.x) {
-        const int *p = partial + (long long)row * K;
-        int e;
-        if (mode != 2) {
+// ---------------------------------------------------------------------------
+// Split-contraction finalize.  Pass 1 sums the int32 partials of every
+// element in int64 and raises its group's maximum smallest exponent; pass 2
+// rounds the sums.  Each thread owns 4 consecutive elements of a row (or 1).
+// ---------------------------------------------------------------------------
+
+// Block = 64 element chunks x 4 split subsets; subset j sums splits j, j+4, ...
+__global__ __launch_bounds__(256) void partial_reduce_kernel(const int *partial, int splits, long long stride,
+                                                             int M, int N, ExpSrc ea, ExpSrc eb, int row_group,
+                                                             long long *sums, int *gneed, int vw,
+                                                             FastDiv dper) {
+    __shared__ long long sh[3][64][4];
+    const uint32_t per_row = N / vw;
+    const uint32_t total = (uint32_t)M * per_row;
+    const int sub = threadIdx.x >> 6, lc = threadIdx.x & 63;
+    for (uint32_t base = blockIdx.x * 64; base < total; base += gridDim.x * 64) {
+        const uint32_t i = base + lc;
+        long long s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+        uint32_t row = 0;
+        int c0 = 0;
+        long long o = 0;
+        if (i < total) {
+            row = fdiv32(i, dper);
+            c0 = (int)(i - row * per_row) * vw;
+            o = (long long)row * N + c0;
+            if (vw == 4) {
+#pragma unroll 4
+                for (int zz = sub; zz < splits; zz += 4) {
+                    v4i v = *(const v4i *)(partial + zz * stride + o);
+                    s0 += v[0];
+                    s1 += v[1];
+                    s2 += v[2];
+                    s3 += v[3];
+                }
+            } else {
+#pragma unroll 4
+                for (int zz = sub; zz < splits; zz += 4) s0 += partial[zz * stride + o];
+            }
+        }
+        if (sub > 0) {
+            sh[sub - 1][lc][0] = s0;
+            sh[sub - 1][lc][1] = s1;
+            sh[sub - 1][lc][2] = s2;
+            sh[sub - 1][lc][3] = s3;
+        }
+        __syncthreads();
+        if (sub == 0) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                s0 += sh[j][lc][0];
+                s1 += sh[j][lc][1];
+                s2 += sh[j][lc][2];
+                s3 += sh[j][lc][3];
+            }
             int m = NEED_NONE;
-            for (int k = threadIdx.x; k < K; k += 256) {
-                long long s = 0;
-                for (int z = 0; z < splits; ++z) s += p[z * stride + k];
-                m = max(m, need64(s, eps));
+            if (i < total) {
+                const int er = exp_at(ea, row);
+                if (vw == 4) {
+                    long long *so = sums + o;
+                    so[0] = s0;
+                    so[1] = s1;
+                    so[2] = s2;
+                    so[3] = s3;
+                    m = max(max(need64(s0, er + exp_at(eb, c0)), need64(s1, er + exp_at(eb, c0 + 1))),
+                            max(need64(s2, er + exp_at(eb, c0 + 2)), need64(s3, er + exp_at(eb, c0 + 3))));
+                } else {
+                    sums[o] = s0;
+                    m = need64(s0, er + exp_at(eb, c0));
+                }
             }
-            m = block_max256(m, sh);
-            if (mode == 1) {
-                if (threadIdx.x == 0 && m != NEED_NONE) atomicMax(gneed, m);
-                continue;
+            // wave 0 (all 64 lanes) reduces its chunks: rows of consecutive
+            // chunks are non-decreasing, so segment at the first lane's row
+            // (lane 0 holds the wave's first chunk; invalid lanes carry no value)
+            const uint32_t r0 = __shfl((int)row, 0);
+            if (i >= total) row = r0;
+            const uint32_t rmax_ = (uint32_t)block_wave_max((int)row);
+            if (!row_group || r0 == rmax_) {
+                m = block_wave_max(m);
+                if (lc == 0 && m != NEED_NONE) raise_max_aux(&gneed[row_group ? r0 : 0], m);
+            } else if (per_row >= 64) {
+                // 64 consecutive chunks of rows of >= 64 chunks: two rows at most
+                int m0 = block_wave_max(row == r0 ? m : NEED_NONE);
+                int m1 = block_wave_max(row == r0 ? NEED_NONE : m);
+                if (lc == 0 && m0 != NEED_NONE) raise_max_aux(&gneed[r0], m0);
+                if (lc == 0 && m1 != NEED_NONE) raise_max_aux(&gneed[rmax_], m1);
+            } else if (m != NEED_NONE) {
+                raise_max_aux(&gneed[row], m);
             }
-            e = clamp_exp_flag(max(E_MIN, m), flags);
-        } else {
-            e = clamp_exp_flag(max(E_MIN, *gneed), flags);
         }
-        for (int k = threadIdx.x; k < K; k += 256) {
-            long long s = 0;
-            for (int z = 0; z < splits; ++z) s += p[z * stride + k];
-            out[(long long)row * K + k] = (int8_t)rne_shift64(s, e - eps);
-        }
-        if (threadIdx.x == 0 && (mode == 0 || row == 0)) out_exp[mode == 0 ? row : 0] = (int8_t)e;
+        __syncthreads();
     }
 }
 
-hipError_t launch_dw_finalize(const int *partial, int splits, long long split_stride, int N, int K,
-                              const int *eps_a, const int *eps_b, int row_group, int *gneed, int8_t *out,
-                              int8_t *out_exp, uint32_t *flags, hipStream_t st) {
-    if (N <= 0) return hipSuccess;
-    int blocks = N < 8192 ? N : 8192;
-    if (row_group) {
-        prof_begin(st);
-        hipLaunchKernelGGL(dw_finalize_kernel, dim3(blocks), dim3(256), 0, st, partial, splits, split_stride,
-                           N, K, eps_a, eps_b, 0, gneed, out, out_exp, flags);
-        prof_end(st, PROF_DW_FINALIZE);
-        return hipGetLastError();
+// Output [M x N]; sums [M x src_pitch]: output column j reads source column j,
+// or (j / c) * cp + j % c when the source pads each group of c columns to cp.
+__global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, int M, int N, int src_pitch,
+                                                         int mc, int mcp, FastDiv dmc, ExpSrc ea, ExpSrc eb,
+                                                         int row_group, const int *gneed, int8_t *out,
+                                                         int8_t *out_exp, uint32_t *flags, int vw, FastDiv dper) {
+    const uint32_t per_row = N / vw;
+    const uint32_t total = (uint32_t)M * per_row;
+    const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
+    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+        const uint32_t row = fdiv32(i, dper);
+        const int c0 = (int)(i - row * per_row) * vw;
+        const long long o = (long long)row * N + c0;
+        const long long so = (long long)row * src_pitch;
+        const int e = row_group ? clamp_exp_flag(max(E_MIN, gneed[row]), flags) : eT;
+        const int er = exp_at(ea, row);
+        uint32_t w = 0;
+        for (int j = 0; j < vw; ++j) {
+            const uint32_t col = c0 + j;
+            uint32_t sc = col;
+            if (mc != mcp) {
+                const uint32_t g = fdiv32(col, dmc);
+                sc = g * mcp + (col - g * mc);
+            }
+            w |= (uint32_t)(uint8_t)rne_shift64(sums[so + sc], e - (er + exp_at(eb, col))) << (8 * j);
+        }
+        if (vw == 4) *(uint32_t *)(out + o) = w;
+        else out[o] = (int8_t)w;
+        if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
     }
-    hipError_t err = launch_fill_i32(gneed, 1, NEED_NONE, st);
+    if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
+}
+
+hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
+                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
+                                 hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    hipError_t err = launch_fill_i32(gneed, row_group ? M : 1, NEED_NONE, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(dw_finalize_kernel, dim3(blocks), dim3(256), 0, st, partial, splits, split_stride, N,
-                       K, eps_a, eps_b, 1, gneed, out, out_exp, flags);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(dw_finalize_kernel, dim3(blocks), dim3(256), 0, st, partial, splits, split_stride, N,
-                       K, eps_a, eps_b, 2, gneed, out, out_exp, flags);
+    const int vw = (N % 4 == 0) ? 4 : 1;
+    const long long total = (long long)M * (N / vw);
+    prof_begin(st);
+    hipLaunchKernelGGL(partial_reduce_kernel, dim3(blocks_for(total, 64, 8192)), dim3(256), 0, st, partial,
+                       splits, split_stride, M, N, ea, eb, row_group, sums, gneed, vw,
+                       make_fastdiv((uint32_t)(N / vw)));
+    prof_end(st, PROF_PARTIAL_REDUCE);
+    return hipGetLastError();
+}
+
+hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
+                             ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
+                             uint32_t *flags, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const int vw = (N % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
+    const long long total = (long long)M * (N / vw);
+    prof_begin(st);
+    hipLaunchKernelGGL(round_sums_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, sums, M, N,
+                       src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb, row_group, gneed,
+                       out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
+    prof_end(st, PROF_ROUND_SUMS);
     return hipGetLastError();
 }
 

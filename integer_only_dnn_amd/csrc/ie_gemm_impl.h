@@ -1,0 +1,610 @@
+// int8 x int8 -> int32 contraction on CDNA4 MFMA with a fused (C, e)
+// requantisation epilogue.
+//
+// Implements the "Product" building block ("Memory-Efficient Integer-Only
+// Training of Deep Neural Networks", Table 6: convolution, linear; Figure 1a:
+// forward and backward of every layer): acc = sum_k A(m,k) B(n,k) exactly in
+// int32, exponent eps = e_A(m) + e_B(n); a result group's exponent is the
+// smallest that brings every |C| to 127 or less (ties to even).
+//
+// A workgroup of 4 waves (2 x 2) computes a (64 MI) x (64 NI) tile with
+// v_mfma_i32_32x32x32_i8; each wave owns (32 MI) x (32 NI).  Operand tiles
+// of 64 contraction bytes are staged through LDS, double buffered, with the
+// next step's global loads in flight during the current step's MFMAs.
+//   - K-contiguous operands sit in LDS as [row][k] (16-byte pad) and are
+//     read with ds_read_b128;
+//   - M-contiguous operands (weight gradients) sit as [k][row] (16-byte
+//     pad), written straight from coalesced 16-byte global loads, and are
+//     transposed on the way out with two ds_read_b64_tr_b8 per fragment:
+//     within each 16-lane group, lanes 2j and 2j+1 name the two halves of
+//     row j of an 8 x 16 byte block and lane i receives its column i.
+// Convolutions are implicit GEMMs: the loaders compute NHWC addresses of the
+// im2col view (forward), of the input-gradient gather and of the transposed
+// im2col view (weight gradient) on the fly; zero padding loads zeros.
+#pragma once
+
+#include "ie_device.h"
+#include "ie_internal.h"
+
+namespace ie {
+
+constexpr int NTHR = 256;
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
+__device__ __forceinline__ void put_byte(uint32_t *w, int b, int8_t v) {
+    w[b >> 2] |= (uint32_t)(uint8_t)v << (8 * (b & 3));
+}
+
+__device__ __forceinline__ v4i pack16(const uint32_t *w) { return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]}; }
+
+template <int KIND>
+struct IsT {
+    static constexpr bool value = KIND == LD_T || KIND == LD_IM2COL_T;
+};
+
+// LDS tile of an operand with ROWS rows (GEMM M or N side).
+template <int KIND, int ROWS>
+struct Lds {
+    static constexpr bool T = IsT<KIND>::value;
+    static constexpr int STRIDE = T ? ROWS + 16 : BK + 16;
+    static constexpr int BYTES = T ? BK * STRIDE : ROWS * STRIDE;
+};
+
+// ---------------------------------------------------------------------------
+// Loaders.  Every operand is read in 16-byte chunks (the host pads channel
+// and contraction extents to multiples of 16).  Loads are branch free: an
+// out-of-range chunk reads a clamped in-range address and is replaced by
+// zeros, so the prefetched loads stay in flight across the MFMA work.
+// Each thread moves ROWS * BK / 4096 chunks per contraction step.
+// ---------------------------------------------------------------------------
+
+template <int KIND, int ROWS>
+struct Ld;
+
+__device__ __forceinline__ v4i zero_unless(bool ok, v4i v) {
+    v4i z = {0, 0, 0, 0};
+    return ok ? v : z;
+}
+
+// [row][k] chunks: chunk c of thread tid -> tile row (tid + 256 c) / CPR,
+// contraction offset ((tid + 256 c) % CPR) * 16 (the same for every c).
+template <int ROWS>
+struct KChunks {
+    static constexpr int CPR = BK / 16;
+    static constexpr int CH = ROWS * CPR / NTHR;
+    static constexpr int STRIDE = BK + 16;
+    __device__ __forceinline__ static int row(int c, int tid) { return (tid + NTHR * c) / CPR; }
+    __device__ __forceinline__ static int col(int tid) { return (tid % CPR) * 16; }
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + row(c, tid) * STRIDE + col(tid)) = reg[c];
+    }
+};
+
+// [k][row] chunks: ROWS/16 chunks per k-row; chunk c -> k-row (tid + 256 c) /
+// (ROWS/16), row offset ((tid + 256 c) % (ROWS/16)) * 16 (the same for every c).
+template <int ROWS>
+struct TChunks {
+    static constexpr int PER = ROWS / 16;
+    static constexpr int CH = ROWS * BK / 16 / NTHR;
+    static constexpr int STRIDE = ROWS + 16;
+    __device__ __forceinline__ static int krow(int c, int tid) { return (tid + NTHR * c) / PER; }
+    __device__ __forceinline__ static int ic(int tid) { return tid % PER; }
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + krow(c, tid) * STRIDE + ic(tid) * 16) = reg[c];
+    }
+};
+
+// Dense K-contiguous operand: element (i, k) at base[i*ld + k].
+template <int ROWS>
+struct Ld<LD_K, ROWS> : KChunks<ROWS> {
+    using B_ = KChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *ptr[CH];
+    bool ok[CH];
+    int col;
+    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
+        col = B_::col(tid);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = i0 + B_::row(c, tid);
+            ok[c] = i < op.rows;
+            ptr[c] = op.base + (long long)(ok[c] ? i : 0) * op.ld + col;
+        }
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+        const bool kin = k0 + col < kend;
+        const int kk = kin ? k0 : kend - 16 - col;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) reg[c] = zero_unless(ok[c] && kin, *(const v4i *)(ptr[c] + kk));
+    }
+};
+
+// Forward convolution: row m = (n, p, q), k = (r, s, c) over the padded
+// channel count cp (activation [N*H*W x cp]).
+template <int ROWS>
+struct Ld<LD_IM2COL, ROWS> : KChunks<ROWS> {
+    using B_ = KChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *x;
+    ConvGeom g;
+    int col;
+    int hb[CH], wb[CH];
+    long long pix[CH];
+    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
+        x = op.base;
+        g = op.g;
+        col = B_::col(tid);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int m = i0 + B_::row(c, tid);
+            const bool ok = m < op.rows;
+            const uint32_t mm = ok ? m : 0;
+            const uint32_t n = fdiv(mm, g.dpq), rem = mm - n * (uint32_t)(g.p * g.q);
+            const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
+            hb[c] = ok ? (int)p * g.stride - g.pad : -(1 << 24);  // invalid rows never hit the image
+            wb[c] = (int)q * g.stride - g.pad;
+            pix[c] = (long long)n * g.h * g.w * g.cp;
+        }
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+        const uint32_t kk = k0 + col;
+        const bool kin = (int)kk < kend;
+        const uint32_t rs = fdiv(kk, g.dc), ch = kk - rs * g.cp;
+        const uint32_t r = fdiv(rs, g.ds), s = rs - r * g.s;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int h = hb[c] + (int)r, w = wb[c] + (int)s;
+            const bool in = kin && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
+            const long long off = in ? pix[c] + ((long long)h * g.w + w) * g.cp + ch : 0;
+            reg[c] = zero_unless(in, *(const v4i *)(x + off));
+        }
+    }
+};
+
+// Input gradient of a convolution: row m = (n, h, w), k = (r, s, ko) over the
+// padded output-channel count kp; element dY[n, p, q, ko] with
+// p * stride = h + pad - r (zero unless exact).
+template <int ROWS>
+struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
+    using B_ = KChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *dy;
+    ConvGeom g;
+    int col;
+    int hp[CH], wp[CH];
+    long long pix[CH];
+    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
+        dy = op.base;
+        g = op.g;
+        col = B_::col(tid);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int m = i0 + B_::row(c, tid);
+            const bool ok = m < op.rows;
+            const uint32_t mm = ok ? m : 0;
+            const uint32_t n = fdiv(mm, g.dhw), rem = mm - n * (uint32_t)(g.h * g.w);
+            const uint32_t h = fdiv(rem, g.dw), w = rem - h * g.w;
+            hp[c] = ok ? (int)h + g.pad : -(1 << 24);
+            wp[c] = (int)w + g.pad;
+            pix[c] = (long long)n * g.p * g.q * g.kp;
+        }
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+        const uint32_t kk = k0 + col;
+        const bool kin = (int)kk < kend;
+        const uint32_t rs = fdiv(kk, g.dk), ko = kk - rs * g.kp;
+        const int r = (int)fdiv(rs, g.ds), s = (int)(rs - (uint32_t)r * g.s);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int a = hp[c] - r, b = wp[c] - s;
+            const int p = a / g.stride, q = b / g.stride;
+            const bool in = kin && a >= 0 && b >= 0 && p * g.stride == a && q * g.stride == b && p < g.p &&
+                            q < g.q;
+            const long long off = in ? pix[c] + ((long long)p * g.q + q) * g.kp + ko : 0;
+            reg[c] = zero_unless(in, *(const v4i *)(dy + off));
+        }
+    }
+};
+
+// M-contiguous dense operand: element (i, k) at base[k*ld + i]; ld >= the
+// row count rounded up to 16.
+template <int ROWS>
+struct Ld<LD_T, ROWS> : TChunks<ROWS> {
+    using B_ = TChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *base;
+    long long ld;
+    bool iok;
+    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
+        const int i = i0 + B_::ic(tid) * 16;
+        iok = i < op.rows;
+        base = op.base + (iok ? i : 0);
+        ld = op.ld;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int k = k0 + B_::krow(c, tid);
+            const bool in = iok && k < kend;
+            reg[c] = zero_unless(in, *(const v4i *)(base + (long long)(k < kend ? k : kend - 1) * ld));
+        }
+    }
+};
+
+// Weight gradient of a convolution, B side: row j = (r, s, c) over the padded
+// channel count cp, k = output pixel (n, p, q); element
+// X[n, p*st + r - pad, q*st + s - pad, c].
+template <int ROWS>
+struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
+    using B_ = TChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *x;
+    ConvGeom g;
+    bool jok;
+    int jr, js, jc;
+    __device__ __forceinline__ void init(const Operand &op, int j0, int tid) {
+        x = op.base;
+        g = op.g;
+        const int jb = j0 + B_::ic(tid) * 16;
+        jok = jb < op.rows;
+        const uint32_t rs = fdiv(jok ? jb : 0, g.dc);
+        jc = (jok ? jb : 0) - (int)rs * g.cp;
+        jr = (int)fdiv(rs, g.ds);
+        js = (int)rs - jr * g.s;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int kk = k0 + B_::krow(c, tid);
+            const uint32_t kc = kk < kend ? kk : 0;
+            const uint32_t n = fdiv(kc, g.dpq), rem = kc - n * (uint32_t)(g.p * g.q);
+            const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
+            const int h = (int)p * g.stride + jr - g.pad, w = (int)q * g.stride + js - g.pad;
+            const bool in = jok && kk < kend && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
+            const long long off = in ? (((long long)n * g.h + h) * g.w + w) * g.cp + jc : 0;
+            reg[c] = zero_unless(in, *(const v4i *)(x + off));
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA fragments: lane l holds row (l % 32) and contraction bytes
+// 16 (l / 32) .. + 15 of a 32-byte step.
+// ---------------------------------------------------------------------------
+
+template <int KIND, int ROWS>
+__device__ __forceinline__ v4i frag(const int8_t *s, int rowbase, int ks, int lane) {
+    constexpr int STRIDE = Lds<KIND, ROWS>::STRIDE;
+    if constexpr (!IsT<KIND>::value) {
+        return *(const v4i *)(s + (rowbase + (lane & 31)) * STRIDE + ks * 32 + (lane >> 5) * 16);
+    } else {
+        const int g = lane & 15;
+        const int i = rowbase + (lane & 16) + (g & 1) * 8;
+        const int k = ks * 32 + (lane >> 5) * 16 + (g >> 1);
+        typedef __attribute__((address_space(3))) v2i lds_v2i;
+        v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(s + k * STRIDE + i));
+        v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(s + (k + 8) * STRIDE + i));
+        return v4i{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+
+// Raise a group maximum: skip the atomic when the stored value is already
+// at least as large (the maximum only grows, so a stale read only costs an
+// unneeded atomic).
+__device__ __forceinline__ void raise_max(int *p, int v) {
+    if (v > __atomic_load_n(p, __ATOMIC_RELAXED)) atomicMax(p, v);
+}
+
+// Workgroups are dispatched to the 8 XCDs round robin.  Tiles are numbered so
+// that each XCD receives a contiguous run of the N-fastest tile order: one
+// XCD walks all column tiles of a row tile before the next, keeping the row
+// tile's operand in its own L2.
+__device__ __forceinline__ void tile_of(int bid, int TM, int TN, int &tm, int &tn) {
+    const int T = TM * TN;
+    const int q = T / 8, r = T % 8;
+    const int x = bid % 8, j = bid / 8;
+    const int logical = x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+    tm = logical / TN;
+    tn = logical - tm * TN;
+}
+
+template <int MI, int NI>
+struct Occ {
+    static constexpr int value = MI * NI <= 4 ? 2 : 1;
+};
+
+template <int KA, int KB, int MI, int NI, bool PARTIAL>
+__global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
+                                                                          int K, int k_chunk, int TM, Epi ep) {
+    constexpr int BMt = 64 * MI, BNt = 64 * NI;
+    using LA = Lds<KA, BMt>;
+    using LB = Lds<KB, BNt>;
+    constexpr int STAGE = LA::BYTES + LB::BYTES;
+    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int TN = (N + BNt - 1) / BNt;
+    int tile_m, tile_n;
+    tile_of(blockIdx.x, TM, TN, tile_m, tile_n);
+    const int m0 = tile_m * BMt, n0 = tile_n * BNt;
+    const int z = blockIdx.z;
+    const int kb = z * k_chunk;
+    const int ke = min(K, kb + k_chunk);
+    const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+    Ld<KA, BMt> la;
+    Ld<KB, BNt> lb;
+    la.init(A, m0, tid);
+    lb.init(B, n0, tid);
+    constexpr int CA = Ld<KA, BMt>::CH, CB = Ld<KB, BNt>::CH;
+
+    // exponents of this tile's rows and columns, for the epilogue
+    __shared__ int seA[PARTIAL ? 1 : BMt], seB[PARTIAL ? 1 : BNt];
+    if constexpr (!PARTIAL) {
+        for (int i = tid; i < BMt; i += NTHR) seA[i] = m0 + i < M ? exp_at(ep.ea, m0 + i) : 0;
+        for (int i = tid; i < BNt; i += NTHR) seB[i] = n0 + i < N ? exp_at(ep.eb, n0 + i) : 0;
+    }
+
+    v16i acc[MI][NI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
+
+    // Two register stages in flight: stage s lives in register set s % 2 and
+    // LDS buffer s % 2.  Step `it` loads stage it+2, computes stage it and
+    // writes stage it+1 (loaded one step earlier) to LDS.
+    v4i ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+    if (nk > 0) {
+        la.load(kb, ke, tid, ra0);
+        lb.load(kb, ke, tid, rb0);
+    }
+    if (nk > 1) {
+        la.load(kb + BK, ke, tid, ra1);
+        lb.load(kb + BK, ke, tid, rb1);
+    }
+    if (nk > 0) {
+        la.store(lds, tid, ra0);
+        lb.store(lds + LA::BYTES, tid, rb0);
+    }
+    __syncthreads();
+
+    auto compute = [&](const int8_t *sA) {
+        const int8_t *sB = sA + LA::BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            v4i af[MI], bf[NI];
+#pragma unroll
+            for (int a = 0; a < MI; ++a) af[a] = frag<KA, BMt>(sA, wm * 32 * MI + a * 32, ks, lane);
+#pragma unroll
+            for (int b = 0; b < NI; ++b) bf[b] = frag<KB, BNt>(sB, wn * 32 * NI + b * 32, ks, lane);
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int b = 0; b < NI; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    for (int it = 0; it < nk; it += 2) {
+        // even step: load set 0, store set 1
+        if (it + 2 < nk) {
+            la.load(kb + (it + 2) * BK, ke, tid, ra0);
+            lb.load(kb + (it + 2) * BK, ke, tid, rb0);
+        }
+        compute(lds);
+        if (it + 1 < nk) {
+            la.store(lds + STAGE, tid, ra1);
+            lb.store(lds + STAGE + LA::BYTES, tid, rb1);
+        }
+        __syncthreads();
+        if (it + 1 >= nk) break;
+        // odd step: load set 1, store set 0
+        if (it + 3 < nk) {
+            la.load(kb + (it + 3) * BK, ke, tid, ra1);
+            lb.load(kb + (it + 3) * BK, ke, tid, rb1);
+        }
+        compute(lds + STAGE);
+        if (it + 2 < nk) {
+            la.store(lds, tid, ra0);
+            lb.store(lds + LA::BYTES, tid, rb0);
+        }
+        __syncthreads();
+    }
+
+    // Element (a, b, r) of this lane sits at tile row / column
+    //   32 MI wm + 32 a + 8 (r/4) + 4 (lane/32) + r%4,   32 NI wn + 32 b + lane%32.
+    auto ROW = [&](int a, int r) { return m0 + wm * 32 * MI + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+    auto COL = [&](int b) { return n0 + wn * 32 * NI + b * 32 + (lane & 31); };
+
+    if constexpr (PARTIAL) {
+        int *P = ep.partial + (long long)z * ep.split_stride;
+#pragma unroll
+        for (int a = 0; a < MI; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = ROW(a, r);
+                if (row >= M) continue;
+#pragma unroll
+                for (int b = 0; b < NI; ++b) {
+                    const int col = COL(b);
+                    if (col < N) P[(long long)row * N + col] = acc[a][b][r];
+                }
+            }
+        return;
+    } else {
+        int *red = (int *)lds;
+        int ebv[NI];
+#pragma unroll
+        for (int b = 0; b < NI; ++b) ebv[b] = seB[COL(b) - n0];
+        const bool uni = !ep.ea.row && !ep.eb.row;
+        const int ea0 = seA[0];
+        const int eb0 = seB[0];
+
+        if (!ep.row_group) {
+            // whole-tensor group: one maximum for the tile
+            int tmax;
+            if (uni) {
+                uint32_t mx = 0;
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int b = 0; b < NI; ++b)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            int v = acc[a][b][r];
+                            mx = max(mx, (uint32_t)(v < 0 ? -v : v));
+                        }
+                tmax = mx ? ea0 + eb0 + mant_shift32(mx) : NEED_NONE;
+            } else {
+                tmax = NEED_NONE;
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int eav = seA[ROW(a, r) - m0];
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) tmax = max(tmax, need32(acc[a][b][r], eav + ebv[b]));
+                    }
+            }
+            tmax = wave_max(tmax);
+            if (lane == 0) red[wave] = tmax;
+            __syncthreads();
+            const int gmax = max(max(red[0], red[1]), max(red[2], red[3]));
+            int e, p = 0;
+            if (ep.mode == EPI_DIRECT) {
+                e = clamp_exp_flag(max(E_MIN, gmax), ep.flags);
+                if (tid == 0 && blockIdx.x == 0) ep.out_exp[0] = (int8_t)e;
+            } else {
+                p = gmax == NEED_NONE ? P_NONE : gmax - 2;
+                if (tid == 0) {
+                    ep.p16[tile_m + TM * tile_n] = (int16_t)p;
+                    if (gmax != NEED_NONE) raise_max(&ep.gneed[0], gmax);
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = ROW(a, r);
+                    if (row >= M) continue;
+                    const int eav = uni ? ea0 : seA[row - m0];
+#pragma unroll
+                    for (int b = 0; b < NI; ++b) {
+                        const int col = COL(b);
+                        if (col >= N) continue;
+                        const long long o = (long long)row * N + col;
+                        if (ep.mode == EPI_DIRECT)
+                            ep.out[o] = (int8_t)rne_shift32(acc[a][b][r], e - (eav + ebv[b]));
+                        else
+                            ep.v16[o] = (int16_t)rto_shift32(acc[a][b][r], p - (eav + ebv[b]));
+                    }
+                }
+        } else {
+            // row groups: maximum per tile row, one 32-row slab at a time
+#pragma unroll
+            for (int a = 0; a < MI; ++a) {
+                int rm[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int eav = seA[ROW(a, r) - m0];
+                    int m = NEED_NONE;
+#pragma unroll
+                    for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b]));
+                    rm[r] = m;
+                }
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) rm[r] = max(rm[r], __shfl_xor(rm[r], off));
+                if ((lane & 31) == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[wn * BMt + ROW(a, r) - m0] = rm[r];
+                }
+            }
+            __syncthreads();
+            const int n_ct = (N + BNt - 1) / BNt;
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = ROW(a, r);
+                    if (row >= M) continue;
+                    const int rm = max(red[row - m0], red[BMt + row - m0]);
+                    const int eav = seA[row - m0];
+                    int e = 0, p = 0;
+                    if (ep.mode == EPI_DIRECT) {
+                        e = clamp_exp_flag(max(E_MIN, rm), ep.flags);
+                        if (wn == 0 && (lane & 31) == 0) ep.out_exp[row] = (int8_t)e;
+                    } else {
+                        p = rm == NEED_NONE ? P_NONE : rm - 2;
+                        if (wn == 0 && (lane & 31) == 0) {
+                            ep.p16[(long long)row * n_ct + tile_n] = (int16_t)p;
+                            if (rm != NEED_NONE) raise_max(&ep.gneed[row], rm);
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < NI; ++b) {
+                        const int col = COL(b);
+                        if (col >= N) continue;
+                        const long long o = (long long)row * N + col;
+                        if (ep.mode == EPI_DIRECT)
+                            ep.out[o] = (int8_t)rne_shift32(acc[a][b][r], e - (eav + ebv[b]));
+                        else
+                            ep.v16[o] = (int16_t)rto_shift32(acc[a][b][r], p - (eav + ebv[b]));
+                    }
+                }
+        }
+    }
+}
+
+template <int KA, int KB, int MI, int NI, bool PARTIAL>
+hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, int splits, int k_chunk,
+                      const Epi &ep, hipStream_t st) {
+    const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
+    dim3 grid(TM * TN, 1, splits);
+    prof_begin(st);
+    hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, PARTIAL>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
+                       k_chunk, TM, ep);
+    prof_end(st, 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB);
+    return hipGetLastError();
+}
+
+}  // namespace ie
+
+// Dispatch over a tile list inside one translation unit.
+#define IE_TILE_CASE(KA, KB, MI_, NI_)                                                                   \
+    if (t.mi == MI_ && t.ni == NI_) {                                                                    \
+        return partial ? launch_one<KA, KB, MI_, NI_, true>(A, B, M, N, K, splits, k_chunk, ep, st)       \
+                       : launch_one<KA, KB, MI_, NI_, false>(A, B, M, N, K, splits, k_chunk, ep, st);     \
+    }
+
+#define IE_TILE_CASE_PARTIAL(KA, KB, MI_, NI_)                                                           \
+    if (t.mi == MI_ && t.ni == NI_) {                                                                    \
+        if (!partial) return hipErrorInvalidValue;                                                       \
+        return launch_one<KA, KB, MI_, NI_, true>(A, B, M, N, K, splits, k_chunk, ep, st);               \
+    }

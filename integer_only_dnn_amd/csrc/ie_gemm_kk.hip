@@ -1,0 +1,18 @@
+// Contraction kernels over K-contiguous dense operands: the linear layer's
+// forward product (X . W^T) and input gradient (dY . W, with W pre-transposed).
+#include "ie_gemm_impl.h"
+
+namespace ie {
+
+hipError_t launch_gemm_kk(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                          int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
+    IE_TILE_CASE(LD_K, LD_K, 2, 2)
+    IE_TILE_CASE(LD_K, LD_K, 4, 1)
+    IE_TILE_CASE(LD_K, LD_K, 1, 4)
+    IE_TILE_CASE(LD_K, LD_K, 2, 1)
+    IE_TILE_CASE(LD_K, LD_K, 1, 2)
+    IE_TILE_CASE(LD_K, LD_K, 1, 1)
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ie

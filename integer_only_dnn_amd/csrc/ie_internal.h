@@ -7,9 +7,8 @@
 
 namespace ie {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 64;
+constexpr int BK = 128;   // contraction step of a workgroup tile (bytes)
+constexpr int NCU = 256;  // compute units of an MI355X
 
 // Exponent of operand rows: per-row int8 array (row != 0), one int8 for the
 // whole tensor (row == 0), or, when e32 is set, one int32 computed on the
@@ -20,19 +19,30 @@ struct ExpSrc {
     int row;
 };
 
+#ifdef __HIPCC__
+__device__ __forceinline__ int exp_at(const ExpSrc &e, int idx) {
+    if (e.e32) return *e.e32;
+    return e.row ? (int)e.e8[idx] : (int)e.e8[0];
+}
+#endif
+
+// Epilogue modes of a contraction kernel.
+//   DIRECT  - every result group lies inside the workgroup tile
+//   RTO     - round-to-odd int16 values at a provisional exponent + group maxima
+//   PARTIAL - exact int32 partial sums of one contraction chunk
 enum EpiKind { EPI_DIRECT = 0, EPI_RTO = 1, EPI_PARTIAL = 2 };
 
 struct Epi {
     ExpSrc ea;        // exponent of GEMM row m
     ExpSrc eb;        // exponent of GEMM column n
+    int mode;         // EPI_DIRECT or EPI_RTO (PARTIAL is a template choice)
     int row_group;    // output groups: 1 = one per row m, 0 = whole tensor
-    int8_t *out;      // EPI_DIRECT: int8 mantissas [M x N]
-    int8_t *out_exp;  // EPI_DIRECT: exponents
-    int16_t *v16;     // EPI_RTO: round-to-odd values [M x N]
-    int16_t *p16;     // EPI_RTO: provisional exponent per (row, column tile)
-    int n_ct;         // number of column tiles
-    int *gneed;       // EPI_RTO: group maxima of the smallest exponents
-    int *partial;     // EPI_PARTIAL: int32 [splits][M][N]
+    int8_t *out;      // DIRECT: int8 mantissas [M x N]
+    int8_t *out_exp;  // DIRECT: exponents
+    int16_t *v16;     // RTO: round-to-odd values [M x N]
+    int16_t *p16;     // RTO: provisional exponent per (row, column tile) or per tile
+    int *gneed;       // RTO: group maxima of the smallest exponents
+    int *partial;     // PARTIAL: int32 [splits][M][N]
     long long split_stride;
     uint32_t *flags;
 };
@@ -45,8 +55,19 @@ enum LoaderKind {
     LD_IM2COL_T = 4   // convolution weight gradient: rows = (r, s, c), k = output pixels
 };
 
+// n / d = (n * m) >> s for 0 <= n < 2^31 (m = ceil(2^s / d), s = 31 + ceil(log2 d)).
+struct FastDiv {
+    uint32_t m;
+    int s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+// Convolution geometry.  cp / kp: input / output channel counts as stored in
+// the operands the kernels read (rounded up to multiples of 16 with zeros);
+// dc divides by cp, dk by kp.
 struct ConvGeom {
-    int n, h, w, c, k, r, s, stride, pad, p, q;
+    int n, h, w, c, k, r, s, stride, pad, p, q, cp, kp;
+    FastDiv dpq, dq, dhw, dw, dc, ds, dk;
 };
 
 struct Operand {
@@ -54,14 +75,31 @@ struct Operand {
     const int8_t *base;
     long long ld;
     int rows;         // valid rows of this operand (GEMM M or N)
-    int vec;          // aligned fast path allowed
     ConvGeom g;
 };
 
-// Launch C[m][n] = sum_k A(m, k) B(n, k) over k in [0, K) (split into
-// `splits` chunks of `k_chunk`, a multiple of BK), then the epilogue.
-hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K,
-                       int splits, int k_chunk, int epi, const Epi &ep, hipStream_t st);
+// Workgroup tile: 4 waves (2 x 2), each 32*mi x 32*ni; workgroup 64*mi x 64*ni.
+struct Tile {
+    int mi, ni;
+    int bm() const { return 64 * mi; }
+    int bn() const { return 64 * ni; }
+};
+
+// C[m][n] = sum_k A(m, k) B(n, k) over k in [0, K), split into `splits`
+// chunks of `k_chunk` (a multiple of BK), then the epilogue.
+hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                       int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+// Per-translation-unit launchers (return hipErrorInvalidValue if the
+// loader / tile combination is not instantiated there).
+hipError_t launch_gemm_kk(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                          int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+hipError_t launch_gemm_im2col(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+hipError_t launch_gemm_dgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                             int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                             int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+bool tile_available(int kind_a, int kind_b, Tile t);
 
 // Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
 void prof_begin(hipStream_t st);
@@ -69,24 +107,32 @@ void prof_end(hipStream_t st, int kind);
 void prof_enable(int on);
 int prof_read(float *ms, int *kind, int max);
 constexpr int PROF_RTO_FINALIZE = 3000;
-constexpr int PROF_DW_FINALIZE = 3100;
+constexpr int PROF_PARTIAL_REDUCE = 3100;
+constexpr int PROF_ROUND_SUMS = 3150;
 constexpr int PROF_ALIGN = 3200;
 
 // Auxiliary kernels (ie_aux.hip).
 hipError_t launch_fill_i32(int *p, long long n, int v, hipStream_t st);
 hipError_t launch_fill_i8(int8_t *p, long long n, int v, hipStream_t st);
 hipError_t launch_exp_max(const int8_t *e, long long n, int *out, hipStream_t st);
-hipError_t launch_align_rows(const int8_t *in, const int8_t *e, const int *estar,
-                             long long rows, long long cols, int8_t *out, hipStream_t st);
+// Copy rows into a zero-padded pitch, re-expressed at *estar when set.
+hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
+                           const int *estar, long long cols_p, int8_t *out, hipStream_t st);
 hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, const int *estar,
-                                  int A, int B, int C, int8_t *out, hipStream_t st);
-hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed,
-                               int M, int N, int n_ct, int row_group, int8_t *out,
-                               int8_t *out_exp, uint32_t *flags, hipStream_t st);
-hipError_t launch_dw_finalize(const int *partial, int splits, long long split_stride, int N,
-                              int K, const int *eps_a, const int *eps_b, int row_group,
-                              int *gneed, int8_t *out, int8_t *out_exp, uint32_t *flags,
-                              hipStream_t st);
+                                  int A, int B, int C, int Ap, int8_t *out, hipStream_t st);
+// Second pass of the round-to-odd epilogue.  ROW groups: p16 per (row,
+// column tile); whole-tensor groups: p16 per tile (tile_m + TM * tile_n).
+hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed, int M, int N,
+                               Tile t, int row_group, int8_t *out, int8_t *out_exp, uint32_t *flags,
+                               hipStream_t st);
+// Split-contraction finalize: sum int32 partials into int64 and raise the
+// group maxima; then round the sums into int8.
+hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
+                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
+                                 hipStream_t st);
+hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
+                             ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
+                             uint32_t *flags, hipStream_t st);
 hipError_t launch_zero_flags(void *ws, hipStream_t st);
 
 // Integer SGD update (ie_update.hip).

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
                 m = max(m, sum_need(nv, a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
         if (pass == 0) {
             m = wave_max64(m);
-            if (lane == 0 && m != NEED_NONE) atomicMax(a.gneed_v, m);
+            if (lane == 0 && m != NEED_NONE && m > __atomic_load_n(a.gneed_v, __ATOMIC_RELAXED)) atomicMax(a.gneed_v, m);
             continue;
         }
         int evn;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
         }
         mw = wave_max64(mw);
         if (w_tensor) {
-            if (lane == 0 && mw != NEED_NONE) atomicMax(a.gneed_w, mw);
+            if (lane == 0 && mw != NEED_NONE && mw > __atomic_load_n(a.gneed_w, __ATOMIC_RELAXED)) atomicMax(a.gneed_w, mw);
             continue;
         }
         const int ewn = clamp_exp_flag(max(E_MIN, mw), a.flags);

@@ -32,7 +32,7 @@ def test_status_strings():
         assert L.ie_status_str(code).decode() == name
 
 
-def _mat(rows, cols, group=0, mant=1, exp=1):
+def _mat(rows, cols, group=0, mant=256, exp=256):
     return ie.ie_mat(mant, exp, rows, cols, group)
 
 
@@ -45,6 +45,7 @@ def test_linear_argument_errors():
     assert L.ie_linear_fwd(by(X), by(W), by(_mat(4, 3, group=7)), 1, 1 << 20, None) == 3
     assert L.ie_linear_fwd(by(X), by(W), by(Y), None, 1 << 20, None) == 4
     assert L.ie_linear_fwd(by(X), by(W), by(Y), 1, 16, None) == 4
+    assert L.ie_linear_fwd(by(_mat(4, 8, mant=1)), by(W), by(Y), 1, 1 << 20, None) == 6
     assert L.ie_linear_fwd(by(_mat(4, 8, mant=0)), by(W), by(Y), 1, 1 << 20, None) == 1
     assert L.ie_linear_fwd(by(_mat(4, 70000)), by(_mat(3, 70000)), by(Y), 1, 1 << 30, None) == 6
     assert L.ie_linear_bwd_dx(by(Y), by(W), by(_mat(4, 9)), 1, 1 << 20, None) == 2
