@@ -1,0 +1,209 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (same entry points, same inputs, same planner).
+
+Per-tensor groups span the whole output, so those results are compared in
+full.  Row-grouped outputs are independent per row (a row's exponent and
+mantissas depend only on that row of the left operand), so for the largest
+ones the oracle runs on sampled rows — always including the first and last —
+and those rows are compared.  Weight gradients and their per-output-channel
+groups are compared in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import workloads as wl
+from integer_only_dnn_amd import ie
+from tests.gpu_util import announce, assert_same, from_dev, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def ws():
+    return ie.Workspace("cuda")
+
+
+def _qt(code):
+    return o.QT(code.mant, code.exp, code.group)
+
+
+def _sample_rows(m, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, size=min(n, m), replace=False)]))
+    return rows
+
+
+def _rows_qt(t: o.QT, rows):
+    exp = t.exp if t.group == o.TENSOR else t.exp[rows]
+    return o.QT(t.mant[rows], exp, t.group)
+
+
+def _assert_rows(dev: ie.Mat, rows, want: o.QT, what):
+    gm, ge = from_dev(dev)
+    gm = gm[rows]
+    if want.group == o.ROW:
+        ge = ge[rows]
+    assert_same_np(gm, ge, want, what)
+
+
+def assert_same_np(gm, ge, want, what):
+    wm = np.asarray(want.mant, dtype=np.int8).reshape(gm.shape)
+    we = np.asarray(want.exp, dtype=np.int8).reshape(ge.shape)
+    assert np.array_equal(ge, we), f"{what}: exponents differ"
+    bad = np.argwhere(gm != wm)
+    assert bad.size == 0, f"{what}: {len(bad)} mantissas differ, first {tuple(bad[0])}"
+
+
+# ---------------------------------------------------------------------------
+# Single linear layer, three full steps (forward, dX, dW, update)
+# ---------------------------------------------------------------------------
+
+def test_linear_small_three_steps(ws):
+    announce("config linear 64x256 -> 128, three steps")
+    inp = wl.linear_small_inputs(seed=1)
+    X, W, dY = _qt(inp.X), _qt(inp.W), _qt(inp.dY)
+    V = o.QT(np.zeros_like(W.mant), np.full(W.mant.shape[0], o.E_MIN, np.int8), o.ROW)
+    Xd, Wd, dYd, Vd = to_dev(X.mant, X.exp, X.group), to_dev(W.mant, W.exp, W.group), \
+        to_dev(dY.mant, dY.exp, dY.group), to_dev(V.mant, V.exp, V.group)
+    for step in range(3):
+        Y, dX, dW = ie.Mat.empty(64, 128, o.TENSOR), ie.Mat.empty(64, 256, o.TENSOR), ie.Mat.empty(128, 256, o.ROW)
+        ie.ie_linear_fwd(Xd, Wd, Y, ws)
+        ie.ie_linear_bwd_dx(dYd, Wd, dX, ws)
+        ie.ie_linear_bwd_dw(dYd, Xd, dW, ws)
+        wY, wdX, wdW = o.linear_fwd(X, W, o.TENSOR), o.linear_bwd_dx(dY, W, o.TENSOR), o.linear_bwd_dw(dY, X, o.ROW)
+        assert_same(Y, wY, f"step {step} Y")
+        assert_same(dX, wdX, f"step {step} dX")
+        assert_same(dW, wdW, f"step {step} dW")
+        ie.ie_sgd_update(Wd, Vd, dW, wl.LR, wl.MOMENTUM, ws=ws)
+        W, V = o.sgd_update(W, V, wdW, o.Scalar(*wl.LR), o.Scalar(*wl.MOMENTUM))
+        assert_same(Wd, W, f"step {step} W")
+        assert_same(Vd, V, f"step {step} V")
+    assert ws.status() == 0
+
+
+# ---------------------------------------------------------------------------
+# ResNet-18 3x3 convolutions, batch 128 (the benchmark's workload)
+# ---------------------------------------------------------------------------
+
+R18 = wl.resnet18_cifar_layers(128)
+
+
+@pytest.mark.parametrize("li", range(len(R18)), ids=[L.name for L in R18])
+def test_resnet18_layer(li, ws):
+    L = R18[li]
+    announce(f"config resnet18 {L.name} batch 128: fwd, dgrad, wgrad, update")
+    inp = wl.resnet18_conv_inputs(L, 2001 + li)
+    d = o.ConvShape(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+    dd = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+    X, W, dY = _qt(inp.X), _qt(inp.W), _qt(inp.dY)
+    M, N, K = L.gemm_mnk()
+    Xd = to_dev(X.mant, X.exp, X.group, rows=L.n * L.h * L.w)
+    Wd = to_dev(W.mant, W.exp, W.group)
+    dYd = to_dev(dY.mant, dY.exp, dY.group, rows=M)
+    Y = ie.Mat.empty(M, N, o.TENSOR)
+    ie.ie_conv_fwd(dd, Xd, Wd, Y, ws)
+    assert_same(Y, o.conv_fwd(d, X, W, o.TENSOR), "conv fwd")
+    dX = None if L.first else ie.Mat.empty(L.n * L.h * L.w, L.c, o.TENSOR)
+    dW = ie.Mat.empty(N, K, o.ROW)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, dW, ws)
+    if dX is not None:
+        assert_same(dX, o.conv_dgrad(d, dY, W, o.TENSOR), "conv dgrad")
+    wdW = o.conv_wgrad(d, dY, X, o.ROW)
+    assert_same(dW, wdW, "conv wgrad")
+    upd = wl.update_inputs(N, K, 52001 + li, w_group=o.TENSOR)
+    V = _qt(upd.V)
+    Vd = to_dev(V.mant, V.exp, V.group)
+    ie.ie_sgd_update(Wd, Vd, dW, wl.LR, wl.MOMENTUM, ws=ws)
+    W2, V2 = o.sgd_update(W, V, wdW, o.Scalar(*wl.LR), o.Scalar(*wl.MOMENTUM))
+    assert_same(Vd, V2, "velocity")
+    assert_same(Wd, W2, "weight")
+    assert ws.status() == 0
+
+
+# ---------------------------------------------------------------------------
+# ViT block linears (per-row activation groups, per-channel weight groups)
+# ---------------------------------------------------------------------------
+
+def _vit_case(L, seed, ws, sample):
+    inp = wl.vit_linear_inputs(L, seed)
+    X, W, dY = _qt(inp.X), _qt(inp.W), _qt(inp.dY)
+    Xd, Wd, dYd = to_dev(X.mant, X.exp, X.group), to_dev(W.mant, W.exp, W.group), to_dev(dY.mant, dY.exp, dY.group)
+    rows = _sample_rows(L.m, sample, seed)
+    Y = ie.Mat.empty(L.m, L.n, o.ROW)
+    ie.ie_linear_fwd(Xd, Wd, Y, ws)
+    _assert_rows(Y, rows, o.linear_fwd(_rows_qt(X, rows), W, o.ROW), f"{L.name} fwd")
+    dX = ie.Mat.empty(L.m, L.k, o.ROW)
+    ie.ie_linear_bwd_dx(dYd, Wd, dX, ws)
+    _assert_rows(dX, rows, o.linear_bwd_dx(_rows_qt(dY, rows), W, o.ROW), f"{L.name} dX")
+    dW = ie.Mat.empty(L.n, L.k, o.ROW)
+    ie.ie_linear_bwd_dw(dYd, Xd, dW, ws)
+    assert_same(dW, o.linear_bwd_dw(dY, X, o.ROW), f"{L.name} dW")
+    assert ws.status() == 0
+
+
+VITTI = wl.vit_ti_linears(256)
+VITB = wl.vit_b_linears(128)
+
+
+@pytest.mark.parametrize("li", range(4), ids=[L.name for L in VITTI])
+def test_vit_ti_linear(li, ws):
+    L = VITTI[li]
+    announce(f"config vit-ti {L.name} M={L.m} N={L.n} K={L.k}")
+    _vit_case(L, 3001 + li, ws, 512)
+
+
+@pytest.mark.parametrize("li", range(4), ids=[L.name for L in VITB])
+def test_vit_b_linear(li, ws):
+    L = VITB[li]
+    announce(f"config vit-b {L.name} M={L.m} N={L.n} K={L.k}")
+    _vit_case(L, 5001 + li, ws, 512)
+
+
+@pytest.mark.parametrize("arena", range(2))
+def test_vit_b_update(arena, ws):
+    rows, cols = wl.vit_b_param_arenas()[arena]
+    announce(f"config vit-b update arena {rows}x{cols}")
+    upd = wl.update_inputs(rows, cols, 6000 + arena)
+    W, V, G = _qt(upd.W), _qt(upd.V), _qt(upd.G)
+    Wd, Vd, Gd = to_dev(W.mant, W.exp, W.group), to_dev(V.mant, V.exp, V.group), to_dev(G.mant, G.exp, G.group)
+    ie.ie_sgd_update(Wd, Vd, Gd, wl.LR, wl.MOMENTUM, ws=ws)
+    sel = _sample_rows(rows, 2048, arena)
+    W2, V2 = o.sgd_update(_rows_qt(W, sel), _rows_qt(V, sel), _rows_qt(G, sel), o.Scalar(*wl.LR),
+                          o.Scalar(*wl.MOMENTUM))
+    _assert_rows(Vd, sel, V2, "velocity")
+    _assert_rows(Wd, sel, W2, "weight")
+    assert ws.status() == 0
+
+
+# ---------------------------------------------------------------------------
+# ResNet-50 bottleneck convolutions (per-channel weight exponents)
+# ---------------------------------------------------------------------------
+
+R50 = {L.name: L for L in wl.resnet50_layers(128)}
+R50_PICK = ["s1_3x3_64@56", "s2_3x3_128_s2@56", "s3_1x1_1024_256@14", "s4_1x1_512_2048@7", "s4_sc_1024_2048_s2@14"]
+
+
+@pytest.mark.parametrize("name", R50_PICK)
+def test_resnet50_layer(name, ws):
+    L = R50[name]
+    announce(f"config resnet50 {name} batch 128: fwd, dgrad, wgrad")
+    inp = wl.resnet50_conv_inputs(L, 4001 + R50_PICK.index(name))
+    d = o.ConvShape(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+    dd = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
+    X, W, dY = _qt(inp.X), _qt(inp.W), _qt(inp.dY)
+    M, N, K = L.gemm_mnk()
+    Xd = to_dev(X.mant, X.exp, X.group, rows=L.n * L.h * L.w)
+    Wd = to_dev(W.mant, W.exp, W.group)
+    dYd = to_dev(dY.mant, dY.exp, dY.group, rows=M)
+    Y = ie.Mat.empty(M, N, o.TENSOR)
+    ie.ie_conv_fwd(dd, Xd, Wd, Y, ws)
+    assert_same(Y, o.conv_fwd(d, X, W, o.TENSOR), "conv fwd")
+    dX = ie.Mat.empty(L.n * L.h * L.w, L.c, o.TENSOR)
+    dW = ie.Mat.empty(N, K, o.ROW)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, dW, ws)
+    assert_same(dX, o.conv_dgrad(d, dY, W, o.TENSOR), "conv dgrad")
+    assert_same(dW, o.conv_wgrad(d, dY, X, o.ROW), "conv wgrad")
+    assert ws.status() == 0
