@@ -94,129 +94,249 @@ __device__ __forceinline__ int sum_round(bool narrow, int X, int pa, int Y, int 
     return sum_round_wide(X, pa, Y, pb, e);
 }
 
-// pass 0: whole-tensor velocity, raise gneed_v with the velocity's needs.
-// pass 1: velocity and (row-grouped) weight step; for a whole-tensor weight,
-//         store V' and raise gneed_w.
-// pass 2: whole-tensor weight, round W with gneed_w.
-template <int D>
+// Rounding of a row with one uniform shift: n * 2^-sh, half to even
+// (sh <= 0: exact left shift); |n| < 2^30.
+struct RneU {
+    int sh;
+    int hm1;
+    int left;
+    bool is_left;
+};
+
+__device__ __forceinline__ RneU rne_u(int sh) {
+    RneU r;
+    r.is_left = sh <= 0;
+    r.left = sh <= 0 ? -sh : 0;
+    r.sh = sh > 31 ? 31 : (sh < 1 ? 1 : sh);
+    r.hm1 = (1 << (r.sh - 1)) - 1;
+    return r;
+}
+
+__device__ __forceinline__ int rne_apply(int n, const RneU &r, bool left) {
+    if (left) return n << r.left;
+    const int bit = (n >> r.sh) & 1;
+    return (n + r.hm1 + bit) >> r.sh;
+}
+
+__device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+// One row of W, V, G is owned by WPR waves (WPR = 1: four rows per block;
+// WPR = 4: one row per block, maxima combined through LDS).  Each lane holds D
+// dwords (4 D bytes) of each tensor.
+//   pass 0: whole-tensor velocity: raise gneed_v with the velocity's needs.
+//   pass 1: velocity step; weight step for row-grouped W, otherwise store V'
+//           and raise gneed_w.
+//   pass 2: whole-tensor weight: round W with gneed_w.
+template <int D, int WPR>
 __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec, const int *old_ev,
                                                       const int *old_ew) {
+    constexpr int RPB = 4 / WPR;  // rows per block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int sub = wave % WPR;
+    __shared__ uint32_t red[2][4];
+    int parity = 0;
+    // maximum over the row (all WPR waves); every wave of the block calls it
+    auto row_umax = [&](uint32_t v) -> uint32_t {
+        v = umax_wave(v);
+        if constexpr (WPR > 1) {
+            if (lane == 0) red[parity][sub] = v;
+            __syncthreads();
+            v = max(max(red[parity][0], red[parity][1]), max(red[parity][2], red[parity][3]));
+            parity ^= 1;
+        }
+        return v;
+    };
+    auto row_imax = [&](int v) -> int { return (int)(row_umax((uint32_t)(v ^ (int)0x80000000)) ^ 0x80000000u); };
     const bool v_tensor = a.v_row == 0, w_tensor = a.w_row == 0;
-    for (long long row = (long long)blockIdx.x * 4 + wave; row < a.rows; row += (long long)gridDim.x * 4) {
+
+    for (long long row0 = (long long)blockIdx.x * RPB; row0 < a.rows; row0 += (long long)gridDim.x * RPB) {
+        const long long row = row0 + wave / WPR;
+        const bool live = row < a.rows;  // WPR = 1 only: trailing waves of the last block
+        if (WPR == 1 && !live) continue;
         const long long off = row * a.cols;
         uint32_t W[D], V[D], G[D];
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            long long col = 4ll * (lane + 64 * j);
+            const long long col = 4ll * (lane + 64 * (sub + WPR * j));
             W[j] = (pass != 0) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
             V[j] = load_dw(a.v + off, col, a.cols, vec);
             G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
         }
         const int ew = w_tensor ? *old_ew : (int)a.w_exp[row];
+
+        // ---- weight step only (whole-tensor weight, second pass) ----
         if (pass == 2) {
-            // V already holds V' with its new exponent
             const int evn = v_tensor ? clamp_exp_flag(max(E_MIN, *a.gneed_v), a.flags) : (int)a.v_exp[row];
-            const int pb = a.lr_e + evn;
-            const bool nw = abs(ew - pb) <= 15;
+            const int pw = a.lr_e + evn;
             const int e = clamp_exp_flag(max(E_MIN, *a.gneed_w), a.flags);
+            if (abs(ew - pw) <= 15) {
+                const int base = min(ew, pw);
+                const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
+                const RneU r = rne_u(e - base);
+                const bool left = r.is_left;
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                uint32_t o = 0;
+                for (int j = 0; j < D; ++j) {
+                    uint32_t o = 0;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    int c = sum_round(nw, sbyte(W[j], t), ew, -a.lr_m * sbyte(V[j], t), pb, e);
-                    o |= (uint32_t)(uint8_t)c << (8 * t);
+                    for (int t = 0; t < 4; ++t) {
+                        const int n = sbyte(W[j], t) * fa + sbyte(V[j], t) * fb;
+                        o |= (uint32_t)(uint8_t)rne_apply(n, r, left) << (8 * t);
+                    }
+                    store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
                 }
-                store_dw(a.w + off, 4ll * (lane + 64 * j), a.cols, vec, o);
+            } else {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    uint32_t o = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int c = sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * sbyte(V[j], t), pw, e);
+                        o |= (uint32_t)(uint8_t)c << (8 * t);
+                    }
+                    store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
+                }
             }
-            if (row == 0 && lane == 0) a.w_exp[0] = (int8_t)e;
+            if (row == 0 && lane == 0 && sub == 0) a.w_exp[0] = (int8_t)e;
             continue;
         }
+
+        // ---- velocity: v = momentum * V + G ----
         const int ev = v_tensor ? *old_ev : (int)a.v_exp[row];
         const int eg = a.g_row ? (int)a.g_exp[row] : (int)a.g_exp[0];
         const int pa = ev + a.mom_e, pb = eg;
         const bool nv = abs(pa - pb) <= 15;
-        int m = NEED_NONE;
+        int vn[D][4];
+        int needv;
+        if (nv) {
+            const int base = min(pa, pb);
+            const int fa = a.mom_m * (1 << (pa - base)), fb = 1 << (pb - base);
+            uint32_t mx = 0;
 #pragma unroll
-        for (int j = 0; j < D; ++j)
+            for (int j = 0; j < D; ++j)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                m = max(m, sum_need(nv, a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+                for (int t = 0; t < 4; ++t) {
+                    const int n = sbyte(V[j], t) * fa + sbyte(G[j], t) * fb;
+                    vn[j][t] = n;
+                    mx = max(mx, (uint32_t)(n < 0 ? -n : n));
+                }
+            mx = row_umax(mx);
+            needv = mx ? base + mant_shift32(mx) : NEED_NONE;
+        } else {
+            int m = NEED_NONE;
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+            needv = row_imax(m);
+        }
         if (pass == 0) {
-            m = wave_max64(m);
-            if (lane == 0 && m != NEED_NONE && m > __atomic_load_n(a.gneed_v, __ATOMIC_RELAXED)) atomicMax(a.gneed_v, m);
+            if (lane == 0 && sub == 0 && needv != NEED_NONE && needv > __atomic_load_n(a.gneed_v, __ATOMIC_RELAXED))
+                atomicMax(a.gneed_v, needv);
             continue;
         }
-        int evn;
-        if (v_tensor) {
-            evn = clamp_exp_flag(max(E_MIN, *a.gneed_v), a.flags);
+        const int evn = v_tensor ? clamp_exp_flag(max(E_MIN, *a.gneed_v), a.flags)
+                                 : clamp_exp_flag(max(E_MIN, needv), a.flags);
+        int c[D][4];
+        if (nv) {
+            const RneU r = rne_u(evn - min(pa, pb));
+            const bool left = r.is_left;
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) c[j][t] = rne_apply(vn[j][t], r, left);
         } else {
-            evn = clamp_exp_flag(max(E_MIN, wave_max64(m)), a.flags);
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
         }
-        // V' and the weight step's needs
-        const int pw = a.lr_e + evn;
-        const bool nw = abs(ew - pw) <= 15;
-        uint32_t Vn[D];
-        int mw = NEED_NONE;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            uint32_t o = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                int c = sum_round(nv, a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
-                o |= (uint32_t)(uint8_t)c << (8 * t);
-                mw = max(mw, sum_need(nw, sbyte(W[j], t), ew, -a.lr_m * c, pw));
-            }
-            Vn[j] = o;
+            const uint32_t o = (uint32_t)(uint8_t)c[j][0] | ((uint32_t)(uint8_t)c[j][1] << 8) |
+                               ((uint32_t)(uint8_t)c[j][2] << 16) | ((uint32_t)(uint8_t)c[j][3] << 24);
+            store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
         }
-#pragma unroll
-        for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * j), a.cols, vec, Vn[j]);
-        if (lane == 0) {
+        if (lane == 0 && sub == 0) {
             if (!v_tensor) a.v_exp[row] = (int8_t)evn;
             else if (row == 0) a.v_exp[0] = (int8_t)evn;
         }
-        mw = wave_max64(mw);
+
+        // ---- weight: w = W - lr * V' ----
+        const int pw = a.lr_e + evn;
+        const bool nw = abs(ew - pw) <= 15;
+        int needw;
+        if (nw) {
+            const int base = min(ew, pw);
+            const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
+            uint32_t mx = 0;
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int n = sbyte(W[j], t) * fa + c[j][t] * fb;
+                    vn[j][t] = n;
+                    mx = max(mx, (uint32_t)(n < 0 ? -n : n));
+                }
+            mx = row_umax(mx);
+            needw = mx ? base + mant_shift32(mx) : NEED_NONE;
+        } else {
+            int m = NEED_NONE;
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw));
+            needw = row_imax(m);
+        }
         if (w_tensor) {
-            if (lane == 0 && mw != NEED_NONE && mw > __atomic_load_n(a.gneed_w, __ATOMIC_RELAXED)) atomicMax(a.gneed_w, mw);
+            if (lane == 0 && sub == 0 && needw != NEED_NONE && needw > __atomic_load_n(a.gneed_w, __ATOMIC_RELAXED))
+                atomicMax(a.gneed_w, needw);
             continue;
         }
-        const int ewn = clamp_exp_flag(max(E_MIN, mw), a.flags);
+        const int ewn = clamp_exp_flag(max(E_MIN, needw), a.flags);
+        if (nw) {
+            const RneU r = rne_u(ewn - min(ew, pw));
+            const bool left = r.is_left;
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            uint32_t o = 0;
+            for (int j = 0; j < D; ++j) {
+                uint32_t o = 0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                int c = sum_round(nw, sbyte(W[j], t), ew, -a.lr_m * sbyte(Vn[j], t), pw, ewn);
-                o |= (uint32_t)(uint8_t)c << (8 * t);
+                for (int t = 0; t < 4; ++t) o |= (uint32_t)(uint8_t)rne_apply(vn[j][t], r, left) << (8 * t);
+                store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
             }
-            store_dw(a.w + off, 4ll * (lane + 64 * j), a.cols, vec, o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                uint32_t o = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    o |= (uint32_t)(uint8_t)sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, ewn) << (8 * t);
+                store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
+            }
         }
-        if (lane == 0) a.w_exp[row] = (int8_t)ewn;
+        if (lane == 0 && sub == 0) a.w_exp[row] = (int8_t)ewn;
     }
 }
 
-template <int D>
+template <int D, int WPR>
 static hipError_t run_passes(const UpdateArgs &a, int vec, const int *old_ev, const int *old_ew, hipStream_t st) {
-    long long blocks = (a.rows + 3) / 4;
+    constexpr int RPB = 4 / WPR;
+    long long blocks = (a.rows + RPB - 1) / RPB;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     hipError_t err;
-    if (a.v_row == 0) {
+    for (int pass = 0; pass < 3; ++pass) {
+        if (pass == 0 && a.v_row) continue;
+        if (pass == 2 && a.w_row) continue;
         prof_begin(st);
-        hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 0, vec, old_ev, old_ew);
-        prof_end(st, 2000 + 0);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    prof_begin(st);
-    hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 1, vec, old_ev, old_ew);
-    prof_end(st, 2000 + 1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.w_row == 0) {
-        prof_begin(st);
-        hipLaunchKernelGGL((sgd_rows_kernel<D>), dim3((int)blocks), dim3(256), 0, st, a, 2, vec, old_ev, old_ew);
-        prof_end(st, 2000 + 2);
+        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR>), dim3((int)blocks), dim3(256), 0, st, a, pass, vec, old_ev,
+                           old_ew);
+        prof_end(st, 2000 + pass);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
@@ -237,21 +357,29 @@ hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
         if (a.w_row == 0 && (err = launch_fill_i8(a.w_exp, 1, E_MIN, st)) != hipSuccess) return err;
         return hipSuccess;
     }
-    int vec = (a.cols % 4 == 0) && ((uintptr_t)a.w % 4 == 0) && ((uintptr_t)a.v % 4 == 0) &&
-              ((uintptr_t)a.g % 4 == 0);
-    long long dw = (a.cols + 3) / 4;
-    long long per_lane = (dw + 63) / 64;
-    if (per_lane <= 1) return run_passes<1>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 2) return run_passes<2>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 3) return run_passes<3>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 4) return run_passes<4>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 6) return run_passes<6>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 8) return run_passes<8>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 12) return run_passes<12>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 16) return run_passes<16>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 18) return run_passes<18>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 24) return run_passes<24>(a, vec, old_ev, old_ew, st);
-    if (per_lane <= 32) return run_passes<32>(a, vec, old_ev, old_ew, st);
+    const int vec = (a.cols % 4 == 0) && ((uintptr_t)a.w % 4 == 0) && ((uintptr_t)a.v % 4 == 0) &&
+                    ((uintptr_t)a.g % 4 == 0);
+    const long long dw = (a.cols + 3) / 4;
+    // Rows of 256 dwords or more: four waves share a row (one row per block),
+    // so a lane holds at most 8 dwords of each tensor up to 8192 columns.
+    const bool wide = dw >= 256;
+    const long long per_lane = wide ? (dw + 255) / 256 : (dw + 63) / 64;
+#define IE_UPD(DD, WW)                                                                                     \
+    if (per_lane <= DD) return run_passes<DD, WW>(a, vec, old_ev, old_ew, st);
+    if (!wide) {
+        IE_UPD(1, 1)
+        IE_UPD(2, 1)
+        IE_UPD(3, 1)
+        IE_UPD(4, 1)
+    } else {
+        IE_UPD(1, 4)
+        IE_UPD(2, 4)
+        IE_UPD(3, 4)
+        IE_UPD(4, 4)
+        IE_UPD(6, 4)
+        IE_UPD(8, 4)
+    }
+#undef IE_UPD
     return hipErrorInvalidValue;
 }
 
