@@ -160,8 +160,9 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
 
 /*
  * Kernel timing, for diagnostics and benchmarks.  While enabled, the launch
- * of every contraction, finalize and update kernel is bracketed by two HIP
- * events recorded on the launch's stream.  ie_profile_read waits for the
+ * of every contraction, finalize and update kernel (or, after
+ * ie_profile_select(kind) with kind != 0, of the kernels of that kind only)
+ * is bracketed by two HIP events recorded on the launch's stream.  ie_profile_read waits for the
  * recorded events, writes up to `max` records in launch order (elapsed
  * milliseconds and a kernel-kind code: 10000*(10*mi + ni) + 1000 +
  * 100*epilogue + 10*loader_A + loader_B for contractions with a
@@ -172,6 +173,7 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * This is the library's only process-wide state; it is not thread-safe.
  */
 ie_status ie_profile_enable(int on);
+ie_status ie_profile_select(int kind);
 int ie_profile_read(float *ms, int *kind, int max);
 
 /* Human-readable name of a status code. */

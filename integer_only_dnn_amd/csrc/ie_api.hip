@@ -119,6 +119,14 @@ bool forced_plan(long long K, Plan &pl) {
     return true;
 }
 
+// Diagnostics: IE_PLAN_LOG set prints every planned product to stderr.
+void log_plan(const char *what, long long M, long long N, long long K, const Plan &pl) {
+    static const bool on = getenv("IE_PLAN_LOG") != nullptr;
+    if (!on) return;
+    fprintf(stderr, "[ie plan] %s M=%lld N=%lld K=%lld tile=%dx%d mode=%d splits=%d k_chunk=%d\n", what, M, N, K,
+            pl.t.bm(), pl.t.bn(), pl.mode, pl.splits, pl.k_chunk);
+}
+
 // family: 0 = dense K-major, 1 = convolution (im2col / dgrad)
 Plan plan_product(long long M, long long N, long long K, int row_group, int family) {
     {
@@ -166,6 +174,14 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
 // Weight gradients: always split over the contraction in chunks of at most
 // 65536 rows (exact int32 partial sums).
 Plan plan_wgrad(long long M, long long N, long long L) {
+    if (const char *v = getenv("IE_WTILE")) {
+        // tuning override: IE_WTILE="mi,ni,splits"
+        int mi = 0, ni = 0, sp = 1;
+        if (sscanf(v, "%d,%d,%d", &mi, &ni, &sp) == 3 && sp >= 1) {
+            int kc = chunk_for(L, sp);
+            if (kc <= SPLIT_MAX_ROWS) return Plan{Tile{mi, ni}, PLAN_SPLIT, (int)((L + kc - 1) / kc), kc};
+        }
+    }
     Plan best{WGRAD_TILES[0], PLAN_SPLIT, 1, chunk_for(L, 1)};
     double bt = 1e30;
     int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
@@ -227,7 +243,13 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
         return hip_status(launch_fill_i8(out->exp, out->group == IE_GROUP_ROW ? M : 1, E_MIN, st));
     }
     const int rg = out->group == IE_GROUP_ROW;
+    if (K == 0) {
+        // empty contraction: every result is zero, every group at E_MIN
+        IE_TRY(launch_fill_i8(out->mant, M * N, 0, st));
+        return hip_status(launch_fill_i8(out->exp, rg ? M : 1, E_MIN, st));
+    }
     Plan pl = plan_product(M, N, K, rg, family);
+    log_plan(family ? "conv" : "dense", M, N, K, pl);
     Epi ep;
     memset(&ep, 0, sizeof ep);
     ep.ea = ea;
@@ -245,15 +267,20 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
         ep.mode = EPI_RTO;
         ep.v16 = pw.v16;
         ep.p16 = pw.p16;
-        ep.gneed = pw.gneed;
-        IE_TRY(launch_fill_i32(pw.gneed, rg ? M : 1, NEED_NONE, st));
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
-        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, pw.gneed, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags,
-                                   st));
+        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st));
         return IE_OK;
     }
     ep.partial = pw.partial;
     ep.split_stride = M * N;
+    if (rg && split_round_rows_fits((int)N, 1, 1)) {
+        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
+        IE_TRY(launch_split_round_rows(pw.partial, pl.splits, M * N, (int)M, (int)N, (int)N, 1, 1, ea, eb, out->mant,
+                                       out->exp, flags, st));
+        return IE_OK;
+    }
+    ep.gneed = pw.gneed;
+    ep.gneed_n = rg ? (int)M : 1;
     IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
     IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed, st));
     IE_TRY(launch_round_sums(pw.sums, (int)M, (int)N, (int)N, 1, 1, ea, eb, rg, pw.gneed, out->mant, out->exp, flags,
@@ -265,7 +292,7 @@ struct WgradWs {
     int *partial;
     long long *sums;
     int *gneed;
-    int *eps;  // [2]
+    int *eps;  // [2]: common exponents of row-grouped operands
 };
 
 // Weight gradient [N x Kg] contracted over L rows; the stored output is
@@ -282,25 +309,35 @@ WgradWs carve_wgrad(Carve &c, long long N, long long Kg, long long L) {
 }
 
 ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long Kg, long long Kout, int mc, int mcp,
-                    long long L, const ie_mat *dW, const WgradWs &w, uint32_t *flags, hipStream_t st) {
+                    long long L, ExpSrc ea, ExpSrc eb, const ie_mat *dW, const WgradWs &w, uint32_t *flags,
+                    hipStream_t st) {
     if (N == 0 || Kout == 0) {
         return hip_status(launch_fill_i8(dW->exp, dW->group == IE_GROUP_ROW ? N : 1, E_MIN, st));
     }
     Plan pl = plan_wgrad(N, Kg, L);
+    log_plan("wgrad", N, Kg, L, pl);
     Epi ep;
     memset(&ep, 0, sizeof ep);
+    const int rg = dW->group == IE_GROUP_ROW;
+    const bool fused = rg && split_round_rows_fits((int)Kout, mc, mcp);
     ep.partial = w.partial;
     ep.split_stride = N * Kg;
     ep.flags = flags;
+    ep.gneed = w.gneed;
+    ep.gneed_n = fused ? 0 : rg ? (int)N : 1;
     int splits = pl.splits;
     if (L == 0) {
         IE_TRY(launch_fill_i32(w.partial, N * Kg, 0, st));
+        IE_TRY(launch_fill_i32(w.gneed, rg ? N : 1, NEED_NONE, st));
         splits = 1;
     } else {
         IE_TRY(launch_gemm(A, B, (int)N, (int)Kg, (int)L, pl.t, pl.splits, pl.k_chunk, true, ep, st));
     }
-    const int rg = dW->group == IE_GROUP_ROW;
-    ExpSrc ea{nullptr, w.eps, 0}, eb{nullptr, w.eps + 1, 0};
+    if (fused) {
+        IE_TRY(launch_split_round_rows(w.partial, splits, N * Kg, (int)N, (int)Kout, (int)Kg, mc, mcp, ea, eb,
+                                       dW->mant, dW->exp, flags, st));
+        return IE_OK;
+    }
     IE_TRY(launch_partial_reduce(w.partial, splits, N * Kg, (int)N, (int)Kg, ea, eb, rg, w.sums, w.gneed, st));
     IE_TRY(launch_round_sums(w.sums, (int)N, (int)Kout, (int)Kg, mc, mcp, ea, eb, rg, w.gneed, dW->mant, dW->exp,
                              flags, st));
@@ -331,6 +368,7 @@ ConvGeom geom(const ie_conv_desc *d) {
     g.dc = make_fastdiv((uint32_t)g.cp);
     g.ds = make_fastdiv((uint32_t)g.s);
     g.dk = make_fastdiv((uint32_t)g.kp);
+    g.dst = make_fastdiv((uint32_t)g.stride);
     return g;
 }
 
@@ -422,7 +460,7 @@ size_t ie_conv_bwd_workspace(const ie_conv_desc *d) {
 size_t ie_sgd_update_workspace(int64_t rows, int64_t cols) {
     (void)rows;
     (void)cols;
-    return HEADER + 256;
+    return HEADER + align256(UPD_WS_INTS * sizeof(int));
 }
 
 ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -482,8 +520,7 @@ ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, 
     int8_t *dyp = Np != N ? c.take<int8_t>((size_t)M * Np) : nullptr;
     ProductWs pw = carve_product(c, M, K, Np, 0);
     if (M == 0 || K == 0) return run_product(Operand{}, Operand{}, M, K, Np, ExpSrc{}, ExpSrc{}, dX, pw, flags, 0, st);
-    IE_TRY(launch_exp_max(W->exp, n_exps(W), estar, st));
-    IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, (int)N, 1, (int)K, (int)Np, wt,
+    IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, (int)N, 1, (int)K, (int)Np, wt, estar,
                                   st));
     const int8_t *dys = dY->mant;
     if (dyp) {
@@ -514,13 +551,18 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, 
     int8_t *dya = c.take<int8_t>((size_t)M * Np);
     int8_t *xa = c.take<int8_t>((size_t)M * Kp);
     WgradWs w = carve_wgrad(c, N, K, M);
-    if (N == 0 || K == 0) return run_wgrad(Operand{}, Operand{}, N, K, K, 1, 1, M, dW, w, flags, st);
+    if (N == 0 || K == 0)
+        return run_wgrad(Operand{}, Operand{}, N, K, K, 1, 1, M, ExpSrc{}, ExpSrc{}, dW, w, flags, st);
     // common exponents over the contraction axis (rows); align ROW operands,
     // pad rows to multiples of 16
-    IE_TRY(launch_exp_max(dY->exp, n_exps(dY), w.eps, st));
-    IE_TRY(launch_exp_max(X->exp, n_exps(X), w.eps + 1, st));
     const int8_t *dys = dY->mant, *xs = X->mant;
     const bool dy_row = dY->group == IE_GROUP_ROW, x_row = X->group == IE_GROUP_ROW;
+    ExpSrc ea{dY->exp, nullptr, 0}, eb{X->exp, nullptr, 0};
+    if (dy_row || x_row) {
+        IE_TRY(launch_exp_max2(dY->exp, n_exps(dY), w.eps, X->exp, n_exps(X), w.eps + 1, st));
+        ea = ExpSrc{nullptr, w.eps, 0};
+        eb = ExpSrc{nullptr, w.eps + 1, 0};
+    }
     if ((dy_row || Np != N) && M > 0) {
         IE_TRY(launch_pad_rows(dY->mant, M, N, dY->exp, dy_row, dy_row ? w.eps : nullptr, Np, dya, st));
         dys = dya;
@@ -531,7 +573,7 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, 
     }
     Operand A{LD_T, dys, Np, (int)N, {}};
     Operand B{LD_T, xs, Kp, (int)K, {}};
-    return run_wgrad(A, B, N, K, K, 1, 1, M, dW, w, flags, st);
+    return run_wgrad(A, B, N, K, K, 1, 1, M, ea, eb, dW, w, flags, st);
 }
 
 ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
@@ -610,9 +652,8 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
         dys = dyp;
     }
     if (dX) {
-        IE_TRY(launch_exp_max(W->exp, n_exps(W), estar, st));
-        IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, estar, g.k, g.r * g.s, g.c, g.kp,
-                                      wt, st));
+        IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, g.k, g.r * g.s, g.c, g.kp, wt,
+                                      estar, st));
         Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
         Operand B{LD_K, wt, rskp, g.c, {}};
         ExpSrc ea{dY->exp, nullptr, 0};
@@ -625,11 +666,10 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
             IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
             xs = xp;
         }
-        IE_TRY(launch_exp_max(dY->exp, 1, w.eps, st));
-        IE_TRY(launch_exp_max(X->exp, 1, w.eps + 1, st));
         Operand A{LD_T, dys, g.kp, g.k, {}};
         Operand B{LD_IM2COL_T, xs, g.cp, (int)rscp, g};
-        IE_CHECK(run_wgrad(A, B, g.k, rscp, rsc, g.c, g.cp, npq, dW, w, flags, st));
+        IE_CHECK(run_wgrad(A, B, g.k, rscp, rsc, g.c, g.cp, npq, ExpSrc{dY->exp, nullptr, 0},
+                           ExpSrc{X->exp, nullptr, 0}, dW, w, flags, st));
     }
     return IE_OK;
 }
@@ -647,7 +687,7 @@ ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sc
     if (ws_bytes < ie_sgd_update_workspace(W->rows, W->cols)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws, HEADER};
-    int *gn = c.take<int>(4);
+    int *tmp = c.take<int>(UPD_WS_INTS);
     UpdateArgs a;
     a.w = W->mant;
     a.w_exp = W->exp;
@@ -664,8 +704,7 @@ ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sc
     a.lr_e = lr.exp;
     a.mom_m = momentum.mant;
     a.mom_e = momentum.exp;
-    a.gneed_v = gn;
-    a.gneed_w = gn + 1;
+    a.tmp = tmp;
     a.flags = (uint32_t *)ws;
     return hip_status(launch_sgd_update(a, st));
 }
@@ -684,6 +723,11 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {
 
 ie_status ie_profile_enable(int on) {
     prof_enable(on);
+    return IE_OK;
+}
+
+ie_status ie_profile_select(int kind) {
+    prof_select(kind);
     return IE_OK;
 }
 

@@ -23,6 +23,7 @@ struct ProfRec {
     int kind;
 };
 bool g_prof_on = false;
+int g_prof_sel = 0;
 std::vector<hipEvent_t> g_pool;
 std::vector<ProfRec> g_recs;
 hipEvent_t g_pending = nullptr;
@@ -39,20 +40,22 @@ hipEvent_t take_event() {
 }
 }  // namespace
 
-void prof_begin(hipStream_t st) {
-    if (!g_prof_on) return;
+void prof_begin(hipStream_t st, int kind) {
+    if (!g_prof_on || (g_prof_sel && kind != g_prof_sel)) return;
     g_pending = take_event();
     if (g_pending) (void)hipEventRecord(g_pending, st);
 }
 
 void prof_end(hipStream_t st, int kind) {
-    if (!g_prof_on || !g_pending) return;
+    if (!g_prof_on || !g_pending || (g_prof_sel && kind != g_prof_sel)) return;
     hipEvent_t e = take_event();
     if (!e) return;
     (void)hipEventRecord(e, st);
     g_recs.push_back({g_pending, e, kind});
     g_pending = nullptr;
 }
+
+void prof_select(int kind) { g_prof_sel = kind; }
 
 void prof_enable(int on) {
     g_prof_on = on != 0;
@@ -134,17 +137,36 @@ __device__ __forceinline__ int block_max256(int v, int *sh) {
     return max(max(sh[0], sh[1]), max(sh[2], sh[3]));
 }
 
-// out[0] = largest of n int8 exponents (E_MIN when n == 0).
-__global__ __launch_bounds__(256) void exp_max_kernel(const int8_t *e, long long n, int *out) {
-    __shared__ int sh[4];
+// Largest of n int8 exponents (E_MIN when n == 0), by one block: four
+// bytes per load when the array is 4-byte aligned.
+__device__ int exp_max_block(const int8_t *e, long long n, int *sh) {
     int m = E_MIN;
-    for (long long i = threadIdx.x; i < n; i += 256) m = max(m, (int)e[i]);
-    m = block_max256(m, sh);
-    if (threadIdx.x == 0) out[0] = m;
+    long long i0 = 0;
+    if (((uintptr_t)e & 3) == 0) {
+        const long long nw = n >> 2;
+        const int *w = (const int *)e;
+#pragma unroll 4
+        for (long long i = threadIdx.x; i < nw; i += blockDim.x) {
+            const int v = w[i];
+            m = max(m, max(max((int)(int8_t)v, (int)(int8_t)(v >> 8)),
+                           max((int)(int8_t)(v >> 16), (int)(int8_t)(v >> 24))));
+        }
+        i0 = nw << 2;
+    }
+    for (long long i = i0 + threadIdx.x; i < n; i += blockDim.x) m = max(m, (int)e[i]);
+    return block_max256(m, sh);
 }
 
-hipError_t launch_exp_max(const int8_t *e, long long n, int *out, hipStream_t st) {
-    hipLaunchKernelGGL(exp_max_kernel, dim3(1), dim3(256), 0, st, e, n, out);
+__global__ __launch_bounds__(256) void exp_max2_kernel(const int8_t *e0, long long n0, int *out0, const int8_t *e1,
+                                                      long long n1, int *out1) {
+    __shared__ int sh[4];
+    const int m = blockIdx.x == 0 ? exp_max_block(e0, n0, sh) : exp_max_block(e1, n1, sh);
+    if (threadIdx.x == 0) (blockIdx.x == 0 ? out0 : out1)[0] = m;
+}
+
+hipError_t launch_exp_max2(const int8_t *e0, long long n0, int *out0, const int8_t *e1, long long n1, int *out1,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(exp_max2_kernel, dim3(out1 ? 2 : 1), dim3(256), 0, st, e0, n0, out0, e1, n1, out1);
     return hipGetLastError();
 }
 
@@ -170,27 +192,29 @@ hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, con
                            const int *estar, long long cols_p, int8_t *out, hipStream_t st) {
     const long long n = rows * cols_p;
     if (n <= 0) return hipSuccess;
-    prof_begin(st);
+    prof_begin(st, PROF_ALIGN);
     hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks_for(n, 256, 16384)), dim3(256), 0, st, in, rows, cols, e,
                        e_row, estar, cols_p, out);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
 
-// w viewed as [A][B][C] (row exponent e[a]): out[c][b][a] = w[a][b][c] at
-// *estar for a < A, zero for A <= a < Ap (output pitch Ap).
-__global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, const int8_t *e, int e_row,
-                                                              const int *estar, int A, int B, int C, int Ap,
-                                                              int8_t *out) {
+// w viewed as [A][B][C] (row exponent e[a], or e[0]): out[c][b][a] =
+// w[a][b][c] at the largest row exponent e*, zero for A <= a < Ap (output
+// pitch Ap).  Every block finds e* itself (A bytes); block 0 stores it.
+__global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, const int8_t *e, int e_row, int A,
+                                                              int B, int C, int Ap, int8_t *out, int *estar_out) {
     __shared__ int8_t tile[64][65];
-    int es = *estar;
+    __shared__ int sh[4];
+    const int es = e_row ? exp_max_block(e, A, sh) : (int)e[0];
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) estar_out[0] = es;
     int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
         int la = i >> 6, lc = i & 63;
         int a = a0 + la, c = c0 + lc;
         int8_t v = 0;
         if (a < A && c < C) {
-            int ea = e_row ? (int)e[a] : (int)e[0];
+            int ea = e_row ? (int)e[a] : es;
             v = (int8_t)rne_shift32(w[((long long)a * B + b) * C + c], es - ea);
         }
         tile[la][lc] = v;
@@ -203,12 +227,12 @@ __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, c
     }
 }
 
-hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, const int *estar, int A, int B,
-                                  int C, int Ap, int8_t *out, hipStream_t st) {
+hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, int A, int B, int C, int Ap,
+                                  int8_t *out, int *estar_out, hipStream_t st) {
     if (Ap <= 0 || B <= 0 || C <= 0) return hipSuccess;
     dim3 grid((C + 63) / 64, (Ap + 63) / 64, B);
-    prof_begin(st);
-    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, estar, A, B, C, Ap, out);
+    prof_begin(st, PROF_ALIGN);
+    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, A, B, C, Ap, out, estar_out);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }
@@ -245,51 +269,111 @@ hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, 
 
 __device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.s); }
 
-__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16,
-                                                           const int *gneed, int M, int N, int bm, int bn,
-                                                           int TM, int n_ct, int row_group, int8_t *out,
-                                                           int8_t *out_exp, uint32_t *flags, int vw,
+// Whole-tensor groups: every block first takes the maximum of all tile
+// needs (T values).  Row groups: a block walks runs of RB rows; the needs of
+// a run (RB * n_ct values) go through LDS and one thread per row reduces them.
+constexpr int FIN_NEEDS = 2048;
+
+__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
+                                                           int bm, int bn, int TM, int n_ct, int row_group, int rb,
+                                                           int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
                                                            FastDiv dper) {
+    __shared__ int sh[4];
+    __shared__ int16_t needs[FIN_NEEDS];
+    __shared__ int rowe[256];
     const uint32_t per_row = N / vw;
-    const uint32_t total = (uint32_t)M * per_row;
-    const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
-    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-        const uint32_t row = fdiv32(i, dper);
-        const int c0 = (int)(i - row * per_row) * vw;
-        const int e = row_group ? clamp_exp_flag(max(E_MIN, gneed[row]), flags) : eT;
-        const int p = row_group ? p16[(long long)row * n_ct + c0 / bn] : p16[row / bm + TM * (c0 / bn)];
-        const int sh = e - p;
-        const long long o = (long long)row * N + c0;
+    auto round8 = [&](long long o, int sh_) {
         if (vw == 8) {
             v4i v = *(const v4i *)(v16 + o);
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 int x = (int)(int16_t)((uint32_t)v[j] & 0xffff), y = (int)(int16_t)((uint32_t)v[j] >> 16);
-                uint32_t b = ((uint32_t)(uint8_t)rne_shift32(x, sh)) | ((uint32_t)(uint8_t)rne_shift32(y, sh) << 8);
+                uint32_t b = ((uint32_t)(uint8_t)rne_shift32(x, sh_)) | ((uint32_t)(uint8_t)rne_shift32(y, sh_) << 8);
                 if (j < 2) lo |= b << (16 * j);
                 else hi |= b << (16 * (j - 2));
             }
             *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
         } else {
-            out[o] = (int8_t)rne_shift32(v16[o], sh);
+            out[o] = (int8_t)rne_shift32(v16[o], sh_);
         }
-        if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
+    };
+    if (!row_group) {
+        const int T = TM * n_ct;
+        int m = NEED_NONE;
+        for (int i = threadIdx.x; i < T; i += 256) {
+            const int v = p16[i];
+            if (v != P_NONE) m = max(m, v);
+        }
+        m = block_max256(m, sh);
+        const int eT = clamp_exp_flag(max(E_MIN, m), flags);
+        const uint32_t total = (uint32_t)M * per_row;
+        for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+            const uint32_t row = fdiv32(i, dper);
+            const int c0 = (int)(i - row * per_row) * vw;
+            const int t = p16[row / bm + TM * (c0 / bn)];
+            round8((long long)row * N + c0, eT - (t == P_NONE ? P_NONE : t - 2));
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
+        return;
     }
-    if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
+    const bool staged = rb * n_ct <= FIN_NEEDS;
+    for (long long r0 = (long long)blockIdx.x * rb; r0 < M; r0 += (long long)gridDim.x * rb) {
+        const int nr = (int)min((long long)rb, M - r0);
+        const int16_t *pr = p16 + r0 * n_ct;
+        if (staged) {
+            for (int i = threadIdx.x; i < nr * n_ct; i += 256) needs[i] = pr[i];
+            __syncthreads();
+            if (threadIdx.x < nr) {
+                int m = NEED_NONE;
+                for (int j = 0; j < n_ct; ++j) {
+                    const int v = needs[threadIdx.x * n_ct + j];
+                    if (v != P_NONE) m = max(m, v);
+                }
+                const int e = clamp_exp_flag(max(E_MIN, m), flags);
+                rowe[threadIdx.x] = e;
+                out_exp[r0 + threadIdx.x] = (int8_t)e;
+            }
+        } else {
+            // one row of more than FIN_NEEDS column tiles
+            int m = NEED_NONE;
+            for (int j = threadIdx.x; j < n_ct; j += 256) {
+                const int v = pr[j];
+                if (v != P_NONE) m = max(m, v);
+            }
+            m = block_max256(m, sh);
+            if (threadIdx.x == 0) {
+                const int e = clamp_exp_flag(max(E_MIN, m), flags);
+                rowe[0] = e;
+                out_exp[r0] = (int8_t)e;
+            }
+        }
+        __syncthreads();
+        const uint32_t cnt = (uint32_t)nr * per_row;
+        for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
+            const uint32_t lr = fdiv32(i, dper);
+            const int c0 = (int)(i - lr * per_row) * vw;
+            const int t = staged ? needs[lr * n_ct + c0 / bn] : pr[c0 / bn];
+            round8((r0 + lr) * N + c0, rowe[lr] - (t == P_NONE ? P_NONE : t - 2));
+        }
+        __syncthreads();
+    }
 }
 
-hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed, int M, int N, Tile t,
-                               int row_group, int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st) {
+hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0) ? 8 : 1;
-    const long long total = (long long)M * (N / vw);
     const int TM = (M + t.bm() - 1) / t.bm();
     const int n_ct = (N + t.bn() - 1) / t.bn();
-    prof_begin(st);
-    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, v16, p16,
-                       gneed, M, N, t.bm(), t.bn(), TM, n_ct, row_group, out, out_exp, flags, vw,
-                       make_fastdiv((uint32_t)(N / vw)));
+    // row runs of about 8192 elements (at most 256 rows)
+    int rb = 8192 / N;
+    rb = rb < 1 ? 1 : (rb > 256 ? 256 : rb);
+    const long long total = (long long)M * (N / vw);
+    const int blocks = row_group ? blocks_for((M + rb - 1) / rb, 1, 8192) : blocks_for(total, 256 * 4, 2048);
+    prof_begin(st, PROF_RTO_FINALIZE);
+    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, M, N, t.bm(), t.bn(), TM,
+                       n_ct, row_group, rb, out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
@@ -420,15 +504,163 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
     if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
 }
 
+// Split-contraction finalize of row groups in one pass.  A block of 512
+// threads owns one output row: the row's nch chunks of vw output columns
+// are summed in int64 over the splits (when the row is short, Q subsets of
+// the splits run side by side and meet in LDS), the row exponent is the
+// largest need, and the row is rounded and stored.
+constexpr int SR_THR = 512;
+constexpr int SR_MAXV = 4;  // chunks per thread when Q == 1
+
+__device__ __forceinline__ int block_max_n(int v, int *sh) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int m = sh[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = max(m, sh[i]);
+    return m;
+}
+
+__global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *partial, int splits, long long stride,
+                                                                 int M, int Nout, int src_pitch, int mc, int mcp,
+                                                                 FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q) {
+    __shared__ int sh[SR_THR / 64];
+    __shared__ long long acc[SR_THR * 4];
+    const int tid = threadIdx.x;
+    const int nch = Nout / vw;
+    auto src_col = [&](int col) -> int {
+        if (mc == mcp) return col;
+        const int g = (int)fdiv32((uint32_t)col, dmc);
+        return g * mcp + (col - g * mc);
+    };
+    for (int row = blockIdx.x; row < M; row += gridDim.x) {
+        const int er = exp_at(ea, row);
+        const int *prow = partial + (long long)row * src_pitch;
+        long long v[SR_MAXV][4];
+        int need = NEED_NONE;
+        if (Q > 1) {
+            // short row: chunk c = tid % nch, split subset q = tid / nch
+            const int c = tid % nch, q = tid / nch;
+            long long a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+            if (q < Q) {
+                if (vw == 4) {
+#pragma unroll 4
+                    for (int z = q; z < splits; z += Q) {
+                        const v4i x = *(const v4i *)(prow + z * stride + 4 * c);
+                        a0 += x[0];
+                        a1 += x[1];
+                        a2 += x[2];
+                        a3 += x[3];
+                    }
+                } else {
+                    const int sc = src_col(c);
+#pragma unroll 4
+                    for (int z = q; z < splits; z += Q) a0 += prow[z * stride + sc];
+                }
+                acc[4 * tid + 0] = a0;
+                acc[4 * tid + 1] = a1;
+                acc[4 * tid + 2] = a2;
+                acc[4 * tid + 3] = a3;
+            }
+            __syncthreads();
+            if (tid < nch) {
+                for (int qq = 1; qq < Q; ++qq) {
+                    const int t = tid + qq * nch;
+                    a0 += acc[4 * t + 0];
+                    a1 += acc[4 * t + 1];
+                    a2 += acc[4 * t + 2];
+                    a3 += acc[4 * t + 3];
+                }
+                v[0][0] = a0;
+                v[0][1] = a1;
+                v[0][2] = a2;
+                v[0][3] = a3;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < vw) need = max(need, need64(v[0][j], er + exp_at(eb, vw * tid + j)));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < SR_MAXV; ++k) {
+                const int c = tid + SR_THR * k;
+                v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0;
+                if (c < nch) {
+                    if (vw == 4) {
+#pragma unroll 4
+                        for (int z = 0; z < splits; ++z) {
+                            const v4i x = *(const v4i *)(prow + z * stride + 4 * c);
+                            v[k][0] += x[0];
+                            v[k][1] += x[1];
+                            v[k][2] += x[2];
+                            v[k][3] += x[3];
+                        }
+                    } else {
+                        const int sc = src_col(c);
+                        for (int z = 0; z < splits; ++z) v[k][0] += prow[z * stride + sc];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (j < vw) need = max(need, need64(v[k][j], er + exp_at(eb, vw * c + j)));
+                }
+            }
+        }
+        need = block_max_n(need, sh);
+        const int e = clamp_exp_flag(max(E_MIN, need), flags);
+        if (tid == 0) out_exp[row] = (int8_t)e;
+        int8_t *orow = out + (long long)row * Nout;
+        const int kmax = Q > 1 ? 1 : SR_MAXV;
+#pragma unroll
+        for (int k = 0; k < SR_MAXV; ++k) {
+            const int c = tid + SR_THR * k;
+            if (k >= kmax || c >= nch) break;
+            if (vw == 4) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - (er + exp_at(eb, 4 * c + j))) << (8 * j);
+                *(uint32_t *)(orow + 4 * c) = w;
+            } else {
+                orow[c] = (int8_t)rne_shift64(v[k][0], e - (er + exp_at(eb, c)));
+            }
+        }
+        __syncthreads();
+    }
+}
+
+bool split_round_rows_fits(int Nout, int mc, int mcp) {
+    const int vw = (mc == mcp && Nout % 4 == 0) ? 4 : 1;
+    return Nout / vw <= SR_THR * SR_MAXV;
+}
+
+hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
+                                   int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
+                                   int8_t *out_exp, uint32_t *flags, hipStream_t st) {
+    if (M <= 0 || Nout <= 0) return hipSuccess;
+    const int vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
+    const int nch = Nout / vw;
+    int Q = 1;
+    if (nch <= SR_THR / 2) {
+        Q = SR_THR / nch;
+        if (Q > splits) Q = splits;
+    }
+    prof_begin(st, PROF_SPLIT_ROUND);
+    hipLaunchKernelGGL(split_round_rows_kernel, dim3(blocks_for(M, 1, 16384)), dim3(SR_THR), 0, st, partial, splits,
+                       split_stride, M, Nout, src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb,
+                       out, out_exp, flags, vw, Q);
+    prof_end(st, PROF_SPLIT_ROUND);
+    return hipGetLastError();
+}
+
 hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
                                  ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
                                  hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    hipError_t err = launch_fill_i32(gneed, row_group ? M : 1, NEED_NONE, st);
-    if (err != hipSuccess) return err;
     const int vw = (N % 4 == 0) ? 4 : 1;
     const long long total = (long long)M * (N / vw);
-    prof_begin(st);
+    prof_begin(st, PROF_PARTIAL_REDUCE);
     hipLaunchKernelGGL(partial_reduce_kernel, dim3(blocks_for(total, 64, 8192)), dim3(256), 0, st, partial,
                        splits, split_stride, M, N, ea, eb, row_group, sums, gneed, vw,
                        make_fastdiv((uint32_t)(N / vw)));
@@ -442,7 +674,7 @@ hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch,
     if (M <= 0 || N <= 0) return hipSuccess;
     const int vw = (N % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
     const long long total = (long long)M * (N / vw);
-    prof_begin(st);
+    prof_begin(st, PROF_ROUND_SUMS);
     hipLaunchKernelGGL(round_sums_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, sums, M, N,
                        src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb, row_group, gneed,
                        out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));

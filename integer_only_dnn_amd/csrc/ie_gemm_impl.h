@@ -23,6 +23,13 @@
 // im2col view (weight gradient) on the fly; zero padding loads zeros.
 #pragma once
 
+#ifndef IE_STAGES
+#define IE_STAGES 4
+#endif
+#ifndef IE_UNROLL
+#define IE_UNROLL 2
+#endif
+
 #include "ie_device.h"
 #include "ie_internal.h"
 
@@ -55,9 +62,11 @@ struct Lds {
 
 // ---------------------------------------------------------------------------
 // Loaders.  Every operand is read in 16-byte chunks (the host pads channel
-// and contraction extents to multiples of 16).  Loads are branch free: an
-// out-of-range chunk reads a clamped in-range address and is replaced by
-// zeros, so the prefetched loads stay in flight across the MFMA work.
+// and contraction extents to multiples of 16).  Loads are unconditional: an
+// out-of-range chunk reads a clamped in-range address and its bit in the
+// stage's validity mask is clear; the zeros are substituted only when the
+// stage is written to LDS, so nothing consumes a loaded register before then
+// and the prefetched loads stay in flight across the MFMA work.
 // Each thread moves ROWS * BK / 4096 chunks per contraction step.
 // ---------------------------------------------------------------------------
 
@@ -78,9 +87,9 @@ struct KChunks {
     static constexpr int STRIDE = BK + 16;
     __device__ __forceinline__ static int row(int c, int tid) { return (tid + NTHR * c) / CPR; }
     __device__ __forceinline__ static int col(int tid) { return (tid % CPR) * 16; }
-    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH], uint32_t msk) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) *(v4i *)(s + row(c, tid) * STRIDE + col(tid)) = reg[c];
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + row(c, tid) * STRIDE + col(tid)) = zero_unless((msk >> c) & 1, reg[c]);
     }
 };
 
@@ -93,9 +102,10 @@ struct TChunks {
     static constexpr int STRIDE = ROWS + 16;
     __device__ __forceinline__ static int krow(int c, int tid) { return (tid + NTHR * c) / PER; }
     __device__ __forceinline__ static int ic(int tid) { return tid % PER; }
-    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH], uint32_t msk) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) *(v4i *)(s + krow(c, tid) * STRIDE + ic(tid) * 16) = reg[c];
+        for (int c = 0; c < CH; ++c)
+            *(v4i *)(s + krow(c, tid) * STRIDE + ic(tid) * 16) = zero_unless((msk >> c) & 1, reg[c]);
     }
 };
 
@@ -105,22 +115,26 @@ struct Ld<LD_K, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
     static constexpr int CH = B_::CH;
     const int8_t *ptr[CH];
-    bool ok[CH];
+    uint32_t okm;
     int col;
     __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
         col = B_::col(tid);
+        okm = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int i = i0 + B_::row(c, tid);
-            ok[c] = i < op.rows;
-            ptr[c] = op.base + (long long)(ok[c] ? i : 0) * op.ld + col;
+            const bool ok = i < op.rows;
+            okm |= (uint32_t)ok << c;
+            ptr[c] = op.base + (long long)(ok ? i : 0) * op.ld + col;
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    // out of range along k: read the row's first chunk instead
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
         const bool kin = k0 + col < kend;
-        const int kk = kin ? k0 : kend - 16 - col;
+        const int kk = kin ? k0 : -col;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) reg[c] = zero_unless(ok[c] && kin, *(const v4i *)(ptr[c] + kk));
+        for (int c = 0; c < CH; ++c) reg[c] = *(const v4i *)(ptr[c] + kk);
+        msk = kin ? okm : 0u;
     }
 };
 
@@ -151,17 +165,19 @@ struct Ld<LD_IM2COL, ROWS> : KChunks<ROWS> {
             pix[c] = (long long)n * g.h * g.w * g.cp;
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
         const uint32_t kk = k0 + col;
         const bool kin = (int)kk < kend;
         const uint32_t rs = fdiv(kk, g.dc), ch = kk - rs * g.cp;
         const uint32_t r = fdiv(rs, g.ds), s = rs - r * g.s;
+        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int h = hb[c] + (int)r, w = wb[c] + (int)s;
             const bool in = kin && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
             const long long off = in ? pix[c] + ((long long)h * g.w + w) * g.cp + ch : 0;
-            reg[c] = zero_unless(in, *(const v4i *)(x + off));
+            reg[c] = *(const v4i *)(x + off);
+            msk |= (uint32_t)in << c;
         }
     }
 };
@@ -194,19 +210,21 @@ struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
             pix[c] = (long long)n * g.p * g.q * g.kp;
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
         const uint32_t kk = k0 + col;
         const bool kin = (int)kk < kend;
         const uint32_t rs = fdiv(kk, g.dk), ko = kk - rs * g.kp;
         const int r = (int)fdiv(rs, g.ds), s = (int)(rs - (uint32_t)r * g.s);
+        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int a = hp[c] - r, b = wp[c] - s;
-            const int p = a / g.stride, q = b / g.stride;
+            const int p = (int)fdiv((uint32_t)max(a, 0), g.dst), q = (int)fdiv((uint32_t)max(b, 0), g.dst);
             const bool in = kin && a >= 0 && b >= 0 && p * g.stride == a && q * g.stride == b && p < g.p &&
                             q < g.q;
             const long long off = in ? pix[c] + ((long long)p * g.q + q) * g.kp + ko : 0;
-            reg[c] = zero_unless(in, *(const v4i *)(dy + off));
+            reg[c] = *(const v4i *)(dy + off);
+            msk |= (uint32_t)in << c;
         }
     }
 };
@@ -226,12 +244,14 @@ struct Ld<LD_T, ROWS> : TChunks<ROWS> {
         base = op.base + (iok ? i : 0);
         ld = op.ld;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
+        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int k = k0 + B_::krow(c, tid);
             const bool in = iok && k < kend;
-            reg[c] = zero_unless(in, *(const v4i *)(base + (long long)(k < kend ? k : kend - 1) * ld));
+            reg[c] = *(const v4i *)(base + (long long)(k < kend ? k : 0) * ld);
+            msk |= (uint32_t)in << c;
         }
     }
 };
@@ -257,7 +277,8 @@ struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
         jr = (int)fdiv(rs, g.ds);
         js = (int)rs - jr * g.s;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
+        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int kk = k0 + B_::krow(c, tid);
@@ -267,7 +288,8 @@ struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
             const int h = (int)p * g.stride + jr - g.pad, w = (int)q * g.stride + js - g.pad;
             const bool in = jok && kk < kend && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
             const long long off = in ? (((long long)n * g.h + h) * g.w + w) * g.cp + jc : 0;
-            reg[c] = zero_unless(in, *(const v4i *)(x + off));
+            reg[c] = *(const v4i *)(x + off);
+            msk |= (uint32_t)in << c;
         }
     }
 };
@@ -307,13 +329,6 @@ __device__ __forceinline__ int wave_max(int v) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-// Raise a group maximum: skip the atomic when the stored value is already
-// at least as large (the maximum only grows, so a stale read only costs an
-// unneeded atomic).
-__device__ __forceinline__ void raise_max(int *p, int v) {
-    if (v > __atomic_load_n(p, __ATOMIC_RELAXED)) atomicMax(p, v);
-}
-
 // Workgroups are dispatched to the 8 XCDs round robin.  Tiles are numbered so
 // that each XCD receives a contiguous run of the N-fastest tile order: one
 // XCD walks all column tiles of a row tile before the next, keeping the row
@@ -327,9 +342,11 @@ __device__ __forceinline__ void tile_of(int bid, int TM, int TN, int &tm, int &t
     tn = logical - tm * TN;
 }
 
+// Register pipeline depth: 3 for the 2 x 2 tile, which runs two workgroups
+// per CU and would spill at 4.
 template <int MI, int NI>
-struct Occ {
-    static constexpr int value = MI * NI <= 4 ? 2 : 1;
+struct Stages {
+    static constexpr int value = (MI == 2 && NI == 2) ? 3 : IE_STAGES;
 };
 
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
@@ -365,6 +382,10 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
     if constexpr (!PARTIAL) {
         for (int i = tid; i < BMt; i += NTHR) seA[i] = m0 + i < M ? exp_at(ep.ea, m0 + i) : 0;
         for (int i = tid; i < BNt; i += NTHR) seB[i] = n0 + i < N ? exp_at(ep.eb, n0 + i) : 0;
+    } else {
+        // group maxima of the split finalize start empty (it runs after this grid)
+        const int nblk = gridDim.x * gridDim.z, blk = blockIdx.x + gridDim.x * blockIdx.z;
+        for (int i = blk * NTHR + tid; i < ep.gneed_n; i += nblk * NTHR) ep.gneed[i] = NEED_NONE;
     }
 
     v16i acc[MI][NI];
@@ -375,21 +396,22 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
-    // Two register stages in flight: stage s lives in register set s % 2 and
-    // LDS buffer s % 2.  Step `it` loads stage it+2, computes stage it and
-    // writes stage it+1 (loaded one step earlier) to LDS.
-    v4i ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+    // NS register stages in flight: stage s is loaded into register set
+    // s % NS at step s - NS, written to LDS buffer s % 2 at the end of step
+    // s - 1 and computed at step s, so a load has NS - 1 steps to land.
+    constexpr int NS = Stages<MI, NI>::value;
+    v4i ra[NS][CA], rb[NS][CB];
+    uint32_t ma[NS], mb[NS];
+    // An empty chunk issues no load at all: with an empty contraction the
+    // operand pointers need not address any memory.
     if (nk > 0) {
-        la.load(kb, ke, tid, ra0);
-        lb.load(kb, ke, tid, rb0);
-    }
-    if (nk > 1) {
-        la.load(kb + BK, ke, tid, ra1);
-        lb.load(kb + BK, ke, tid, rb1);
-    }
-    if (nk > 0) {
-        la.store(lds, tid, ra0);
-        lb.store(lds + LA::BYTES, tid, rb0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            la.load(kb + s * BK, ke, tid, ra[s], ma[s]);
+            lb.load(kb + s * BK, ke, tid, rb[s], mb[s]);
+        }
+        la.store(lds, tid, ra[0], ma[0]);
+        lb.store(lds + LA::BYTES, tid, rb[0], mb[0]);
     }
     __syncthreads();
 
@@ -410,30 +432,30 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
         }
     };
 
-    for (int it = 0; it < nk; it += 2) {
-        // even step: load set 0, store set 1
-        if (it + 2 < nk) {
-            la.load(kb + (it + 2) * BK, ke, tid, ra0);
-            lb.load(kb + (it + 2) * BK, ke, tid, rb0);
+    // NU sub-steps per trip: the back edge costs one full drain of the loads
+    // in flight, so it is taken once per NU steps
+    constexpr int NU = IE_UNROLL * NS * (NS % 2 ? 2 : 1);  // even: step parity picks the LDS buffer
+    for (int it = 0; it < nk; it += NU) {
+#pragma unroll
+        for (int uu = 0; uu < NU; ++uu) {
+            const int u = uu % NS;
+            const int s = it + uu;
+            if (s >= nk) break;
+            // set u held stage s, already in LDS: refill it with stage s + NS
+            // (past the end: clamped reads, all masked)
+            la.load(kb + (s + NS) * BK, ke, tid, ra[u], ma[u]);
+            lb.load(kb + (s + NS) * BK, ke, tid, rb[u], mb[u]);
+#ifndef IE_NO_SCHED_BARRIER
+            // keep the refill ahead of the fragment reads, so that no fragment
+            // lands in registers whose loads are still in flight
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+            compute(lds + (uu & 1) * STAGE);
+            // stage s + 1 (all zeros past the end, a buffer nobody reads)
+            la.store(lds + ((uu + 1) & 1) * STAGE, tid, ra[(u + 1) % NS], ma[(u + 1) % NS]);
+            lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS], mb[(u + 1) % NS]);
+            __syncthreads();
         }
-        compute(lds);
-        if (it + 1 < nk) {
-            la.store(lds + STAGE, tid, ra1);
-            lb.store(lds + STAGE + LA::BYTES, tid, rb1);
-        }
-        __syncthreads();
-        if (it + 1 >= nk) break;
-        // odd step: load set 1, store set 0
-        if (it + 3 < nk) {
-            la.load(kb + (it + 3) * BK, ke, tid, ra1);
-            lb.load(kb + (it + 3) * BK, ke, tid, rb1);
-        }
-        compute(lds + STAGE);
-        if (it + 2 < nk) {
-            la.store(lds, tid, ra0);
-            lb.store(lds + LA::BYTES, tid, rb0);
-        }
-        __syncthreads();
     }
 
     // Element (a, b, r) of this lane sits at tile row / column
@@ -500,11 +522,10 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                 e = clamp_exp_flag(max(E_MIN, gmax), ep.flags);
                 if (tid == 0 && blockIdx.x == 0) ep.out_exp[0] = (int8_t)e;
             } else {
+                // round to odd two bits below the tile's own need; the tile's
+                // need goes to p16, where the second pass takes the maximum
                 p = gmax == NEED_NONE ? P_NONE : gmax - 2;
-                if (tid == 0) {
-                    ep.p16[tile_m + TM * tile_n] = (int16_t)p;
-                    if (gmax != NEED_NONE) raise_max(&ep.gneed[0], gmax);
-                }
+                if (tid == 0) ep.p16[tile_m + TM * tile_n] = (int16_t)(gmax == NEED_NONE ? P_NONE : gmax);
             }
 #pragma unroll
             for (int a = 0; a < MI; ++a)
@@ -562,10 +583,8 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                         if (wn == 0 && (lane & 31) == 0) ep.out_exp[row] = (int8_t)e;
                     } else {
                         p = rm == NEED_NONE ? P_NONE : rm - 2;
-                        if (wn == 0 && (lane & 31) == 0) {
-                            ep.p16[(long long)row * n_ct + tile_n] = (int16_t)p;
-                            if (rm != NEED_NONE) raise_max(&ep.gneed[row], rm);
-                        }
+                        if (wn == 0 && (lane & 31) == 0)
+                            ep.p16[(long long)row * n_ct + tile_n] = (int16_t)(rm == NEED_NONE ? P_NONE : rm);
                     }
 #pragma unroll
                     for (int b = 0; b < NI; ++b) {
@@ -587,10 +606,11 @@ hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, i
                       const Epi &ep, hipStream_t st) {
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     dim3 grid(TM * TN, 1, splits);
-    prof_begin(st);
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB;
+    prof_begin(st, kind);
     hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, PARTIAL>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
                        k_chunk, TM, ep);
-    prof_end(st, 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB);
+    prof_end(st, kind);
     return hipGetLastError();
 }
 

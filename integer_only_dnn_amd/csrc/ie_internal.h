@@ -40,8 +40,9 @@ struct Epi {
     int8_t *out;      // DIRECT: int8 mantissas [M x N]
     int8_t *out_exp;  // DIRECT: exponents
     int16_t *v16;     // RTO: round-to-odd values [M x N]
-    int16_t *p16;     // RTO: provisional exponent per (row, column tile) or per tile
-    int *gneed;       // RTO: group maxima of the smallest exponents
+    int16_t *p16;     // RTO: the tile's need per (row, column tile) or per tile
+    int *gneed;       // PARTIAL: group maxima of the finalize, set empty here
+    int gneed_n;      //   (count)
     int *partial;     // PARTIAL: int32 [splits][M][N]
     long long split_stride;
     uint32_t *flags;
@@ -64,10 +65,10 @@ FastDiv make_fastdiv(uint32_t d);
 
 // Convolution geometry.  cp / kp: input / output channel counts as stored in
 // the operands the kernels read (rounded up to multiples of 16 with zeros);
-// dc divides by cp, dk by kp.
+// dc divides by cp, dk by kp, dst by the stride.
 struct ConvGeom {
     int n, h, w, c, k, r, s, stride, pad, p, q, cp, kp;
-    FastDiv dpq, dq, dhw, dw, dc, ds, dk;
+    FastDiv dpq, dq, dhw, dw, dc, ds, dk, dst;
 };
 
 struct Operand {
@@ -102,37 +103,52 @@ hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, i
 bool tile_available(int kind_a, int kind_b, Tile t);
 
 // Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
-void prof_begin(hipStream_t st);
+void prof_begin(hipStream_t st, int kind);
 void prof_end(hipStream_t st, int kind);
 void prof_enable(int on);
+void prof_select(int kind);
 int prof_read(float *ms, int *kind, int max);
 constexpr int PROF_RTO_FINALIZE = 3000;
 constexpr int PROF_PARTIAL_REDUCE = 3100;
 constexpr int PROF_ROUND_SUMS = 3150;
 constexpr int PROF_ALIGN = 3200;
+constexpr int PROF_SPLIT_ROUND = 3300;
 
 // Auxiliary kernels (ie_aux.hip).
 hipError_t launch_fill_i32(int *p, long long n, int v, hipStream_t st);
 hipError_t launch_fill_i8(int8_t *p, long long n, int v, hipStream_t st);
-hipError_t launch_exp_max(const int8_t *e, long long n, int *out, hipStream_t st);
+// out0[0] = max(e0[0..n0)), out1[0] = max(e1[0..n1)) (one launch; n1 may be 0).
+hipError_t launch_exp_max2(const int8_t *e0, long long n0, int *out0, const int8_t *e1, long long n1, int *out1,
+                           hipStream_t st);
 // Copy rows into a zero-padded pitch, re-expressed at *estar when set.
 hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
                            const int *estar, long long cols_p, int8_t *out, hipStream_t st);
-hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, const int *estar,
-                                  int A, int B, int C, int Ap, int8_t *out, hipStream_t st);
-// Second pass of the round-to-odd epilogue.  ROW groups: p16 per (row,
-// column tile); whole-tensor groups: p16 per tile (tile_m + TM * tile_n).
-hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, const int *gneed, int M, int N,
-                               Tile t, int row_group, int8_t *out, int8_t *out_exp, uint32_t *flags,
-                               hipStream_t st);
+// w viewed as [A][B][C] with row exponents e[a] (e_row) or e[0]:
+// out[c][b][a] = w[a][b][c] re-expressed at the largest row exponent, zero
+// for A <= a < Ap; that exponent is also written to *estar_out.
+hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, int A, int B, int C, int Ap,
+                                  int8_t *out, int *estar_out, hipStream_t st);
+// Second pass of the round-to-odd epilogue: the group exponent is the
+// maximum of the tile needs in p16 (ROW groups: per (row, column tile);
+// whole-tensor groups: per tile, tile_m + TM * tile_n).
+hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st);
 // Split-contraction finalize: sum int32 partials into int64 and raise the
-// group maxima; then round the sums into int8.
+// group maxima (set empty by the split kernel, or by launch_fill_i32 when no
+// split kernel ran); then round the sums into int8.
 hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
                                  ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
                                  hipStream_t st);
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
                              uint32_t *flags, hipStream_t st);
+// Split finalize of row groups in one pass (sums never stored): output
+// [M x Nout] from partials [splits][M][src_pitch] with the column map of
+// launch_round_sums.  Requires split_round_rows_fits(Nout, mc, mcp).
+bool split_round_rows_fits(int Nout, int mc, int mcp);
+hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
+                                   int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
+                                   int8_t *out_exp, uint32_t *flags, hipStream_t st);
 hipError_t launch_zero_flags(void *ws, hipStream_t st);
 
 // Integer SGD update (ie_update.hip).
@@ -143,10 +159,11 @@ struct UpdateArgs {
     int w_row, v_row, g_row;
     long long rows, cols;
     int lr_m, lr_e, mom_m, mom_e;
-    int *gneed_v;      // [1] for a whole-tensor velocity group
-    int *gneed_w;      // [1] for a whole-tensor weight group
+    int *tmp;          // [UPD_WS_INTS]: exponent snapshots, per-block maxima
     uint32_t *flags;
 };
+constexpr int UPD_MAX_BLOCKS = 1024;  // grid of the update when a group spans the tensor
+constexpr int UPD_WS_INTS = 2 + 2 * UPD_MAX_BLOCKS;
 hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st);
 
 }  // namespace ie

@@ -127,19 +127,37 @@ __device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
 // One row of W, V, G is owned by WPR waves (WPR = 1: four rows per block;
 // WPR = 4: one row per block, maxima combined through LDS).  Each lane holds D
 // dwords (4 D bytes) of each tensor.
-//   pass 0: whole-tensor velocity: raise gneed_v with the velocity's needs.
+//   pass 0: whole-tensor velocity: each block stores the largest need of its
+//           rows' velocities in bmax_v[block].
 //   pass 1: velocity step; weight step for row-grouped W, otherwise store V'
-//           and raise gneed_w.
-//   pass 2: whole-tensor weight: round W with gneed_w.
+//           and the block's largest weight need in bmax_w[block].
+//   pass 2: whole-tensor weight: round W at the maximum of bmax_w.
+// Whole-tensor exponents that a pass overwrites are read from snapshots taken
+// by the pass before (tmp[0]: old velocity exponent, tmp[1]: old weight
+// exponent).  All passes run on the same grid.
 template <int D, int WPR>
-__global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec, const int *old_ev,
-                                                      const int *old_ew) {
+__global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec) {
     constexpr int RPB = 4 / WPR;  // rows per block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = wave % WPR;
     __shared__ uint32_t red[2][4];
+    __shared__ int bred[4];
     int parity = 0;
+    int *bmax_v = a.tmp + 2, *bmax_w = a.tmp + 2 + UPD_MAX_BLOCKS;
+    auto block_imax = [&](int v) -> int {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+        __syncthreads();
+        if (lane == 0) bred[wave] = v;
+        __syncthreads();
+        return max(max(bred[0], bred[1]), max(bred[2], bred[3]));
+    };
+    auto max_of = [&](const int *p) -> int {
+        int m = NEED_NONE;
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) m = max(m, p[i]);
+        return block_imax(m);
+    };
     // maximum over the row (all WPR waves); every wave of the block calls it
     auto row_umax = [&](uint32_t v) -> uint32_t {
         v = umax_wave(v);
@@ -153,6 +171,25 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
     };
     auto row_imax = [&](int v) -> int { return (int)(row_umax((uint32_t)(v ^ (int)0x80000000)) ^ 0x80000000u); };
     const bool v_tensor = a.v_row == 0, w_tensor = a.w_row == 0;
+    // whole-tensor exponents of this pass (before any write of this pass)
+    int ev_t = 0, ew_t = 0, evn_t = 0, ewn_t = 0;
+    if (pass == 0) {
+        ev_t = a.v_exp[0];
+        if (blockIdx.x == 0 && threadIdx.x == 0) a.tmp[0] = ev_t;
+    } else if (pass == 1) {
+        if (v_tensor) {
+            ev_t = a.tmp[0];
+            evn_t = clamp_exp_flag(max(E_MIN, max_of(bmax_v)), a.flags);
+        }
+        if (w_tensor) {
+            ew_t = a.w_exp[0];
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.tmp[1] = ew_t;
+        }
+    } else {
+        ew_t = a.tmp[1];
+        ewn_t = clamp_exp_flag(max(E_MIN, max_of(bmax_w)), a.flags);
+    }
+    int bneed = NEED_NONE;  // largest need of this block's rows (passes 0, 1)
 
     for (long long row0 = (long long)blockIdx.x * RPB; row0 < a.rows; row0 += (long long)gridDim.x * RPB) {
         const long long row = row0 + wave / WPR;
@@ -167,13 +204,13 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
             V[j] = load_dw(a.v + off, col, a.cols, vec);
             G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
         }
-        const int ew = w_tensor ? *old_ew : (int)a.w_exp[row];
+        const int ew = w_tensor ? ew_t : (int)a.w_exp[row];
 
         // ---- weight step only (whole-tensor weight, second pass) ----
         if (pass == 2) {
-            const int evn = v_tensor ? clamp_exp_flag(max(E_MIN, *a.gneed_v), a.flags) : (int)a.v_exp[row];
+            const int evn = (int)a.v_exp[v_tensor ? 0 : row];
             const int pw = a.lr_e + evn;
-            const int e = clamp_exp_flag(max(E_MIN, *a.gneed_w), a.flags);
+            const int e = ewn_t;
             if (abs(ew - pw) <= 15) {
                 const int base = min(ew, pw);
                 const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
         }
 
         // ---- velocity: v = momentum * V + G ----
-        const int ev = v_tensor ? *old_ev : (int)a.v_exp[row];
+        const int ev = v_tensor ? ev_t : (int)a.v_exp[row];
         const int eg = a.g_row ? (int)a.g_exp[row] : (int)a.g_exp[0];
         const int pa = ev + a.mom_e, pb = eg;
         const bool nv = abs(pa - pb) <= 15;
@@ -235,12 +272,10 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
             needv = row_imax(m);
         }
         if (pass == 0) {
-            if (lane == 0 && sub == 0 && needv != NEED_NONE && needv > __atomic_load_n(a.gneed_v, __ATOMIC_RELAXED))
-                atomicMax(a.gneed_v, needv);
+            bneed = max(bneed, needv);
             continue;
         }
-        const int evn = v_tensor ? clamp_exp_flag(max(E_MIN, *a.gneed_v), a.flags)
-                                 : clamp_exp_flag(max(E_MIN, needv), a.flags);
+        const int evn = v_tensor ? evn_t : clamp_exp_flag(max(E_MIN, needv), a.flags);
         int c[D][4];
         if (nv) {
             const RneU r = rne_u(evn - min(pa, pb));
@@ -294,8 +329,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
             needw = row_imax(m);
         }
         if (w_tensor) {
-            if (lane == 0 && sub == 0 && needw != NEED_NONE && needw > __atomic_load_n(a.gneed_w, __ATOMIC_RELAXED))
-                atomicMax(a.gneed_w, needw);
+            bneed = max(bneed, needw);
             continue;
         }
         const int ewn = clamp_exp_flag(max(E_MIN, needw), a.flags);
@@ -321,36 +355,33 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
         }
         if (lane == 0 && sub == 0) a.w_exp[row] = (int8_t)ewn;
     }
+    if (pass == 0 || (pass == 1 && w_tensor)) {
+        const int m = block_imax(bneed);
+        if (threadIdx.x == 0) (pass == 0 ? bmax_v : bmax_w)[blockIdx.x] = m;
+    }
 }
 
 template <int D, int WPR>
-static hipError_t run_passes(const UpdateArgs &a, int vec, const int *old_ev, const int *old_ew, hipStream_t st) {
+static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
     constexpr int RPB = 4 / WPR;
     long long blocks = (a.rows + RPB - 1) / RPB;
-    if (blocks > 65536) blocks = 65536;
+    const long long cap = (a.v_row && a.w_row) ? 65536 : UPD_MAX_BLOCKS;
+    if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     hipError_t err;
     for (int pass = 0; pass < 3; ++pass) {
         if (pass == 0 && a.v_row) continue;
         if (pass == 2 && a.w_row) continue;
-        prof_begin(st);
-        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR>), dim3((int)blocks), dim3(256), 0, st, a, pass, vec, old_ev,
-                           old_ew);
+        prof_begin(st, 2000 + pass);
+        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR>), dim3((int)blocks), dim3(256), 0, st, a, pass, vec);
         prof_end(st, 2000 + pass);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
 }
 
-// Workspace ints used here: gneed_v, gneed_w and two snapshots of the old
-// whole-tensor exponents, which later passes must not read back after the
-// first pass has overwritten the exponent byte.
 hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
-    int *old_ev = a.gneed_v + 2, *old_ew = a.gneed_v + 3;
     hipError_t err;
-    if ((err = launch_fill_i32(a.gneed_v, 2, NEED_NONE, st)) != hipSuccess) return err;
-    if (a.v_row == 0 && (err = launch_exp_max(a.v_exp, 1, old_ev, st)) != hipSuccess) return err;
-    if (a.w_row == 0 && (err = launch_exp_max(a.w_exp, 1, old_ew, st)) != hipSuccess) return err;
     if (a.rows <= 0) {
         // Empty tensor: whole-tensor groups are all-zero.
         if (a.v_row == 0 && (err = launch_fill_i8(a.v_exp, 1, E_MIN, st)) != hipSuccess) return err;
@@ -365,7 +396,7 @@ hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
     const bool wide = dw >= 256;
     const long long per_lane = wide ? (dw + 255) / 256 : (dw + 63) / 64;
 #define IE_UPD(DD, WW)                                                                                     \
-    if (per_lane <= DD) return run_passes<DD, WW>(a, vec, old_ev, old_ew, st);
+    if (per_lane <= DD) return run_passes<DD, WW>(a, vec, st);
     if (!wide) {
         IE_UPD(1, 1)
         IE_UPD(2, 1)

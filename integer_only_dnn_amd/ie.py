@@ -61,6 +61,7 @@ EXPORTS = [
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_device_status", c_int, [c_void_p, c_void_p, POINTER(c_uint32), c_int]),
     ("ie_profile_enable", c_int, [c_int]),
+    ("ie_profile_select", c_int, [c_int]),
     ("ie_profile_read", c_int, [POINTER(ctypes.c_float), POINTER(c_int), c_int]),
     ("ie_status_str", c_char_p, [c_int]),
 ]
@@ -200,6 +201,11 @@ def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws:
 
 def ie_profile_enable(on: bool = True) -> None:
     _check(lib().ie_profile_enable(int(on)), "ie_profile_enable")
+
+
+def ie_profile_select(kind: int = 0) -> None:
+    """Time only kernels of this kind (0: all)."""
+    _check(lib().ie_profile_select(int(kind)), "ie_profile_select")
 
 
 def ie_profile_read(max_records: int = 1 << 16):

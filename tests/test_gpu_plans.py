@@ -1,0 +1,131 @@
+"""GPU parity of every execution plan: each instantiated workgroup tile, with
+each epilogue (groups inside one tile, two-pass round-to-odd, split
+contraction with the fused row finalize or the two-pass whole-tensor
+finalize), forced through the planner's tuning overrides on ragged shapes,
+bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle as o
+from integer_only_dnn_amd import ie
+from tests.gpu_util import announce, assert_same, qt_to_dev, rand_qt
+
+pytestmark = pytest.mark.gpu
+
+T, R = o.TENSOR, o.ROW
+DENSE_TILES = [(2, 2), (4, 1), (1, 4), (2, 1), (1, 2), (1, 1)]
+CONV_TILES = [(2, 2), (4, 1), (2, 1), (1, 1)]
+WGRAD_TILES = [(2, 2), (1, 4), (4, 1), (1, 1)]
+# (mode, splits): 1 = round-to-odd two-pass, 2 = split contraction
+MODES = [(1, 1), (2, 2), (2, 3)]
+
+
+@pytest.fixture(scope="module")
+def ws():
+    return ie.Workspace("cuda")
+
+
+@pytest.fixture
+def plan(monkeypatch):
+    def force(tile=None, mode=None, splits=1, wtile=None, wsplits=1):
+        if tile is None:
+            monkeypatch.delenv("IE_TILE", raising=False)
+        else:
+            monkeypatch.setenv("IE_TILE", f"{tile[0]},{tile[1]},{mode},{splits}")
+        if wtile is None:
+            monkeypatch.delenv("IE_WTILE", raising=False)
+        else:
+            monkeypatch.setenv("IE_WTILE", f"{wtile[0]},{wtile[1]},{wsplits}")
+    yield force
+    monkeypatch.delenv("IE_TILE", raising=False)
+    monkeypatch.delenv("IE_WTILE", raising=False)
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: f"m{m[0]}s{m[1]}")
+def test_dense_plans(tile, mode, ws, plan):
+    M, N, K = 200, 150, 392
+    announce(f"dense plans tile={tile} mode={mode} M={M} N={N} K={K}")
+    rng = np.random.default_rng(11 * tile[0] + 7 * tile[1] + 3 * mode[0] + mode[1])
+    X = rand_qt(rng, (M, K), R)
+    W = rand_qt(rng, (N, K), R)
+    dY = rand_qt(rng, (M, N), R)
+    Xd, Wd, dYd = qt_to_dev(X), qt_to_dev(W), qt_to_dev(dY)
+    plan(tile, *mode)
+    for gy in (T, R):
+        Y = ie.Mat.empty(M, N, gy)
+        ie.ie_linear_fwd(Xd, Wd, Y, ws)
+        assert_same(Y, o.linear_fwd(X, W, gy), f"fwd group {gy}")
+        dX = ie.Mat.empty(M, K, gy)
+        ie.ie_linear_bwd_dx(dYd, Wd, dX, ws)
+        assert_same(dX, o.linear_bwd_dx(dY, W, gy), f"dX group {gy}")
+    assert ws.status() == 0
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
+def test_dense_direct(tile, ws, plan):
+    # one tile holds every group: the epilogue rounds in place
+    M, N, K = 64 * tile[0] - 3, 64 * tile[1] - 5, 200
+    announce(f"dense direct tile={tile} M={M} N={N} K={K}")
+    rng = np.random.default_rng(5 + tile[0] * 3 + tile[1])
+    X = rand_qt(rng, (M, K), R)
+    W = rand_qt(rng, (N, K), T)
+    plan(tile, 0, 1)
+    for gy in (T, R):
+        Y = ie.Mat.empty(M, N, gy)
+        ie.ie_linear_fwd(qt_to_dev(X), qt_to_dev(W), Y, ws)
+        assert_same(Y, o.linear_fwd(X, W, gy), f"direct group {gy}")
+
+
+CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1)]
+
+
+@pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"st{s[7]}")
+@pytest.mark.parametrize("tile", CONV_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("mode", MODES[:2], ids=lambda m: f"m{m[0]}s{m[1]}")
+def test_conv_plans(shape, tile, mode, ws, plan):
+    n, h, w, c, k, r, s, st, pad = shape
+    announce(f"conv plans shape={shape} tile={tile} mode={mode}")
+    d = o.ConvShape(*shape)
+    dd = ie.conv_desc(*shape)
+    rng = np.random.default_rng(sum(shape) + 13 * tile[0] + tile[1] + mode[1])
+    X = rand_qt(rng, (n, h, w, c), T, zero_frac=0.2)
+    W = rand_qt(rng, (k, r * s * c), R)
+    dY = rand_qt(rng, (n, d.p, d.q, k), T)
+    Xd, Wd, dYd = qt_to_dev(X, rows=n * h * w), qt_to_dev(W), qt_to_dev(dY, rows=n * d.p * d.q)
+    plan(tile, *mode)
+    Y = ie.Mat.empty(n * d.p * d.q, k, T)
+    ie.ie_conv_fwd(dd, Xd, Wd, Y, ws)
+    assert_same(Y, o.conv_fwd(d, X, W, T), "conv fwd")
+    dX = ie.Mat.empty(n * h * w, c, T)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, None, ws)
+    assert_same(dX, o.conv_dgrad(d, dY, W, T), "conv dgrad")
+    assert ws.status() == 0
+
+
+@pytest.mark.parametrize("tile", WGRAD_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_wgrad_plans(tile, splits, ws, plan):
+    announce(f"wgrad plans tile={tile} splits={splits}")
+    rng = np.random.default_rng(17 * tile[0] + 5 * tile[1] + splits)
+    M, N, K = 700, 150, 100
+    dY = rand_qt(rng, (M, N), R)
+    X = rand_qt(rng, (M, K), T)
+    plan(wtile=tile, wsplits=splits)
+    for g in (T, R):
+        dW = ie.Mat.empty(N, K, g)
+        ie.ie_linear_bwd_dw(qt_to_dev(dY), qt_to_dev(X), dW, ws)
+        assert_same(dW, o.linear_bwd_dw(dY, X, g), f"linear dW group {g}")
+    shape = (2, 9, 9, 3, 40, 3, 3, 2, 1)   # 3 channels: padded source columns
+    d = o.ConvShape(*shape)
+    dd = ie.conv_desc(*shape)
+    Xc = rand_qt(rng, (2, 9, 9, 3), T)
+    Wc = rand_qt(rng, (40, 27), T)
+    dYc = rand_qt(rng, (2, d.p, d.q, 40), T)
+    for g in (T, R):
+        dW = ie.Mat.empty(40, 27, g)
+        ie.ie_conv_bwd(dd, qt_to_dev(Xc, rows=2 * 81), qt_to_dev(Wc), qt_to_dev(dYc, rows=2 * d.p * d.q), None, dW,
+                       ws)
+        assert_same(dW, o.conv_wgrad(d, dYc, Xc, g), f"conv dW group {g}")
+    assert ws.status() == 0
