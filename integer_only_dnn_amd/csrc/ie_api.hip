@@ -65,28 +65,19 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Planning: tile shape, epilogue and contraction split of a product.
 // ---------------------------------------------------------------------------
 
-// Tiles instantiated per loader family (must match the ie_gemm_*.hip lists).
-const Tile FUSED_KK[] = {{2, 2}, {4, 1}, {1, 4}, {2, 1}, {1, 2}, {1, 1}};
-const Tile PARTIAL_KK[] = {{2, 2}, {4, 1}, {1, 4}, {2, 1}, {1, 2}, {1, 1}};
-const Tile FUSED_CONV[] = {{2, 2}, {4, 1}, {2, 1}, {1, 1}};
-const Tile PARTIAL_CONV[] = {{2, 2}, {4, 1}, {2, 1}, {1, 1}};
-const Tile WGRAD_TILES[] = {{2, 2}, {1, 4}, {4, 1}, {1, 1}};
 
-constexpr double CU_OPS = 1.9e15 / NCU;   // sustained int8 MFMA ops/s per CU (staged loop)
-constexpr double HBM_BPS = 4.0e12;         // sustained HBM bytes/s
-constexpr double LAUNCH_S = 4e-6;          // cost of one extra kernel launch
-
-// Relative MFMA efficiency of a wave tile (LDS bytes per MFMA grow as it shrinks).
-double tile_eff(Tile t) {
-    const int a = t.mi * t.ni;
-    return a >= 4 ? (t.mi == t.ni ? 1.0 : 0.85) : a >= 2 ? 0.6 : 0.4;
-}
-
-double tile_time(Tile t, long long M, long long N, long long Kc, int splits) {
-    long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn()) * splits;
-    long long rounds = (tiles + NCU - 1) / NCU;
-    return rounds * (2.0 * t.bm() * t.bn() * (double)(Kc > 0 ? Kc : 1) / tile_eff(t)) / CU_OPS;
-}
+// Planning rules, calibrated by timing every plan of the ResNet-18 and ViT-B
+// products on an MI355X:
+//  * a workgroup runs MI*NI waves' worth of 32x32 MFMA tiles and keeps its
+//    loads in flight for a few steps, so small grids are latency bound: the
+//    128x128 tile pays off only with at least four workgroups per CU (and a
+//    full tile width), 128x64 with two, otherwise 64x64;
+//  * a split contraction costs an extra pass over splits x M x N int32
+//    partials, so products split only when even 64x64 tiles leave most CUs
+//    idle;
+//  * weight gradients (short outputs, long contractions) split so that
+//    about 2.25 workgroups run per CU.
+constexpr long long WG_TARGET = 576;
 
 enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2 };
 
@@ -133,39 +124,20 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
         Plan f;
         if (forced_plan(K, f)) return f;
     }
-    const Tile *fused = family == 0 ? FUSED_KK : FUSED_CONV;
-    const int nf = family == 0 ? (int)(sizeof FUSED_KK / sizeof(Tile)) : (int)(sizeof FUSED_CONV / sizeof(Tile));
-    const Tile *part = family == 0 ? PARTIAL_KK : PARTIAL_CONV;
-    const int np = family == 0 ? (int)(sizeof PARTIAL_KK / sizeof(Tile)) : (int)(sizeof PARTIAL_CONV / sizeof(Tile));
-    Plan best{fused[0], PLAN_RTO, 1, chunk_for(K, 1)};
-    double bt = 1e30;
-    for (int i = 0; i < nf; ++i) {
-        Tile t = fused[i];
-        long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
-        bool direct = row_group ? N <= t.bn() : tiles == 1;
-        double tt = tile_time(t, M, N, K, 1);
-        if (!direct) tt += (double)M * N * 5 / HBM_BPS + 2 * LAUNCH_S;
-        if (tt < bt) {
-            bt = tt;
-            best = Plan{t, direct ? PLAN_DIRECT : PLAN_RTO, 1, chunk_for(K, 1)};
-        }
-    }
-    // split contraction for small outputs with long contractions
-    if (K >= 4 * BK && M * N <= (4ll << 20)) {
-        for (int i = 0; i < np; ++i) {
-            Tile t = part[i];
-            long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
-            for (int sp = 2; sp <= 32; sp *= 2) {
-                if (tiles * sp > 4 * NCU || K / sp < 2 * BK) break;
-                int kc = chunk_for(K, sp);
-                int sreal = (int)((K + kc - 1) / kc);
-                double tt = tile_time(t, M, N, kc, sreal) + (double)M * N * (8.0 * sreal + 17) / HBM_BPS +
-                            3 * LAUNCH_S;
-                if (tt < bt) {
-                    bt = tt;
-                    best = Plan{t, PLAN_SPLIT, sreal, kc};
-                }
-            }
+    (void)family;
+    auto tiles = [&](Tile t) { return (long long)cdiv(M, t.bm()) * cdiv(N, t.bn()); };
+    Tile t{1, 1};
+    if (N > 64 && tiles(Tile{2, 2}) >= 4ll * NCU) t = Tile{2, 2};
+    else if (tiles(Tile{2, 1}) >= 2ll * NCU) t = Tile{2, 1};
+    const bool direct = row_group ? N <= t.bn() : tiles(t) == 1;
+    Plan best{t, direct ? PLAN_DIRECT : PLAN_RTO, 1, chunk_for(K, 1)};
+    if (!direct && tiles(Tile{1, 1}) < NCU / 2 && K >= 8 * BK) {
+        const long long n11 = tiles(Tile{1, 1});
+        int sp = 1;
+        while (sp < 16 && n11 * sp * 2 <= WG_TARGET && K / (sp * 2) >= 4 * BK) sp *= 2;
+        if (sp > 1) {
+            const int kc = chunk_for(K, sp);
+            best = Plan{Tile{1, 1}, PLAN_SPLIT, (int)((K + kc - 1) / kc), kc};
         }
     }
     return best;
@@ -182,25 +154,15 @@ Plan plan_wgrad(long long M, long long N, long long L) {
             if (kc <= SPLIT_MAX_ROWS) return Plan{Tile{mi, ni}, PLAN_SPLIT, (int)((L + kc - 1) / kc), kc};
         }
     }
-    Plan best{WGRAD_TILES[0], PLAN_SPLIT, 1, chunk_for(L, 1)};
-    double bt = 1e30;
-    int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
-    if (smin < 1) smin = 1;
-    for (const Tile &t : WGRAD_TILES) {
-        long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
-        for (int sp = smin; sp <= 1024; sp = sp < 4 ? sp + 1 : sp * 2) {
-            int kc = chunk_for(L, sp);
-            if (kc > SPLIT_MAX_ROWS) continue;
-            int sreal = (int)((L + kc - 1) / kc);
-            double tt = tile_time(t, M, N, kc, sreal) + (double)M * N * (8.0 * sreal + 17) / HBM_BPS;
-            if (tt < bt) {
-                bt = tt;
-                best = Plan{t, PLAN_SPLIT, sreal, kc};
-            }
-            if (tiles * sp > 4 * NCU || kc <= 4 * BK) break;
-        }
-    }
-    return best;
+    const long long t22 = (long long)cdiv(M, 128) * cdiv(N, 128);
+    const Tile t = t22 >= 32 ? Tile{2, 2} : Tile{1, 1};
+    const long long nt = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+    const int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
+    int sp = 1;
+    while (sp < 1024 && nt * sp * 2 <= WG_TARGET * 3 / 2 && L / (sp * 2) >= 4 * BK) sp *= 2;
+    if (sp < smin) sp = smin;
+    const int kc = chunk_for(L, sp);
+    return Plan{t, PLAN_SPLIT, (int)((L + kc - 1) / kc), kc};
 }
 
 // Workspace of a product's epilogue.

@@ -171,30 +171,55 @@ hipError_t launch_exp_max2(const int8_t *e0, long long n0, int *out0, const int8
 }
 
 // out[i][k] = in[i][k] re-expressed at *estar (row exponents e[i]; no shift
-// when estar is null), for k < cols; zeros for cols <= k < cols_p.
-__global__ void pad_rows_kernel(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
-                                const int *estar, long long cols_p, int8_t *out) {
+// when estar is null), for k < cols; zeros for cols <= k < cols_p.  Each
+// thread writes 16 output bytes of one row (cols_p is a multiple of 16);
+// the input is read 16 bytes at a time when its rows are 16-byte aligned.
+__device__ __forceinline__ uint32_t rne_bytes4(uint32_t w, int sh) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o |= (uint32_t)(uint8_t)rne_shift32((int)(int8_t)(w >> (8 * t)), sh) << (8 * t);
+    return o;
+}
+
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int8_t *in, long long rows, long long cols,
+                                                       const int8_t *e, int e_row, const int *estar, long long cols_p,
+                                                       int8_t *out, int vec_in, FastDiv dcpr) {
     const int es = estar ? *estar : 0;
-    const long long n = rows * cols_p;
-    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
-         i += (long long)gridDim.x * blockDim.x) {
-        const long long r = i / cols_p, c = i - r * cols_p;
-        int v = 0;
-        if (c < cols) {
-            v = in[r * cols + c];
-            if (estar) v = rne_shift32(v, es - (e_row ? (int)e[r] : (int)e[0]));
+    const uint32_t cpr = (uint32_t)(cols_p >> 4);  // 16-byte chunks per row
+    const uint32_t n = (uint32_t)(rows * cpr);      // < 2^31 (checked by the launcher)
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        const uint32_t r32 = (uint32_t)(((uint64_t)i * dcpr.m) >> dcpr.s);
+        const long long r = r32, c0 = (long long)(i - r32 * cpr) << 4;
+        const int8_t *src = in + r * cols + c0;
+        v4i v;
+        if (vec_in && c0 + 16 <= cols) {
+            v = *(const v4i *)src;
+        } else {
+            uint32_t w[4] = {0, 0, 0, 0};
+            for (int j = 0; j < 16; ++j)
+                if (c0 + j < cols) w[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+            v = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
         }
-        out[i] = (int8_t)v;
+        if (estar) {
+            const int sh = es - (e_row ? (int)e[r] : (int)e[0]);
+            if (sh != 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = (int)rne_bytes4((uint32_t)v[j], sh);
+            }
+        }
+        *(v4i *)(out + r * cols_p + c0) = v;
     }
 }
 
 hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
                            const int *estar, long long cols_p, int8_t *out, hipStream_t st) {
-    const long long n = rows * cols_p;
+    const long long n = rows * (cols_p >> 4);
     if (n <= 0) return hipSuccess;
+    if (n >= (1ll << 31)) return hipErrorInvalidValue;
+    const int vec_in = (cols % 16 == 0) && ((uintptr_t)in % 16 == 0);
     prof_begin(st, PROF_ALIGN);
-    hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks_for(n, 256, 16384)), dim3(256), 0, st, in, rows, cols, e,
-                       e_row, estar, cols_p, out);
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks_for(n, 256, 8192)), dim3(256), 0, st, in, rows, cols, e, e_row,
+                       estar, cols_p, out, vec_in, make_fastdiv((uint32_t)(cols_p >> 4)));
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }

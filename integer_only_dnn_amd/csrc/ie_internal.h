@@ -100,7 +100,6 @@ hipError_t launch_gemm_dgrad(const Operand &A, const Operand &B, int M, int N, i
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
 hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
-bool tile_available(int kind_a, int kind_b, Tile t);
 
 // Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
 void prof_begin(hipStream_t st, int kind);
