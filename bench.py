@@ -78,11 +78,13 @@ def kind_symbol(kind: int) -> str:
 class Call:
     """One library call of the step: a closure plus what it computes."""
 
-    def __init__(self, label, fn, ops=0.0, bytes_=0.0):
+    def __init__(self, label, fn, ops=0.0, bytes_=0.0, io=0.0, outs=()):
         self.label = label
         self.fn = fn
-        self.ops = ops          # algorithmic int8 ops of its contraction
+        self.ops = ops          # algorithmic int8 ops of its contraction(s)
         self.bytes = bytes_     # algorithmic HBM bytes (update)
+        self.io = io            # algorithmic bytes of each contraction: operands read once, result written once
+        self.outs = list(outs)  # int8 result bytes of each contraction, in launch order
         self.kinds = None
 
 
@@ -112,11 +114,14 @@ def build_resnet18(torch, ie, ws, batch):
             upd = wl.update_inputs(N, K, seed + 50000, w_group=wl.TENSOR)
             V = _dev(torch, ie, upd.V)
             ops = 2.0 * M * N * K
+            io = float(L.n * L.h * L.w * L.c + N * K + M * N)
             name = f"{L.name}#{inst}"
-            calls.append(Call(f"{name}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops))
+            calls.append(Call(f"{name}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops, io=io,
+                              outs=[M * N]))
             bwd_ops = ops * (1 if L.first else 2)
             calls.append(Call(f"{name}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
-                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), bwd_ops))
+                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), bwd_ops, io=io,
+                              outs=([] if L.first else [L.n * L.h * L.w * L.c]) + [N * K]))
             params = N * K
             # read W, V, G and write W, V (1 byte each) + group exponents
             ubytes = 5.0 * params + 3.0 * N + 2.0
@@ -142,10 +147,13 @@ def build_resnet50(torch, ie, ws, batch):
         dX = ie.Mat.empty(L.n * L.h * L.w, L.c, wl.TENSOR)
         dW = ie.Mat.empty(N, K, wl.ROW)
         ops = 2.0 * M * N * K
+        io = float(L.n * L.h * L.w * L.c + N * K + M * N)
         for inst in range(L.count):   # identical shapes: reuse the tensors
-            calls.append(Call(f"{L.name}#{inst}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops))
+            calls.append(Call(f"{L.name}#{inst}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops,
+                              io=io, outs=[M * N]))
             calls.append(Call(f"{L.name}#{inst}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
-                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), 2 * ops))
+                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), 2 * ops, io=io,
+                              outs=[L.n * L.h * L.w * L.c, N * K]))
         meta["layers"].append({"name": L.name, "count": L.count, "gemm_mnk": [M, N, K]})
     return calls, meta
 
@@ -161,9 +169,13 @@ def build_vit(torch, ie, ws, layers, with_update):
         dX = ie.Mat.empty(L.m, L.k, inp.dx_group)
         dW = ie.Mat.empty(L.n, L.k, inp.dw_group)
         ops = 2.0 * L.m * L.n * L.k
-        calls.append(Call(f"{L.name}:fwd", lambda X=X, W=W, Y=Y: ie.ie_linear_fwd(X, W, Y, ws), ops))
-        calls.append(Call(f"{L.name}:dx", lambda dY=dY, W=W, dX=dX: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops))
-        calls.append(Call(f"{L.name}:dw", lambda dY=dY, X=X, dW=dW: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops))
+        io = float(L.m * L.k + L.n * L.k + L.m * L.n)
+        calls.append(Call(f"{L.name}:fwd", lambda X=X, W=W, Y=Y: ie.ie_linear_fwd(X, W, Y, ws), ops, io=io,
+                          outs=[L.m * L.n]))
+        calls.append(Call(f"{L.name}:dx", lambda dY=dY, W=W, dX=dX: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops, io=io,
+                          outs=[L.m * L.k]))
+        calls.append(Call(f"{L.name}:dw", lambda dY=dY, X=X, dW=dW: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops, io=io,
+                          outs=[L.n * L.k]))
         meta["layers"].append({"name": L.name, "gemm_mnk": [L.m, L.n, L.k]})
     if with_update:
         for i, (rows, cols) in enumerate(wl.vit_b_param_arenas()):
@@ -183,9 +195,10 @@ def build_linear_small(torch, ie, ws):
     import torch as t
     V = ie.Mat(t.zeros((128, 256), dtype=t.int8, device="cuda"), t.full((128,), -128, dtype=t.int8, device="cuda"), 1)
     ops = 2.0 * 64 * 128 * 256
-    calls = [Call("fwd", lambda: ie.ie_linear_fwd(X, W, Y, ws), ops),
-             Call("dx", lambda: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops),
-             Call("dw", lambda: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops),
+    io = float(64 * 256 + 128 * 256 + 64 * 128)
+    calls = [Call("fwd", lambda: ie.ie_linear_fwd(X, W, Y, ws), ops, io=io, outs=[64 * 128]),
+             Call("dx", lambda: ie.ie_linear_bwd_dx(dY, W, dX, ws), ops, io=io, outs=[64 * 256]),
+             Call("dw", lambda: ie.ie_linear_bwd_dw(dY, X, dW, ws), ops, io=io, outs=[128 * 256]),
              Call("update", lambda: ie.ie_sgd_update(W, V, dW, wl.LR, wl.MOMENTUM, ws=ws), 0.0,
                   5.0 * 128 * 256 + 3 * 128 + 2)]
     return calls, {"layers": [{"name": "linear", "gemm_mnk": [64, 128, 256]}], "params": 128 * 256}
@@ -266,6 +279,34 @@ def cpu_baseline(name: str):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from the committed counter table
+# ---------------------------------------------------------------------------
+
+def measured_traffic(workload: str, kernel: str) -> dict:
+    """HBM bytes per launch of `kernel` from profiles/hbm_traffic_<workload>.txt
+    (two rocprofv3 --pmc runs, copy-calibrated); null when there is no table,
+    the kernel is missing from it or the library sources changed since."""
+    from integer_only_dnn_amd import prof_summary
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    out = {"traffic": None}
+    if not os.path.exists(path):
+        out["traffic_note"] = "no counter table"
+        return out
+    digest, table = prof_summary.read_traffic(path)
+    if digest != prof_summary.source_digest():
+        out["traffic_note"] = "kernels changed since the counters were taken"
+        return out
+    if kernel not in table:
+        out["traffic_note"] = "kernel not in the counter table"
+        return out
+    fetch, write = table[kernel]
+    out["traffic"] = round(fetch + write)
+    out["traffic_fetch"] = round(fetch)
+    out["traffic_write"] = round(write)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Main
 # ---------------------------------------------------------------------------
 
@@ -324,7 +365,10 @@ def main():
             for c in calls:
                 n_gemm = sum(1 for k in c.kinds if is_gemm(k))
                 n_upd = sum(1 for k in c.kinds if 2000 <= k < 3000)
+                prod = -1  # index of the contraction a launch belongs to
                 for k in c.kinds:
+                    if is_gemm(k):
+                        prod += 1
                     if only is not None and k != only:
                         continue
                     ms, kind = recs[pos]
@@ -335,8 +379,12 @@ def main():
                     a["launches"] += 1
                     if is_gemm(kind):
                         a["ops"] += c.ops / n_gemm
+                        a["bytes"] += c.io
                     elif 2000 <= kind < 3000 and c.bytes:
                         a["bytes"] += c.bytes / n_upd
+                    elif c.outs:
+                        # finalize or pre-pass of a contraction: its int8 result
+                        a["bytes"] += c.outs[min(max(prod, 0), len(c.outs) - 1)]
         assert pos == len(recs), (pos, len(recs))
         return agg
 
@@ -383,6 +431,8 @@ def main():
     roof["kernel"] = kind_symbol(dom)
     roof["avg_launch_us"] = round(A["ms"] * 1e3 / A["launches"], 2)
     roof["launches_per_step"] = A["launches"] // args.steps
+    roof["algorithmic_bytes_per_launch"] = round(A["bytes"] / A["launches"])
+    roof.update(measured_traffic(args.workload, roof["kernel"]))
     agg = breakdown
     upd_ms = sum(v["ms"] for k, v in agg.items() if 2000 <= k < 3000) / n_bd
     upd_bytes = sum(c.bytes for c in calls)
