@@ -1,8 +1,9 @@
 """Benchmark of the integer-only (C, e) layer step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-for every layer, the forward product, the input gradient, the weight
-gradient and the integer SGD-momentum update of that layer's weights.
+for every layer, the forward product, the input gradient and the weight
+gradient, then one integer SGD-momentum update of every layer's weights (a
+single multi-tensor call, as an optimiser step runs after the backward pass).
 
 Default workload: the 3x3 convolutions of a ResNet-18 on 32x32x3 inputs at
 batch 128 (NHWC, per-tensor activation exponents, per-output-channel weight
@@ -97,6 +98,7 @@ def _dev(torch, ie, code, rows=None):
 
 def build_resnet18(torch, ie, ws, batch):
     calls, meta = [], {"layers": [], "params": 0}
+    upd_w, upd_v, upd_g, upd_bytes = [], [], [], 0.0
     layers = wl.resnet18_cifar_layers(batch)
     seed = 2000
     for L in layers:
@@ -124,11 +126,15 @@ def build_resnet18(torch, ie, ws, batch):
                               outs=([] if L.first else [L.n * L.h * L.w * L.c]) + [N * K]))
             params = N * K
             # read W, V, G and write W, V (1 byte each) + group exponents
-            ubytes = 5.0 * params + 3.0 * N + 2.0
-            calls.append(Call(f"{name}:update", lambda W=W, V=V, dW=dW:
-                              ie.ie_sgd_update(W, V, dW, wl.LR, wl.MOMENTUM, ws=ws), 0.0, ubytes))
+            upd_bytes += 5.0 * params + 3.0 * N + 2.0
+            upd_w.append(W)
+            upd_v.append(V)
+            upd_g.append(dW)
             meta["params"] += params
         meta["layers"].append({"name": L.name, "count": L.count, "gemm_mnk": list(L.gemm_mnk())})
+    # one optimiser step over every layer, after the products
+    calls.append(Call("update_all", lambda: ie.ie_sgd_update_multi(upd_w, upd_v, upd_g, wl.LR, wl.MOMENTUM, ws=ws),
+                      0.0, upd_bytes))
     return calls, meta
 
 
@@ -178,13 +184,16 @@ def build_vit(torch, ie, ws, layers, with_update):
                           outs=[L.n * L.k]))
         meta["layers"].append({"name": L.name, "gemm_mnk": [L.m, L.n, L.k]})
     if with_update:
+        ws_, vs_, gs_, ubytes = [], [], [], 0.0
         for i, (rows, cols) in enumerate(wl.vit_b_param_arenas()):
             upd = wl.update_inputs(rows, cols, 6000 + i)
-            W, V, G = _dev(torch, ie, upd.W), _dev(torch, ie, upd.V), _dev(torch, ie, upd.G)
-            ubytes = 5.0 * rows * cols + 5.0 * rows
-            calls.append(Call(f"update_{cols}", lambda W=W, V=V, G=G:
-                              ie.ie_sgd_update(W, V, G, wl.LR, wl.MOMENTUM, ws=ws), 0.0, ubytes))
+            ws_.append(_dev(torch, ie, upd.W))
+            vs_.append(_dev(torch, ie, upd.V))
+            gs_.append(_dev(torch, ie, upd.G))
+            ubytes += 5.0 * rows * cols + 5.0 * rows
             meta["params"] += rows * cols
+        calls.append(Call("update_all", lambda: ie.ie_sgd_update_multi(ws_, vs_, gs_, wl.LR, wl.MOMENTUM, ws=ws),
+                          0.0, ubytes))
     return calls, meta
 
 

@@ -92,6 +92,7 @@ size_t ie_linear_bwd_dw_workspace(int64_t M, int64_t N, int64_t K);
 size_t ie_conv_fwd_workspace(const ie_conv_desc *d);
 size_t ie_conv_bwd_workspace(const ie_conv_desc *d);
 size_t ie_sgd_update_workspace(int64_t rows, int64_t cols);
+size_t ie_sgd_update_multi_workspace(int32_t n);
 
 /* Zero the workspace's sticky flags (enqueued on `stream`). */
 ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream);
@@ -137,6 +138,10 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
  * in X, W aligned over output channels when ROW-grouped) and weight gradient
  * dW (its adjoint in W, per output channel groups when ROW).  dX or dW may be
  * NULL to skip that output.  dX: TENSOR; dW: TENSOR or ROW.
+ * With both outputs requested, the weight gradient runs on a second stream
+ * that the library keeps per device (default priority, created on first
+ * use); it forks from `stream` and joins back into it with events before the
+ * call returns, so all work stays ordered on `stream` for the caller.
  */
 ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
                       const ie_mat *dY, const ie_mat *dX, const ie_mat *dW,
@@ -154,6 +159,17 @@ ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G,
                         ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,
                         void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The same update for n independent (W[i], V[i], G[i]) triples (arrays of
+ * n ie_mat each), e.g. every layer of a network in one optimiser step, with
+ * one set of scalars.  The result equals n calls of ie_sgd_update; tensors
+ * of similar row length share kernel launches (one per pass).  Every triple
+ * is checked before anything is enqueued.  n >= 0.
+ */
+ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const ie_mat *G,
+                              ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,
+                              void *ws, size_t ws_bytes, void *stream);
+
 /* Wait for `stream`, then copy the workspace's sticky flags to *flags and,
  * if clear != 0, zero them. */
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
@@ -170,7 +186,8 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
  * alignment copies) and returns how
  * many were recorded since the last read; the records are then cleared.
- * This is the library's only process-wide state; it is not thread-safe.
+ * The timing records and the per-device second stream of ie_conv_bwd are the
+ * library's only process-wide state; the timing records are not thread-safe.
  */
 ie_status ie_profile_enable(int on);
 ie_status ie_profile_select(int kind);

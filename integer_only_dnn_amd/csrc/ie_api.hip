@@ -4,6 +4,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/ie.h"
 #include "ie_device.h"
 #include "ie_internal.h"
@@ -308,6 +311,34 @@ ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K
 
 long long r16(long long x) { return (x + 15) / 16 * 16; }
 
+// A second stream per device, on which independent work of one call runs
+// beside the caller's stream (fork and join through events).  Default
+// priority; created on first use and kept for the life of the process.
+struct AuxStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool tried = false;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_aux_mu;  // guards g_aux and every fork ... join sequence
+AuxStream g_aux[MAX_DEVICES];
+
+// Caller holds g_aux_mu.  Null when no second stream can be had (the work
+// then runs on the caller's stream alone).
+AuxStream *aux_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    AuxStream &a = g_aux[dev];
+    if (!a.tried) {
+        a.tried = true;
+        if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
+            a.s = nullptr;
+    }
+    return a.s ? &a : nullptr;
+}
+
 ConvGeom geom(const ie_conv_desc *d) {
     ConvGeom g;
     g.n = d->n;
@@ -395,6 +426,40 @@ size_t conv_bwd_ws(const ie_conv_desc *d) {
     return align256(c.off);
 }
 
+ie_status check_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar weight_decay) {
+    IE_CHECK(check_mat(W));
+    IE_CHECK(check_mat(V));
+    IE_CHECK(check_mat(G));
+    if (V->rows != W->rows || V->cols != W->cols || G->rows != W->rows || G->cols != W->cols)
+        return IE_ERR_SHAPE;
+    if (weight_decay.mant != 0) return IE_ERR_UNSUPPORTED;
+    if (W->cols > 64 * 4 * 32) return IE_ERR_UNSUPPORTED;
+    return IE_OK;
+}
+
+UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar lr, ie_scalar momentum,
+                       int *tmp, void *ws) {
+    UpdateArgs a;
+    a.w = W->mant;
+    a.w_exp = W->exp;
+    a.v = V->mant;
+    a.v_exp = V->exp;
+    a.g = G->mant;
+    a.g_exp = G->exp;
+    a.w_row = W->group == IE_GROUP_ROW;
+    a.v_row = V->group == IE_GROUP_ROW;
+    a.g_row = G->group == IE_GROUP_ROW;
+    a.rows = W->rows;
+    a.cols = W->cols;
+    a.lr_m = lr.mant;
+    a.lr_e = lr.exp;
+    a.mom_m = momentum.mant;
+    a.mom_e = momentum.exp;
+    a.tmp = tmp;
+    a.flags = (uint32_t *)ws;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +488,10 @@ size_t ie_sgd_update_workspace(int64_t rows, int64_t cols) {
     (void)rows;
     (void)cols;
     return HEADER + align256(UPD_WS_INTS * sizeof(int));
+}
+size_t ie_sgd_update_multi_workspace(int32_t n) {
+    if (n < 0) return 0;
+    return HEADER + (size_t)(n > 0 ? n : 1) * align256(UPD_WS_INTS * sizeof(int));
 }
 
 ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -613,63 +682,71 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
         IE_TRY(launch_pad_rows(dY->mant, npq, g.k, nullptr, 0, nullptr, g.kp, dyp, st));
         dys = dyp;
     }
-    if (dX) {
+    auto dgrad = [&](hipStream_t s) -> ie_status {
         IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, g.k, g.r * g.s, g.c, g.kp, wt,
-                                      estar, st));
+                                      estar, s));
         Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
         Operand B{LD_K, wt, rskp, g.c, {}};
         ExpSrc ea{dY->exp, nullptr, 0};
         ExpSrc eb{nullptr, estar, 0};
-        IE_CHECK(run_product(A, B, nhw, g.c, rskp, ea, eb, dX, pw, flags, 1, st));
-    }
-    if (dW) {
+        return run_product(A, B, nhw, g.c, rskp, ea, eb, dX, pw, flags, 1, s);
+    };
+    auto wgrad = [&](hipStream_t s) -> ie_status {
         const int8_t *xs = X->mant;
         if (xp) {
-            IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
+            IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, s));
             xs = xp;
         }
         Operand A{LD_T, dys, g.kp, g.k, {}};
         Operand B{LD_IM2COL_T, xs, g.cp, (int)rscp, g};
-        IE_CHECK(run_wgrad(A, B, g.k, rscp, rsc, g.c, g.cp, npq, ExpSrc{dY->exp, nullptr, 0},
-                           ExpSrc{X->exp, nullptr, 0}, dW, w, flags, st));
+        return run_wgrad(A, B, g.k, rscp, rsc, g.c, g.cp, npq, ExpSrc{dY->exp, nullptr, 0},
+                         ExpSrc{X->exp, nullptr, 0}, dW, w, flags, s);
+    };
+    if (dX && dW) {
+        // the two products are independent: the weight gradient runs on a
+        // second stream beside the input gradient
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        if (AuxStream *ax = aux_stream()) {
+            IE_TRY(hipEventRecord(ax->fork, st));
+            IE_TRY(hipStreamWaitEvent(ax->s, ax->fork, 0));
+            const ie_status sw = wgrad(ax->s);
+            const hipError_t ej = hipEventRecord(ax->join, ax->s);
+            const ie_status sd = dgrad(st);
+            const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(st, ax->join, 0) : ej;
+            if (sw != IE_OK) return sw;
+            if (sd != IE_OK) return sd;
+            return hip_status(ew);
+        }
     }
+    if (dX) IE_CHECK(dgrad(st));
+    if (dW) IE_CHECK(wgrad(st));
     return IE_OK;
 }
 
 ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar lr, ie_scalar momentum,
                         ie_scalar weight_decay, void *ws, size_t ws_bytes, void *stream) {
-    IE_CHECK(check_mat(W));
-    IE_CHECK(check_mat(V));
-    IE_CHECK(check_mat(G));
-    if (V->rows != W->rows || V->cols != W->cols || G->rows != W->rows || G->cols != W->cols)
-        return IE_ERR_SHAPE;
-    if (weight_decay.mant != 0) return IE_ERR_UNSUPPORTED;
-    if (W->cols > 64 * 4 * 32) return IE_ERR_UNSUPPORTED;
+    IE_CHECK(check_update(W, V, G, weight_decay));
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < ie_sgd_update_workspace(W->rows, W->cols)) return IE_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
     Carve c{(char *)ws, HEADER};
-    int *tmp = c.take<int>(UPD_WS_INTS);
-    UpdateArgs a;
-    a.w = W->mant;
-    a.w_exp = W->exp;
-    a.v = V->mant;
-    a.v_exp = V->exp;
-    a.g = G->mant;
-    a.g_exp = G->exp;
-    a.w_row = W->group == IE_GROUP_ROW;
-    a.v_row = V->group == IE_GROUP_ROW;
-    a.g_row = G->group == IE_GROUP_ROW;
-    a.rows = W->rows;
-    a.cols = W->cols;
-    a.lr_m = lr.mant;
-    a.lr_e = lr.exp;
-    a.mom_m = momentum.mant;
-    a.mom_e = momentum.exp;
-    a.tmp = tmp;
-    a.flags = (uint32_t *)ws;
-    return hip_status(launch_sgd_update(a, st));
+    UpdateArgs a = update_args(W, V, G, lr, momentum, c.take<int>(UPD_WS_INTS), ws);
+    return hip_status(launch_sgd_update(a, (hipStream_t)stream));
 }
+
+ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar lr,
+                              ie_scalar momentum, ie_scalar weight_decay, void *ws, size_t ws_bytes, void *stream) {
+    if (n < 0) return IE_ERR_SHAPE;
+    if (n == 0) return IE_OK;
+    if (!W || !V || !G) return IE_ERR_NULL;
+    for (int i = 0; i < n; ++i) IE_CHECK(check_update(W + i, V + i, G + i, weight_decay));
+    if (!ws) return IE_ERR_WORKSPACE;
+    if (ws_bytes < ie_sgd_update_multi_workspace(n)) return IE_ERR_WORKSPACE;
+    Carve c{(char *)ws, HEADER};
+    std::vector<UpdateArgs> a((size_t)n);
+    for (int i = 0; i < n; ++i) a[i] = update_args(W + i, V + i, G + i, lr, momentum, c.take<int>(UPD_WS_INTS), ws);
+    return hip_status(launch_sgd_update_multi(a.data(), n, (hipStream_t)stream));
+}
+
 
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {
     if (!ws || !flags) return IE_ERR_NULL;

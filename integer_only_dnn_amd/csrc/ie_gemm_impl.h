@@ -27,8 +27,10 @@
 #define IE_STAGES 4
 #endif
 #ifndef IE_UNROLL
-#define IE_UNROLL 2
+#define IE_UNROLL 4
 #endif
+
+#include <type_traits>
 
 #include "ie_device.h"
 #include "ie_internal.h"
@@ -63,20 +65,19 @@ struct Lds {
 // ---------------------------------------------------------------------------
 // Loaders.  Every operand is read in 16-byte chunks (the host pads channel
 // and contraction extents to multiples of 16).  Loads are unconditional: an
-// out-of-range chunk reads a clamped in-range address and its bit in the
-// stage's validity mask is clear; the zeros are substituted only when the
-// stage is written to LDS, so nothing consumes a loaded register before then
-// and the prefetched loads stay in flight across the MFMA work.
-// Each thread moves ROWS * BK / 4096 chunks per contraction step.
+// out-of-range chunk reads a 16-byte chunk of zeros instead, so no loaded
+// register is touched before the stage is written to LDS and the prefetched
+// loads stay in flight across the MFMA work.  Each thread moves
+// ROWS * BK / 4096 chunks per contraction step.
 // ---------------------------------------------------------------------------
+
+// Read-only zeros (device globals start zeroed and nothing writes this one).
+static __device__ __attribute__((aligned(16))) int8_t g_zero_chunk[16];
+
+__device__ __forceinline__ const int8_t *zero_chunk() { return g_zero_chunk; }
 
 template <int KIND, int ROWS>
 struct Ld;
-
-__device__ __forceinline__ v4i zero_unless(bool ok, v4i v) {
-    v4i z = {0, 0, 0, 0};
-    return ok ? v : z;
-}
 
 // [row][k] chunks: chunk c of thread tid -> tile row (tid + 256 c) / CPR,
 // contraction offset ((tid + 256 c) % CPR) * 16 (the same for every c).
@@ -87,9 +88,9 @@ struct KChunks {
     static constexpr int STRIDE = BK + 16;
     __device__ __forceinline__ static int row(int c, int tid) { return (tid + NTHR * c) / CPR; }
     __device__ __forceinline__ static int col(int tid) { return (tid % CPR) * 16; }
-    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH], uint32_t msk) {
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) *(v4i *)(s + row(c, tid) * STRIDE + col(tid)) = zero_unless((msk >> c) & 1, reg[c]);
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + row(c, tid) * STRIDE + col(tid)) = reg[c];
     }
 };
 
@@ -102,10 +103,9 @@ struct TChunks {
     static constexpr int STRIDE = ROWS + 16;
     __device__ __forceinline__ static int krow(int c, int tid) { return (tid + NTHR * c) / PER; }
     __device__ __forceinline__ static int ic(int tid) { return tid % PER; }
-    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH], uint32_t msk) {
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
-            *(v4i *)(s + krow(c, tid) * STRIDE + ic(tid) * 16) = zero_unless((msk >> c) & 1, reg[c]);
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + krow(c, tid) * STRIDE + ic(tid) * 16) = reg[c];
     }
 };
 
@@ -115,26 +115,21 @@ struct Ld<LD_K, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
     static constexpr int CH = B_::CH;
     const int8_t *ptr[CH];
-    uint32_t okm;
+    bool ok[CH];
     int col;
     __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
         col = B_::col(tid);
-        okm = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int i = i0 + B_::row(c, tid);
-            const bool ok = i < op.rows;
-            okm |= (uint32_t)ok << c;
-            ptr[c] = op.base + (long long)(ok ? i : 0) * op.ld + col;
+            ok[c] = i < op.rows;
+            ptr[c] = op.base + (long long)(ok[c] ? i : 0) * op.ld + col;
         }
     }
-    // out of range along k: read the row's first chunk instead
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
         const bool kin = k0 + col < kend;
-        const int kk = kin ? k0 : -col;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) reg[c] = *(const v4i *)(ptr[c] + kk);
-        msk = kin ? okm : 0u;
+        for (int c = 0; c < CH; ++c) reg[c] = *(const v4i *)(ok[c] && kin ? ptr[c] + k0 : zero_chunk());
     }
 };
 
@@ -165,19 +160,17 @@ struct Ld<LD_IM2COL, ROWS> : KChunks<ROWS> {
             pix[c] = (long long)n * g.h * g.w * g.cp;
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
         const uint32_t kk = k0 + col;
         const bool kin = (int)kk < kend;
         const uint32_t rs = fdiv(kk, g.dc), ch = kk - rs * g.cp;
         const uint32_t r = fdiv(rs, g.ds), s = rs - r * g.s;
-        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int h = hb[c] + (int)r, w = wb[c] + (int)s;
             const bool in = kin && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
-            const long long off = in ? pix[c] + ((long long)h * g.w + w) * g.cp + ch : 0;
-            reg[c] = *(const v4i *)(x + off);
-            msk |= (uint32_t)in << c;
+            const long long off = pix[c] + ((long long)h * g.w + w) * g.cp + ch;
+            reg[c] = *(const v4i *)(in ? x + off : zero_chunk());
         }
     }
 };
@@ -210,21 +203,19 @@ struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
             pix[c] = (long long)n * g.p * g.q * g.kp;
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
         const uint32_t kk = k0 + col;
         const bool kin = (int)kk < kend;
         const uint32_t rs = fdiv(kk, g.dk), ko = kk - rs * g.kp;
         const int r = (int)fdiv(rs, g.ds), s = (int)(rs - (uint32_t)r * g.s);
-        msk = 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int a = hp[c] - r, b = wp[c] - s;
             const int p = (int)fdiv((uint32_t)max(a, 0), g.dst), q = (int)fdiv((uint32_t)max(b, 0), g.dst);
             const bool in = kin && a >= 0 && b >= 0 && p * g.stride == a && q * g.stride == b && p < g.p &&
                             q < g.q;
-            const long long off = in ? pix[c] + ((long long)p * g.q + q) * g.kp + ko : 0;
-            reg[c] = *(const v4i *)(dy + off);
-            msk |= (uint32_t)in << c;
+            const long long off = pix[c] + ((long long)p * g.q + q) * g.kp + ko;
+            reg[c] = *(const v4i *)(in ? dy + off : zero_chunk());
         }
     }
 };
@@ -244,14 +235,12 @@ struct Ld<LD_T, ROWS> : TChunks<ROWS> {
         base = op.base + (iok ? i : 0);
         ld = op.ld;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
-        msk = 0;
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int k = k0 + B_::krow(c, tid);
             const bool in = iok && k < kend;
-            reg[c] = *(const v4i *)(base + (long long)(k < kend ? k : 0) * ld);
-            msk |= (uint32_t)in << c;
+            reg[c] = *(const v4i *)(in ? base + (long long)k * ld : zero_chunk());
         }
     }
 };
@@ -277,8 +266,7 @@ struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
         jr = (int)fdiv(rs, g.ds);
         js = (int)rs - jr * g.s;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH], uint32_t &msk) {
-        msk = 0;
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int kk = k0 + B_::krow(c, tid);
@@ -287,9 +275,8 @@ struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
             const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
             const int h = (int)p * g.stride + jr - g.pad, w = (int)q * g.stride + js - g.pad;
             const bool in = jok && kk < kend && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
-            const long long off = in ? (((long long)n * g.h + h) * g.w + w) * g.cp + jc : 0;
-            reg[c] = *(const v4i *)(x + off);
-            msk |= (uint32_t)in << c;
+            const long long off = (((long long)n * g.h + h) * g.w + w) * g.cp + jc;
+            reg[c] = *(const v4i *)(in ? x + off : zero_chunk());
         }
     }
 };
@@ -350,7 +337,7 @@ struct Stages {
 };
 
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
-__global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
+__global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
                                                                           int K, int k_chunk, int TM, Epi ep) {
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
     using LA = Lds<KA, BMt>;
@@ -401,17 +388,16 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
     // s - 1 and computed at step s, so a load has NS - 1 steps to land.
     constexpr int NS = Stages<MI, NI>::value;
     v4i ra[NS][CA], rb[NS][CB];
-    uint32_t ma[NS], mb[NS];
     // An empty chunk issues no load at all: with an empty contraction the
     // operand pointers need not address any memory.
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            la.load(kb + s * BK, ke, tid, ra[s], ma[s]);
-            lb.load(kb + s * BK, ke, tid, rb[s], mb[s]);
+            la.load(kb + s * BK, ke, tid, ra[s]);
+            lb.load(kb + s * BK, ke, tid, rb[s]);
         }
-        la.store(lds, tid, ra[0], ma[0]);
-        lb.store(lds + LA::BYTES, tid, rb[0], mb[0]);
+        la.store(lds, tid, ra[0]);
+        lb.store(lds + LA::BYTES, tid, rb[0]);
     }
     __syncthreads();
 
@@ -432,9 +418,9 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
         }
     };
 
-    // NU sub-steps per trip: the back edge costs one full drain of the loads
-    // in flight, so it is taken once per NU steps
-    constexpr int NU = IE_UNROLL * NS * (NS % 2 ? 2 : 1);  // even: step parity picks the LDS buffer
+    // NU sub-steps per trip: the back edge costs a drain of the loads in
+    // flight, so it is taken once per NU steps (never for short contractions)
+    constexpr int NU = NS % 2 ? 4 * NS : IE_UNROLL * NS;  // even: step parity picks the LDS buffer
     for (int it = 0; it < nk; it += NU) {
 #pragma unroll
         for (int uu = 0; uu < NU; ++uu) {
@@ -442,50 +428,88 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
             const int s = it + uu;
             if (s >= nk) break;
             // set u held stage s, already in LDS: refill it with stage s + NS
-            // (past the end: clamped reads, all masked)
-            la.load(kb + (s + NS) * BK, ke, tid, ra[u], ma[u]);
-            lb.load(kb + (s + NS) * BK, ke, tid, rb[u], mb[u]);
+            // (past the end: zero chunks)
+            la.load(kb + (s + NS) * BK, ke, tid, ra[u]);
+            lb.load(kb + (s + NS) * BK, ke, tid, rb[u]);
 #ifndef IE_NO_SCHED_BARRIER
             // keep the refill ahead of the fragment reads, so that no fragment
             // lands in registers whose loads are still in flight
             __builtin_amdgcn_sched_barrier(0);
 #endif
             compute(lds + (uu & 1) * STAGE);
-            // stage s + 1 (all zeros past the end, a buffer nobody reads)
-            la.store(lds + ((uu + 1) & 1) * STAGE, tid, ra[(u + 1) % NS], ma[(u + 1) % NS]);
-            lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS], mb[(u + 1) % NS]);
+            // stage s + 1 (past the end: zeros into a buffer nobody reads)
+            la.store(lds + ((uu + 1) & 1) * STAGE, tid, ra[(u + 1) % NS]);
+            lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS]);
             __syncthreads();
         }
     }
 
     // Element (a, b, r) of this lane sits at tile row / column
-    //   32 MI wm + 32 a + 8 (r/4) + 4 (lane/32) + r%4,   32 NI wn + 32 b + lane%32.
-    auto ROW = [&](int a, int r) { return m0 + wm * 32 * MI + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
-    auto COL = [&](int b) { return n0 + wn * 32 * NI + b * 32 + (lane & 31); };
+    //   TR = 32 MI wm + 32 a + 8 (r/4) + 4 (lane/32) + r%4,   TC = 32 NI wn + 32 b + lane%32.
+    const int tr0 = wm * 32 * MI + 4 * (lane >> 5);
+    const int tc0 = wn * 32 * NI + (lane & 31);
+    auto TR = [&](int a, int r) { return tr0 + a * 32 + 8 * (r >> 2) + (r & 3); };
+    auto TC = [&](int b) { return tc0 + b * 32; };
+
+    // Results leave through LDS: every lane writes its values into a
+    // row-major staging tile (element size ES bytes, row pitch padded so that
+    // the two half-waves, four rows apart, hit different banks), then the
+    // tile is written out in 16-byte row chunks.
+    auto flush = [&](auto es_tag, void *dst, long long ld, bool vec) {
+        constexpr int ES = decltype(es_tag)::value;
+        constexpr int PITCH = BNt * ES + (ES == 4 ? 32 : 16);
+        constexpr int CPR = BNt * ES / 16;  // chunks per tile row
+        constexpr int EPC = 16 / ES;        // elements per chunk
+#pragma unroll
+        for (int q0 = 0; q0 < BMt * CPR; q0 += NTHR) {
+            const int q = q0 + tid;
+            const int row = q / CPR, cb = (q % CPR) * 16;
+            const int grow = m0 + row, gcol = n0 + cb / ES;
+            if (grow >= M || gcol >= N) continue;
+            const v4i v = *(const v4i *)(lds + row * PITCH + cb);
+            int8_t *g = (int8_t *)dst + ((long long)grow * ld + gcol) * ES;
+            if (vec && gcol + EPC <= N) {
+                *(v4i *)g = v;
+            } else {
+                const int8_t *b8 = (const int8_t *)&v;
+                for (int j = 0; j < EPC && gcol + j < N; ++j)
+                    for (int t = 0; t < ES; ++t) g[j * ES + t] = b8[j * ES + t];
+            }
+        }
+    };
+    auto stage = [&](auto es_tag, int a, int b, int r, int v) {
+        constexpr int ES = decltype(es_tag)::value;
+        constexpr int PITCH = BNt * ES + (ES == 4 ? 32 : 16);
+        int8_t *d = lds + TR(a, r) * PITCH + TC(b) * ES;
+        if constexpr (ES == 1) *d = (int8_t)v;
+        else if constexpr (ES == 2) *(int16_t *)d = (int16_t)v;
+        else *(int *)d = v;
+    };
+    using ES1 = std::integral_constant<int, 1>;
+    using ES2 = std::integral_constant<int, 2>;
+    using ES4 = std::integral_constant<int, 4>;
 
     if constexpr (PARTIAL) {
-        int *P = ep.partial + (long long)z * ep.split_stride;
+        static_assert(BMt * (BNt * 4 + 32) <= 2 * STAGE, "staging tile exceeds LDS");
 #pragma unroll
         for (int a = 0; a < MI; ++a)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = ROW(a, r);
-                if (row >= M) continue;
+            for (int b = 0; b < NI; ++b)
 #pragma unroll
-                for (int b = 0; b < NI; ++b) {
-                    const int col = COL(b);
-                    if (col < N) P[(long long)row * N + col] = acc[a][b][r];
-                }
-            }
+                for (int r = 0; r < 16; ++r) stage(ES4{}, a, b, r, acc[a][b][r]);
+        __syncthreads();
+        flush(ES4{}, ep.partial + (long long)z * ep.split_stride, N, (N & 3) == 0);
         return;
     } else {
-        int *red = (int *)lds;
+        int *red = (int *)(lds + 2 * STAGE) - 2 * BMt;  // maxima, at the top of LDS
+        static_assert(BMt * (BNt * 2 + 16) + 2 * BMt * 4 <= 2 * STAGE, "staging tile exceeds LDS");
         int ebv[NI];
 #pragma unroll
-        for (int b = 0; b < NI; ++b) ebv[b] = seB[COL(b) - n0];
+        for (int b = 0; b < NI; ++b) ebv[b] = seB[TC(b)];
         const bool uni = !ep.ea.row && !ep.eb.row;
         const int ea0 = seA[0];
         const int eb0 = seB[0];
+        const bool direct = ep.mode == EPI_DIRECT;
 
         if (!ep.row_group) {
             // whole-tensor group: one maximum for the tile
@@ -508,7 +532,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                 for (int a = 0; a < MI; ++a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int eav = seA[ROW(a, r) - m0];
+                        const int eav = seA[TR(a, r)];
 #pragma unroll
                         for (int b = 0; b < NI; ++b) tmax = max(tmax, need32(acc[a][b][r], eav + ebv[b]));
                     }
@@ -517,8 +541,9 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
             if (lane == 0) red[wave] = tmax;
             __syncthreads();
             const int gmax = max(max(red[0], red[1]), max(red[2], red[3]));
-            int e, p = 0;
-            if (ep.mode == EPI_DIRECT) {
+            // the result's exponent (direct) or the round-to-odd position
+            int e = 0, p = 0;
+            if (direct) {
                 e = clamp_exp_flag(max(E_MIN, gmax), ep.flags);
                 if (tid == 0 && blockIdx.x == 0) ep.out_exp[0] = (int8_t)e;
             } else {
@@ -527,24 +552,58 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                 p = gmax == NEED_NONE ? P_NONE : gmax - 2;
                 if (tid == 0) ep.p16[tile_m + TM * tile_n] = (int16_t)(gmax == NEED_NONE ? P_NONE : gmax);
             }
+            if (uni) {
+                // one shift for the whole tile: a * 2^-t with t in [-31, 31]
+                int t = (direct ? e : p) - (ea0 + eb0);
+                t = t > 31 ? 31 : (t < -31 ? -31 : t);
+                if (t <= 0) {
+                    const int l = -t;
 #pragma unroll
-            for (int a = 0; a < MI; ++a)
+                    for (int a = 0; a < MI; ++a)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = ROW(a, r);
-                    if (row >= M) continue;
-                    const int eav = uni ? ea0 : seA[row - m0];
+                        for (int b = 0; b < NI; ++b)
 #pragma unroll
-                    for (int b = 0; b < NI; ++b) {
-                        const int col = COL(b);
-                        if (col >= N) continue;
-                        const long long o = (long long)row * N + col;
-                        if (ep.mode == EPI_DIRECT)
-                            ep.out[o] = (int8_t)rne_shift32(acc[a][b][r], e - (eav + ebv[b]));
-                        else
-                            ep.v16[o] = (int16_t)rto_shift32(acc[a][b][r], p - (eav + ebv[b]));
-                    }
+                            for (int r = 0; r < 16; ++r) {
+                                if (direct) stage(ES1{}, a, b, r, acc[a][b][r] << l);
+                                else stage(ES2{}, a, b, r, acc[a][b][r] << l);
+                            }
+                } else if (direct) {
+                    const int hm1 = (1 << (t - 1)) - 1;
+#pragma unroll
+                    for (int a = 0; a < MI; ++a)
+#pragma unroll
+                        for (int b = 0; b < NI; ++b)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int v = acc[a][b][r];
+                                stage(ES1{}, a, b, r, (v + hm1 + ((v >> t) & 1)) >> t);
+                            }
+                } else {
+                    const uint32_t mask = (1u << t) - 1u;
+#pragma unroll
+                    for (int a = 0; a < MI; ++a)
+#pragma unroll
+                        for (int b = 0; b < NI; ++b)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int v = acc[a][b][r];
+                                const int sticky = (int)((((uint32_t)v & mask) + mask) >> t);
+                                stage(ES2{}, a, b, r, (v >> t) | sticky);
+                            }
                 }
+            } else {
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int eav = seA[TR(a, r)];
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) {
+                            if (direct) stage(ES1{}, a, b, r, rne_shift32(acc[a][b][r], e - (eav + ebv[b])));
+                            else stage(ES2{}, a, b, r, rto_shift32(acc[a][b][r], p - (eav + ebv[b])));
+                        }
+                    }
+            }
         } else {
             // row groups: maximum per tile row, one 32-row slab at a time
 #pragma unroll
@@ -552,7 +611,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                 int rm[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int eav = seA[ROW(a, r) - m0];
+                    const int eav = seA[TR(a, r)];
                     int m = NEED_NONE;
 #pragma unroll
                     for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b]));
@@ -564,7 +623,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
                     for (int r = 0; r < 16; ++r) rm[r] = max(rm[r], __shfl_xor(rm[r], off));
                 if ((lane & 31) == 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) red[wn * BMt + ROW(a, r) - m0] = rm[r];
+                    for (int r = 0; r < 16; ++r) red[wn * BMt + TR(a, r)] = rm[r];
                 }
             }
             __syncthreads();
@@ -573,31 +632,28 @@ __global__ __launch_bounds__(NTHR, (MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(O
             for (int a = 0; a < MI; ++a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = ROW(a, r);
-                    if (row >= M) continue;
-                    const int rm = max(red[row - m0], red[BMt + row - m0]);
-                    const int eav = seA[row - m0];
+                    const int tr = TR(a, r), row = m0 + tr;
+                    const int rm = max(red[tr], red[BMt + tr]);
+                    const int eav = seA[tr];
                     int e = 0, p = 0;
-                    if (ep.mode == EPI_DIRECT) {
+                    if (direct) {
                         e = clamp_exp_flag(max(E_MIN, rm), ep.flags);
-                        if (wn == 0 && (lane & 31) == 0) ep.out_exp[row] = (int8_t)e;
+                        if (wn == 0 && (lane & 31) == 0 && row < M) ep.out_exp[row] = (int8_t)e;
                     } else {
                         p = rm == NEED_NONE ? P_NONE : rm - 2;
-                        if (wn == 0 && (lane & 31) == 0)
+                        if (wn == 0 && (lane & 31) == 0 && row < M)
                             ep.p16[(long long)row * n_ct + tile_n] = (int16_t)(rm == NEED_NONE ? P_NONE : rm);
                     }
 #pragma unroll
                     for (int b = 0; b < NI; ++b) {
-                        const int col = COL(b);
-                        if (col >= N) continue;
-                        const long long o = (long long)row * N + col;
-                        if (ep.mode == EPI_DIRECT)
-                            ep.out[o] = (int8_t)rne_shift32(acc[a][b][r], e - (eav + ebv[b]));
-                        else
-                            ep.v16[o] = (int16_t)rto_shift32(acc[a][b][r], p - (eav + ebv[b]));
+                        if (direct) stage(ES1{}, a, b, r, rne_shift32(acc[a][b][r], e - (eav + ebv[b])));
+                        else stage(ES2{}, a, b, r, rto_shift32(acc[a][b][r], p - (eav + ebv[b])));
                     }
                 }
         }
+        __syncthreads();
+        if (direct) flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0);
+        else flush(ES2{}, ep.v16, N, (N & 7) == 0);
     }
 }
 

@@ -164,5 +164,7 @@ struct UpdateArgs {
 constexpr int UPD_MAX_BLOCKS = 1024;  // grid of the update when a group spans the tensor
 constexpr int UPD_WS_INTS = 2 + 2 * UPD_MAX_BLOCKS;
 hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st);
+// The same for n tensors (each with its own tmp), in few launches.
+hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st);
 
 }  // namespace ie

@@ -134,9 +134,10 @@ __device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
 //   pass 2: whole-tensor weight: round W at the maximum of bmax_w.
 // Whole-tensor exponents that a pass overwrites are read from snapshots taken
 // by the pass before (tmp[0]: old velocity exponent, tmp[1]: old weight
-// exponent).  All passes run on the same grid.
+// exponent).  All passes run on the same grid of nblk blocks (this block is
+// blk of them).
 template <int D, int WPR>
-__global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec) {
+__device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int vec, int blk, int nblk) {
     constexpr int RPB = 4 / WPR;  // rows per block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
     };
     auto max_of = [&](const int *p) -> int {
         int m = NEED_NONE;
-        for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) m = max(m, p[i]);
+        for (int i = threadIdx.x; i < nblk; i += 256) m = max(m, p[i]);
         return block_imax(m);
     };
     // maximum over the row (all WPR waves); every wave of the block calls it
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
     int ev_t = 0, ew_t = 0, evn_t = 0, ewn_t = 0;
     if (pass == 0) {
         ev_t = a.v_exp[0];
-        if (blockIdx.x == 0 && threadIdx.x == 0) a.tmp[0] = ev_t;
+        if (blk == 0 && threadIdx.x == 0) a.tmp[0] = ev_t;
     } else if (pass == 1) {
         if (v_tensor) {
             ev_t = a.tmp[0];
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
         }
         if (w_tensor) {
             ew_t = a.w_exp[0];
-            if (blockIdx.x == 0 && threadIdx.x == 0) a.tmp[1] = ew_t;
+            if (blk == 0 && threadIdx.x == 0) a.tmp[1] = ew_t;
         }
     } else {
         ew_t = a.tmp[1];
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
     }
     int bneed = NEED_NONE;  // largest need of this block's rows (passes 0, 1)
 
-    for (long long row0 = (long long)blockIdx.x * RPB; row0 < a.rows; row0 += (long long)gridDim.x * RPB) {
+    for (long long row0 = (long long)blk * RPB; row0 < a.rows; row0 += (long long)nblk * RPB) {
         const long long row = row0 + wave / WPR;
         const bool live = row < a.rows;  // WPR = 1 only: trailing waves of the last block
         if (WPR == 1 && !live) continue;
@@ -357,17 +358,46 @@ __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, i
     }
     if (pass == 0 || (pass == 1 && w_tensor)) {
         const int m = block_imax(bneed);
-        if (threadIdx.x == 0) (pass == 0 ? bmax_v : bmax_w)[blockIdx.x] = m;
+        if (threadIdx.x == 0) (pass == 0 ? bmax_v : bmax_w)[blk] = m;
     }
 }
 
 template <int D, int WPR>
-static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
-    constexpr int RPB = 4 / WPR;
-    long long blocks = (a.rows + RPB - 1) / RPB;
+__global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec) {
+    update_rows<D, WPR>(a, pass, vec, blockIdx.x, gridDim.x);
+}
+
+// Several tensors of one (D, WPR) class in one launch: segment i owns blocks
+// [block0[i], block0[i + 1]).
+constexpr int UPD_SEGS = 12;
+struct UpdSegs {
+    UpdateArgs a[UPD_SEGS];
+    int vec[UPD_SEGS];
+    int block0[UPD_SEGS + 1];
+    int n;
+};
+
+template <int D, int WPR>
+__global__ __launch_bounds__(256) void sgd_multi_kernel(UpdSegs sg, int pass) {
+    int i = 0;
+    while (i + 1 < sg.n && (int)blockIdx.x >= sg.block0[i + 1]) ++i;
+    i = __builtin_amdgcn_readfirstlane(i);  // block-uniform: keep the segment's arguments scalar
+    update_rows<D, WPR>(sg.a[i], pass, sg.vec[i], blockIdx.x - sg.block0[i], sg.block0[i + 1] - sg.block0[i]);
+}
+
+// Grid of one tensor's passes.
+static int update_blocks(const UpdateArgs &a, int wpr) {
+    const int rpb = 4 / wpr;
+    long long blocks = (a.rows + rpb - 1) / rpb;
     const long long cap = (a.v_row && a.w_row) ? 65536 : UPD_MAX_BLOCKS;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
+    return (int)blocks;
+}
+
+template <int D, int WPR>
+static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
+    const int blocks = update_blocks(a, WPR);
     hipError_t err;
     for (int pass = 0; pass < 3; ++pass) {
         if (pass == 0 && a.v_row) continue;
@@ -380,38 +410,108 @@ static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
     return hipSuccess;
 }
 
-hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
-    hipError_t err;
-    if (a.rows <= 0) {
-        // Empty tensor: whole-tensor groups are all-zero.
-        if (a.v_row == 0 && (err = launch_fill_i8(a.v_exp, 1, E_MIN, st)) != hipSuccess) return err;
-        if (a.w_row == 0 && (err = launch_fill_i8(a.w_exp, 1, E_MIN, st)) != hipSuccess) return err;
-        return hipSuccess;
+template <int D, int WPR>
+static hipError_t run_multi(const UpdateArgs *a, const int *vec, int n, hipStream_t st) {
+    for (int pass = 0; pass < 3; ++pass) {
+        UpdSegs sg;
+        sg.n = 0;
+        int blocks = 0;
+        for (int i = 0; i < n; ++i) {
+            if ((pass == 0 && a[i].v_row) || (pass == 2 && a[i].w_row)) continue;
+            sg.a[sg.n] = a[i];
+            sg.vec[sg.n] = vec[i];
+            sg.block0[sg.n] = blocks;
+            blocks += update_blocks(a[i], WPR);
+            ++sg.n;
+        }
+        if (sg.n == 0) continue;
+        sg.block0[sg.n] = blocks;
+        prof_begin(st, 2000 + pass);
+        hipLaunchKernelGGL((sgd_multi_kernel<D, WPR>), dim3(blocks), dim3(256), 0, st, sg, pass);
+        prof_end(st, 2000 + pass);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    const int vec = (a.cols % 4 == 0) && ((uintptr_t)a.w % 4 == 0) && ((uintptr_t)a.v % 4 == 0) &&
-                    ((uintptr_t)a.g % 4 == 0);
+    return hipSuccess;
+}
+
+// Launch class of a tensor: rows of 256 dwords or more put four waves on a
+// row (one row per block), so a lane holds at most 8 dwords of each tensor
+// up to 8192 columns.  Returns 0..9 (an index into the instantiated (D, WPR)
+// pairs) or -1.
+static const int CLASS_D[10] = {1, 2, 3, 4, 1, 2, 3, 4, 6, 8};
+static int update_class(const UpdateArgs &a) {
     const long long dw = (a.cols + 3) / 4;
-    // Rows of 256 dwords or more: four waves share a row (one row per block),
-    // so a lane holds at most 8 dwords of each tensor up to 8192 columns.
     const bool wide = dw >= 256;
     const long long per_lane = wide ? (dw + 255) / 256 : (dw + 63) / 64;
-#define IE_UPD(DD, WW)                                                                                     \
-    if (per_lane <= DD) return run_passes<DD, WW>(a, vec, st);
-    if (!wide) {
-        IE_UPD(1, 1)
-        IE_UPD(2, 1)
-        IE_UPD(3, 1)
-        IE_UPD(4, 1)
-    } else {
-        IE_UPD(1, 4)
-        IE_UPD(2, 4)
-        IE_UPD(3, 4)
-        IE_UPD(4, 4)
-        IE_UPD(6, 4)
-        IE_UPD(8, 4)
+    for (int c = wide ? 4 : 0; c < (wide ? 10 : 4); ++c)
+        if (per_lane <= CLASS_D[c]) return c;
+    return -1;
+}
+
+static int update_vec(const UpdateArgs &a) {
+    return (a.cols % 4 == 0) && ((uintptr_t)a.w % 4 == 0) && ((uintptr_t)a.v % 4 == 0) &&
+           ((uintptr_t)a.g % 4 == 0);
+}
+
+static hipError_t run_class(int c, const UpdateArgs *a, const int *vec, int n, hipStream_t st) {
+    switch (c) {
+        case 0: return n == 1 ? run_passes<1, 1>(a[0], vec[0], st) : run_multi<1, 1>(a, vec, n, st);
+        case 1: return n == 1 ? run_passes<2, 1>(a[0], vec[0], st) : run_multi<2, 1>(a, vec, n, st);
+        case 2: return n == 1 ? run_passes<3, 1>(a[0], vec[0], st) : run_multi<3, 1>(a, vec, n, st);
+        case 3: return n == 1 ? run_passes<4, 1>(a[0], vec[0], st) : run_multi<4, 1>(a, vec, n, st);
+        case 4: return n == 1 ? run_passes<1, 4>(a[0], vec[0], st) : run_multi<1, 4>(a, vec, n, st);
+        case 5: return n == 1 ? run_passes<2, 4>(a[0], vec[0], st) : run_multi<2, 4>(a, vec, n, st);
+        case 6: return n == 1 ? run_passes<3, 4>(a[0], vec[0], st) : run_multi<3, 4>(a, vec, n, st);
+        case 7: return n == 1 ? run_passes<4, 4>(a[0], vec[0], st) : run_multi<4, 4>(a, vec, n, st);
+        case 8: return n == 1 ? run_passes<6, 4>(a[0], vec[0], st) : run_multi<6, 4>(a, vec, n, st);
+        case 9: return n == 1 ? run_passes<8, 4>(a[0], vec[0], st) : run_multi<8, 4>(a, vec, n, st);
     }
-#undef IE_UPD
     return hipErrorInvalidValue;
+}
+
+static hipError_t empty_update(const UpdateArgs &a, hipStream_t st) {
+    // Empty tensor: whole-tensor groups are all-zero.
+    hipError_t err;
+    if (a.v_row == 0 && (err = launch_fill_i8(a.v_exp, 1, E_MIN, st)) != hipSuccess) return err;
+    if (a.w_row == 0 && (err = launch_fill_i8(a.w_exp, 1, E_MIN, st)) != hipSuccess) return err;
+    return hipSuccess;
+}
+
+hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
+    if (a.rows <= 0) return empty_update(a, st);
+    const int c = update_class(a);
+    if (c < 0) return hipErrorInvalidValue;
+    const int vec = update_vec(a);
+    return run_class(c, &a, &vec, 1, st);
+}
+
+hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st) {
+    // one launch per pass for up to UPD_SEGS tensors of a launch class
+    for (int c = 0; c < 10; ++c) {
+        UpdateArgs seg[UPD_SEGS];
+        int vec[UPD_SEGS];
+        int k = 0;
+        for (int i = 0; i <= n; ++i) {
+            const bool take = i < n && a[i].rows > 0 && update_class(a[i]) == c;
+            if (take) {
+                seg[k] = a[i];
+                vec[k] = update_vec(a[i]);
+                ++k;
+            }
+            if (k == UPD_SEGS || (i == n && k > 0)) {
+                hipError_t err = run_class(c, seg, vec, k, st);
+                if (err != hipSuccess) return err;
+                k = 0;
+            }
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        if (a[i].rows > 0) continue;
+        hipError_t err = empty_update(a[i], st);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ie

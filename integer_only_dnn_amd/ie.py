@@ -52,6 +52,7 @@ EXPORTS = [
     ("ie_conv_fwd_workspace", c_size_t, [POINTER(ie_conv_desc)]),
     ("ie_conv_bwd_workspace", c_size_t, [POINTER(ie_conv_desc)]),
     ("ie_sgd_update_workspace", c_size_t, [c_int64, c_int64]),
+    ("ie_sgd_update_multi_workspace", c_size_t, [c_int32]),
     ("ie_workspace_init", c_int, [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_fwd", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_bwd_dx", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
@@ -59,6 +60,7 @@ EXPORTS = [
     ("ie_conv_fwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_sgd_update_multi", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_device_status", c_int, [c_void_p, c_void_p, POINTER(c_uint32), c_int]),
     ("ie_profile_enable", c_int, [c_int]),
     ("ie_profile_select", c_int, [c_int]),
@@ -197,6 +199,20 @@ def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws:
     p, b = ws.get(lib().ie_sgd_update_workspace(w.rows, w.cols))
     _check(lib().ie_sgd_update(byref(w), byref(v), byref(g), ie_scalar(*lr), ie_scalar(*momentum),
                                ie_scalar(*weight_decay), p, b, _stream(ws.device)), "ie_sgd_update")
+
+
+def ie_sgd_update_multi(Ws, Vs, Gs, lr, momentum, weight_decay=(0, 0), ws: Workspace = None) -> None:
+    """ie_sgd_update over lists of tensors (one optimiser step for many layers)."""
+    n = len(Ws)
+    if len(Vs) != n or len(Gs) != n:
+        raise ValueError("W, V and G lists differ in length")
+    arr = ie_mat * max(n, 1)
+    w = arr(*[m.c() for m in Ws])
+    v = arr(*[m.c() for m in Vs])
+    g = arr(*[m.c() for m in Gs])
+    p, b = ws.get(lib().ie_sgd_update_multi_workspace(n))
+    _check(lib().ie_sgd_update_multi(n, w, v, g, ie_scalar(*lr), ie_scalar(*momentum), ie_scalar(*weight_decay),
+                                     p, b, _stream(ws.device)), "ie_sgd_update_multi")
 
 
 def ie_profile_enable(on: bool = True) -> None:

@@ -507,7 +507,7 @@ def requant_exact(num, base, group_of: np.ndarray, n_groups: int):
 
 def _group_index(t: QT) -> tuple:
     rows = t.mant.shape[0]
-    per_row = t.mant.reshape(rows, -1).shape[1]
+    per_row = int(np.prod(t.mant.shape[1:], dtype=np.int64))
     if t.group == ROW:
         g = np.repeat(np.arange(rows), per_row).reshape(rows, per_row)
         return g, rows
@@ -586,7 +586,7 @@ def sgd_update(W: QT, V: QT, G: QT, lr: Scalar, beta: Scalar,
     Returns (W', V') as QT.
     """
     rows = W.mant.shape[0]
-    shp = W.mant.reshape(rows, -1).shape
+    shp = (rows, int(np.prod(W.mant.shape[1:], dtype=np.int64)))
     mw = W.mant.reshape(shp).astype(np.int64)
     mv = V.mant.reshape(shp).astype(np.int64)
     mg = G.mant.reshape(shp).astype(np.int64)

@@ -65,6 +65,15 @@ def test_conv_and_update_argument_errors():
     assert L.ie_sgd_update(by(W), by(_mat(32, 144)), by(_mat(31, 144)), S(1, -7), S(7, -3), S(0, 0),
                            1, 4096, None) == 2
     assert L.ie_sgd_update(by(W), by(W), by(W), S(1, -7), S(7, -3), S(1, -13), 1, 4096, None) == 6
+    arr = ie.ie_mat * 2
+    Ws, Vs, Gs = arr(W, W), arr(W, W), arr(W, _mat(31, 144))
+    big = 1 << 20
+    assert L.ie_sgd_update_multi(-1, Ws, Ws, Ws, S(1, -7), S(7, -3), S(0, 0), 1, big, None) == 2
+    assert L.ie_sgd_update_multi(0, None, None, None, S(1, -7), S(7, -3), S(0, 0), None, 0, None) == 0
+    assert L.ie_sgd_update_multi(2, None, Vs, Gs, S(1, -7), S(7, -3), S(0, 0), 1, big, None) == 1
+    assert L.ie_sgd_update_multi(2, Ws, Vs, Gs, S(1, -7), S(7, -3), S(0, 0), 1, big, None) == 2
+    assert L.ie_sgd_update_multi(2, Ws, Vs, Vs, S(1, -7), S(7, -3), S(0, 0), 1, 16, None) == 4
+    assert L.ie_sgd_update_multi_workspace(3) > L.ie_sgd_update_multi_workspace(1)
 
 
 def test_workspace_sizes_grow_with_shape():

@@ -217,6 +217,28 @@ def test_sgd_update(shape, groups, ws):
         assert ws.status() == 0
 
 
+def test_sgd_update_multi(ws):
+    """One call over a mixed batch equals the oracle tensor by tensor: several
+    launch classes, more tensors of one class than one launch holds, every
+    group combination, an empty tensor."""
+    announce("sgd_update_multi mixed batch")
+    rng = np.random.default_rng(4242)
+    shapes = [(17, 64)] * 14 + [(40, 256), (9, 1000), (12, 3072), (5, 4608), (3, 7), (0, 64), (33, 768)]
+    cases, devs = [], []
+    for i, (rows, cols) in enumerate(shapes):
+        groups = GROUPS[i % len(GROUPS)]
+        W, V, G = _upd_case(rng, rows, cols, groups, 40)
+        cases.append((W, V, G))
+        devs.append((qt_to_dev(W, rows=rows), qt_to_dev(V, rows=rows), qt_to_dev(G, rows=rows)))
+    lr, mom = (5, -9), (7, -3)
+    ie.ie_sgd_update_multi([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], lr, mom, ws=ws)
+    for i, ((W, V, G), (Wd, Vd, Gd)) in enumerate(zip(cases, devs)):
+        W2, V2 = o.sgd_update(W, V, G, o.Scalar(*lr), o.Scalar(*mom))
+        assert_same(Vd, V2, f"velocity of tensor {i} {shapes[i]}")
+        assert_same(Wd, W2, f"weight of tensor {i} {shapes[i]}")
+    assert ws.status() == 0
+
+
 def test_sgd_update_gap_sweep(ws):
     """Every exponent gap from -255 to 255 between the two terms of a sum."""
     announce("sgd_update gap sweep")
