@@ -683,13 +683,17 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
         dys = dyp;
     }
     auto dgrad = [&](hipStream_t s) -> ie_status {
+        Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
+        ExpSrc ea{dY->exp, nullptr, 0};
+        if (W->group == IE_GROUP_TENSOR && g.c % 16 == 0 && aligned(W->mant, 16)) {
+            // one weight exponent: nothing to align, read W in place
+            Operand B{LD_WT, W->mant, 0, g.c, g};
+            return run_product(A, B, nhw, g.c, rskp, ea, ExpSrc{W->exp, nullptr, 0}, dX, pw, flags, 1, s);
+        }
         IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, g.k, g.r * g.s, g.c, g.kp, wt,
                                       estar, s));
-        Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
         Operand B{LD_K, wt, rskp, g.c, {}};
-        ExpSrc ea{dY->exp, nullptr, 0};
-        ExpSrc eb{nullptr, estar, 0};
-        return run_product(A, B, nhw, g.c, rskp, ea, eb, dX, pw, flags, 1, s);
+        return run_product(A, B, nhw, g.c, rskp, ea, ExpSrc{nullptr, estar, 0}, dX, pw, flags, 1, s);
     };
     auto wgrad = [&](hipStream_t s) -> ie_status {
         const int8_t *xs = X->mant;

@@ -280,7 +280,7 @@ hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, 
     if (A.kind == LD_K && B.kind == LD_K) return launch_gemm_kk(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
     if (A.kind == LD_IM2COL && B.kind == LD_K)
         return launch_gemm_im2col(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
-    if (A.kind == LD_DGRAD && B.kind == LD_K)
+    if (A.kind == LD_DGRAD && (B.kind == LD_K || B.kind == LD_WT))
         return launch_gemm_dgrad(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
     if (A.kind == LD_T) return launch_gemm_wgrad(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
     return hipErrorInvalidValue;

@@ -6,6 +6,7 @@ namespace ie {
 
 hipError_t launch_gemm_dgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
+    if (B.kind == LD_WT) return launch_gemm_dgrad_wt(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
     IE_TILE_CASE(LD_DGRAD, LD_K, 2, 2)
     IE_TILE_CASE(LD_DGRAD, LD_K, 4, 1)
     IE_TILE_CASE(LD_DGRAD, LD_K, 2, 1)

@@ -1,0 +1,16 @@
+// Contraction kernels of the convolution input gradient that read a
+// whole-tensor-exponent weight in its stored layout (no transposed copy).
+#include "ie_gemm_impl.h"
+
+namespace ie {
+
+hipError_t launch_gemm_dgrad_wt(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                                int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
+    IE_TILE_CASE(LD_DGRAD, LD_WT, 2, 2)
+    IE_TILE_CASE(LD_DGRAD, LD_WT, 4, 1)
+    IE_TILE_CASE(LD_DGRAD, LD_WT, 2, 1)
+    IE_TILE_CASE(LD_DGRAD, LD_WT, 1, 1)
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ie

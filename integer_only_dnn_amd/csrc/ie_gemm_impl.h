@@ -51,7 +51,7 @@ __device__ __forceinline__ v4i pack16(const uint32_t *w) { return v4i{(int)w[0],
 
 template <int KIND>
 struct IsT {
-    static constexpr bool value = KIND == LD_T || KIND == LD_IM2COL_T;
+    static constexpr bool value = KIND == LD_T || KIND == LD_IM2COL_T || KIND == LD_WT;
 };
 
 // LDS tile of an operand with ROWS rows (GEMM M or N side).
@@ -277,6 +277,37 @@ struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
             const bool in = jok && kk < kend && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
             const long long off = (((long long)n * g.h + h) * g.w + w) * g.cp + jc;
             reg[c] = *(const v4i *)(in ? x + off : zero_chunk());
+        }
+    }
+};
+
+// Input gradient of a convolution, B side, straight from the weight
+// [k_out][r][s][c] (whole-tensor exponent, c a multiple of 16): row j = input
+// channel, k = (r, s, ko) over the padded output-channel count kp; 16
+// consecutive channels of one (r, s, ko) are contiguous.
+template <int ROWS>
+struct Ld<LD_WT, ROWS> : TChunks<ROWS> {
+    using B_ = TChunks<ROWS>;
+    static constexpr int CH = B_::CH;
+    const int8_t *base;
+    ConvGeom g;
+    long long rsc;
+    bool jok;
+    __device__ __forceinline__ void init(const Operand &op, int j0, int tid) {
+        g = op.g;
+        const int j = j0 + B_::ic(tid) * 16;
+        jok = j < op.rows;
+        base = op.base + (jok ? j : 0);
+        rsc = (long long)g.r * g.s * g.c;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int kk = k0 + B_::krow(c, tid);
+            const uint32_t kc = kk < kend ? kk : 0;
+            const uint32_t rs = fdiv(kc, g.dk), ko = kc - rs * g.kp;
+            const bool in = jok && kk < kend && (int)ko < g.k;
+            reg[c] = *(const v4i *)(in ? base + (long long)ko * rsc + (long long)rs * g.c : zero_chunk());
         }
     }
 };

@@ -53,7 +53,9 @@ enum LoaderKind {
     LD_T = 1,         // element (i, k) at base[k*ld + i]
     LD_IM2COL = 2,    // convolution forward: rows = output pixels, k = (r, s, c)
     LD_DGRAD = 3,     // convolution input gradient: rows = input pixels, k = (r, s, k_out)
-    LD_IM2COL_T = 4   // convolution weight gradient: rows = (r, s, c), k = output pixels
+    LD_IM2COL_T = 4,  // convolution weight gradient: rows = (r, s, c), k = output pixels
+    LD_WT = 5         // convolution input gradient, B side: rows = input channels c,
+                      // k = (r, s, k_out) over kp; weight read in place [k_out][r][s][c]
 };
 
 // n / d = (n * m) >> s for 0 <= n < 2^31 (m = ceil(2^s / d), s = 31 + ceil(log2 d)).
@@ -98,6 +100,8 @@ hipError_t launch_gemm_im2col(const Operand &A, const Operand &B, int M, int N, 
                               int k_chunk, bool partial, const Epi &ep, hipStream_t st);
 hipError_t launch_gemm_dgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+hipError_t launch_gemm_dgrad_wt(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
+                                int k_chunk, bool partial, const Epi &ep, hipStream_t st);
 hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
 

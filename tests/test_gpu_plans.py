@@ -78,20 +78,24 @@ def test_dense_direct(tile, ws, plan):
         assert_same(Y, o.linear_fwd(X, W, gy), f"direct group {gy}")
 
 
-CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1)]
+# 24 channels: the input gradient reads a transposed, aligned copy of W;
+# 32 / 48 channels with a whole-tensor W: it reads W in place
+CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1),
+              (2, 10, 10, 32, 40, 3, 3, 1, 1), (2, 9, 9, 48, 24, 3, 3, 2, 1)]
 
 
-@pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"st{s[7]}")
+@pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"c{s[3]}st{s[7]}")
 @pytest.mark.parametrize("tile", CONV_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
 @pytest.mark.parametrize("mode", MODES[:2], ids=lambda m: f"m{m[0]}s{m[1]}")
-def test_conv_plans(shape, tile, mode, ws, plan):
+@pytest.mark.parametrize("wg", [T, R], ids=["WT", "WR"])
+def test_conv_plans(shape, tile, mode, wg, ws, plan):
     n, h, w, c, k, r, s, st, pad = shape
-    announce(f"conv plans shape={shape} tile={tile} mode={mode}")
+    announce(f"conv plans shape={shape} tile={tile} mode={mode} w_group={wg}")
     d = o.ConvShape(*shape)
     dd = ie.conv_desc(*shape)
-    rng = np.random.default_rng(sum(shape) + 13 * tile[0] + tile[1] + mode[1])
+    rng = np.random.default_rng(sum(shape) + 13 * tile[0] + tile[1] + mode[1] + 7 * wg)
     X = rand_qt(rng, (n, h, w, c), T, zero_frac=0.2)
-    W = rand_qt(rng, (k, r * s * c), R)
+    W = rand_qt(rng, (k, r * s * c), wg)
     dY = rand_qt(rng, (n, d.p, d.q, k), T)
     Xd, Wd, dYd = qt_to_dev(X, rows=n * h * w), qt_to_dev(W), qt_to_dev(dY, rows=n * d.p * d.q)
     plan(tile, *mode)
