@@ -78,8 +78,9 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 //  * a split contraction costs an extra pass over splits x M x N int32
 //    partials, so products split only when even 64x64 tiles leave most CUs
 //    idle;
-//  * weight gradients (short outputs, long contractions) split so that
-//    about 2.25 workgroups run per CU.
+//  * weight gradients (short outputs, long contractions) split into chunks
+//    of at least eight steps, doubling while fewer than 2.25 workgroups per
+//    CU result.
 constexpr long long WG_TARGET = 576;
 
 enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2 };
@@ -162,7 +163,7 @@ Plan plan_wgrad(long long M, long long N, long long L) {
     const long long nt = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
     const int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
     int sp = 1;
-    while (sp < 1024 && nt * sp * 2 <= WG_TARGET * 3 / 2 && L / (sp * 2) >= 4 * BK) sp *= 2;
+    while (sp < 1024 && nt * sp * 2 < WG_TARGET && L / (sp * 2) >= 8 * BK) sp *= 2;
     if (sp < smin) sp = smin;
     const int kc = chunk_for(L, sp);
     return Plan{t, PLAN_SPLIT, (int)((L + kc - 1) / kc), kc};

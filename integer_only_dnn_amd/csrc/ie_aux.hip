@@ -548,6 +548,44 @@ __device__ __forceinline__ int block_max_n(int v, int *sh) {
     return m;
 }
 
+// a[j] += p[z * stride + j] over z = z0, z0 + dz, ... < n, eight loads in
+// flight at a time (VW = 4: one 16-byte load per split; VW = 1: one int).
+template <int VW>
+__device__ __forceinline__ void sum_splits(const int *p, long long stride, int z0, int dz, int n, long long (&a)[4]) {
+    int z = z0;
+    for (; z + 7 * dz < n; z += 8 * dz) {
+        if constexpr (VW == 4) {
+            v4i x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = *(const v4i *)(p + (long long)(z + u * dz) * stride);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a[0] += x[u][0];
+                a[1] += x[u][1];
+                a[2] += x[u][2];
+                a[3] += x[u][3];
+            }
+        } else {
+            int x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = p[(long long)(z + u * dz) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[0] += x[u];
+        }
+    }
+    for (; z < n; z += dz) {
+        if constexpr (VW == 4) {
+            const v4i x = *(const v4i *)(p + (long long)z * stride);
+            a[0] += x[0];
+            a[1] += x[1];
+            a[2] += x[2];
+            a[3] += x[3];
+        } else {
+            a[0] += p[(long long)z * stride];
+        }
+    }
+}
+
 __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
@@ -569,22 +607,13 @@ __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *par
         if (Q > 1) {
             // short row: chunk c = tid % nch, split subset q = tid / nch
             const int c = tid % nch, q = tid / nch;
-            long long a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+            long long a4[4] = {0, 0, 0, 0};
             if (q < Q) {
-                if (vw == 4) {
-#pragma unroll 4
-                    for (int z = q; z < splits; z += Q) {
-                        const v4i x = *(const v4i *)(prow + z * stride + 4 * c);
-                        a0 += x[0];
-                        a1 += x[1];
-                        a2 += x[2];
-                        a3 += x[3];
-                    }
-                } else {
-                    const int sc = src_col(c);
-#pragma unroll 4
-                    for (int z = q; z < splits; z += Q) a0 += prow[z * stride + sc];
-                }
+                if (vw == 4) sum_splits<4>(prow + 4 * c, stride, q, Q, splits, a4);
+                else sum_splits<1>(prow + src_col(c), stride, q, Q, splits, a4);
+            }
+            long long a0 = a4[0], a1 = a4[1], a2 = a4[2], a3 = a4[3];
+            if (q < Q) {
                 acc[4 * tid + 0] = a0;
                 acc[4 * tid + 1] = a1;
                 acc[4 * tid + 2] = a2;
@@ -613,19 +642,8 @@ __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *par
                 const int c = tid + SR_THR * k;
                 v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0;
                 if (c < nch) {
-                    if (vw == 4) {
-#pragma unroll 4
-                        for (int z = 0; z < splits; ++z) {
-                            const v4i x = *(const v4i *)(prow + z * stride + 4 * c);
-                            v[k][0] += x[0];
-                            v[k][1] += x[1];
-                            v[k][2] += x[2];
-                            v[k][3] += x[3];
-                        }
-                    } else {
-                        const int sc = src_col(c);
-                        for (int z = 0; z < splits; ++z) v[k][0] += prow[z * stride + sc];
-                    }
+                    if (vw == 4) sum_splits<4>(prow + 4 * c, stride, 0, 1, splits, v[k]);
+                    else sum_splits<1>(prow + src_col(c), stride, 0, 1, splits, v[k]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         if (j < vw) need = max(need, need64(v[k][j], er + exp_at(eb, vw * c + j)));

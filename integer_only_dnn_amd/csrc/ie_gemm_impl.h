@@ -343,6 +343,46 @@ __device__ __forceinline__ int wave_max(int v) {
     return v;
 }
 
+// Maxima of 16 rows over the 32 lanes of a half-wave, transposing as it
+// reduces (16 exchanges instead of 80): at each step a lane keeps half of its
+// rows and takes the partner's values for them.  The lane ends with the
+// maximum of row 8 b4 + 4 b3 + 2 b2 + b1 (b_i = bit i of the lane).
+__device__ __forceinline__ int rows16_max(const int (&v)[16], int lane) {
+    int w[8], x[4], y[2];
+    const bool u16 = lane & 16, u8 = lane & 8, u4 = lane & 4, u2 = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = max(u16 ? v[i + 8] : v[i], __shfl_xor(u16 ? v[i] : v[i + 8], 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = max(u8 ? w[i + 4] : w[i], __shfl_xor(u8 ? w[i] : w[i + 4], 8));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) y[i] = max(u4 ? x[i + 2] : x[i], __shfl_xor(u4 ? x[i] : x[i + 2], 4));
+    int z = max(u2 ? y[1] : y[0], __shfl_xor(u2 ? y[0] : y[1], 2));
+    return max(z, __shfl_xor(z, 1));
+}
+
+__device__ __forceinline__ int rows16_row(int lane) {
+    return 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+}
+
+// Branch-free forms of rne_shift32 / rto_shift32 (the same results, shift
+// clamped to [-31, 31]): x = a * 2^L, then a right shift by R, with L or R zero.
+__device__ __forceinline__ int rne_bf(int a, int s) {
+    s = min(max(s, -31), 31);
+    const int L = max(-s, 0), R = max(s, 0);
+    const int x = a << L;
+    const int hm1 = R > 0 ? (1 << (R - 1)) - 1 : 0;
+    const int bit = R > 0 ? (x >> R) & 1 : 0;
+    return (x + hm1 + bit) >> R;
+}
+
+__device__ __forceinline__ int rto_bf(int a, int t) {
+    t = min(max(t, -31), 31);
+    const int L = max(-t, 0), R = max(t, 0);
+    const int x = a << L;
+    const uint32_t mask = (1u << R) - 1u;
+    return (x >> R) | (int)((((uint32_t)x & mask) + mask) >> R);
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -533,7 +573,8 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
         return;
     } else {
         int *red = (int *)(lds + 2 * STAGE) - 2 * BMt;  // maxima, at the top of LDS
-        static_assert(BMt * (BNt * 2 + 16) + 2 * BMt * 4 <= 2 * STAGE, "staging tile exceeds LDS");
+        int *scr = red - 16;                             // block reductions
+        static_assert(BMt * (BNt * 2 + 16) + 4 * BMt * 4 + 64 <= 2 * STAGE, "staging tile exceeds LDS");
         int ebv[NI];
 #pragma unroll
         for (int b = 0; b < NI; ++b) ebv[b] = seB[TC(b)];
@@ -623,64 +664,154 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
                             }
                 }
             } else {
+                // per-element exponents: every shift computed, branch free
+                auto elems = [&](auto dir_tag) {
+                    constexpr bool DIR = decltype(dir_tag)::value;
+                    const int tgt = DIR ? e : p;
+#pragma unroll
+                    for (int a = 0; a < MI; ++a)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int off = tgt - seA[TR(a, r)];
+#pragma unroll
+                            for (int b = 0; b < NI; ++b) {
+                                if constexpr (DIR) stage(ES1{}, a, b, r, rne_bf(acc[a][b][r], off - ebv[b]));
+                                else stage(ES2{}, a, b, r, rto_bf(acc[a][b][r], off - ebv[b]));
+                            }
+                        }
+                };
+                if (direct) elems(std::true_type{});
+                else elems(std::false_type{});
+            }
+        } else {
+            // row groups.  The float path (contractions of at most 1024, so
+            // |acc| <= 2^24 converts to fp32 exactly, and a column-exponent
+            // spread of at most 96 within the tile) compares |acc| 2^(eb - ebmin)
+            // in fp32 and rounds by an exact power-of-two scaling; otherwise
+            // every element's need and shift are computed in integers.
+            int *rowi = scr - 2 * BMt;              // per tile row: integer offset
+            float *rowf = (float *)(scr - BMt);     //   or fp32 scale
+            int lo = ebv[0], hi = ebv[0];
+#pragma unroll
+            for (int b = 1; b < NI; ++b) {
+                lo = min(lo, ebv[b]);
+                hi = max(hi, ebv[b]);
+            }
+            lo = -wave_max(-lo);
+            hi = wave_max(hi);
+            if (lane == 0) {
+                scr[wave] = lo;
+                scr[4 + wave] = hi;
+            }
+            __syncthreads();
+            const int ebmin = min(min(scr[0], scr[1]), min(scr[2], scr[3]));
+            const int ebmax = max(max(scr[4], scr[5]), max(scr[6], scr[7]));
+            const bool fpath = ke - kb <= 1024 && ebmax - ebmin <= 96;
+            float cs[NI];
+#pragma unroll
+            for (int b = 0; b < NI; ++b) cs[b] = __builtin_ldexpf(1.0f, fpath ? ebv[b] - ebmin : 0);
+
+            // 1. per-row maxima (fp32 bit patterns of non-negative values, or needs)
+#pragma unroll
+            for (int a = 0; a < MI; ++a) {
+                int key[16];
+                if (fpath) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float m = 0.f;
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) m = fmaxf(m, fabsf((float)acc[a][b][r] * cs[b]));
+                        key[r] = __float_as_int(m);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int eav = seA[TR(a, r)];
+                        int m = NEED_NONE;
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b]));
+                        key[r] = m;
+                    }
+                }
+                const int k = rows16_max(key, lane);
+                if ((lane & 1) == 0) {
+                    const int rr = rows16_row(lane);
+                    red[wn * BMt + tr0 + a * 32 + 8 * (rr >> 2) + (rr & 3)] = k;
+                }
+            }
+            __syncthreads();
+            // 2. one thread per tile row: the row's exponent, and the offset
+            //    (integer path) or scale (float path) its elements use
+            const int n_ct = (N + BNt - 1) / BNt;
+            bool ovf = false;
+            for (int tr = tid; tr < BMt; tr += NTHR) {
+                const int row = m0 + tr;
+                const int kmax = max(red[tr], red[BMt + tr]);
+                const int eav = seA[tr];
+                int rm, s = 0;
+                if (fpath) {
+                    // need of m = |acc| 2^(eb - ebmin) from its fp32 exponent and top
+                    // mantissa bits: bit length - 7, plus one at 255 * 2^(len - 8)
+                    s = ((kmax >> 23) - 127) - 6 + (((kmax >> 16) & 0x7f) == 0x7f);
+                    rm = kmax == 0 ? NEED_NONE : eav + ebmin + s;
+                } else {
+                    rm = kmax;
+                }
+                int tgt;
+                if (direct) {
+                    tgt = max(E_MIN, rm);
+                    ovf |= tgt > E_MAX;
+                    tgt = min(tgt, E_MAX);
+                    if (row < M) ep.out_exp[row] = (int8_t)tgt;
+                    rowf[tr] = __builtin_ldexpf(1.0f, eav + ebmin - tgt);
+                } else {
+                    tgt = rm == NEED_NONE ? P_NONE : rm - 2;
+                    if (row < M) ep.p16[(long long)row * n_ct + tile_n] = (int16_t)(rm == NEED_NONE ? P_NONE : rm);
+                    rowf[tr] = rm == NEED_NONE ? 1.0f : __builtin_ldexpf(1.0f, 2 - s);
+                }
+                rowi[tr] = tgt - eav;
+            }
+            if (ovf) atomicOr(ep.flags, 1u);
+            __syncthreads();
+            // 3. the elements, with the mode and the path fixed per instance
+            auto elems = [&](auto dir_tag, auto fp_tag) {
+                constexpr bool DIR = decltype(dir_tag)::value, FP = decltype(fp_tag)::value;
 #pragma unroll
                 for (int a = 0; a < MI; ++a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int eav = seA[TR(a, r)];
+                        const int tr = TR(a, r);
+                        if constexpr (FP) {
+                            // acc 2^(eps - target), exact in fp32 (or below 2^-126,
+                            // where the result is 0 either way)
+                            const float rs = rowf[tr];
 #pragma unroll
-                        for (int b = 0; b < NI; ++b) {
-                            if (direct) stage(ES1{}, a, b, r, rne_shift32(acc[a][b][r], e - (eav + ebv[b])));
-                            else stage(ES2{}, a, b, r, rto_shift32(acc[a][b][r], p - (eav + ebv[b])));
+                            for (int b = 0; b < NI; ++b) {
+                                const float y = (float)acc[a][b][r] * cs[b] * rs;
+                                if constexpr (DIR) {
+                                    stage(ES1{}, a, b, r, (int)__builtin_rintf(y));
+                                } else {
+                                    const float q = floorf(y);
+                                    stage(ES2{}, a, b, r, (int)q | (int)(y != q));
+                                }
+                            }
+                        } else {
+                            const int off = rowi[tr];
+#pragma unroll
+                            for (int b = 0; b < NI; ++b) {
+                                if constexpr (DIR) stage(ES1{}, a, b, r, rne_bf(acc[a][b][r], off - ebv[b]));
+                                else stage(ES2{}, a, b, r, rto_bf(acc[a][b][r], off - ebv[b]));
+                            }
                         }
                     }
+            };
+            if (direct) {
+                if (fpath) elems(std::true_type{}, std::true_type{});
+                else elems(std::true_type{}, std::false_type{});
+            } else {
+                if (fpath) elems(std::false_type{}, std::true_type{});
+                else elems(std::false_type{}, std::false_type{});
             }
-        } else {
-            // row groups: maximum per tile row, one 32-row slab at a time
-#pragma unroll
-            for (int a = 0; a < MI; ++a) {
-                int rm[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int eav = seA[TR(a, r)];
-                    int m = NEED_NONE;
-#pragma unroll
-                    for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b]));
-                    rm[r] = m;
-                }
-#pragma unroll
-                for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) rm[r] = max(rm[r], __shfl_xor(rm[r], off));
-                if ((lane & 31) == 0) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red[wn * BMt + TR(a, r)] = rm[r];
-                }
-            }
-            __syncthreads();
-            const int n_ct = (N + BNt - 1) / BNt;
-#pragma unroll
-            for (int a = 0; a < MI; ++a)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int tr = TR(a, r), row = m0 + tr;
-                    const int rm = max(red[tr], red[BMt + tr]);
-                    const int eav = seA[tr];
-                    int e = 0, p = 0;
-                    if (direct) {
-                        e = clamp_exp_flag(max(E_MIN, rm), ep.flags);
-                        if (wn == 0 && (lane & 31) == 0 && row < M) ep.out_exp[row] = (int8_t)e;
-                    } else {
-                        p = rm == NEED_NONE ? P_NONE : rm - 2;
-                        if (wn == 0 && (lane & 31) == 0 && row < M)
-                            ep.p16[(long long)row * n_ct + tile_n] = (int16_t)(rm == NEED_NONE ? P_NONE : rm);
-                    }
-#pragma unroll
-                    for (int b = 0; b < NI; ++b) {
-                        if (direct) stage(ES1{}, a, b, r, rne_shift32(acc[a][b][r], e - (eav + ebv[b])));
-                        else stage(ES2{}, a, b, r, rto_shift32(acc[a][b][r], p - (eav + ebv[b])));
-                    }
-                }
         }
         __syncthreads();
         if (direct) flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0);
