@@ -363,8 +363,48 @@ ConvGeom geom(const ie_conv_desc *d) {
     g.ds = make_fastdiv((uint32_t)g.s);
     g.dk = make_fastdiv((uint32_t)g.kp);
     g.dst = make_fastdiv((uint32_t)g.stride);
+    const int cp = g.cp, kp = g.kp, st = g.stride;
+    int t = BK / cp;
+    g.im_dc = BK % cp;
+    g.im_ds = t % g.s;
+    g.im_dr = t / g.s;
+    g.im_d0 = g.im_dc + g.im_ds * cp + g.im_dr * g.w * cp;
+    g.im_d1 = (g.w - g.s) * cp;
+    t = BK / kp;
+    g.dg_dc = BK % kp;
+    g.dg_ds = t % g.s;
+    g.dg_dr = t / g.s;
+    const long long rsc = (long long)g.r * g.s * g.c;
+    g.wt_d0 = (int)(g.dg_dc * rsc + (long long)t * g.c);
+    g.wt_d1 = (int)(g.c - kp * rsc);
+    const long long pq = (long long)g.p * g.q, img = (long long)g.h * g.w * cp;
+    g.px_dq = BK % g.q;
+    g.px_dp = (BK / g.q) % g.p;
+    g.px_d0 = (int)((long long)g.px_dq * st * cp + (long long)g.px_dp * st * g.w * cp + (BK / pq) * img);
+    g.px_d1 = (st * g.w - g.q * st) * cp;
+    g.px_d2 = (int)(img - (long long)g.p * st * g.w * cp);
+    g.px_nw = (int)(BK / pq + 2);
+    g.st_inv = (65536 + st - 1) / st;
     return g;
 }
+
+// The GEMM loaders address operands through buffer descriptors of at most
+// 2^30 bytes (a tile's images, a step's contraction rows) with 32-bit
+// offsets, and keep filter-tap masks of 15 bits per axis.
+constexpr long long WINDOW = 1ll << 30;
+
+bool conv_fits(const ConvGeom &g) {
+    if (g.r > 15 || g.s > 15 || g.h > 65535 || g.w > 65535 || g.cp > (1 << 22) || g.kp > (1 << 22)) return false;
+    const long long pq = (long long)g.p * g.q, hw = (long long)g.h * g.w;
+    const long long img_x = hw * g.cp, img_y = pq * g.kp;
+    if ((256 / pq + 2) * img_x > WINDOW) return false;   // forward im2col rows, weight-gradient pixels
+    if ((256 / hw + 2) * img_y > WINDOW) return false;   // input-gradient gather
+    const long long rs = (long long)g.r * g.s;
+    return 256 * rs * g.cp <= WINDOW && 256 * rs * g.kp <= WINDOW && 128ll * g.kp <= WINDOW;
+}
+
+// The in-place weight read of the input gradient spans the whole weight.
+bool weight_window_fits(const ConvGeom &g) { return (long long)g.kp * g.r * g.s * g.c <= WINDOW; }
 
 ie_status check_conv(const ie_conv_desc *d) {
     if (!d) return IE_ERR_NULL;
@@ -574,6 +614,7 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, 
     long long M = dY->rows, N = dY->cols, K = X->cols;
     if (X->rows != M || dW->rows != N || dW->cols != K) return IE_ERR_SHAPE;
     if (!aligned(dY->mant, 16) || !aligned(X->mant, 16)) return IE_ERR_UNSUPPORTED;
+    if ((long long)BK * r16(N) > WINDOW || (long long)BK * r16(K) > WINDOW) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < linear_dw_ws(M, N, K)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -622,7 +663,7 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     if (W->rows != g.k || W->cols != rsc) return IE_ERR_SHAPE;
     if (Y->rows != npq || Y->cols != g.k) return IE_ERR_SHAPE;
     if (X->group != IE_GROUP_TENSOR) return IE_ERR_UNSUPPORTED;
-    if (rsc > MAX_CONTRACT || npq > DIM_MAX) return IE_ERR_UNSUPPORTED;
+    if (rsc > MAX_CONTRACT || npq > DIM_MAX || !conv_fits(g)) return IE_ERR_UNSUPPORTED;
     if (!aligned(X->mant, 16) || !aligned(W->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < conv_fwd_ws(d)) return IE_ERR_WORKSPACE;
@@ -664,7 +705,7 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     if (dX && (dX->rows != nhw || dX->cols != g.c)) return IE_ERR_SHAPE;
     if (dW && (dW->rows != g.k || dW->cols != rsc)) return IE_ERR_SHAPE;
     if (X->group != IE_GROUP_TENSOR || dY->group != IE_GROUP_TENSOR) return IE_ERR_UNSUPPORTED;
-    if ((long long)g.k * g.r * g.s > MAX_CONTRACT || nhw > DIM_MAX) return IE_ERR_UNSUPPORTED;
+    if ((long long)g.k * g.r * g.s > MAX_CONTRACT || nhw > DIM_MAX || !conv_fits(g)) return IE_ERR_UNSUPPORTED;
     if (!aligned(X->mant, 16) || !aligned(dY->mant, 16)) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < conv_bwd_ws(d)) return IE_ERR_WORKSPACE;
@@ -686,7 +727,7 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     auto dgrad = [&](hipStream_t s) -> ie_status {
         Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
         ExpSrc ea{dY->exp, nullptr, 0};
-        if (W->group == IE_GROUP_TENSOR && g.c % 16 == 0 && aligned(W->mant, 16)) {
+        if (W->group == IE_GROUP_TENSOR && g.c % 16 == 0 && aligned(W->mant, 16) && weight_window_fits(g)) {
             // one weight exponent: nothing to align, read W in place
             Operand B{LD_WT, W->mant, 0, g.c, g};
             return run_product(A, B, nhw, g.c, rskp, ea, ExpSrc{W->exp, nullptr, 0}, dX, pw, flags, 1, s);

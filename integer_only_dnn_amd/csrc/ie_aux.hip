@@ -300,13 +300,25 @@ __device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint
 constexpr int FIN_NEEDS = 2048;
 
 __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
-                                                           int bm, int bn, int TM, int n_ct, int row_group, int rb,
+                                                           int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
                                                            FastDiv dper) {
     __shared__ int sh[4];
     __shared__ int16_t needs[FIN_NEEDS];
     __shared__ int rowe[256];
     const uint32_t per_row = N / vw;
+    // eight values held in registers -> eight bytes at out + o
+    auto store8 = [&](long long o, const v4i &v, int sh_) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int x = (int)(int16_t)((uint32_t)v[j] & 0xffff), y = (int)(int16_t)((uint32_t)v[j] >> 16);
+            uint32_t b = ((uint32_t)(uint8_t)rne_shift32(x, sh_)) | ((uint32_t)(uint8_t)rne_shift32(y, sh_) << 8);
+            if (j < 2) lo |= b << (16 * j);
+            else hi |= b << (16 * (j - 2));
+        }
+        *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
+    };
     auto round8 = [&](long long o, int sh_) {
         if (vw == 8) {
             v4i v = *(const v4i *)(v16 + o);
@@ -324,20 +336,43 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
         }
     };
     if (!row_group) {
-        const int T = TM * n_ct;
+        // largest tile need, eight per 16-byte load (p16 is 16-byte aligned);
+        // all-zero tiles (P_NONE) stay below every real need and E_MIN
+        const int T = TM * n_ct, T8 = T >> 3;
         int m = NEED_NONE;
-        for (int i = threadIdx.x; i < T; i += 256) {
-            const int v = p16[i];
-            if (v != P_NONE) m = max(m, v);
+        for (int i = threadIdx.x; i < T8; i += 256) {
+            const v4i v = *(const v4i *)(p16 + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m = max(m, max((int)(int16_t)(v[j] & 0xffff), (int)(int16_t)((uint32_t)v[j] >> 16)));
         }
+        for (int i = 8 * T8 + threadIdx.x; i < T; i += 256) m = max(m, (int)p16[i]);
         m = block_max256(m, sh);
         const int eT = clamp_exp_flag(max(E_MIN, m), flags);
         const uint32_t total = (uint32_t)M * per_row;
-        for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-            const uint32_t row = fdiv32(i, dper);
-            const int c0 = (int)(i - row * per_row) * vw;
-            const int t = p16[row / bm + TM * (c0 / bn)];
-            round8((long long)row * N + c0, eT - (t == P_NONE ? P_NONE : t - 2));
+        // four independent chunks per thread and trip, all loads first
+        constexpr int U = 4;
+        for (uint32_t i0 = blockIdx.x * 256 * U + threadIdx.x; i0 < total; i0 += gridDim.x * 256 * U) {
+            long long o[U];
+            int t[U];
+            v4i v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + 256 * u;
+                const uint32_t ii = i < total ? i : i0;
+                const uint32_t row = fdiv32(ii, dper);
+                const int c0 = (int)(ii - row * per_row) * vw;
+                o[u] = (long long)row * N + c0;
+                t[u] = p16[(row >> lbm) + TM * (c0 >> lbn)];
+                if (vw == 8) v[u] = *(const v4i *)(v16 + o[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i0 + 256 * u >= total) break;
+                const int sh_ = eT - (t[u] == P_NONE ? P_NONE : t[u] - 2);
+                if (vw == 8) store8(o[u], v[u], sh_);
+                else round8(o[u], sh_);
+            }
         }
         if (blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
         return;
@@ -378,7 +413,7 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
         for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
             const uint32_t lr = fdiv32(i, dper);
             const int c0 = (int)(i - lr * per_row) * vw;
-            const int t = staged ? needs[lr * n_ct + c0 / bn] : pr[c0 / bn];
+            const int t = staged ? needs[lr * n_ct + (c0 >> lbn)] : pr[c0 >> lbn];
             round8((r0 + lr) * N + c0, rowe[lr] - (t == P_NONE ? P_NONE : t - 2));
         }
         __syncthreads();
@@ -396,9 +431,10 @@ hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, in
     rb = rb < 1 ? 1 : (rb > 256 ? 256 : rb);
     const long long total = (long long)M * (N / vw);
     const int blocks = row_group ? blocks_for((M + rb - 1) / rb, 1, 8192) : blocks_for(total, 256 * 4, 2048);
+    auto lg = [](int v) { int l = 0; while ((1 << l) < v) ++l; return l; };  // tile sides are powers of two
     prof_begin(st, PROF_RTO_FINALIZE);
-    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, M, N, t.bm(), t.bn(), TM,
-                       n_ct, row_group, rb, out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
+    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, M, N, lg(t.bm()), lg(t.bn()),
+                       TM, n_ct, row_group, rb, out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }

@@ -9,8 +9,8 @@
 //
 // A workgroup of 4 waves (2 x 2) computes a (64 MI) x (64 NI) tile with
 // v_mfma_i32_32x32x32_i8; each wave owns (32 MI) x (32 NI).  Operand tiles
-// of 64 contraction bytes are staged through LDS, double buffered, with the
-// next step's global loads in flight during the current step's MFMAs.
+// of BK (128) contraction bytes are staged through LDS, double buffered, with
+// the next steps' buffer loads in flight during the current step's MFMAs.
 //   - K-contiguous operands sit in LDS as [row][k] (16-byte pad) and are
 //     read with ds_read_b128;
 //   - M-contiguous operands (weight gradients) sit as [k][row] (16-byte
@@ -20,7 +20,8 @@
 //     row j of an 8 x 16 byte block and lane i receives its column i.
 // Convolutions are implicit GEMMs: the loaders compute NHWC addresses of the
 // im2col view (forward), of the input-gradient gather and of the transposed
-// im2col view (weight gradient) on the fly; zero padding loads zeros.
+// im2col view (weight gradient) on the fly, stepping offsets incrementally;
+// zero padding loads zeros.
 #pragma once
 
 #ifndef IE_STAGES
@@ -64,17 +65,67 @@ struct Lds {
 
 // ---------------------------------------------------------------------------
 // Loaders.  Every operand is read in 16-byte chunks (the host pads channel
-// and contraction extents to multiples of 16).  Loads are unconditional: an
-// out-of-range chunk reads a 16-byte chunk of zeros instead, so no loaded
-// register is touched before the stage is written to LDS and the prefetched
-// loads stay in flight across the MFMA work.  Each thread moves
+// and contraction extents to multiples of 16) with raw buffer loads: the
+// workgroup builds a buffer descriptor over the window of the operand it
+// reads, and a chunk whose 32-bit offset lies at or past the window's end
+// loads zeros in hardware.  Invalid chunks (padding taps, rows past the
+// operand, contraction past the end) are given such an offset, so loads are
+// unconditional, never fault, and no loaded register is touched before its
+// stage is written to LDS.  Offsets advance from step to step by constants
+// the host precomputes: the main loop holds no divisions.
+//
+// Windows hold at most 2^30 bytes, so a valid offset plus OOB_ROW (2^30) or
+// OOB_K (2^31), or both, lies past every window.
+//
+// Only one operand of a product zeroes the contraction past its end (ZK);
+// the other one's chunks there meet zeros, so they need only be safe to
+// read, which the descriptor guarantees.  Each thread moves
 // ROWS * BK / 4096 chunks per contraction step.
 // ---------------------------------------------------------------------------
 
-// Read-only zeros (device globals start zeroed and nothing writes this one).
-static __device__ __attribute__((aligned(16))) int8_t g_zero_chunk[16];
+constexpr uint32_t OOB_ROW = 1u << 30, OOB_K = 1u << 31;
 
-__device__ __forceinline__ const int8_t *zero_chunk() { return g_zero_chunk; }
+typedef __amdgpu_buffer_rsrc_t Res;
+
+// Descriptor of `bytes` bytes at p (none when bytes <= 0; the host keeps
+// every window within 2^30 bytes).  Raw buffer, no stride, 32-bit data format.
+// p and bytes are the same in every lane (window bases and sizes derive from
+// the workgroup's tile and step only); reading them from the first lane lets
+// the descriptor live in scalar registers, as a buffer load needs.
+__device__ __forceinline__ Res make_res(const int8_t *p, int bytes) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(max(bytes, 0));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ v4i bload(Res r, uint32_t off) {
+    return (v4i)__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// bits t in [0, n) with 0 <= b + t < lim (n <= 15)
+__device__ __forceinline__ uint32_t span_bits(int b, int n, int lim) {
+    const int lo = max(-b, 0), hi = min(n, lim - b);
+    return hi > lo ? (1u << hi) - (1u << lo) : 0u;
+}
+
+// filter taps t < n that land on an output row: (b - t) a multiple of st and
+// 0 <= (b - t) / st < lim
+__device__ __forceinline__ uint32_t stride_bits(int b, int n, int lim, int st, FastDiv dst) {
+    uint32_t m = 0;
+    for (int t = 0; t < n; ++t) {
+        const int a = b - t;
+        if (a < 0) break;
+        const int q = (int)fdiv((uint32_t)a, dst);
+        if (q * st == a && q < lim) m |= 1u << t;
+    }
+    return m;
+}
+
+// tap bit of a filter position (r, s); masks keep rows in bits 0..14 and
+// columns in bits 16..30
+__device__ __forceinline__ uint32_t tap_bits(int r, int s) { return (1u << (r & 15)) | (1u << (16 + (s & 15))); }
 
 template <int KIND, int ROWS>
 struct Ld;
@@ -109,206 +160,351 @@ struct TChunks {
     }
 };
 
-// Dense K-contiguous operand: element (i, k) at base[i*ld + k].
+// [k][row] chunks, two threads per contraction row: thread tid takes k-row
+// tid / 2 and its chunks 2 c + tid % 2, so it decodes one contraction index
+// per step for all of its chunks.
+template <int ROWS>
+struct TPairChunks {
+    static_assert(BK == 128 && NTHR == 256, "two threads per contraction row");
+    static constexpr int CH = ROWS / 32;
+    static constexpr int STRIDE = ROWS + 16;
+    __device__ __forceinline__ static int krow(int tid) { return tid >> 1; }
+    __device__ __forceinline__ static int ic(int c, int tid) { return 2 * c + (tid & 1); }
+    __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) *(v4i *)(s + krow(tid) * STRIDE + ic(c, tid) * 16) = reg[c];
+    }
+};
+
+// Dense K-contiguous operand: element (i, k) at base[i*ld + k].  Window: the
+// tile's rows.
 template <int ROWS>
 struct Ld<LD_K, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *ptr[CH];
-    bool ok[CH];
+    static constexpr bool ZK = true;
+    Res res;
+    uint32_t off[CH];
     int col;
-    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
+    __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid) {
+        (void)kb;
         col = B_::col(tid);
+        const int vr = min(max(op.rows - i0, 0), ROWS);
+        res = make_res(op.base + (long long)i0 * op.ld, vr * (int)op.ld);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int i = i0 + B_::row(c, tid);
-            ok[c] = i < op.rows;
-            ptr[c] = op.base + (long long)(ok[c] ? i : 0) * op.ld + col;
-        }
+        for (int c = 0; c < CH; ++c) off[c] = (uint32_t)(B_::row(c, tid) * (int)op.ld + col);
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
-        const bool kin = k0 + col < kend;
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        const uint32_t kk = k0 + col < kend ? (uint32_t)k0 : OOB_K;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) reg[c] = *(const v4i *)(ok[c] && kin ? ptr[c] + k0 : zero_chunk());
+        for (int c = 0; c < CH; ++c) reg[c] = bload(res, off[c] + kk);
     }
 };
 
 // Forward convolution: row m = (n, p, q), k = (r, s, c) over the padded
-// channel count cp (activation [N*H*W x cp]).
+// channel count cp (activation [N*H*W x cp]).  Window: the images of the
+// tile's rows.  Taps outside the image read zeros (mask of valid r and s
+// per row); the contraction past its end is zeroed by the weight operand.
 template <int ROWS>
 struct Ld<LD_IM2COL, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *x;
-    ConvGeom g;
-    int col;
-    int hb[CH], wb[CH];
-    long long pix[CH];
-    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
-        x = op.base;
-        g = op.g;
-        col = B_::col(tid);
+    static constexpr bool ZK = false;
+    Res res;
+    int pix[CH];       // offset of tap (0, 0), channel 0 of the row's pixel (may be negative)
+    uint32_t msk[CH];  // valid taps of the row (tap_bits layout)
+    int r, s, ch, tap; // contraction index of the next load: (r, s, ch), tap = (r W + s) cp + ch
+    int cp, S, dc, ds, dr, d0, d1;
+    __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid) {
+        const ConvGeom &g = op.g;
+        cp = g.cp;
+        S = g.s;
+        dc = g.im_dc;
+        ds = g.im_ds;
+        dr = g.im_dr;
+        d0 = g.im_d0;
+        d1 = g.im_d1;
+        const int last = min(i0 + ROWS, op.rows) - 1;
+        const int nf = (int)fdiv((uint32_t)i0, g.dpq), nl = (int)fdiv((uint32_t)max(last, i0), g.dpq);
+        const int img = g.h * g.w * g.cp;
+        res = make_res(op.base + (long long)nf * img, (nl - nf + 1) * img);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int m = i0 + B_::row(c, tid);
             const bool ok = m < op.rows;
-            const uint32_t mm = ok ? m : 0;
+            const uint32_t mm = ok ? m : i0;
             const uint32_t n = fdiv(mm, g.dpq), rem = mm - n * (uint32_t)(g.p * g.q);
             const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
-            hb[c] = ok ? (int)p * g.stride - g.pad : -(1 << 24);  // invalid rows never hit the image
-            wb[c] = (int)q * g.stride - g.pad;
-            pix[c] = (long long)n * g.h * g.w * g.cp;
+            const int hb = (int)p * g.stride - g.pad, wb = (int)q * g.stride - g.pad;
+            pix[c] = (((int)(n - nf) * g.h + hb) * g.w + wb) * g.cp;
+            msk[c] = ok ? span_bits(hb, g.r, g.h) | span_bits(wb, g.s, g.w) << 16 : 0u;
         }
+        const uint32_t kk = kb + B_::col(tid);
+        const uint32_t rs = fdiv(kk, g.dc);
+        ch = (int)(kk - rs * g.cp);
+        r = (int)fdiv(rs, g.ds);
+        s = (int)rs - r * g.s;
+        tap = (r * g.w + s) * g.cp + ch;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
-        const uint32_t kk = k0 + col;
-        const bool kin = (int)kk < kend;
-        const uint32_t rs = fdiv(kk, g.dc), ch = kk - rs * g.cp;
-        const uint32_t r = fdiv(rs, g.ds), s = rs - r * g.s;
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        (void)k0;
+        (void)kend;
+        const uint32_t bits = tap_bits(r, s);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int h = hb[c] + (int)r, w = wb[c] + (int)s;
-            const bool in = kin && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
-            const long long off = pix[c] + ((long long)h * g.w + w) * g.cp + ch;
-            reg[c] = *(const v4i *)(in ? x + off : zero_chunk());
-        }
+        for (int c = 0; c < CH; ++c) reg[c] = bload(res, (msk[c] & bits) == bits ? (uint32_t)(pix[c] + tap) : OOB_K);
+        // next step: (r, s, ch) += BK over (R, S, cp)
+        ch += dc;
+        const bool c1 = ch >= cp;
+        ch = c1 ? ch - cp : ch;
+        s += ds + (int)c1;
+        const bool c2 = s >= S;
+        s = c2 ? s - S : s;
+        r += dr + (int)c2;
+        tap += c2 ? d0 + d1 : d0;
     }
 };
 
 // Input gradient of a convolution: row m = (n, h, w), k = (r, s, ko) over the
 // padded output-channel count kp; element dY[n, p, q, ko] with
-// p * stride = h + pad - r (zero unless exact).
+// p * stride = h + pad - r (zero unless exact).  With h + pad = st a + b, the
+// taps that hit are r = b + st j, at p = a - j = a - floor(r / st).  Window:
+// the output images of the tile's rows.
 template <int ROWS>
 struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *dy;
-    ConvGeom g;
-    int col;
-    int hp[CH], wp[CH];
-    long long pix[CH];
-    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
-        dy = op.base;
-        g = op.g;
-        col = B_::col(tid);
+    static constexpr bool ZK = false;
+    Res res;
+    int pix[CH];       // offset of output pixel (a_h, a_w), channel 0
+    uint32_t msk[CH];  // taps that hit an output pixel (tap_bits layout)
+    int r, s, ko;      // contraction index of the next load
+    int kp, S, Q, dc, ds, dr, st_inv;
+    __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid) {
+        const ConvGeom &g = op.g;
+        kp = g.kp;
+        S = g.s;
+        Q = g.q;
+        dc = g.dg_dc;
+        ds = g.dg_ds;
+        dr = g.dg_dr;
+        st_inv = g.st_inv;
+        const int last = min(i0 + ROWS, op.rows) - 1;
+        const int nf = (int)fdiv((uint32_t)i0, g.dhw), nl = (int)fdiv((uint32_t)max(last, i0), g.dhw);
+        const int img = g.p * g.q * g.kp;
+        res = make_res(op.base + (long long)nf * img, (nl - nf + 1) * img);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int m = i0 + B_::row(c, tid);
             const bool ok = m < op.rows;
-            const uint32_t mm = ok ? m : 0;
+            const uint32_t mm = ok ? m : i0;
             const uint32_t n = fdiv(mm, g.dhw), rem = mm - n * (uint32_t)(g.h * g.w);
             const uint32_t h = fdiv(rem, g.dw), w = rem - h * g.w;
-            hp[c] = ok ? (int)h + g.pad : -(1 << 24);
-            wp[c] = (int)w + g.pad;
-            pix[c] = (long long)n * g.p * g.q * g.kp;
+            const int hp = (int)h + g.pad, wp = (int)w + g.pad;
+            const int ah = (int)fdiv((uint32_t)hp, g.dst), aw = (int)fdiv((uint32_t)wp, g.dst);
+            pix[c] = (((int)(n - nf) * g.p + ah) * g.q + aw) * g.kp;
+            msk[c] = ok ? stride_bits(hp, g.r, g.p, g.stride, g.dst) | stride_bits(wp, g.s, g.q, g.stride, g.dst) << 16
+                        : 0u;
         }
+        const uint32_t kk = kb + B_::col(tid);
+        const uint32_t rs = fdiv(kk, g.dk);
+        ko = (int)(kk - rs * g.kp);
+        r = (int)fdiv(rs, g.ds);
+        s = (int)rs - r * g.s;
     }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
-        const uint32_t kk = k0 + col;
-        const bool kin = (int)kk < kend;
-        const uint32_t rs = fdiv(kk, g.dk), ko = kk - rs * g.kp;
-        const int r = (int)fdiv(rs, g.ds), s = (int)(rs - (uint32_t)r * g.s);
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        (void)k0;
+        (void)kend;
+        const uint32_t bits = tap_bits(r, s);
+        // floor(r / st) for r < 16: (r * ceil(2^16 / st)) >> 16
+        const int rq = (int)(__umul24((uint32_t)r, (uint32_t)st_inv) >> 16);
+        const int sq = (int)(__umul24((uint32_t)s, (uint32_t)st_inv) >> 16);
+        const int tap = ko - __mul24(__mul24(rq, Q) + sq, kp);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int a = hp[c] - r, b = wp[c] - s;
-            const int p = (int)fdiv((uint32_t)max(a, 0), g.dst), q = (int)fdiv((uint32_t)max(b, 0), g.dst);
-            const bool in = kin && a >= 0 && b >= 0 && p * g.stride == a && q * g.stride == b && p < g.p &&
-                            q < g.q;
-            const long long off = pix[c] + ((long long)p * g.q + q) * g.kp + ko;
-            reg[c] = *(const v4i *)(in ? dy + off : zero_chunk());
-        }
+        for (int c = 0; c < CH; ++c) reg[c] = bload(res, (msk[c] & bits) == bits ? (uint32_t)(pix[c] + tap) : OOB_K);
+        ko += dc;
+        const bool c1 = ko >= kp;
+        ko = c1 ? ko - kp : ko;
+        s += ds + (int)c1;
+        const bool c2 = s >= S;
+        s = c2 ? s - S : s;
+        r += dr + (int)c2;
     }
 };
 
 // M-contiguous dense operand: element (i, k) at base[k*ld + i]; ld >= the
-// row count rounded up to 16.
+// row count rounded up to 16.  Window: the step's BK contraction rows, so
+// rows past the end read zeros.
 template <int ROWS>
 struct Ld<LD_T, ROWS> : TChunks<ROWS> {
     using B_ = TChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *base;
-    long long ld;
-    bool iok;
-    __device__ __forceinline__ void init(const Operand &op, int i0, int tid) {
-        const int i = i0 + B_::ic(tid) * 16;
-        iok = i < op.rows;
-        base = op.base + (iok ? i : 0);
-        ld = op.ld;
-    }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    static constexpr bool ZK = true;
+    const int8_t *cur;  // element (i0, k0) of the next load
+    int ld, i0;
+    uint32_t off[CH];
+    __device__ __forceinline__ void init(const Operand &op, int i0_, int kb, int tid) {
+        i0 = i0_;
+        ld = (int)op.ld;
+        cur = op.base + i0 + (long long)kb * ld;
+        const bool iok = i0 + B_::ic(tid) * 16 < op.rows;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int k = k0 + B_::krow(c, tid);
-            const bool in = iok && k < kend;
-            reg[c] = *(const v4i *)(in ? base + (long long)k * ld : zero_chunk());
-        }
+        for (int c = 0; c < CH; ++c) off[c] = iok ? (uint32_t)(B_::krow(c, tid) * ld + B_::ic(tid) * 16) : OOB_ROW;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        // contraction rows left in this step (written without a min / max
+        // pair against constants, which would become a vector med3)
+        const int rows = min(kend - k0, BK);
+        const Res res = make_res(cur, rows > 0 ? rows * ld - i0 : 0);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) reg[c] = bload(res, off[c]);
+        cur += BK * ld;
     }
 };
 
 // Weight gradient of a convolution, B side: row j = (r, s, c) over the padded
 // channel count cp, k = output pixel (n, p, q); element
-// X[n, p*st + r - pad, q*st + s - pad, c].
+// X[n, p*st + r - pad, q*st + s - pad, c].  Window: the images the step's BK
+// pixels fall in; the contraction past its end is zeroed by the dY operand.
 template <int ROWS>
-struct Ld<LD_IM2COL_T, ROWS> : TChunks<ROWS> {
-    using B_ = TChunks<ROWS>;
+struct Ld<LD_IM2COL_T, ROWS> : TPairChunks<ROWS> {
+    using B_ = TPairChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *x;
-    ConvGeom g;
-    bool jok;
-    int jr, js, jc;
-    __device__ __forceinline__ void init(const Operand &op, int j0, int tid) {
-        x = op.base;
-        g = op.g;
-        const int jb = j0 + B_::ic(tid) * 16;
-        jok = jb < op.rows;
-        const uint32_t rs = fdiv(jok ? jb : 0, g.dc);
-        jc = (jok ? jb : 0) - (int)rs * g.cp;
-        jr = (int)fdiv(rs, g.ds);
-        js = (int)rs - jr * g.s;
-    }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    static constexpr bool ZK = false;
+    const int8_t *win;      // the window's first image
+    int img;                // bytes per image
+    int n_img, nw;          // images of the tensor, images per window
+    int ns, urem;           // window's first image; k0 - ns P Q
+    int hb, wb, pix;        // this thread's pixel: p st - pad, q st - pad, offset from the window
+    // Validity of a chunk: its filter position (jr, js) puts the pixel's tap
+    // inside the image.  Up to 4 chunks per thread test it directly; more
+    // share per-step masks of the valid rows and columns.
+    static constexpr bool MASKS = CH > 4;
+    uint32_t jbit[MASKS ? CH : 1];  // tap bits of (jr, js) (bit 15 when past the rows)
+    int jr[MASKS ? 1 : CH], js[MASKS ? 1 : CH];  // (jr = 2^20 when past the rows)
+    int joff[CH];           // (jr W + js) cp + jc
+    int pq, u_dr, u_dn, wlim, hlim, qs, ps, dwb, dhb, st, d0, d1, d2, R, S, H, W;
+    __device__ __forceinline__ void init(const Operand &op, int j0, int kb, int tid) {
+        const ConvGeom &g = op.g;
+        img = g.h * g.w * g.cp;
+        n_img = g.n;
+        nw = g.px_nw;
+        pq = g.p * g.q;
+        u_dr = BK % pq;
+        u_dn = BK / pq;
+        st = g.stride;
+        qs = g.q * g.stride;
+        ps = g.p * g.stride;
+        wlim = qs - g.pad;
+        hlim = ps - g.pad;
+        dwb = g.px_dq * g.stride;
+        dhb = g.px_dp * g.stride;
+        d0 = g.px_d0;
+        d1 = g.px_d1;
+        d2 = g.px_d2;
+        R = g.r;
+        S = g.s;
+        H = g.h;
+        W = g.w;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int kk = k0 + B_::krow(c, tid);
-            const uint32_t kc = kk < kend ? kk : 0;
-            const uint32_t n = fdiv(kc, g.dpq), rem = kc - n * (uint32_t)(g.p * g.q);
-            const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
-            const int h = (int)p * g.stride + jr - g.pad, w = (int)q * g.stride + js - g.pad;
-            const bool in = jok && kk < kend && (unsigned)h < (unsigned)g.h && (unsigned)w < (unsigned)g.w;
-            const long long off = (((long long)n * g.h + h) * g.w + w) * g.cp + jc;
-            reg[c] = *(const v4i *)(in ? x + off : zero_chunk());
+            const int j = j0 + B_::ic(c, tid) * 16;
+            const bool ok = j < op.rows;
+            const uint32_t rs = fdiv(ok ? j : 0, g.dc);
+            const int jc = (ok ? j : 0) - (int)rs * g.cp;
+            const int r_ = (int)fdiv(rs, g.ds), s_ = (int)rs - r_ * g.s;
+            if constexpr (MASKS) {
+                jbit[c] = ok ? tap_bits(r_, s_) : 1u << 15;
+            } else {
+                jr[c] = ok ? r_ : 1 << 20;
+                js[c] = s_;
+            }
+            joff[c] = (r_ * g.w + s_) * g.cp + jc;
         }
+        ns = (int)fdiv((uint32_t)kb, g.dpq);
+        urem = kb - ns * pq;
+        win = op.base + (long long)ns * img;
+        const uint32_t k = kb + B_::krow(tid);
+        const uint32_t n = fdiv(k, g.dpq), rem = k - n * (uint32_t)pq;
+        const uint32_t p = fdiv(rem, g.dq), q = rem - p * g.q;
+        hb = (int)p * g.stride - g.pad;
+        wb = (int)q * g.stride - g.pad;
+        pix = (((int)n - ns) * g.h + hb) * g.w * g.cp + wb * g.cp;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        (void)k0;
+        (void)kend;
+        const int left = min(n_img - ns, nw);
+        const Res res = make_res(win, left > 0 ? left * img : 0);
+        if constexpr (MASKS) {
+            const uint32_t hw = span_bits(hb, R, H) | span_bits(wb, S, W) << 16;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                reg[c] = bload(res, (hw & jbit[c]) == jbit[c] ? (uint32_t)(pix + joff[c]) : OOB_K);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const bool ok = (uint32_t)(hb + jr[c]) < (uint32_t)H && (uint32_t)(wb + js[c]) < (uint32_t)W;
+                reg[c] = bload(res, ok ? (uint32_t)(pix + joff[c]) : OOB_K);
+            }
+        }
+        // next step: the window's first image and this thread's pixel move by BK pixels
+        urem += u_dr;
+        const int cs = urem >= pq;
+        urem = cs ? urem - pq : urem;
+        const int dns = u_dn + cs;
+        ns += dns;
+        win += dns * img;
+        wb += dwb;
+        const bool c1 = wb >= wlim;
+        wb = c1 ? wb - qs : wb;
+        hb += c1 ? dhb + st : dhb;
+        const bool c2 = hb >= hlim;
+        hb = c2 ? hb - ps : hb;
+        pix += d0 - dns * img + (c1 ? d1 : 0) + (c2 ? d2 : 0);
     }
 };
 
 // Input gradient of a convolution, B side, straight from the weight
 // [k_out][r][s][c] (whole-tensor exponent, c a multiple of 16): row j = input
 // channel, k = (r, s, ko) over the padded output-channel count kp; 16
-// consecutive channels of one (r, s, ko) are contiguous.
+// consecutive channels of one (r, s, ko) are contiguous.  Window: the whole
+// weight, so padded output channels read zeros.
 template <int ROWS>
-struct Ld<LD_WT, ROWS> : TChunks<ROWS> {
-    using B_ = TChunks<ROWS>;
+struct Ld<LD_WT, ROWS> : TPairChunks<ROWS> {
+    using B_ = TPairChunks<ROWS>;
     static constexpr int CH = B_::CH;
-    const int8_t *base;
-    ConvGeom g;
-    long long rsc;
-    bool jok;
-    __device__ __forceinline__ void init(const Operand &op, int j0, int tid) {
-        g = op.g;
-        const int j = j0 + B_::ic(tid) * 16;
-        jok = j < op.rows;
-        base = op.base + (jok ? j : 0);
-        rsc = (long long)g.r * g.s * g.c;
-    }
-    __device__ __forceinline__ void load(int k0, int kend, int tid, v4i (&reg)[CH]) {
+    static constexpr bool ZK = true;
+    Res res;
+    uint32_t joff[CH];
+    int krow, ko, koff;     // this thread's k-row; ko of the next load and ko R S C + rs C
+    int kp, dc, d0, d1;
+    __device__ __forceinline__ void init(const Operand &op, int j0, int kb, int tid) {
+        const ConvGeom &g = op.g;
+        kp = g.kp;
+        dc = g.dg_dc;
+        d0 = g.wt_d0;
+        d1 = g.wt_d1;
+        const int rsc = g.r * g.s * g.c;
+        res = make_res(op.base + j0, g.k * rsc - j0);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int kk = k0 + B_::krow(c, tid);
-            const uint32_t kc = kk < kend ? kk : 0;
-            const uint32_t rs = fdiv(kc, g.dk), ko = kc - rs * g.kp;
-            const bool in = jok && kk < kend && (int)ko < g.k;
-            reg[c] = *(const v4i *)(in ? base + (long long)ko * rsc + (long long)rs * g.c : zero_chunk());
+            const int j = j0 + B_::ic(c, tid) * 16;
+            joff[c] = j < op.rows ? (uint32_t)(B_::ic(c, tid) * 16) : OOB_ROW;
         }
+        krow = B_::krow(tid);
+        const uint32_t kk = kb + krow;
+        const uint32_t rs = fdiv(kk, g.dk);
+        ko = (int)(kk - rs * g.kp);
+        koff = ko * rsc + (int)rs * g.c;
+    }
+    __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
+        const uint32_t kbase = k0 + krow < kend ? (uint32_t)koff : OOB_K;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) reg[c] = bload(res, kbase + joff[c]);
+        ko += dc;
+        const bool c1 = ko >= kp;
+        ko = c1 ? ko - kp : ko;
+        koff += c1 ? d0 + d1 : d0;
     }
 };
 
@@ -396,15 +592,17 @@ __device__ __forceinline__ void tile_of(int bid, int TM, int TN, int &tm, int &t
     const int q = T / 8, r = T % 8;
     const int x = bid % 8, j = bid / 8;
     const int logical = x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
-    tm = logical / TN;
-    tn = logical - tm * TN;
+    // the division runs on the vector unit; the tile is the same in every
+    // lane, so its indices go back to scalar registers
+    tm = __builtin_amdgcn_readfirstlane(logical / TN);
+    tn = __builtin_amdgcn_readfirstlane(logical - tm * TN);
 }
 
 // Register pipeline depth: 3 for the 2 x 2 tile, which runs two workgroups
 // per CU and would spill at 4.
 template <int MI, int NI>
 struct Stages {
-    static constexpr int value = (MI == 2 && NI == 2) ? 3 : IE_STAGES;
+    static constexpr int value = (MI == 2 && NI == 2) || MI * NI == 1 ? 3 : IE_STAGES;
 };
 
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
@@ -431,8 +629,9 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
 
     Ld<KA, BMt> la;
     Ld<KB, BNt> lb;
-    la.init(A, m0, tid);
-    lb.init(B, n0, tid);
+    static_assert(Ld<KA, BMt>::ZK || Ld<KB, BNt>::ZK, "one operand must zero the contraction past its end");
+    la.init(A, m0, kb, tid);
+    lb.init(B, n0, kb, tid);
     constexpr int CA = Ld<KA, BMt>::CH, CB = Ld<KB, BNt>::CH;
 
     // exponents of this tile's rows and columns, for the epilogue
@@ -464,8 +663,8 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            la.load(kb + s * BK, ke, tid, ra[s]);
-            lb.load(kb + s * BK, ke, tid, rb[s]);
+            la.load(kb + s * BK, ke, ra[s]);
+            lb.load(kb + s * BK, ke, rb[s]);
         }
         la.store(lds, tid, ra[0]);
         lb.store(lds + LA::BYTES, tid, rb[0]);
@@ -499,9 +698,9 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
             const int s = it + uu;
             if (s >= nk) break;
             // set u held stage s, already in LDS: refill it with stage s + NS
-            // (past the end: zero chunks)
-            la.load(kb + (s + NS) * BK, ke, tid, ra[u]);
-            lb.load(kb + (s + NS) * BK, ke, tid, rb[u]);
+            // (past the end: loaded, never computed)
+            la.load(kb + (s + NS) * BK, ke, ra[u]);
+            lb.load(kb + (s + NS) * BK, ke, rb[u]);
 #ifndef IE_NO_SCHED_BARRIER
             // keep the refill ahead of the fragment reads, so that no fragment
             // lands in registers whose loads are still in flight

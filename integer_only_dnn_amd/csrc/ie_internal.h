@@ -71,6 +71,20 @@ FastDiv make_fastdiv(uint32_t d);
 struct ConvGeom {
     int n, h, w, c, k, r, s, stride, pad, p, q, cp, kp;
     FastDiv dpq, dq, dhw, dw, dc, ds, dk, dst;
+    // Advance of the contraction index by one BK step, for the loaders:
+    //   (r, s, c) over cp:  im_dc = BK % cp, im_ds = (BK / cp) % s, im_dr = BK / (cp s);
+    //                       the tap offset (r w + s) cp + c moves by im_d0, plus im_d1
+    //                       when s wraps;
+    //   (r, s, ko) over kp: dg_dc, dg_ds, dg_dr likewise; ko r s c + (r s_ + s) c moves
+    //                       by wt_d0, plus wt_d1 when ko wraps;
+    //   output pixels:      px_dq = BK % q, px_dp = (BK / q) % p; the NHWC offset of
+    //                       tap (0, 0) moves by px_d0, plus px_d1 when q wraps and px_d2
+    //                       when p wraps; px_nw images cover any BK consecutive pixels;
+    //   st_inv = ceil(2^16 / stride).
+    int im_dc, im_ds, im_dr, im_d0, im_d1;
+    int dg_dc, dg_ds, dg_dr, wt_d0, wt_d1;
+    int px_dq, px_dp, px_d0, px_d1, px_d2, px_nw;
+    int st_inv;
 };
 
 struct Operand {
