@@ -119,7 +119,9 @@ ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX,
  * Table 5 groups: ROW = per output channel).
  *   dY [M x N], X [M x K], dW [N x K].  ROW-grouped dY or X are aligned over
  *   their rows (the contraction axis) first.  Any M (exact int32 partial sums
- *   over chunks of at most 65536 rows, merged in int64).
+ *   over chunks of at most 65536 rows, merged in int64).  N and K up to 2^23
+ *   (IE_ERR_UNSUPPORTED beyond: 128 rows of either operand must fit in 2^30
+ *   bytes).
  */
 ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW,
                            void *ws, size_t ws_bytes, void *stream);
@@ -129,6 +131,9 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW,
  *   Y[n,p,q,k] = sum_{r,s,c} X[n, p*st+r-pad, q*st+s-pad, c] * W[k,r,s,c].
  *   X: rows n*h*w, cols c, TENSOR.  W: rows k, cols r*s*c, TENSOR or ROW.
  *   Y: rows n*p*q, cols k, TENSOR.  r*s*c <= 65536.
+ * Convolution limits (both directions; IE_ERR_UNSUPPORTED beyond): r, s <= 15;
+ * h, w <= 65535; c, k <= 2^22; the images a tile of 256 output (or input)
+ * pixels spans must fit in 2^30 bytes, and so must 256 rows of the weight.
  */
 ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
                       const ie_mat *Y, void *ws, size_t ws_bytes, void *stream);

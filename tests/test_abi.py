@@ -61,6 +61,14 @@ def test_conv_and_update_argument_errors():
     assert L.ie_conv_fwd(by(ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 0, 1)), by(X), by(W), by(Y), 1, 1 << 30, None) == 2
     assert L.ie_conv_fwd(by(d), by(_mat(2 * 64, 16, group=1)), by(W), by(Y), 1, 1 << 30, None) == 6
     assert L.ie_conv_bwd(by(d), by(X), by(W), by(Y), by(_mat(5, 16)), None, 1, 1 << 30, None) == 2
+    # filters of more than 15 taps per axis are out of the loaders' tap masks
+    d16 = ie.conv_desc(1, 16, 16, 16, 16, 16, 1, 1, 0)
+    X16, W16, Y16 = _mat(256, 16), _mat(16, 256), _mat(16, 16)
+    assert L.ie_conv_fwd(by(d16), by(X16), by(W16), by(Y16), 1, 1 << 30, None) == 6
+    assert L.ie_conv_bwd(by(d16), by(X16), by(W16), by(Y16), by(X16), None, 1, 1 << 30, None) == 6
+    # weight-gradient rows wider than a 2^30-byte window of 128 contraction rows
+    wide = (1 << 23) + 16
+    assert L.ie_linear_bwd_dw(by(_mat(4, wide)), by(_mat(4, 8)), by(_mat(wide, 8)), 1, 1 << 30, None) == 6
     S = ie.ie_scalar
     assert L.ie_sgd_update(by(W), by(_mat(32, 144)), by(_mat(31, 144)), S(1, -7), S(7, -3), S(0, 0),
                            1, 4096, None) == 2
