@@ -541,6 +541,10 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
     const uint32_t per_row = N / vw;
     const uint32_t total = (uint32_t)M * per_row;
     const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
+    // exponents and sums are read before this chunk's store (out may alias
+    // them as far as the compiler knows)
+    const bool eb_uni = eb.e32 != nullptr || !eb.row;
+    const int eb0 = exp_at(eb, 0);
     for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
         const uint32_t row = fdiv32(i, dper);
         const int c0 = (int)(i - row * per_row) * vw;
@@ -548,7 +552,8 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
         const long long so = (long long)row * src_pitch;
         const int e = row_group ? clamp_exp_flag(max(E_MIN, gneed[row]), flags) : eT;
         const int er = exp_at(ea, row);
-        uint32_t w = 0;
+        long long sv[4];
+        int ev[4];
         for (int j = 0; j < vw; ++j) {
             const uint32_t col = c0 + j;
             uint32_t sc = col;
@@ -556,8 +561,11 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
                 const uint32_t g = fdiv32(col, dmc);
                 sc = g * mcp + (col - g * mc);
             }
-            w |= (uint32_t)(uint8_t)rne_shift64(sums[so + sc], e - (er + exp_at(eb, col))) << (8 * j);
+            sv[j] = sums[so + sc];
+            ev[j] = er + (eb_uni ? eb0 : exp_at(eb, col));
         }
+        uint32_t w = 0;
+        for (int j = 0; j < vw; ++j) w |= (uint32_t)(uint8_t)rne_shift64(sv[j], e - ev[j]) << (8 * j);
         if (vw == 4) *(uint32_t *)(out + o) = w;
         else out[o] = (int8_t)w;
         if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
@@ -570,8 +578,12 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
 // are summed in int64 over the splits (when the row is short, Q subsets of
 // the splits run side by side and meet in LDS), the row exponent is the
 // largest need, and the row is rounded and stored.
+// Short rows (at most 512 chunks) take 1024 threads, so more split subsets
+// load at once; long rows take 512 threads with up to SR_MAXV chunks each.
 constexpr int SR_THR = 512;
+constexpr int SR_THR_SHORT = 1024;
 constexpr int SR_MAXV = 4;  // chunks per thread when Q == 1
+constexpr int SR_FEW = 2;   // up to this many splits, a thread loads all of its chunks before summing
 
 __device__ __forceinline__ int block_max_n(int v, int *sh) {
 #pragma unroll
@@ -622,12 +634,17 @@ __device__ __forceinline__ void sum_splits(const int *p, long long stride, int z
     }
 }
 
-__global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *partial, int splits, long long stride,
+// At least four waves per SIMD (two 512-thread blocks per CU, at most 128
+// VGPRs), so that consecutive rows overlap.
+template <int THR>
+__global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void split_round_rows_kernel(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
                                                                  int8_t *out_exp, uint32_t *flags, int vw, int Q) {
-    __shared__ int sh[SR_THR / 64];
-    __shared__ long long acc[SR_THR * 4];
+    // short rows (THR == SR_THR_SHORT) hold at most one chunk per thread
+    constexpr int MAXV = THR == SR_THR_SHORT ? 1 : SR_MAXV;
+    __shared__ int sh[THR / 64];
+    __shared__ long long acc[THR * 4];
     const int tid = threadIdx.x;
     const int nch = Nout / vw;
     auto src_col = [&](int col) -> int {
@@ -635,10 +652,17 @@ __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *par
         const int g = (int)fdiv32((uint32_t)col, dmc);
         return g * mcp + (col - g * mc);
     };
+    // A column exponent shared by every column (the usual case) is read once,
+    // before any store: out may alias it as far as the compiler knows, and a
+    // reload after each store would put a memory round trip behind every
+    // element.
+    const bool eb_uni = eb.e32 != nullptr || !eb.row;
+    const int eb0 = exp_at(eb, 0);
     for (int row = blockIdx.x; row < M; row += gridDim.x) {
         const int er = exp_at(ea, row);
         const int *prow = partial + (long long)row * src_pitch;
-        long long v[SR_MAXV][4];
+        long long v[MAXV][4];
+        auto eps = [&](int col) { return er + (eb_uni ? eb0 : exp_at(eb, col)); };
         int need = NEED_NONE;
         if (Q > 1) {
             // short row: chunk c = tid % nch, split subset q = tid / nch
@@ -670,19 +694,44 @@ __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *par
                 v[0][3] = a3;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (j < vw) need = max(need, need64(v[0][j], er + exp_at(eb, vw * tid + j)));
+                    if (j < vw) need = max(need, need64(v[0][j], eps(vw * tid + j)));
             }
         } else {
+            if (vw == 4 && splits <= SR_FEW) {
+                // few splits: every load of the row's chunks in flight at once
+                v4i x[MAXV][SR_FEW];
 #pragma unroll
-            for (int k = 0; k < SR_MAXV; ++k) {
-                const int c = tid + SR_THR * k;
-                v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0;
-                if (c < nch) {
-                    if (vw == 4) sum_splits<4>(prow + 4 * c, stride, 0, 1, splits, v[k]);
-                    else sum_splits<1>(prow + src_col(c), stride, 0, 1, splits, v[k]);
+                for (int k = 0; k < MAXV; ++k) {
+                    const int c = tid + THR * k;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (j < vw) need = max(need, need64(v[k][j], er + exp_at(eb, vw * c + j)));
+                    for (int z = 0; z < SR_FEW; ++z)
+                        x[k][z] = c < nch && z < splits ? *(const v4i *)(prow + 4 * c + (long long)z * stride)
+                                                        : v4i{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int k = 0; k < MAXV; ++k) {
+                    const int c = tid + THR * k;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        long long a = 0;
+#pragma unroll
+                        for (int z = 0; z < SR_FEW; ++z) a += x[k][z][j];
+                        v[k][j] = a;
+                        if (c < nch) need = max(need, need64(a, eps(4 * c + j)));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < MAXV; ++k) {
+                    const int c = tid + THR * k;
+                    v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0;
+                    if (c < nch) {
+                        if (vw == 4) sum_splits<4>(prow + 4 * c, stride, 0, 1, splits, v[k]);
+                        else sum_splits<1>(prow + src_col(c), stride, 0, 1, splits, v[k]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (j < vw) need = max(need, need64(v[k][j], eps(vw * c + j)));
+                    }
                 }
             }
         }
@@ -690,19 +739,19 @@ __global__ __launch_bounds__(SR_THR) void split_round_rows_kernel(const int *par
         const int e = clamp_exp_flag(max(E_MIN, need), flags);
         if (tid == 0) out_exp[row] = (int8_t)e;
         int8_t *orow = out + (long long)row * Nout;
-        const int kmax = Q > 1 ? 1 : SR_MAXV;
+        const int kmax = Q > 1 ? 1 : MAXV;
 #pragma unroll
-        for (int k = 0; k < SR_MAXV; ++k) {
-            const int c = tid + SR_THR * k;
+        for (int k = 0; k < MAXV; ++k) {
+            const int c = tid + THR * k;
             if (k >= kmax || c >= nch) break;
             if (vw == 4) {
                 uint32_t w = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - (er + exp_at(eb, 4 * c + j))) << (8 * j);
+                    w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - eps(4 * c + j)) << (8 * j);
                 *(uint32_t *)(orow + 4 * c) = w;
             } else {
-                orow[c] = (int8_t)rne_shift64(v[k][0], e - (er + exp_at(eb, c)));
+                orow[c] = (int8_t)rne_shift64(v[k][0], e - eps(c));
             }
         }
         __syncthreads();
@@ -720,15 +769,22 @@ hipError_t launch_split_round_rows(const int *partial, int splits, long long spl
     if (M <= 0 || Nout <= 0) return hipSuccess;
     const int vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
     const int nch = Nout / vw;
+    const bool shortrow = nch <= SR_THR;
+    const int thr = shortrow ? SR_THR_SHORT : SR_THR;
     int Q = 1;
-    if (nch <= SR_THR / 2) {
-        Q = SR_THR / nch;
+    if (shortrow && nch <= thr / 2) {
+        Q = thr / nch;
         if (Q > splits) Q = splits;
     }
+    const dim3 grid(blocks_for(M, 1, 16384));
+    const FastDiv dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
     prof_begin(st, PROF_SPLIT_ROUND);
-    hipLaunchKernelGGL(split_round_rows_kernel, dim3(blocks_for(M, 1, 16384)), dim3(SR_THR), 0, st, partial, splits,
-                       split_stride, M, Nout, src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb,
-                       out, out_exp, flags, vw, Q);
+    if (shortrow)
+        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, grid, dim3(SR_THR_SHORT), 0, st, partial, splits,
+                           split_stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q);
+    else
+        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, grid, dim3(SR_THR), 0, st, partial, splits,
+                           split_stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q);
     prof_end(st, PROF_SPLIT_ROUND);
     return hipGetLastError();
 }

@@ -583,31 +583,48 @@ __device__ __forceinline__ int rto_bf(int a, int t) {
 // The kernel
 // ---------------------------------------------------------------------------
 
-// Workgroups are dispatched to the 8 XCDs round robin.  Tiles are numbered so
-// that each XCD receives a contiguous run of the N-fastest tile order: one
-// XCD walks all column tiles of a row tile before the next, keeping the row
-// tile's operand in its own L2.
-__device__ __forceinline__ void tile_of(int bid, int TM, int TN, int &tm, int &tn) {
-    const int T = TM * TN;
-    const int q = T / 8, r = T % 8;
+// Workgroups are dispatched to the 8 XCDs round robin (id % 8).  Work items
+// are numbered so that each XCD receives a contiguous run of the logical
+// order -- contraction chunk slowest, then row tile, then column tile: one
+// XCD walks all column tiles of a row tile, and all tiles of a chunk, before
+// the next, keeping the shared operand rows (and a chunk's rows of both
+// operands) in its own L2.
+__device__ __forceinline__ void work_of(int bid, int TM, int TN, int S, int &tm, int &tn, int &z) {
+    const int T = TM * TN, W = T * S;
+    const int q = W / 8, r = W % 8;
     const int x = bid % 8, j = bid / 8;
     const int logical = x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
-    // the division runs on the vector unit; the tile is the same in every
-    // lane, so its indices go back to scalar registers
-    tm = __builtin_amdgcn_readfirstlane(logical / TN);
-    tn = __builtin_amdgcn_readfirstlane(logical - tm * TN);
+    // the divisions run on the vector unit; the work item is the same in
+    // every lane, so its indices go back to scalar registers
+    z = __builtin_amdgcn_readfirstlane(logical / T);
+    const int t = logical - z * T;
+    tm = __builtin_amdgcn_readfirstlane(t / TN);
+    tn = __builtin_amdgcn_readfirstlane(t - tm * TN);
 }
 
 // Register pipeline depth: 3 for the 2 x 2 tile, which runs two workgroups
-// per CU and would spill at 4.
+// per CU and would spill at 4, and for the 64 x 64 tile.
 template <int MI, int NI>
 struct Stages {
     static constexpr int value = (MI == 2 && NI == 2) || MI * NI == 1 ? 3 : IE_STAGES;
 };
 
+// Contraction slicing of the 64 x 64 tile: wave w takes the w-th 32-byte
+// sub-step of every stage for the whole tile (four independent accumulators,
+// half the fragment reads of a 2 x 2 split of the tile between the waves);
+// the four partial tiles are summed through LDS after the main loop, leaving
+// each wave its own quadrant as in the other tiles.
+#ifndef IE_KSLICE
+#define IE_KSLICE 1
+#endif
+template <int MI, int NI>
+struct KSlice {
+    static constexpr bool value = IE_KSLICE && MI == 1 && NI == 1;
+};
+
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
-__global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
-                                                                          int K, int k_chunk, int TM, Epi ep) {
+__global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
+                                                                          int K, int k_chunk, int TM, int S, Epi ep) {
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
     using LA = Lds<KA, BMt>;
     using LB = Lds<KB, BNt>;
@@ -619,10 +636,9 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int TN = (N + BNt - 1) / BNt;
-    int tile_m, tile_n;
-    tile_of(blockIdx.x, TM, TN, tile_m, tile_n);
+    int tile_m, tile_n, z;
+    work_of(blockIdx.x, TM, TN, S, tile_m, tile_n, z);
     const int m0 = tile_m * BMt, n0 = tile_n * BNt;
-    const int z = blockIdx.z;
     const int kb = z * k_chunk;
     const int ke = min(K, kb + k_chunk);
     const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
@@ -641,15 +657,17 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
         for (int i = tid; i < BNt; i += NTHR) seB[i] = n0 + i < N ? exp_at(ep.eb, n0 + i) : 0;
     } else {
         // group maxima of the split finalize start empty (it runs after this grid)
-        const int nblk = gridDim.x * gridDim.z, blk = blockIdx.x + gridDim.x * blockIdx.z;
+        const int nblk = gridDim.x, blk = blockIdx.x;
         for (int i = blk * NTHR + tid; i < ep.gneed_n; i += nblk * NTHR) ep.gneed[i] = NEED_NONE;
     }
 
-    v16i acc[MI][NI];
+    constexpr bool KS = KSlice<MI, NI>::value;
+    constexpr int AM = KS ? 2 : MI, AN = KS ? 2 : NI;  // accumulators per wave
+    v16i acc[AM][AN];
 #pragma unroll
-    for (int a = 0; a < MI; ++a)
+    for (int a = 0; a < AM; ++a)
 #pragma unroll
-        for (int b = 0; b < NI; ++b)
+        for (int b = 0; b < AN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
@@ -673,6 +691,20 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
 
     auto compute = [&](const int8_t *sA) {
         const int8_t *sB = sA + LA::BYTES;
+        if constexpr (KS) {
+            static_assert(BK / 32 == NTHR / 64, "one contraction sub-step per wave");
+            v4i af[2], bf[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) af[a] = frag<KA, BMt>(sA, a * 32, wave, lane);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) bf[b] = frag<KB, BNt>(sB, b * 32, wave, lane);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+            return;
+        }
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             v4i af[MI], bf[NI];
@@ -712,6 +744,47 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? 4 : MI * NI <= 4 ? 2 : 1)) vo
             lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS]);
             __syncthreads();
         }
+    }
+
+    if constexpr (KS) {
+        // Sum the four partial tiles: quadrant q = 2 a + b (rows 32 a, columns
+        // 32 b) ends with wave q.  Chunk j (ints 4j..4j+3) of a lane's partial
+        // quadrant sits at slot * 1024 + j * 256 + lane (in 16-byte units).
+        // Phase 1: wave w posts quadrants w+1, w+2 (mod 4); phase 2: w+3.
+        v4i *red = (v4i *)lds;
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        auto quad = [&](int q) -> v16i {
+            return q == 0 ? acc[0][0] : q == 1 ? acc[0][1] : q == 2 ? acc[1][0] : acc[1][1];
+        };
+        auto post = [&](int slot, const v16i &v) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[slot * 256 + j * 64 + lane] = v4i{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        };
+        auto take = [&](int slot, v16i &v) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4i t = red[slot * 256 + j * 64 + lane];
+                v[4 * j] += t[0];
+                v[4 * j + 1] += t[1];
+                v[4 * j + 2] += t[2];
+                v[4 * j + 3] += t[3];
+            }
+        };
+        static_assert(8 * 4096 <= 2 * STAGE, "partial tiles exceed LDS");
+        v16i mine = quad(w);
+        __syncthreads();  // every wave is done with the last stage
+        post(2 * w, quad((w + 1) & 3));
+        post(2 * w + 1, quad((w + 2) & 3));
+        __syncthreads();
+        take(2 * ((w + 3) & 3), mine);      // wave w - 1 posted quadrant w first
+        take(2 * ((w + 2) & 3) + 1, mine);  // wave w - 2 posted it second
+        __syncthreads();
+        post(w, quad((w + 3) & 3));
+        __syncthreads();
+        take((w + 1) & 3, mine);  // wave w + 1 posted quadrant (w + 1) + 3 = w
+        __syncthreads();
+        acc[0][0] = mine;
     }
 
     // Element (a, b, r) of this lane sits at tile row / column
@@ -1022,11 +1095,11 @@ template <int KA, int KB, int MI, int NI, bool PARTIAL>
 hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, int splits, int k_chunk,
                       const Epi &ep, hipStream_t st) {
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
-    dim3 grid(TM * TN, 1, splits);
+    dim3 grid(TM * TN * splits, 1, 1);
     const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB;
     prof_begin(st, kind);
     hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, PARTIAL>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
-                       k_chunk, TM, ep);
+                       k_chunk, TM, splits, ep);
     prof_end(st, kind);
     return hipGetLastError();
 }
