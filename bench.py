@@ -55,21 +55,34 @@ def is_gemm(kind: int) -> bool:
     return kind >= 10000 and 1000 <= kind % 10000 < 2000
 
 
+def is_pair(kind: int) -> bool:
+    """Input and weight gradient of a convolution in one grid (two products)."""
+    return is_gemm(kind) and (kind % 10000 - 1000) // 100 == 3
+
+
+def _decode(kind: int):
+    t1, t2 = (kind // 10000) % 100, kind // 1000000
+    k = kind % 10000 - 1000
+    return t1 // 10, t1 % 10, t2 // 10, t2 % 10, (k % 100) // 10, k % 10, k // 100
+
+
 def kind_name(kind: int) -> str:
     if not is_gemm(kind):
         return OTHER.get(kind, (str(kind), ""))[0]
-    mi, ni = (kind // 10000) // 10, (kind // 10000) % 10
-    k = kind % 10000 - 1000
-    return f"gemm_{LOADER[(k % 100) // 10]}_{LOADER[k % 10]}_{EPI[k // 100]}_{64 * mi}x{64 * ni}"
+    mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
+    if is_pair(kind):
+        return f"gemm_pair_{LOADER[ka]}_{LOADER[kb]}_rto_{64 * mi}x{64 * ni}+T_im2colT_partial_{64 * mi2}x{64 * ni2}"
+    return f"gemm_{LOADER[ka]}_{LOADER[kb]}_{EPI[epi]}_{64 * mi}x{64 * ni}"
 
 
 def kind_symbol(kind: int) -> str:
     """The kernel's name as rocprofv3 reports it."""
     if not is_gemm(kind):
         return OTHER.get(kind, ("", str(kind)))[1]
-    mi, ni = (kind // 10000) // 10, (kind // 10000) % 10
-    k = kind % 10000 - 1000
-    return f"gemm_i8_kernel<{(k % 100) // 10}, {k % 10}, {mi}, {ni}, {'true' if k // 100 == 2 else 'false'}>"
+    mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
+    if is_pair(kind):
+        return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
+    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}>"
 
 
 # ---------------------------------------------------------------------------
@@ -374,10 +387,12 @@ def main():
             for c in calls:
                 n_gemm = sum(1 for k in c.kinds if is_gemm(k))
                 n_upd = sum(1 for k in c.kinds if 2000 <= k < 3000)
-                prod = -1  # index of the contraction a launch belongs to
+                prod = -1  # index of the last contraction launched
+                fin = 0    # index of the contraction the next finalize belongs to
                 for k in c.kinds:
                     if is_gemm(k):
-                        prod += 1
+                        prod += 2 if is_pair(k) else 1
+                        fin = prod - 1 if is_pair(k) else prod
                     if only is not None and k != only:
                         continue
                     ms, kind = recs[pos]
@@ -393,7 +408,9 @@ def main():
                         a["bytes"] += c.bytes / n_upd
                     elif c.outs:
                         # finalize or pre-pass of a contraction: its int8 result
-                        a["bytes"] += c.outs[min(max(prod, 0), len(c.outs) - 1)]
+                        a["bytes"] += c.outs[min(max(fin, 0), len(c.outs) - 1)]
+                        if prod >= 0:
+                            fin = min(fin + 1, prod)
         assert pos == len(recs), (pos, len(recs))
         return agg
 

@@ -467,6 +467,57 @@ size_t conv_bwd_ws(const ie_conv_desc *d) {
     return align256(c.off);
 }
 
+// Input and weight gradient of a convolution in one paired launch, when
+// both plans allow it: the input gradient as a round-to-odd product reading
+// W in place, the weight gradient as a split contraction with the fused row
+// finalize.  IE_ERR_UNSUPPORTED, with nothing launched, otherwise.
+ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const ie_mat *W, const ie_mat *dY, const ie_mat *dX,
+                        const ie_mat *dW, const int8_t *dys, int8_t *xp, const ProductWs &pw, const WgradWs &w,
+                        uint32_t *flags, hipStream_t st) {
+    const long long nhw = (long long)g.n * g.h * g.w, npq = (long long)g.n * g.p * g.q;
+    const long long rskp = (long long)g.r * g.s * g.kp, rscp = (long long)g.r * g.s * g.cp;
+    const long long rsc = (long long)g.r * g.s * g.c;
+    if (W->group != IE_GROUP_TENSOR || g.c % 16 != 0 || !aligned(W->mant, 16) || !weight_window_fits(g))
+        return IE_ERR_UNSUPPORTED;
+    if (nhw == 0 || npq == 0 || dW->group != IE_GROUP_ROW || !split_round_rows_fits((int)rsc, g.c, g.cp))
+        return IE_ERR_UNSUPPORTED;
+    const Plan p1 = plan_product(nhw, g.c, rskp, 0, 1);
+    if (p1.mode != PLAN_RTO) return IE_ERR_UNSUPPORTED;
+    const Plan p2 = plan_wgrad(g.k, rscp, npq);
+    const Operand A1{LD_DGRAD, dys, g.kp, (int)nhw, g};
+    const Operand B1{LD_WT, W->mant, 0, g.c, g};
+    const Operand A2{LD_T, dys, g.kp, g.k, {}};
+    const Operand B2{LD_IM2COL_T, xp ? xp : X->mant, g.cp, (int)rscp, g};
+    if (!gemm_pair_supported(A1, B1, p1.t, A2, B2, p2.t)) return IE_ERR_UNSUPPORTED;
+    log_plan("conv", nhw, g.c, rskp, p1);
+    log_plan("wgrad", g.k, rscp, npq, p2);
+    if (xp) IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
+    const ExpSrc edy{dY->exp, nullptr, 0}, ew{W->exp, nullptr, 0}, ex{X->exp, nullptr, 0};
+    Epi e1;
+    memset(&e1, 0, sizeof e1);
+    e1.ea = edy;
+    e1.eb = ew;
+    e1.out = dX->mant;
+    e1.out_exp = dX->exp;
+    e1.flags = flags;
+    e1.mode = EPI_RTO;
+    e1.v16 = pw.v16;
+    e1.p16 = pw.p16;
+    Epi e2;
+    memset(&e2, 0, sizeof e2);
+    e2.partial = w.partial;
+    e2.split_stride = g.k * rscp;
+    e2.flags = flags;
+    e2.gneed = w.gneed;
+    e2.gneed_n = 0;
+    IE_TRY(launch_gemm_pair(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
+                            (int)npq, p2.t, p2.splits, p2.k_chunk, e2, st));
+    IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)nhw, g.c, p1.t, 0, dX->mant, dX->exp, flags, st));
+    IE_TRY(launch_split_round_rows(w.partial, p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex,
+                                   dW->mant, dW->exp, flags, st));
+    return IE_OK;
+}
+
 ie_status check_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar weight_decay) {
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(V));
@@ -749,8 +800,12 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
                          ExpSrc{X->exp, nullptr, 0}, dW, w, flags, s);
     };
     if (dX && dW) {
-        // the two products are independent: the weight gradient runs on a
-        // second stream beside the input gradient
+        // the two products are independent: one grid runs both when a paired
+        // kernel covers their plans ...
+        const ie_status sp = conv_bwd_pair(g, X, W, dY, dX, dW, dys, xp, pw, w, flags, st);
+        if (sp != IE_ERR_UNSUPPORTED) return sp;
+        // ... else the weight gradient runs on a second stream beside the
+        // input gradient
         std::lock_guard<std::mutex> lock(g_aux_mu);
         if (AuxStream *ax = aux_stream()) {
             IE_TRY(hipEventRecord(ax->fork, st));

@@ -622,14 +622,28 @@ struct KSlice {
     static constexpr bool value = IE_KSLICE && MI == 1 && NI == 1;
 };
 
+// Workgroups per CU that a tile's register budget is sized for.
+template <int MI, int NI>
+struct Occ {
+    static constexpr int value = MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI <= 4 ? 2 : 1;
+};
+
+// LDS of a tile: two stages of both operands (also the epilogue's staging).
+template <int KA, int KB, int MI, int NI>
+struct TileLds {
+    static constexpr int value = 2 * (Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES);
+};
+
+// One workgroup's work item: bid and nblk are its index and the number of
+// workgroups of its grid (or of its part of a paired grid); lds points to
+// TileLds bytes of shared memory.
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
-__global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI <= 4 ? 2 : 1)) void gemm_i8_kernel(Operand A, Operand B, int M, int N,
-                                                                          int K, int k_chunk, int TM, int S, Epi ep) {
+__device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, int M, int N, int K, int k_chunk,
+                                          int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
     using LA = Lds<KA, BMt>;
     using LB = Lds<KB, BNt>;
     constexpr int STAGE = LA::BYTES + LB::BYTES;
-    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 
     const int wm = wave >> 1, wn = wave & 1;
     const int TN = (N + BNt - 1) / BNt;
     int tile_m, tile_n, z;
-    work_of(blockIdx.x, TM, TN, S, tile_m, tile_n, z);
+    work_of(bid, TM, TN, S, tile_m, tile_n, z);
     const int m0 = tile_m * BMt, n0 = tile_n * BNt;
     const int kb = z * k_chunk;
     const int ke = min(K, kb + k_chunk);
@@ -657,8 +671,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 
         for (int i = tid; i < BNt; i += NTHR) seB[i] = n0 + i < N ? exp_at(ep.eb, n0 + i) : 0;
     } else {
         // group maxima of the split finalize start empty (it runs after this grid)
-        const int nblk = gridDim.x, blk = blockIdx.x;
-        for (int i = blk * NTHR + tid; i < ep.gneed_n; i += nblk * NTHR) ep.gneed[i] = NEED_NONE;
+        for (int i = bid * NTHR + tid; i < ep.gneed_n; i += nblk * NTHR) ep.gneed[i] = NEED_NONE;
     }
 
     constexpr bool KS = KSlice<MI, NI>::value;
@@ -889,7 +902,7 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 
             int e = 0, p = 0;
             if (direct) {
                 e = clamp_exp_flag(max(E_MIN, gmax), ep.flags);
-                if (tid == 0 && blockIdx.x == 0) ep.out_exp[0] = (int8_t)e;
+                if (tid == 0 && bid == 0) ep.out_exp[0] = (int8_t)e;
             } else {
                 // round to odd two bits below the tile's own need; the tile's
                 // need goes to p16, where the second pass takes the maximum
@@ -1089,6 +1102,69 @@ __global__ __launch_bounds__(NTHR, (MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 
         if (direct) flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0);
         else flush(ES2{}, ep.v16, N, (N & 7) == 0);
     }
+}
+
+template <int KA, int KB, int MI, int NI, bool PARTIAL>
+__global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_i8_kernel(Operand A, Operand B, int M, int N, int K,
+                                                                         int k_chunk, int TM, int S, Epi ep) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
+    gemm_tile<KA, KB, MI, NI, PARTIAL>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
+}
+
+// Two independent products in one grid: the first part's workgroups (a
+// round-to-odd or direct product), padded to a multiple of 8 so that the
+// second part's work order still meets the XCDs as planned, then the second
+// part's (a split contraction).  One launch instead of two streams joined
+// by events.
+struct PairPart {
+    Operand A, B;
+    int M, N, K, k_chunk, TM, S, nblk;
+    Epi ep;
+};
+
+template <int KA1, int KB1, int MI1, int NI1, int KA2, int KB2, int MI2, int NI2>
+__global__ __launch_bounds__(NTHR, (Occ<MI1, NI1>::value < Occ<MI2, NI2>::value ? Occ<MI1, NI1>::value
+                                                                                : Occ<MI2, NI2>::value))
+void gemm_pair_kernel(PairPart p1, PairPart p2, int g1) {
+    constexpr int L1 = TileLds<KA1, KB1, MI1, NI1>::value, L2 = TileLds<KA2, KB2, MI2, NI2>::value;
+    __shared__ __attribute__((aligned(16))) int8_t lds[L1 > L2 ? L1 : L2];
+    const int b = blockIdx.x;
+    if (b < g1) {
+        if (b < p1.nblk)
+            gemm_tile<KA1, KB1, MI1, NI1, false>(p1.A, p1.B, p1.M, p1.N, p1.K, p1.k_chunk, p1.TM, p1.S, p1.ep, b,
+                                                 p1.nblk, lds);
+    } else {
+        gemm_tile<KA2, KB2, MI2, NI2, true>(p2.A, p2.B, p2.M, p2.N, p2.K, p2.k_chunk, p2.TM, p2.S, p2.ep, b - g1,
+                                            p2.nblk, lds);
+    }
+}
+
+// Part descriptor of a product of tile (MI, NI).
+inline PairPart pair_part(const Operand &A, const Operand &B, int M, int N, int K, int MI, int NI, int splits,
+                          int k_chunk, const Epi &ep) {
+    PairPart p;
+    p.A = A;
+    p.B = B;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.k_chunk = k_chunk;
+    p.TM = (M + 64 * MI - 1) / (64 * MI);
+    p.S = splits;
+    p.nblk = p.TM * ((N + 64 * NI - 1) / (64 * NI)) * splits;
+    p.ep = ep;
+    return p;
+}
+
+template <int KA1, int KB1, int MI1, int NI1, int KA2, int KB2, int MI2, int NI2>
+hipError_t launch_pair(const PairPart &p1, const PairPart &p2, hipStream_t st) {
+    const int g1 = (p1.nblk + 7) / 8 * 8;
+    const int kind = 1000000 * (10 * MI2 + NI2) + 10000 * (10 * MI1 + NI1) + 1000 + 100 * 3 + 10 * KA1 + KB1;
+    prof_begin(st, kind);
+    hipLaunchKernelGGL((gemm_pair_kernel<KA1, KB1, MI1, NI1, KA2, KB2, MI2, NI2>), dim3(g1 + p2.nblk), dim3(NTHR), 0,
+                       st, p1, p2, g1);
+    prof_end(st, kind);
+    return hipGetLastError();
 }
 
 template <int KA, int KB, int MI, int NI, bool PARTIAL>

@@ -118,6 +118,14 @@ hipError_t launch_gemm_dgrad_wt(const Operand &A, const Operand &B, int M, int N
                                 int k_chunk, bool partial, const Epi &ep, hipStream_t st);
 hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+// Input gradient (LD_DGRAD x LD_WT, round-to-odd epilogue, tile t1) and weight
+// gradient (LD_T x LD_IM2COL_T, split contraction, tile t2) in one grid.
+// hipErrorInvalidValue when the combination has no kernel (nothing launched).
+bool gemm_pair_supported(const Operand &A1, const Operand &B1, Tile t1, const Operand &A2, const Operand &B2,
+                         Tile t2);
+hipError_t launch_gemm_pair(const Operand &A1, const Operand &B1, int M1, int N1, int K1, Tile t1, int k_chunk1,
+                            const Epi &ep1, const Operand &A2, const Operand &B2, int M2, int N2, int K2, Tile t2,
+                            int splits2, int k_chunk2, const Epi &ep2, hipStream_t st);
 
 // Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
 void prof_begin(hipStream_t st, int kind);

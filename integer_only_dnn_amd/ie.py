@@ -105,6 +105,7 @@ class Mat:
         self.mant = mant
         self.exp = exp
         self.group = int(group)
+        self._desc = {}  # (rows, cols) -> (mant, exp, ie_mat): descriptors built once per view
 
     @staticmethod
     def empty(rows: int, cols: int, group: int, device="cuda") -> "Mat":
@@ -113,11 +114,19 @@ class Mat:
         return Mat(m, e, group)
 
     def c(self, rows=None, cols=None) -> ie_mat:
-        """The C descriptor; `rows`/`cols` view an NHWC tensor as [N*H*W x C]."""
-        if rows is None:
+        """The C descriptor; `rows`/`cols` view an NHWC tensor as [N*H*W x C].
+        Built once per view and reused while `mant` and `exp` are the same
+        tensors."""
+        hit = self._desc.get((rows, cols))
+        if hit is not None and hit[0] is self.mant and hit[1] is self.exp:
+            return hit[2]
+        r, c = rows, cols
+        if r is None:
             assert self.mant.dim() == 2
-            rows, cols = self.mant.shape
-        return ie_mat(self.mant.data_ptr(), self.exp.data_ptr(), rows, cols, self.group)
+            r, c = self.mant.shape
+        d = ie_mat(self.mant.data_ptr(), self.exp.data_ptr(), r, c, self.group)
+        self._desc[(rows, cols)] = (self.mant, self.exp, d)
+        return d
 
 
 class Workspace:
@@ -151,21 +160,38 @@ def conv_desc(n, h, w, c, k, r, s, stride, pad) -> ie_conv_desc:
     return ie_conv_desc(n, h, w, c, k, r, s, stride, pad)
 
 
+_ws_sizes = {}
+
+
+def _ws_size(name: str, *args) -> int:
+    """The library's workspace size for a call shape (memoised: the library
+    plans the call to answer; the planner's tuning overrides are part of the
+    key)."""
+    key = (name, os.environ.get("IE_TILE"), os.environ.get("IE_WTILE")) + tuple((a.n, a.h, a.w, a.c, a.k, a.r, a.s, a.stride, a.pad) if isinstance(a, ie_conv_desc) else a
+                          for a in args)
+    n = _ws_sizes.get(key)
+    if n is None:
+        fn = getattr(lib(), name)
+        n = fn(*[byref(a) if isinstance(a, ie_conv_desc) else a for a in args])
+        _ws_sizes[key] = n
+    return n
+
+
 def ie_linear_fwd(X: Mat, W: Mat, Y: Mat, ws: Workspace) -> None:
     x, w, y = X.c(), W.c(), Y.c()
-    p, b = ws.get(lib().ie_linear_fwd_workspace(x.rows, w.rows, x.cols))
+    p, b = ws.get(_ws_size("ie_linear_fwd_workspace", x.rows, w.rows, x.cols))
     _check(lib().ie_linear_fwd(byref(x), byref(w), byref(y), p, b, _stream(ws.device)), "ie_linear_fwd")
 
 
 def ie_linear_bwd_dx(dY: Mat, W: Mat, dX: Mat, ws: Workspace) -> None:
     dy, w, dx = dY.c(), W.c(), dX.c()
-    p, b = ws.get(lib().ie_linear_bwd_dx_workspace(dy.rows, dy.cols, w.cols))
+    p, b = ws.get(_ws_size("ie_linear_bwd_dx_workspace", dy.rows, dy.cols, w.cols))
     _check(lib().ie_linear_bwd_dx(byref(dy), byref(w), byref(dx), p, b, _stream(ws.device)), "ie_linear_bwd_dx")
 
 
 def ie_linear_bwd_dw(dY: Mat, X: Mat, dW: Mat, ws: Workspace) -> None:
     dy, x, dw = dY.c(), X.c(), dW.c()
-    p, b = ws.get(lib().ie_linear_bwd_dw_workspace(dy.rows, dy.cols, x.cols))
+    p, b = ws.get(_ws_size("ie_linear_bwd_dw_workspace", dy.rows, dy.cols, x.cols))
     _check(lib().ie_linear_bwd_dw(byref(dy), byref(x), byref(dw), p, b, _stream(ws.device)), "ie_linear_bwd_dw")
 
 
@@ -175,7 +201,7 @@ def ie_conv_fwd(d: ie_conv_desc, X: Mat, W: Mat, Y: Mat, ws: Workspace) -> None:
     P = (d.h + 2 * d.pad - d.r) // d.stride + 1
     Q = (d.w + 2 * d.pad - d.s) // d.stride + 1
     y = Y.c(d.n * P * Q, d.k)
-    p, b = ws.get(lib().ie_conv_fwd_workspace(byref(d)))
+    p, b = ws.get(_ws_size("ie_conv_fwd_workspace", d))
     _check(lib().ie_conv_fwd(byref(d), byref(x), byref(w), byref(y), p, b, _stream(ws.device)), "ie_conv_fwd")
 
 
@@ -188,7 +214,7 @@ def ie_conv_bwd(d: ie_conv_desc, X: Mat, W: Mat, dY: Mat, dX: Mat | None, dW: Ma
     dy = dY.c(d.n * P * Q, d.k)
     dx = dX.c(d.n * d.h * d.w, d.c) if dX is not None else None
     dw = dW.c(d.k, d.r * d.s * d.c) if dW is not None else None
-    p, b = ws.get(lib().ie_conv_bwd_workspace(byref(d)))
+    p, b = ws.get(_ws_size("ie_conv_bwd_workspace", d))
     _check(lib().ie_conv_bwd(byref(d), byref(x), byref(w), byref(dy),
                              byref(dx) if dx is not None else None,
                              byref(dw) if dw is not None else None, p, b, _stream(ws.device)), "ie_conv_bwd")
@@ -196,7 +222,7 @@ def ie_conv_bwd(d: ie_conv_desc, X: Mat, W: Mat, dY: Mat, dX: Mat | None, dW: Ma
 
 def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws: Workspace = None) -> None:
     w, v, g = W.c(), V.c(), G.c()
-    p, b = ws.get(lib().ie_sgd_update_workspace(w.rows, w.cols))
+    p, b = ws.get(_ws_size("ie_sgd_update_workspace", w.rows, w.cols))
     _check(lib().ie_sgd_update(byref(w), byref(v), byref(g), ie_scalar(*lr), ie_scalar(*momentum),
                                ie_scalar(*weight_decay), p, b, _stream(ws.device)), "ie_sgd_update")
 
@@ -210,7 +236,7 @@ def ie_sgd_update_multi(Ws, Vs, Gs, lr, momentum, weight_decay=(0, 0), ws: Works
     w = arr(*[m.c() for m in Ws])
     v = arr(*[m.c() for m in Vs])
     g = arr(*[m.c() for m in Gs])
-    p, b = ws.get(lib().ie_sgd_update_multi_workspace(n))
+    p, b = ws.get(_ws_size("ie_sgd_update_multi_workspace", n))
     _check(lib().ie_sgd_update_multi(n, w, v, g, ie_scalar(*lr), ie_scalar(*momentum), ie_scalar(*weight_decay),
                                      p, b, _stream(ws.device)), "ie_sgd_update_multi")
 

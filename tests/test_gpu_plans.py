@@ -133,3 +133,31 @@ def test_wgrad_plans(tile, splits, ws, plan):
                        ws)
         assert_same(dW, o.conv_wgrad(d, dYc, Xc, g), f"conv dW group {g}")
     assert ws.status() == 0
+
+
+# Input and weight gradient together: the paired kernel (both products in one
+# grid) for every instantiated tile pair, forced through the overrides.
+PAIR_D = [(2, 1), (1, 1), (2, 2)]
+PAIR_W = [(1, 1), (2, 2)]
+
+
+@pytest.mark.parametrize("dtile", PAIR_D, ids=lambda t: f"d{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("wtile", PAIR_W, ids=lambda t: f"w{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("wsplits", [1, 3])
+def test_conv_bwd_pair(dtile, wtile, wsplits, ws, plan):
+    shape = (2, 9, 9, 32, 40, 3, 3, 2, 1)
+    n, h, w, c, k, r, s, st, pad = shape
+    announce(f"conv bwd pair dtile={dtile} wtile={wtile} wsplits={wsplits} shape={shape}")
+    d = o.ConvShape(*shape)
+    dd = ie.conv_desc(*shape)
+    rng = np.random.default_rng(31 * dtile[0] + 7 * dtile[1] + 5 * wtile[0] + wsplits)
+    X = rand_qt(rng, (n, h, w, c), T, zero_frac=0.3)
+    W = rand_qt(rng, (k, r * s * c), T)
+    dY = rand_qt(rng, (n, d.p, d.q, k), T)
+    plan(dtile, 1, 1, wtile, wsplits)
+    dX = ie.Mat.empty(n * h * w, c, T)
+    dW = ie.Mat.empty(k, r * s * c, R)
+    ie.ie_conv_bwd(dd, qt_to_dev(X, rows=n * h * w), qt_to_dev(W), qt_to_dev(dY, rows=n * d.p * d.q), dX, dW, ws)
+    assert_same(dX, o.conv_dgrad(d, dY, W, T), "conv dgrad")
+    assert_same(dW, o.conv_wgrad(d, dY, X, R), "conv wgrad")
+    assert ws.status() == 0
