@@ -122,15 +122,10 @@ __device__ __forceinline__ void raise_max_aux(int *p, int v) {
     if (v > __atomic_load_n(p, __ATOMIC_RELAXED)) atomicMax(p, v);
 }
 
-__device__ __forceinline__ int block_wave_max(int v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
-    return v;
-}
+__device__ __forceinline__ int block_wave_max(int v) { return wave_max_dpp(v); }
 
 __device__ __forceinline__ int block_max256(int v, int *sh) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+    v = wave_max_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -586,8 +581,7 @@ constexpr int SR_MAXV = 4;  // chunks per thread when Q == 1
 constexpr int SR_FEW = 2;   // up to this many splits, a thread loads all of its chunks before summing
 
 __device__ __forceinline__ int block_max_n(int v, int *sh) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+    v = wave_max_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();

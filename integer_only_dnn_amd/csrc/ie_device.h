@@ -85,4 +85,24 @@ __device__ __forceinline__ int clamp_exp_flag(int e, uint32_t *flags) {
     return e;
 }
 
+// Maximum over the 64 lanes of a wave, returned in every lane (all lanes
+// active).  DPP row shifts by 1, 2, 4, 8 leave each 16-lane row's maximum in
+// its lane 15; row broadcasts 15 and 31 carry it across the rows to lane 63,
+// which is read back.  Lanes whose DPP source is outside the row keep `lo`.
+__device__ __forceinline__ int wave_max_dpp(int v) {
+    constexpr int lo = (int)0x80000000;
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x142, 0xa, 0xf, false));  // row_bcast:15 -> rows 1, 3
+    v = max(v, __builtin_amdgcn_update_dpp(lo, v, 0x143, 0xc, 0xf, false));  // row_bcast:31 -> rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Unsigned form (flipping the sign bit maps unsigned order onto signed).
+__device__ __forceinline__ uint32_t wave_umax_dpp(uint32_t v) {
+    return (uint32_t)wave_max_dpp((int)(v ^ 0x80000000u)) ^ 0x80000000u;
+}
+
 }  // namespace ie

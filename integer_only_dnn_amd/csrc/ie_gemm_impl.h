@@ -533,11 +533,7 @@ __device__ __forceinline__ v4i frag(const int8_t *s, int rowbase, int ks, int la
 // Epilogue helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
-    return v;
-}
+__device__ __forceinline__ int wave_max(int v) { return wave_max_dpp(v); }
 
 // Maxima of 16 rows over the 32 lanes of a half-wave, transposing as it
 // reduces (16 exchanges instead of 80): at each step a lane keeps half of its

@@ -39,11 +39,7 @@ __device__ __forceinline__ Ex64 combine64(int X, int pa, int Y, int pb) {
 
 __device__ __forceinline__ int sbyte(uint32_t w, int j) { return (int)(int8_t)(w >> (8 * j)); }
 
-__device__ __forceinline__ int wave_max64(int v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
-    return v;
-}
+__device__ __forceinline__ int wave_max64(int v) { return wave_max_dpp(v); }
 
 __device__ __forceinline__ uint32_t load_dw(const int8_t *row, long long col, long long cols, int vec) {
     if (vec && col + 4 <= cols) return *(const uint32_t *)(row + col);
@@ -63,7 +59,8 @@ __device__ __forceinline__ void store_dw(int8_t *row, long long col, long long c
 }
 
 // The wide (int64) forms are out of line: rows with exponent gaps above 15
-// are rare and the inlined code would multiply the kernel size.
+// are rare, and inlined they raise the register pressure of every row's path
+// (measured: spills and half the throughput).
 __device__ __noinline__ int sum_need_wide(int X, int pa, int Y, int pb) {
     Ex64 s = combine64(X, pa, Y, pb);
     return need64(s.n, s.base);
@@ -112,17 +109,42 @@ __device__ __forceinline__ RneU rne_u(int sh) {
     return r;
 }
 
-__device__ __forceinline__ int rne_apply(int n, const RneU &r, bool left) {
-    if (left) return n << r.left;
-    const int bit = (n >> r.sh) & 1;
-    return (n + r.hm1 + bit) >> r.sh;
+
+// c = rne(n, r) for D x 4 held values; the shift direction is uniform over
+// the row, so it is decided once, outside the element loops.
+template <int D>
+__device__ __forceinline__ void rne_rows(const int (&n)[D][4], const RneU &r, int (&c)[D][4]) {
+    if (r.is_left) {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) c[j][t] = n[j][t] << r.left;
+    } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) c[j][t] = (n[j][t] + r.hm1 + ((n[j][t] >> r.sh) & 1)) >> r.sh;
+    }
 }
 
-__device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
-    return v;
+__device__ __forceinline__ uint32_t pack4(const int (&c)[4]) {
+    return (uint32_t)(uint8_t)c[0] | ((uint32_t)(uint8_t)c[1] << 8) | ((uint32_t)(uint8_t)c[2] << 16) |
+           ((uint32_t)(uint8_t)c[3] << 24);
 }
+
+// Largest |n| of D x 4 values (signed maximum and minimum, combined once).
+template <int D>
+__device__ __forceinline__ uint32_t absmax_rows(const int (&n)[D][4]) {
+    int hi = 0, lo = 0;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        hi = max(hi, max(max(n[j][0], n[j][1]), max(n[j][2], n[j][3])));
+        lo = min(lo, min(min(n[j][0], n[j][1]), min(n[j][2], n[j][3])));
+    }
+    return (uint32_t)max(hi, -lo);
+}
+
+__device__ __forceinline__ uint32_t umax_wave(uint32_t v) { return wave_umax_dpp(v); }
 
 // One row of W, V, G is owned by WPR waves (WPR = 1: four rows per block;
 // WPR = 4: one row per block, maxima combined through LDS).  Each lane holds D
@@ -147,8 +169,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     int parity = 0;
     int *bmax_v = a.tmp + 2, *bmax_w = a.tmp + 2 + UPD_MAX_BLOCKS;
     auto block_imax = [&](int v) -> int {
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+        v = wave_max_dpp(v);
         __syncthreads();
         if (lane == 0) bred[wave] = v;
         __syncthreads();
@@ -213,20 +234,17 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
             const int pw = a.lr_e + evn;
             const int e = ewn_t;
             if (abs(ew - pw) <= 15) {
+                // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
                 const int base = min(ew, pw);
                 const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
-                const RneU r = rne_u(e - base);
-                const bool left = r.is_left;
+                int n[D][4], c[D][4];
 #pragma unroll
-                for (int j = 0; j < D; ++j) {
-                    uint32_t o = 0;
+                for (int j = 0; j < D; ++j)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int n = sbyte(W[j], t) * fa + sbyte(V[j], t) * fb;
-                        o |= (uint32_t)(uint8_t)rne_apply(n, r, left) << (8 * t);
-                    }
-                    store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
-                }
+                    for (int t = 0; t < 4; ++t) n[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(sbyte(V[j], t), fb);
+                rne_rows<D>(n, rne_u(e - base), c);
+#pragma unroll
+                for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
             } else {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
@@ -251,18 +269,14 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
         int vn[D][4];
         int needv;
         if (nv) {
+            // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
             const int base = min(pa, pb);
             const int fa = a.mom_m * (1 << (pa - base)), fb = 1 << (pb - base);
-            uint32_t mx = 0;
 #pragma unroll
             for (int j = 0; j < D; ++j)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int n = sbyte(V[j], t) * fa + sbyte(G[j], t) * fb;
-                    vn[j][t] = n;
-                    mx = max(mx, (uint32_t)(n < 0 ? -n : n));
-                }
-            mx = row_umax(mx);
+                for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(V[j], t), fa) + __mul24(sbyte(G[j], t), fb);
+            const uint32_t mx = row_umax(absmax_rows<D>(vn));
             needv = mx ? base + mant_shift32(mx) : NEED_NONE;
         } else {
             int m = NEED_NONE;
@@ -279,12 +293,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
         const int evn = v_tensor ? evn_t : clamp_exp_flag(max(E_MIN, needv), a.flags);
         int c[D][4];
         if (nv) {
-            const RneU r = rne_u(evn - min(pa, pb));
-            const bool left = r.is_left;
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) c[j][t] = rne_apply(vn[j][t], r, left);
+            rne_rows<D>(vn, rne_u(evn - min(pa, pb)), c);
         } else {
 #pragma unroll
             for (int j = 0; j < D; ++j)
@@ -293,11 +302,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
                     c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
         }
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const uint32_t o = (uint32_t)(uint8_t)c[j][0] | ((uint32_t)(uint8_t)c[j][1] << 8) |
-                               ((uint32_t)(uint8_t)c[j][2] << 16) | ((uint32_t)(uint8_t)c[j][3] << 24);
-            store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
-        }
+        for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
         if (lane == 0 && sub == 0) {
             if (!v_tensor) a.v_exp[row] = (int8_t)evn;
             else if (row == 0) a.v_exp[0] = (int8_t)evn;
@@ -310,16 +315,11 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
         if (nw) {
             const int base = min(ew, pw);
             const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
-            uint32_t mx = 0;
 #pragma unroll
             for (int j = 0; j < D; ++j)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int n = sbyte(W[j], t) * fa + c[j][t] * fb;
-                    vn[j][t] = n;
-                    mx = max(mx, (uint32_t)(n < 0 ? -n : n));
-                }
-            mx = row_umax(mx);
+                for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(c[j][t], fb);
+            const uint32_t mx = row_umax(absmax_rows<D>(vn));
             needw = mx ? base + mant_shift32(mx) : NEED_NONE;
         } else {
             int m = NEED_NONE;
@@ -335,15 +335,10 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
         }
         const int ewn = clamp_exp_flag(max(E_MIN, needw), a.flags);
         if (nw) {
-            const RneU r = rne_u(ewn - min(ew, pw));
-            const bool left = r.is_left;
+            int cw[D][4];
+            rne_rows<D>(vn, rne_u(ewn - min(ew, pw)), cw);
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                uint32_t o = 0;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o |= (uint32_t)(uint8_t)rne_apply(vn[j][t], r, left) << (8 * t);
-                store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
-            }
+            for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(cw[j]));
         } else {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
