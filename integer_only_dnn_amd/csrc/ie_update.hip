@@ -213,143 +213,170 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     }
     int bneed = NEED_NONE;  // largest need of this block's rows (passes 0, 1)
 
-    for (long long row0 = (long long)blk * RPB; row0 < a.rows; row0 += (long long)nblk * RPB) {
-        const long long row = row0 + wave / WPR;
-        const bool live = row < a.rows;  // WPR = 1 only: trailing waves of the last block
-        if (WPR == 1 && !live) continue;
-        const long long off = row * a.cols;
+    // Rows of this block: row, row + stride, ...  The next row's tensors and
+    // exponents are loaded before the current row is worked on, so a wave
+    // keeps loads in flight across its rows.  (Exponents are read with the
+    // data: a read after this row's stores could not be moved ahead of them.)
+    struct RowIn {
         uint32_t W[D], V[D], G[D];
+        int ew, ev, eg;
+    };
+    auto load_row = [&](long long row, RowIn &x) {
+        const long long off = row * a.cols;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const long long col = 4ll * (lane + 64 * (sub + WPR * j));
-            W[j] = (pass != 0) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
-            V[j] = load_dw(a.v + off, col, a.cols, vec);
-            G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
+            x.W[j] = (pass != 0) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
+            x.V[j] = load_dw(a.v + off, col, a.cols, vec);
+            x.G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
         }
-        const int ew = w_tensor ? ew_t : (int)a.w_exp[row];
+        x.ew = w_tensor ? ew_t : (int)a.w_exp[row];
+        x.ev = pass == 2 ? (int)a.v_exp[v_tensor ? 0 : row] : v_tensor ? ev_t : (int)a.v_exp[row];
+        x.eg = pass == 2 ? 0 : a.g_row ? (int)a.g_exp[row] : (int)a.g_exp[0];
+    };
+    auto process = [&](long long row, const RowIn &x) {
+        const long long off = row * a.cols;
+        const uint32_t(&W)[D] = x.W;
+        const uint32_t(&V)[D] = x.V;
+        const uint32_t(&G)[D] = x.G;
+            const int ew = x.ew;
 
-        // ---- weight step only (whole-tensor weight, second pass) ----
-        if (pass == 2) {
-            const int evn = (int)a.v_exp[v_tensor ? 0 : row];
-            const int pw = a.lr_e + evn;
-            const int e = ewn_t;
-            if (abs(ew - pw) <= 15) {
+            // ---- weight step only (whole-tensor weight, second pass) ----
+            if (pass == 2) {
+                const int evn = x.ev;
+                const int pw = a.lr_e + evn;
+                const int e = ewn_t;
+                if (abs(ew - pw) <= 15) {
+                    // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
+                    const int base = min(ew, pw);
+                    const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
+                    int n[D][4], c[D][4];
+    #pragma unroll
+                    for (int j = 0; j < D; ++j)
+    #pragma unroll
+                        for (int t = 0; t < 4; ++t) n[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(sbyte(V[j], t), fb);
+                    rne_rows<D>(n, rne_u(e - base), c);
+    #pragma unroll
+                    for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
+                } else {
+    #pragma unroll
+                    for (int j = 0; j < D; ++j) {
+                        uint32_t o = 0;
+    #pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int c = sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * sbyte(V[j], t), pw, e);
+                            o |= (uint32_t)(uint8_t)c << (8 * t);
+                        }
+                        store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
+                    }
+                }
+                if (row == 0 && lane == 0 && sub == 0) a.w_exp[0] = (int8_t)e;
+                return;
+            }
+
+            // ---- velocity: v = momentum * V + G ----
+            const int ev = x.ev;
+            const int eg = x.eg;
+            const int pa = ev + a.mom_e, pb = eg;
+            const bool nv = abs(pa - pb) <= 15;
+            int vn[D][4];
+            int needv;
+            if (nv) {
                 // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
+                const int base = min(pa, pb);
+                const int fa = a.mom_m * (1 << (pa - base)), fb = 1 << (pb - base);
+    #pragma unroll
+                for (int j = 0; j < D; ++j)
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(V[j], t), fa) + __mul24(sbyte(G[j], t), fb);
+                const uint32_t mx = row_umax(absmax_rows<D>(vn));
+                needv = mx ? base + mant_shift32(mx) : NEED_NONE;
+            } else {
+                int m = NEED_NONE;
+    #pragma unroll
+                for (int j = 0; j < D; ++j)
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+                needv = row_imax(m);
+            }
+            if (pass == 0) {
+                bneed = max(bneed, needv);
+                return;
+            }
+            const int evn = v_tensor ? evn_t : clamp_exp_flag(max(E_MIN, needv), a.flags);
+            int c[D][4];
+            if (nv) {
+                rne_rows<D>(vn, rne_u(evn - min(pa, pb)), c);
+            } else {
+    #pragma unroll
+                for (int j = 0; j < D; ++j)
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
+            }
+    #pragma unroll
+            for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
+            if (lane == 0 && sub == 0) {
+                if (!v_tensor) a.v_exp[row] = (int8_t)evn;
+                else if (row == 0) a.v_exp[0] = (int8_t)evn;
+            }
+
+            // ---- weight: w = W - lr * V' ----
+            const int pw = a.lr_e + evn;
+            const bool nw = abs(ew - pw) <= 15;
+            int needw;
+            if (nw) {
                 const int base = min(ew, pw);
                 const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
-                int n[D][4], c[D][4];
-#pragma unroll
+    #pragma unroll
                 for (int j = 0; j < D; ++j)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) n[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(sbyte(V[j], t), fb);
-                rne_rows<D>(n, rne_u(e - base), c);
-#pragma unroll
-                for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(c[j][t], fb);
+                const uint32_t mx = row_umax(absmax_rows<D>(vn));
+                needw = mx ? base + mant_shift32(mx) : NEED_NONE;
             } else {
-#pragma unroll
+                int m = NEED_NONE;
+    #pragma unroll
+                for (int j = 0; j < D; ++j)
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw));
+                needw = row_imax(m);
+            }
+            if (w_tensor) {
+                bneed = max(bneed, needw);
+                return;
+            }
+            const int ewn = clamp_exp_flag(max(E_MIN, needw), a.flags);
+            if (nw) {
+                int cw[D][4];
+                rne_rows<D>(vn, rne_u(ewn - min(ew, pw)), cw);
+    #pragma unroll
+                for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(cw[j]));
+            } else {
+    #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     uint32_t o = 0;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int c = sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * sbyte(V[j], t), pw, e);
-                        o |= (uint32_t)(uint8_t)c << (8 * t);
-                    }
+    #pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        o |= (uint32_t)(uint8_t)sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, ewn) << (8 * t);
                     store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
                 }
             }
-            if (row == 0 && lane == 0 && sub == 0) a.w_exp[0] = (int8_t)e;
-            continue;
-        }
-
-        // ---- velocity: v = momentum * V + G ----
-        const int ev = v_tensor ? ev_t : (int)a.v_exp[row];
-        const int eg = a.g_row ? (int)a.g_exp[row] : (int)a.g_exp[0];
-        const int pa = ev + a.mom_e, pb = eg;
-        const bool nv = abs(pa - pb) <= 15;
-        int vn[D][4];
-        int needv;
-        if (nv) {
-            // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
-            const int base = min(pa, pb);
-            const int fa = a.mom_m * (1 << (pa - base)), fb = 1 << (pb - base);
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(V[j], t), fa) + __mul24(sbyte(G[j], t), fb);
-            const uint32_t mx = row_umax(absmax_rows<D>(vn));
-            needv = mx ? base + mant_shift32(mx) : NEED_NONE;
-        } else {
-            int m = NEED_NONE;
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
-            needv = row_imax(m);
-        }
-        if (pass == 0) {
-            bneed = max(bneed, needv);
-            continue;
-        }
-        const int evn = v_tensor ? evn_t : clamp_exp_flag(max(E_MIN, needv), a.flags);
-        int c[D][4];
-        if (nv) {
-            rne_rows<D>(vn, rne_u(evn - min(pa, pb)), c);
-        } else {
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
-        }
-#pragma unroll
-        for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
-        if (lane == 0 && sub == 0) {
-            if (!v_tensor) a.v_exp[row] = (int8_t)evn;
-            else if (row == 0) a.v_exp[0] = (int8_t)evn;
-        }
-
-        // ---- weight: w = W - lr * V' ----
-        const int pw = a.lr_e + evn;
-        const bool nw = abs(ew - pw) <= 15;
-        int needw;
-        if (nw) {
-            const int base = min(ew, pw);
-            const int fa = 1 << (ew - base), fb = -a.lr_m * (1 << (pw - base));
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(c[j][t], fb);
-            const uint32_t mx = row_umax(absmax_rows<D>(vn));
-            needw = mx ? base + mant_shift32(mx) : NEED_NONE;
-        } else {
-            int m = NEED_NONE;
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw));
-            needw = row_imax(m);
-        }
-        if (w_tensor) {
-            bneed = max(bneed, needw);
-            continue;
-        }
-        const int ewn = clamp_exp_flag(max(E_MIN, needw), a.flags);
-        if (nw) {
-            int cw[D][4];
-            rne_rows<D>(vn, rne_u(ewn - min(ew, pw)), cw);
-#pragma unroll
-            for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(cw[j]));
-        } else {
-#pragma unroll
-            for (int j = 0; j < D; ++j) {
-                uint32_t o = 0;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    o |= (uint32_t)(uint8_t)sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, ewn) << (8 * t);
-                store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
-            }
-        }
-        if (lane == 0 && sub == 0) a.w_exp[row] = (int8_t)ewn;
+            if (lane == 0 && sub == 0) a.w_exp[row] = (int8_t)ewn;
+    };
+    const long long stride = (long long)nblk * RPB;
+    long long row = (long long)blk * RPB + wave / WPR;  // WPR > 1: the same row in every wave of the block
+    RowIn A, B;
+    if (row < a.rows) load_row(row, A);
+    while (row < a.rows) {
+        const long long r1 = row + stride;
+        if (r1 < a.rows) load_row(r1, B);
+        process(row, A);
+        if (r1 >= a.rows) break;
+        const long long r2 = r1 + stride;
+        if (r2 < a.rows) load_row(r2, A);
+        process(r1, B);
+        row = r2;
     }
     if (pass == 0 || (pass == 1 && w_tensor)) {
         const int m = block_imax(bneed);
@@ -380,12 +407,13 @@ __global__ __launch_bounds__(256) void sgd_multi_kernel(UpdSegs sg, int pass) {
     update_rows<D, WPR>(sg.a[i], pass, sg.vec[i], blockIdx.x - sg.block0[i], sg.block0[i + 1] - sg.block0[i]);
 }
 
-// Grid of one tensor's passes.
+// Grid of one tensor's passes: at most UPD_MAX_BLOCKS blocks (about what
+// the CUs hold at once), so that a wave walks several rows and overlaps the
+// next row's loads with the current row's work.
 static int update_blocks(const UpdateArgs &a, int wpr) {
     const int rpb = 4 / wpr;
     long long blocks = (a.rows + rpb - 1) / rpb;
-    const long long cap = (a.v_row && a.w_row) ? 65536 : UPD_MAX_BLOCKS;
-    if (blocks > cap) blocks = cap;
+    if (blocks > UPD_MAX_BLOCKS) blocks = UPD_MAX_BLOCKS;
     if (blocks < 1) blocks = 1;
     return (int)blocks;
 }
