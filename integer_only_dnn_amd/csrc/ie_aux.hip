@@ -331,26 +331,15 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
         }
     };
     if (!row_group) {
-        // largest tile need, eight per 16-byte load (p16 is 16-byte aligned);
-        // all-zero tiles (P_NONE) stay below every real need and E_MIN
-        const int T = TM * n_ct, T8 = T >> 3;
-        int m = NEED_NONE;
-        for (int i = threadIdx.x; i < T8; i += 256) {
-            const v4i v = *(const v4i *)(p16 + 8 * i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                m = max(m, max((int)(int16_t)(v[j] & 0xffff), (int)(int16_t)((uint32_t)v[j] >> 16)));
-        }
-        for (int i = 8 * T8 + threadIdx.x; i < T; i += 256) m = max(m, (int)p16[i]);
-        m = block_max256(m, sh);
-        const int eT = clamp_exp_flag(max(E_MIN, m), flags);
-        const uint32_t total = (uint32_t)M * per_row;
-        // four independent chunks per thread and trip, all loads first
+        // four independent chunks per thread and trip, all loads first; the
+        // first trip's loads go out before the tile needs are reduced, so the
+        // two memory round trips overlap
         constexpr int U = 4;
-        for (uint32_t i0 = blockIdx.x * 256 * U + threadIdx.x; i0 < total; i0 += gridDim.x * 256 * U) {
-            long long o[U];
-            int t[U];
-            v4i v[U];
+        const uint32_t total = (uint32_t)M * per_row;
+        long long o[U];
+        int t[U];
+        v4i v[U];
+        auto fetch = [&](uint32_t i0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = i0 + 256 * u;
@@ -361,6 +350,24 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
                 t[u] = p16[(row >> lbm) + TM * (c0 >> lbn)];
                 if (vw == 8) v[u] = *(const v4i *)(v16 + o[u]);
             }
+        };
+        uint32_t i0 = blockIdx.x * 256 * U + threadIdx.x;
+        if (i0 < total) fetch(i0);
+        // largest tile need, eight per 16-byte load (p16 is 16-byte aligned);
+        // all-zero tiles (P_NONE) stay below every real need and E_MIN
+        const int T = TM * n_ct, T8 = T >> 3;
+        int m = NEED_NONE;
+        for (int i = threadIdx.x; i < T8; i += 256) {
+            const v4i w = *(const v4i *)(p16 + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m = max(m, max((int)(int16_t)(w[j] & 0xffff), (int)(int16_t)((uint32_t)w[j] >> 16)));
+        }
+        for (int i = 8 * T8 + threadIdx.x; i < T; i += 256) m = max(m, (int)p16[i]);
+        m = block_max256(m, sh);
+        const int eT = clamp_exp_flag(max(E_MIN, m), flags);
+        for (; i0 < total; i0 += gridDim.x * 256 * U) {
+            if (i0 != blockIdx.x * 256 * U + threadIdx.x) fetch(i0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (i0 + 256 * u >= total) break;

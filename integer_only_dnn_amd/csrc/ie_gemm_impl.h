@@ -729,15 +729,12 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
         }
     };
 
-    // NU sub-steps per trip: the back edge costs a drain of the loads in
-    // flight, so it is taken once per NU steps (never for short contractions)
-    constexpr int NU = NS % 2 ? 4 * NS : IE_UNROLL * NS;  // even: step parity picks the LDS buffer
-    for (int it = 0; it < nk; it += NU) {
-#pragma unroll
-        for (int uu = 0; uu < NU; ++uu) {
+    // Trips of NU steps with no exit inside: the loads of the next stages stay
+    // in flight across the back edge (an exit inside the trip would make the
+    // loop head wait for all of them).  The last nk % NU steps follow the loop.
+    {
+        auto step = [&](const int uu, const int s) {
             const int u = uu % NS;
-            const int s = it + uu;
-            if (s >= nk) break;
             // set u held stage s, already in LDS: refill it with stage s + NS
             // (past the end: loaded, never computed)
             la.load(kb + (s + NS) * BK, ke, ra[u]);
@@ -752,6 +749,17 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             la.store(lds + ((uu + 1) & 1) * STAGE, tid, ra[(u + 1) % NS]);
             lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS]);
             __syncthreads();
+        };
+        constexpr int NU = NS % 2 ? 4 * NS : IE_UNROLL * NS;  // even: step parity picks the LDS buffer
+        const int full = nk - nk % NU;
+        for (int it = 0; it < full; it += NU) {
+#pragma unroll
+            for (int uu = 0; uu < NU; ++uu) step(uu, it + uu);
+        }
+#pragma unroll
+        for (int uu = 0; uu < NU - 1; ++uu) {
+            if (full + uu >= nk) break;
+            step(uu, full + uu);
         }
     }
 
