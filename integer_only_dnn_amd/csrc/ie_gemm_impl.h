@@ -39,6 +39,13 @@
 namespace ie {
 
 constexpr int NTHR = 256;
+// Row padding of a [k][row] LDS tile (bytes): 32 for 64-row tiles, whose
+// bank conflicts it removes; 16 for wider ones, which would not fit two
+// workgroups per CU with 32.
+template <int ROWS>
+struct TPad {
+    static constexpr int value = ROWS <= 64 ? 32 : 16;
+};
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
     return (uint32_t)(((uint64_t)n * f.m) >> f.s);
@@ -55,11 +62,12 @@ struct IsT {
     static constexpr bool value = KIND == LD_T || KIND == LD_IM2COL_T || KIND == LD_WT;
 };
 
-// LDS tile of an operand with ROWS rows (GEMM M or N side).
+// LDS tile of an operand with ROWS rows (GEMM M or N side).  [row][k] tiles
+// pad each row by 16 bytes, [k][row] tiles by TPad.
 template <int KIND, int ROWS>
 struct Lds {
     static constexpr bool T = IsT<KIND>::value;
-    static constexpr int STRIDE = T ? ROWS + 16 : BK + 16;
+    static constexpr int STRIDE = T ? ROWS + TPad<ROWS>::value : BK + 16;
     static constexpr int BYTES = T ? BK * STRIDE : ROWS * STRIDE;
 };
 
@@ -151,7 +159,7 @@ template <int ROWS>
 struct TChunks {
     static constexpr int PER = ROWS / 16;
     static constexpr int CH = ROWS * BK / 16 / NTHR;
-    static constexpr int STRIDE = ROWS + 16;
+    static constexpr int STRIDE = ROWS + TPad<ROWS>::value;
     __device__ __forceinline__ static int krow(int c, int tid) { return (tid + NTHR * c) / PER; }
     __device__ __forceinline__ static int ic(int tid) { return tid % PER; }
     __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
@@ -167,7 +175,7 @@ template <int ROWS>
 struct TPairChunks {
     static_assert(BK == 128 && NTHR == 256, "two threads per contraction row");
     static constexpr int CH = ROWS / 32;
-    static constexpr int STRIDE = ROWS + 16;
+    static constexpr int STRIDE = ROWS + TPad<ROWS>::value;
     __device__ __forceinline__ static int krow(int tid) { return tid >> 1; }
     __device__ __forceinline__ static int ic(int c, int tid) { return 2 * c + (tid & 1); }
     __device__ __forceinline__ static void store(int8_t *s, int tid, const v4i (&reg)[CH]) {
@@ -627,7 +635,9 @@ struct Occ {
 // LDS of a tile: two stages of both operands (also the epilogue's staging).
 template <int KA, int KB, int MI, int NI>
 struct TileLds {
-    static constexpr int value = 2 * (Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES);
+    static constexpr int stages = 2 * (Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES);
+    static constexpr int partial = 64 * MI * (64 * NI * 4 + 32);  // int32 staging of a split product
+    static constexpr int value = stages > partial ? stages : partial;
 };
 
 // One workgroup's work item: bid and nblk are its index and the number of
@@ -640,6 +650,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
     using LA = Lds<KA, BMt>;
     using LB = Lds<KB, BNt>;
     constexpr int STAGE = LA::BYTES + LB::BYTES;
+    constexpr int LDSB = TileLds<KA, KB, MI, NI>::value;  // bytes at lds
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -788,7 +799,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                 v[4 * j + 3] += t[3];
             }
         };
-        static_assert(8 * 4096 <= 2 * STAGE, "partial tiles exceed LDS");
+        static_assert(8 * 4096 <= LDSB, "partial tiles exceed LDS");
         v16i mine = quad(w);
         __syncthreads();  // every wave is done with the last stage
         post(2 * w, quad((w + 1) & 3));
@@ -850,7 +861,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
     using ES4 = std::integral_constant<int, 4>;
 
     if constexpr (PARTIAL) {
-        static_assert(BMt * (BNt * 4 + 32) <= 2 * STAGE, "staging tile exceeds LDS");
+        static_assert(BMt * (BNt * 4 + 32) <= LDSB, "staging tile exceeds LDS");
 #pragma unroll
         for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -861,9 +872,9 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
         flush(ES4{}, ep.partial + (long long)z * ep.split_stride, N, (N & 3) == 0);
         return;
     } else {
-        int *red = (int *)(lds + 2 * STAGE) - 2 * BMt;  // maxima, at the top of LDS
+        int *red = (int *)(lds + LDSB) - 2 * BMt;  // maxima, at the top of LDS
         int *scr = red - 16;                             // block reductions
-        static_assert(BMt * (BNt * 2 + 16) + 4 * BMt * 4 + 64 <= 2 * STAGE, "staging tile exceeds LDS");
+        static_assert(BMt * (BNt * 2 + 16) + 4 * BMt * 4 + 64 <= LDSB, "staging tile exceeds LDS");
         int ebv[NI];
 #pragma unroll
         for (int b = 0; b < NI; ++b) ebv[b] = seB[TC(b)];
