@@ -399,12 +399,46 @@ struct UpdSegs {
     int n;
 };
 
+__device__ __forceinline__ int segment_of(const int *block0, int n) {
+    int i = 0;
+    while (i + 1 < n && (int)blockIdx.x >= block0[i + 1]) ++i;
+    return __builtin_amdgcn_readfirstlane(i);  // block-uniform: keep the segment's arguments scalar
+}
+
 template <int D, int WPR>
 __global__ __launch_bounds__(256) void sgd_multi_kernel(UpdSegs sg, int pass) {
-    int i = 0;
-    while (i + 1 < sg.n && (int)blockIdx.x >= sg.block0[i + 1]) ++i;
-    i = __builtin_amdgcn_readfirstlane(i);  // block-uniform: keep the segment's arguments scalar
+    const int i = segment_of(sg.block0, sg.n);
     update_rows<D, WPR>(sg.a[i], pass, sg.vec[i], blockIdx.x - sg.block0[i], sg.block0[i + 1] - sg.block0[i]);
+}
+
+// Tensors of the narrow classes (at most 4 dwords of each tensor per lane)
+// together in one launch per pass, each segment with its own class: a
+// model's many small tensors then cost two or three launches in all.
+constexpr int UPD_MIX = 24;
+constexpr int UPD_MIX_CLASSES = 8;  // classes 0..7 of update_class
+struct UpdMix {
+    UpdateArgs a[UPD_MIX];
+    int vec[UPD_MIX];
+    int cls[UPD_MIX];
+    int block0[UPD_MIX + 1];
+    int n;
+};
+static_assert(sizeof(UpdMix) <= 4096, "kernel arguments of the mixed update");
+
+__global__ __launch_bounds__(256) void sgd_mixed_kernel(UpdMix sg, int pass) {
+    const int i = segment_of(sg.block0, sg.n);
+    const int b = blockIdx.x - sg.block0[i], nb = sg.block0[i + 1] - sg.block0[i];
+    switch (sg.cls[i]) {
+        case 0: update_rows<1, 1>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 1: update_rows<2, 1>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 2: update_rows<3, 1>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 3: update_rows<4, 1>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 4: update_rows<1, 4>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 5: update_rows<2, 4>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 6: update_rows<3, 4>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        case 7: update_rows<4, 4>(sg.a[i], pass, sg.vec[i], b, nb); break;
+        default: break;
+    }
 }
 
 // Grid of one tensor's passes: at most UPD_MAX_BLOCKS blocks (about what
@@ -477,20 +511,76 @@ static int update_vec(const UpdateArgs &a) {
            ((uintptr_t)a.g % 4 == 0);
 }
 
-static hipError_t run_class(int c, const UpdateArgs *a, const int *vec, int n, hipStream_t st) {
+// One tensor: a launch per pass of its class's kernel.
+static hipError_t run_class(int c, const UpdateArgs &a, int vec, hipStream_t st) {
     switch (c) {
-        case 0: return n == 1 ? run_passes<1, 1>(a[0], vec[0], st) : run_multi<1, 1>(a, vec, n, st);
-        case 1: return n == 1 ? run_passes<2, 1>(a[0], vec[0], st) : run_multi<2, 1>(a, vec, n, st);
-        case 2: return n == 1 ? run_passes<3, 1>(a[0], vec[0], st) : run_multi<3, 1>(a, vec, n, st);
-        case 3: return n == 1 ? run_passes<4, 1>(a[0], vec[0], st) : run_multi<4, 1>(a, vec, n, st);
-        case 4: return n == 1 ? run_passes<1, 4>(a[0], vec[0], st) : run_multi<1, 4>(a, vec, n, st);
-        case 5: return n == 1 ? run_passes<2, 4>(a[0], vec[0], st) : run_multi<2, 4>(a, vec, n, st);
-        case 6: return n == 1 ? run_passes<3, 4>(a[0], vec[0], st) : run_multi<3, 4>(a, vec, n, st);
-        case 7: return n == 1 ? run_passes<4, 4>(a[0], vec[0], st) : run_multi<4, 4>(a, vec, n, st);
-        case 8: return n == 1 ? run_passes<6, 4>(a[0], vec[0], st) : run_multi<6, 4>(a, vec, n, st);
-        case 9: return n == 1 ? run_passes<8, 4>(a[0], vec[0], st) : run_multi<8, 4>(a, vec, n, st);
+        case 0: return run_passes<1, 1>(a, vec, st);
+        case 1: return run_passes<2, 1>(a, vec, st);
+        case 2: return run_passes<3, 1>(a, vec, st);
+        case 3: return run_passes<4, 1>(a, vec, st);
+        case 4: return run_passes<1, 4>(a, vec, st);
+        case 5: return run_passes<2, 4>(a, vec, st);
+        case 6: return run_passes<3, 4>(a, vec, st);
+        case 7: return run_passes<4, 4>(a, vec, st);
+        case 8: return run_passes<6, 4>(a, vec, st);
+        case 9: return run_passes<8, 4>(a, vec, st);
     }
     return hipErrorInvalidValue;
+}
+
+// Several tensors of one class: a launch per pass.
+static hipError_t run_class_multi(int c, const UpdateArgs *a, const int *vec, int n, hipStream_t st) {
+    if (n == 1) return run_class(c, a[0], vec[0], st);
+    switch (c) {
+        case 0: return run_multi<1, 1>(a, vec, n, st);
+        case 1: return run_multi<2, 1>(a, vec, n, st);
+        case 2: return run_multi<3, 1>(a, vec, n, st);
+        case 3: return run_multi<4, 1>(a, vec, n, st);
+        case 4: return run_multi<1, 4>(a, vec, n, st);
+        case 5: return run_multi<2, 4>(a, vec, n, st);
+        case 6: return run_multi<3, 4>(a, vec, n, st);
+        case 7: return run_multi<4, 4>(a, vec, n, st);
+        case 8: return run_multi<6, 4>(a, vec, n, st);
+        case 9: return run_multi<8, 4>(a, vec, n, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Mixed launches take the narrow classes' small tensors; a large tensor
+// keeps its class's own kernel, which holds more waves per CU.
+constexpr long long UPD_MIX_MAX_ELEMS = 1ll << 21;
+static int mixed_class(const UpdateArgs &a) {
+    const int c = update_class(a);
+    return c >= 0 && c < UPD_MIX_CLASSES && a.rows * a.cols <= UPD_MIX_MAX_ELEMS ? c : -1;
+}
+
+// Narrow-class tensors: a launch per pass (per UPD_MIX tensors).
+static hipError_t run_mixed(const UpdateArgs *a, const int *vec, const int *cls, int n, hipStream_t st) {
+    for (int pass = 0; pass < 3; ++pass) {
+        for (int i0 = 0; i0 < n;) {
+            UpdMix sg;
+            sg.n = 0;
+            int blocks = 0, i = i0;
+            for (; i < n && sg.n < UPD_MIX; ++i) {
+                if ((pass == 0 && a[i].v_row) || (pass == 2 && a[i].w_row)) continue;
+                sg.a[sg.n] = a[i];
+                sg.vec[sg.n] = vec[i];
+                sg.cls[sg.n] = cls[i];
+                sg.block0[sg.n] = blocks;
+                blocks += update_blocks(a[i], cls[i] >= 4 ? 4 : 1);
+                ++sg.n;
+            }
+            i0 = i;
+            if (sg.n == 0) continue;
+            sg.block0[sg.n] = blocks;
+            prof_begin(st, 2000 + pass);
+            hipLaunchKernelGGL(sgd_mixed_kernel, dim3(blocks), dim3(256), 0, st, sg, pass);
+            prof_end(st, 2000 + pass);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
+    }
+    return hipSuccess;
 }
 
 static hipError_t empty_update(const UpdateArgs &a, hipStream_t st) {
@@ -505,25 +595,46 @@ hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
     if (a.rows <= 0) return empty_update(a, st);
     const int c = update_class(a);
     if (c < 0) return hipErrorInvalidValue;
-    const int vec = update_vec(a);
-    return run_class(c, &a, &vec, 1, st);
+    return run_class(c, a, update_vec(a), st);
 }
 
 hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st) {
-    // one launch per pass for up to UPD_SEGS tensors of a launch class
+    for (int i = 0; i < n; ++i)
+        if (a[i].rows > 0 && update_class(a[i]) < 0) return hipErrorInvalidValue;
+    // small tensors of the narrow classes: all together, one launch per pass
+    {
+        UpdateArgs seg[UPD_MIX];
+        int vec[UPD_MIX], cls[UPD_MIX];
+        int k = 0;
+        for (int i = 0; i <= n; ++i) {
+            const int c = i < n && a[i].rows > 0 ? mixed_class(a[i]) : -1;
+            if (c >= 0) {
+                seg[k] = a[i];
+                vec[k] = update_vec(a[i]);
+                cls[k] = c;
+                ++k;
+            }
+            if (k == UPD_MIX || (i == n && k > 0)) {
+                hipError_t err = run_mixed(seg, vec, cls, k, st);
+                if (err != hipSuccess) return err;
+                k = 0;
+            }
+        }
+    }
+    // the others: one launch per pass for up to UPD_SEGS tensors of a class
     for (int c = 0; c < 10; ++c) {
         UpdateArgs seg[UPD_SEGS];
         int vec[UPD_SEGS];
         int k = 0;
         for (int i = 0; i <= n; ++i) {
-            const bool take = i < n && a[i].rows > 0 && update_class(a[i]) == c;
+            const bool take = i < n && a[i].rows > 0 && mixed_class(a[i]) < 0 && update_class(a[i]) == c;
             if (take) {
                 seg[k] = a[i];
                 vec[k] = update_vec(a[i]);
                 ++k;
             }
             if (k == UPD_SEGS || (i == n && k > 0)) {
-                hipError_t err = run_class(c, seg, vec, k, st);
+                hipError_t err = run_class_multi(c, seg, vec, k, st);
                 if (err != hipSuccess) return err;
                 k = 0;
             }

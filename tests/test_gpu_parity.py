@@ -219,11 +219,11 @@ def test_sgd_update(shape, groups, ws):
 
 def test_sgd_update_multi(ws):
     """One call over a mixed batch equals the oracle tensor by tensor: several
-    launch classes, more tensors of one class than one launch holds, every
-    group combination, an empty tensor."""
+    launch classes, more small tensors than one launch holds, a large tensor
+    of a narrow class, every group combination, an empty tensor."""
     announce("sgd_update_multi mixed batch")
     rng = np.random.default_rng(4242)
-    shapes = [(17, 64)] * 14 + [(40, 256), (9, 1000), (12, 3072), (5, 4608), (3, 7), (0, 64), (33, 768)]
+    shapes = [(17, 64)] * 26 + [(40, 256), (9, 1000), (12, 3072), (5, 4608), (3, 7), (0, 64), (33, 768), (1025, 2048)]
     cases, devs = [], []
     for i, (rows, cols) in enumerate(shapes):
         groups = GROUPS[i % len(GROUPS)]
