@@ -48,7 +48,8 @@ OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_k
          2002: ("sgd_pass2", "sgd_rows_kernel"), 3000: ("rto_finalize", "rto_finalize_kernel"),
          3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
          3200: ("pad_align", "pad_rows_kernel / align_transpose_kernel"),
-         3300: ("split_round", "split_round_rows_kernel")}
+         3300: ("split_round", "split_round_rows_kernel"),
+         3400: ("finalize_pair", "finalize_pair_kernel")}
 
 
 def is_gemm(kind: int) -> bool:
@@ -406,6 +407,9 @@ def main():
                         a["bytes"] += c.io
                     elif 2000 <= kind < 3000 and c.bytes:
                         a["bytes"] += c.bytes / n_upd
+                    elif kind == 3400:
+                        # both finalizes of a convolution's backward pass
+                        a["bytes"] += sum(c.outs)
                     elif c.outs:
                         # finalize or pre-pass of a contraction: its int8 result
                         a["bytes"] += c.outs[min(max(fin, 0), len(c.outs) - 1)]

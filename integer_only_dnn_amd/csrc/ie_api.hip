@@ -512,9 +512,9 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const ie_mat *W, con
     e2.gneed_n = 0;
     IE_TRY(launch_gemm_pair(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
                             (int)npq, p2.t, p2.splits, p2.k_chunk, e2, st));
-    IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)nhw, g.c, p1.t, 0, dX->mant, dX->exp, flags, st));
-    IE_TRY(launch_split_round_rows(w.partial, p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex,
-                                   dW->mant, dW->exp, flags, st));
+    IE_TRY(launch_finalize_pair(pw.v16, pw.p16, (int)nhw, g.c, p1.t, dX->mant, dX->exp, w.partial, p2.splits,
+                                g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex, dW->mant, dW->exp, flags,
+                                st));
     return IE_OK;
 }
 

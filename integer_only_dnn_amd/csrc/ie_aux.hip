@@ -294,10 +294,10 @@ __device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint
 // a run (RB * n_ct values) go through LDS and one thread per row reduces them.
 constexpr int FIN_NEEDS = 2048;
 
-__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
+__device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int16_t *p16, int M, int N,
                                                            int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
-                                                           FastDiv dper) {
+                                                           FastDiv dper, int bid, int nblk) {
     __shared__ int sh[4];
     __shared__ int16_t needs[FIN_NEEDS];
     __shared__ int rowe[256];
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
                 if (vw == 8) v[u] = *(const v4i *)(v16 + o[u]);
             }
         };
-        uint32_t i0 = blockIdx.x * 256 * U + threadIdx.x;
+        uint32_t i0 = bid * 256 * U + threadIdx.x;
         if (i0 < total) fetch(i0);
         // largest tile need, eight per 16-byte load (p16 is 16-byte aligned);
         // all-zero tiles (P_NONE) stay below every real need and E_MIN
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
         for (int i = 8 * T8 + threadIdx.x; i < T; i += 256) m = max(m, (int)p16[i]);
         m = block_max256(m, sh);
         const int eT = clamp_exp_flag(max(E_MIN, m), flags);
-        for (; i0 < total; i0 += gridDim.x * 256 * U) {
-            if (i0 != blockIdx.x * 256 * U + threadIdx.x) fetch(i0);
+        for (; i0 < total; i0 += nblk * 256 * U) {
+            if (i0 != bid * 256 * U + threadIdx.x) fetch(i0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (i0 + 256 * u >= total) break;
@@ -376,11 +376,11 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
                 else round8(o[u], sh_);
             }
         }
-        if (blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
+        if (bid == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
         return;
     }
     const bool staged = rb * n_ct <= FIN_NEEDS;
-    for (long long r0 = (long long)blockIdx.x * rb; r0 < M; r0 += (long long)gridDim.x * rb) {
+    for (long long r0 = (long long)bid * rb; r0 < M; r0 += (long long)nblk * rb) {
         const int nr = (int)min((long long)rb, M - r0);
         const int16_t *pr = p16 + r0 * n_ct;
         if (staged) {
@@ -422,21 +422,57 @@ __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, c
     }
 }
 
+__global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
+                                                           int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
+                                                           int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
+                                                           FastDiv dper) {
+    rto_finalize_body(v16, p16, M, N, lbm, lbn, TM, n_ct, row_group, rb, out, out_exp, flags, vw, dper, blockIdx.x, gridDim.x);
+}
+
+// Arguments of a round-to-odd finalize and its grid.
+struct RtoFin {
+    const int16_t *v16, *p16;
+    int M, N, lbm, lbn, TM, n_ct, row_group, rb;
+    int8_t *out, *out_exp;
+    uint32_t *flags;
+    int vw;
+    FastDiv dper;
+    int blocks;
+};
+
+static RtoFin rto_fin(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group, int8_t *out,
+                      int8_t *out_exp, uint32_t *flags) {
+    RtoFin f;
+    f.v16 = v16;
+    f.p16 = p16;
+    f.M = M;
+    f.N = N;
+    f.vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0) ? 8 : 1;
+    f.TM = (M + t.bm() - 1) / t.bm();
+    f.n_ct = (N + t.bn() - 1) / t.bn();
+    // row runs of about 8192 elements (at most 256 rows)
+    int rb = 8192 / N;
+    f.rb = rb < 1 ? 1 : (rb > 256 ? 256 : rb);
+    const long long total = (long long)M * (N / f.vw);
+    f.blocks = row_group ? blocks_for((M + f.rb - 1) / f.rb, 1, 8192) : blocks_for(total, 256 * 4, 2048);
+    auto lg = [](int v) { int l = 0; while ((1 << l) < v) ++l; return l; };  // tile sides are powers of two
+    f.lbm = lg(t.bm());
+    f.lbn = lg(t.bn());
+    f.row_group = row_group;
+    f.out = out;
+    f.out_exp = out_exp;
+    f.flags = flags;
+    f.dper = make_fastdiv((uint32_t)(N / f.vw));
+    return f;
+}
+
 hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
                                int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0) ? 8 : 1;
-    const int TM = (M + t.bm() - 1) / t.bm();
-    const int n_ct = (N + t.bn() - 1) / t.bn();
-    // row runs of about 8192 elements (at most 256 rows)
-    int rb = 8192 / N;
-    rb = rb < 1 ? 1 : (rb > 256 ? 256 : rb);
-    const long long total = (long long)M * (N / vw);
-    const int blocks = row_group ? blocks_for((M + rb - 1) / rb, 1, 8192) : blocks_for(total, 256 * 4, 2048);
-    auto lg = [](int v) { int l = 0; while ((1 << l) < v) ++l; return l; };  // tile sides are powers of two
+    const RtoFin f = rto_fin(v16, p16, M, N, t, row_group, out, out_exp, flags);
     prof_begin(st, PROF_RTO_FINALIZE);
-    hipLaunchKernelGGL(rto_finalize_kernel, dim3(blocks), dim3(256), 0, st, v16, p16, M, N, lg(t.bm()), lg(t.bn()),
-                       TM, n_ct, row_group, rb, out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
+    hipLaunchKernelGGL(rto_finalize_kernel, dim3(f.blocks), dim3(256), 0, st, f.v16, f.p16, f.M, f.N, f.lbm, f.lbn,
+                       f.TM, f.n_ct, f.row_group, f.rb, f.out, f.out_exp, f.flags, f.vw, f.dper);
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
@@ -638,10 +674,10 @@ __device__ __forceinline__ void sum_splits(const int *p, long long stride, int z
 // At least four waves per SIMD (two 512-thread blocks per CU, at most 128
 // VGPRs), so that consecutive rows overlap.
 template <int THR>
-__global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void split_round_rows_kernel(const int *partial, int splits, long long stride,
+__device__ __forceinline__ void split_round_body(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q) {
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q, int bid, int nblk) {
     // short rows (THR == SR_THR_SHORT) hold at most one chunk per thread
     constexpr int MAXV = THR == SR_THR_SHORT ? 1 : SR_MAXV;
     __shared__ int sh[THR / 64];
@@ -659,7 +695,7 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void s
     // element.
     const bool eb_uni = eb.e32 != nullptr || !eb.row;
     const int eb0 = exp_at(eb, 0);
-    for (int row = blockIdx.x; row < M; row += gridDim.x) {
+    for (int row = bid; row < M; row += nblk) {
         const int er = exp_at(ea, row);
         const int *prow = partial + (long long)row * src_pitch;
         long long v[MAXV][4];
@@ -759,34 +795,121 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
 }
 
+template <int THR>
+__global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void split_round_rows_kernel(const int *partial, int splits, long long stride,
+                                                                 int M, int Nout, int src_pitch, int mc, int mcp,
+                                                                 FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q) {
+    split_round_body<THR>(partial, splits, stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q,
+                          blockIdx.x, gridDim.x);
+}
+
 bool split_round_rows_fits(int Nout, int mc, int mcp) {
     const int vw = (mc == mcp && Nout % 4 == 0) ? 4 : 1;
     return Nout / vw <= SR_THR * SR_MAXV;
+}
+
+// Arguments of a split finalize by rows and its grid.
+struct SplitFin {
+    const int *partial;
+    int splits;
+    long long stride;
+    int M, Nout, src_pitch, mc, mcp;
+    FastDiv dmc;
+    ExpSrc ea, eb;
+    int8_t *out, *out_exp;
+    uint32_t *flags;
+    int vw, Q, blocks;
+    bool shortrow;
+};
+
+static SplitFin split_fin(const int *partial, int splits, long long split_stride, int M, int Nout, int src_pitch,
+                          int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out, int8_t *out_exp, uint32_t *flags) {
+    SplitFin f;
+    f.partial = partial;
+    f.splits = splits;
+    f.stride = split_stride;
+    f.M = M;
+    f.Nout = Nout;
+    f.src_pitch = src_pitch;
+    f.mc = mc;
+    f.mcp = mcp;
+    f.ea = ea;
+    f.eb = eb;
+    f.out = out;
+    f.out_exp = out_exp;
+    f.flags = flags;
+    f.vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
+    const int nch = Nout / f.vw;
+    f.shortrow = nch <= SR_THR;
+    const int thr = f.shortrow ? SR_THR_SHORT : SR_THR;
+    f.Q = 1;
+    if (f.shortrow && nch <= thr / 2) {
+        f.Q = thr / nch;
+        if (f.Q > splits) f.Q = splits;
+    }
+    f.blocks = blocks_for(M, 1, 16384);
+    f.dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
+    return f;
 }
 
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
                                    int8_t *out_exp, uint32_t *flags, hipStream_t st) {
     if (M <= 0 || Nout <= 0) return hipSuccess;
-    const int vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
-    const int nch = Nout / vw;
-    const bool shortrow = nch <= SR_THR;
-    const int thr = shortrow ? SR_THR_SHORT : SR_THR;
-    int Q = 1;
-    if (shortrow && nch <= thr / 2) {
-        Q = thr / nch;
-        if (Q > splits) Q = splits;
-    }
-    const dim3 grid(blocks_for(M, 1, 16384));
-    const FastDiv dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
+    const SplitFin f = split_fin(partial, splits, split_stride, M, Nout, src_pitch, mc, mcp, ea, eb, out, out_exp,
+                                 flags);
     prof_begin(st, PROF_SPLIT_ROUND);
-    if (shortrow)
-        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, grid, dim3(SR_THR_SHORT), 0, st, partial, splits,
-                           split_stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q);
+    if (f.shortrow)
+        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, dim3(f.blocks), dim3(SR_THR_SHORT), 0, st,
+                           f.partial, f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb,
+                           f.out, f.out_exp, f.flags, f.vw, f.Q);
     else
-        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, grid, dim3(SR_THR), 0, st, partial, splits,
-                           split_stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q);
+        hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, dim3(f.blocks), dim3(SR_THR), 0, st, f.partial,
+                           f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb, f.out,
+                           f.out_exp, f.flags, f.vw, f.Q);
     prof_end(st, PROF_SPLIT_ROUND);
+    return hipGetLastError();
+}
+
+// The two finalizes of a convolution's backward pass (input gradient by
+// round-to-odd, weight gradient by split rows) in one grid: the first
+// r.blocks blocks run the former on 256 of their threads, the rest the
+// latter.
+template <int THR>
+__global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void finalize_pair_kernel(RtoFin r,
+                                                                                                  SplitFin q) {
+    if ((int)blockIdx.x < r.blocks) {
+        if (threadIdx.x >= 256) return;
+        rto_finalize_body(r.v16, r.p16, r.M, r.N, r.lbm, r.lbn, r.TM, r.n_ct, r.row_group, r.rb, r.out, r.out_exp,
+                          r.flags, r.vw, r.dper, blockIdx.x, r.blocks);
+    } else {
+        split_round_body<THR>(q.partial, q.splits, q.stride, q.M, q.Nout, q.src_pitch, q.mc, q.mcp, q.dmc, q.ea,
+                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, blockIdx.x - r.blocks,
+                              gridDim.x - r.blocks);
+    }
+}
+
+hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
+                                int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
+                                int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
+                                int8_t *out2_exp, uint32_t *flags, hipStream_t st) {
+    if (M1 <= 0 || N1 <= 0 || M2 <= 0 || Nout <= 0) {
+        hipError_t e = launch_rto_finalize(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags, st);
+        if (e != hipSuccess) return e;
+        return launch_split_round_rows(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2,
+                                       out2_exp, flags, st);
+    }
+    const RtoFin r = rto_fin(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags);
+    const SplitFin q = split_fin(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2, out2_exp,
+                                 flags);
+    const dim3 grid(r.blocks + q.blocks);
+    prof_begin(st, PROF_FIN_PAIR);
+    if (q.shortrow)
+        hipLaunchKernelGGL(finalize_pair_kernel<SR_THR_SHORT>, grid, dim3(SR_THR_SHORT), 0, st, r, q);
+    else
+        hipLaunchKernelGGL(finalize_pair_kernel<SR_THR>, grid, dim3(SR_THR), 0, st, r, q);
+    prof_end(st, PROF_FIN_PAIR);
     return hipGetLastError();
 }
 

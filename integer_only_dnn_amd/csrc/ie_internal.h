@@ -138,6 +138,7 @@ constexpr int PROF_PARTIAL_REDUCE = 3100;
 constexpr int PROF_ROUND_SUMS = 3150;
 constexpr int PROF_ALIGN = 3200;
 constexpr int PROF_SPLIT_ROUND = 3300;
+constexpr int PROF_FIN_PAIR = 3400;
 
 // Auxiliary kernels (ie_aux.hip).
 hipError_t launch_fill_i32(int *p, long long n, int v, hipStream_t st);
@@ -174,6 +175,13 @@ bool split_round_rows_fits(int Nout, int mc, int mcp);
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
                                    int8_t *out_exp, uint32_t *flags, hipStream_t st);
+// A round-to-odd finalize (whole-tensor group, M1 x N1 from tile t1) and a
+// split finalize by rows (the arguments of launch_split_round_rows) in one
+// launch.
+hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
+                                int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
+                                int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
+                                int8_t *out2_exp, uint32_t *flags, hipStream_t st);
 hipError_t launch_zero_flags(void *ws, hipStream_t st);
 
 // Integer SGD update (ie_update.hip).
