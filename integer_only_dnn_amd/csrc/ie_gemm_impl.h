@@ -887,16 +887,19 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             // whole-tensor group: one maximum for the tile
             int tmax;
             if (uni) {
-                uint32_t mx = 0;
+                // largest |acc| from the signed maximum and minimum, two
+                // values per three-input max / min
+                int hi = 0, lo = 0;
 #pragma unroll
                 for (int a = 0; a < MI; ++a)
 #pragma unroll
                     for (int b = 0; b < NI; ++b)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            int v = acc[a][b][r];
-                            mx = max(mx, (uint32_t)(v < 0 ? -v : v));
+                        for (int r = 0; r < 16; r += 2) {
+                            hi = max(hi, max(acc[a][b][r], acc[a][b][r + 1]));
+                            lo = min(lo, min(acc[a][b][r], acc[a][b][r + 1]));
                         }
+                const uint32_t mx = max((uint32_t)hi, 0u - (uint32_t)lo);
                 tmax = mx ? ea0 + eb0 + mant_shift32(mx) : NEED_NONE;
             } else {
                 tmax = NEED_NONE;
@@ -951,7 +954,8 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                                 stage(ES1{}, a, b, r, (v + hm1 + ((v >> t) & 1)) >> t);
                             }
                 } else {
-                    const uint32_t mask = (1u << t) - 1u;
+                    // sticky bit: any of the t bits shifted out (t in [1, 31])
+                    const int tl = 32 - t;
 #pragma unroll
                     for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -959,7 +963,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int v = acc[a][b][r];
-                                const int sticky = (int)((((uint32_t)v & mask) + mask) >> t);
+                                const int sticky = (int)min((uint32_t)v << tl, 1u);
                                 stage(ES2{}, a, b, r, (v >> t) | sticky);
                             }
                 }
