@@ -25,6 +25,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -432,8 +433,12 @@ def main():
 
     # Timed region: K steps; HIP events bracket the launches of the dominant
     # kernel only (on the stream they are launched on).
+    # The collector stays off while steps are issued: a full collection
+    # between two launches would leave the GPU idle.
     ie.ie_profile_select(dom)
     ie.ie_profile_enable(True)
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -441,6 +446,7 @@ def main():
             c.fn()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     A = attribute(ie.ie_profile_read(), args.steps, only=dom)[dom]
     ie.ie_profile_enable(False)
     ie.ie_profile_select(0)
