@@ -521,8 +521,9 @@ def _group_index(t: QT) -> tuple:
 def sum_op(A: QT, B: QT, out_group: int) -> QT:
     """Exact elementwise A + B, requantised once into out_group."""
     rows = A.mant.shape[0]
-    ma = A.mant.reshape(rows, -1)
-    mb = B.mant.reshape(rows, -1)
+    per_row = int(np.prod(A.mant.shape[1:], dtype=np.int64))
+    ma = A.mant.reshape(rows, per_row)
+    mb = B.mant.reshape(rows, per_row)
     ea = np.broadcast_to(A.row_exp()[:, None], ma.shape)
     eb = np.broadcast_to(B.row_exp()[:, None], mb.shape)
     num, base = exact_sum([(ma, ea), (mb, eb)])
