@@ -143,10 +143,12 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
  * in X, W aligned over output channels when ROW-grouped) and weight gradient
  * dW (its adjoint in W, per output channel groups when ROW).  dX or dW may be
  * NULL to skip that output.  dX: TENSOR; dW: TENSOR or ROW.
- * With both outputs requested, the weight gradient runs on a second stream
- * that the library keeps per device (default priority, created on first
- * use); it forks from `stream` and joins back into it with events before the
- * call returns, so all work stays ordered on `stream` for the caller.
+ * With both outputs requested, the two products run as one grid where a
+ * paired kernel covers their plans (16-channel multiples, row-grouped dW);
+ * otherwise the weight gradient runs on a second stream that the library
+ * keeps per device (default priority, created on first use), forked from
+ * `stream` and joined back into it with events before the call returns.
+ * Either way all work stays ordered on `stream` for the caller.
  */
 ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
                       const ie_mat *dY, const ie_mat *dX, const ie_mat *dW,
@@ -175,6 +177,31 @@ ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const
                               ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,
                               void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * ReLU and ReLU6 of a (C, e) tensor (Table 7, "Clip activations"), on the
+ * mantissas; the exponents are copied:
+ *   relu:  Y.C = max(X.C, 0)
+ *   relu6: Y.C = min(max(X.C, 0), c6),  c6 = min(floor(6 * 2^-e), 127)
+ * with e the element's group exponent (6 expressed in the group's units).
+ * X, Y: same shape and group.  Y may be X (in place).  relu6: 0 or 1.
+ */
+ie_status ie_relu_fwd(const ie_mat *X, const ie_mat *Y, int relu6, void *stream);
+
+/*
+ * Backward of ie_relu_fwd (Table 7): dX.C = dY.C where the forward output
+ * Y.C > 0 (and Y.C < c6 of Y's group for relu6), else 0; dX.exp = dY.exp.
+ * dY, Y, dX: same shape; dX has dY's group.  dX may be dY (in place).
+ */
+ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int relu6, void *stream);
+
+/*
+ * Sum (Table 6, "Residual add, gradient merge -> Sum"): Z = R_Z(A + B), the
+ * exact elementwise sum rounded once into Z's groups.  A, B, Z: same shape,
+ * each TENSOR or ROW.  Z must not alias A or B.
+ */
+size_t ie_add_workspace(int64_t rows, int64_t cols);
+ie_status ie_add(const ie_mat *A, const ie_mat *B, const ie_mat *Z, void *ws, size_t ws_bytes, void *stream);
+
 /* Wait for `stream`, then copy the workspace's sticky flags to *flags and,
  * if clear != 0, zero them. */
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
@@ -189,7 +216,8 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * 100*epilogue + 10*loader_A + loader_B for contractions with a
  * (64 mi) x (64 ni) tile, 2000 + pass for the update, 3000 round-to-odd
  * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
- * alignment copies) and returns how
+ * alignment copies, 3300 split rounding by rows, 3400 the paired finalize of
+ * a convolution's backward pass) and returns how
  * many were recorded since the last read; the records are then cleared.
  * The timing records and the per-device second stream of ie_conv_bwd are the
  * library's only process-wide state; the timing records are not thread-safe.

@@ -849,6 +849,54 @@ ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const
 }
 
 
+// ---------------------------------------------------------------------------
+// Pointwise steps
+// ---------------------------------------------------------------------------
+
+static bool same_shape(const ie_mat *a, const ie_mat *b) { return a->rows == b->rows && a->cols == b->cols; }
+
+ie_status ie_relu_fwd(const ie_mat *X, const ie_mat *Y, int relu6, void *stream) {
+    IE_CHECK(check_mat(X));
+    IE_CHECK(check_mat(Y));
+    if (!same_shape(X, Y)) return IE_ERR_SHAPE;
+    if (X->group != Y->group) return IE_ERR_GROUP;
+    if (relu6 != 0 && relu6 != 1) return IE_ERR_SHAPE;
+    return hip_status(launch_relu_fwd(X->mant, X->exp, X->group == IE_GROUP_ROW, Y->mant, Y->exp, X->rows, X->cols,
+                                      relu6, (hipStream_t)stream));
+}
+
+ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int relu6, void *stream) {
+    IE_CHECK(check_mat(dY));
+    IE_CHECK(check_mat(Y));
+    IE_CHECK(check_mat(dX));
+    if (!same_shape(dY, Y) || !same_shape(dY, dX)) return IE_ERR_SHAPE;
+    if (dX->group != dY->group) return IE_ERR_GROUP;
+    if (relu6 != 0 && relu6 != 1) return IE_ERR_SHAPE;
+    return hip_status(launch_relu_bwd(dY->mant, dY->exp, dY->group == IE_GROUP_ROW, Y->mant, Y->exp,
+                                      Y->group == IE_GROUP_ROW, dX->mant, dX->exp, dY->rows, dY->cols, relu6,
+                                      (hipStream_t)stream));
+}
+
+size_t ie_add_workspace(int64_t rows, int64_t cols) {
+    (void)rows;
+    (void)cols;
+    return HEADER + (size_t)ADD_MAX_BLOCKS * sizeof(int);
+}
+
+ie_status ie_add(const ie_mat *A, const ie_mat *B, const ie_mat *Z, void *ws, size_t ws_bytes, void *stream) {
+    IE_CHECK(check_mat(A));
+    IE_CHECK(check_mat(B));
+    IE_CHECK(check_mat(Z));
+    if (!same_shape(A, B) || !same_shape(A, Z)) return IE_ERR_SHAPE;
+    if (!ws) return IE_ERR_WORKSPACE;
+    if (ws_bytes < ie_add_workspace(A->rows, A->cols)) return IE_ERR_WORKSPACE;
+    Carve c{(char *)ws, HEADER};
+    int *bmax = c.take<int>(ADD_MAX_BLOCKS);
+    return hip_status(launch_add(A->mant, A->exp, A->group == IE_GROUP_ROW, B->mant, B->exp,
+                                 B->group == IE_GROUP_ROW, Z->mant, Z->exp, Z->group == IE_GROUP_ROW, A->rows,
+                                 A->cols, bmax, (uint32_t *)ws, (hipStream_t)stream));
+}
+
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {
     if (!ws || !flags) return IE_ERR_NULL;
     hipStream_t st = (hipStream_t)stream;

@@ -201,4 +201,16 @@ hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st);
 // The same for n tensors (each with its own tmp), in few launches.
 hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st);
 
+// Pointwise steps (ie_pointwise.hip).  Whole-tensor sums keep one int per
+// block in `bmax` (at most ADD_MAX_BLOCKS).
+constexpr int ADD_MAX_BLOCKS = 1024;
+hipError_t launch_relu_fwd(const int8_t *x, const int8_t *xe, int x_row, int8_t *y, int8_t *ye, long long rows,
+                           long long cols, int relu6, hipStream_t st);
+hipError_t launch_relu_bwd(const int8_t *dy, const int8_t *dye, int dy_row, const int8_t *yc, const int8_t *ye,
+                           int y_row, int8_t *dx, int8_t *dxe, long long rows, long long cols, int relu6,
+                           hipStream_t st);
+hipError_t launch_add(const int8_t *a, const int8_t *ae, int a_row, const int8_t *b, const int8_t *be, int b_row,
+                      int8_t *z, int8_t *ze, int z_row, long long rows, long long cols, int *bmax, uint32_t *flags,
+                      hipStream_t st);
+
 }  // namespace ie

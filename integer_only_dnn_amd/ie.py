@@ -61,6 +61,10 @@ EXPORTS = [
     ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update_multi", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_relu_fwd", c_int, [POINTER(ie_mat)] * 2 + [c_int, c_void_p]),
+    ("ie_relu_bwd", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p]),
+    ("ie_add_workspace", c_size_t, [c_int64, c_int64]),
+    ("ie_add", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_device_status", c_int, [c_void_p, c_void_p, POINTER(c_uint32), c_int]),
     ("ie_profile_enable", c_int, [c_int]),
     ("ie_profile_select", c_int, [c_int]),
@@ -239,6 +243,25 @@ def ie_sgd_update_multi(Ws, Vs, Gs, lr, momentum, weight_decay=(0, 0), ws: Works
     p, b = ws.get(_ws_size("ie_sgd_update_multi_workspace", n))
     _check(lib().ie_sgd_update_multi(n, w, v, g, ie_scalar(*lr), ie_scalar(*momentum), ie_scalar(*weight_decay),
                                      p, b, _stream(ws.device)), "ie_sgd_update_multi")
+
+
+def ie_relu_fwd(X: Mat, Y: Mat, relu6: bool = False) -> None:
+    """ReLU (or ReLU6) of X's mantissas into Y; Y may be X."""
+    x, y = X.c(), Y.c()
+    _check(lib().ie_relu_fwd(byref(x), byref(y), int(relu6), _stream(X.mant.device)), "ie_relu_fwd")
+
+
+def ie_relu_bwd(dY: Mat, Y: Mat, dX: Mat, relu6: bool = False) -> None:
+    """dY masked where the forward output Y was clipped, into dX; dX may be dY."""
+    dy, y, dx = dY.c(), Y.c(), dX.c()
+    _check(lib().ie_relu_bwd(byref(dy), byref(y), byref(dx), int(relu6), _stream(dY.mant.device)), "ie_relu_bwd")
+
+
+def ie_add(A: Mat, B: Mat, Z: Mat, ws: Workspace) -> None:
+    """Z = A + B, exact, rounded once into Z's groups."""
+    a, b, z = A.c(), B.c(), Z.c()
+    p, nb = ws.get(_ws_size("ie_add_workspace", a.rows, a.cols))
+    _check(lib().ie_add(byref(a), byref(b), byref(z), p, nb, _stream(ws.device)), "ie_add")
 
 
 def ie_profile_enable(on: bool = True) -> None:

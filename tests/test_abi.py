@@ -92,3 +92,19 @@ def test_workspace_sizes_grow_with_shape():
     assert L.ie_linear_fwd_workspace(-1, 1, 1) == 0
     d = ie.conv_desc(128, 32, 32, 64, 64, 3, 3, 1, 1)
     assert L.ie_conv_bwd_workspace(ctypes.byref(d)) > L.ie_conv_fwd_workspace(ctypes.byref(d)) > 0
+
+
+def test_pointwise_argument_errors():
+    L = ie.lib()
+    by = ctypes.byref
+    A, B = _mat(4, 8), _mat(4, 8)
+    assert L.ie_relu_fwd(by(A), by(_mat(4, 9)), 0, None) == 2
+    assert L.ie_relu_fwd(by(A), by(_mat(4, 8, group=1)), 0, None) == 3
+    assert L.ie_relu_fwd(by(A), by(B), 2, None) == 2
+    assert L.ie_relu_fwd(None, by(B), 0, None) == 1
+    assert L.ie_relu_bwd(by(A), by(_mat(5, 8)), by(B), 0, None) == 2
+    assert L.ie_relu_bwd(by(A), by(B), by(_mat(4, 8, group=1)), 1, None) == 3
+    assert L.ie_add(by(A), by(B), by(_mat(4, 8)), None, 0, None) == 4
+    assert L.ie_add(by(A), by(B), by(_mat(4, 8)), 1, 16, None) == 4
+    assert L.ie_add(by(A), by(_mat(4, 7)), by(_mat(4, 8)), 1, 1 << 20, None) == 2
+    assert L.ie_add_workspace(4, 8) >= 256
