@@ -50,7 +50,10 @@ OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_k
          3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
          3200: ("pad_align", "pad_rows_kernel / align_transpose_kernel"),
          3300: ("split_round", "split_round_rows_kernel"),
-         3400: ("finalize_pair", "finalize_pair_kernel")}
+         3400: ("finalize_pair", "finalize_pair_kernel"),
+         3500: ("relu_fwd", "relu_fwd_kernel"), 3510: ("relu_bwd", "relu_bwd_kernel"),
+         3520: ("add_need", "add_need_kernel"), 3521: ("add_round", "add_round_kernel"),
+         3530: ("add_rows", "add_rows_kernel")}
 
 
 def is_gemm(kind: int) -> bool:
@@ -228,12 +231,39 @@ def build_linear_small(torch, ie, ws):
     return calls, {"layers": [{"name": "linear", "gemm_mnk": [64, 128, 256]}], "params": 128 * 256}
 
 
+def build_pointwise(torch, ie, ws, batch):
+    """For every ResNet-18 conv output [N*P*Q x K] (per instance): ReLU in
+    place, the ReLU mask of an incoming gradient (in place) and the residual
+    Sum into a third tensor; whole-tensor groups as in the step.  Algorithmic
+    bytes: 2, 3 and 3 per element."""
+    calls, meta = [], {"layers": [], "params": 0}
+    for i, L in enumerate(wl.resnet18_cifar_layers(batch)):
+        M, N, _ = L.gemm_mnk()
+        g = torch.Generator(device="cuda").manual_seed(7000 + i)
+        def rnd(lo=-127, hi=128):
+            return torch.randint(lo, hi, (M, N), dtype=torch.int8, device="cuda", generator=g)
+        e = lambda v: torch.tensor([v], dtype=torch.int8, device="cuda")
+        Y = ie.Mat(rnd(), e(-6), wl.TENSOR)
+        dY = ie.Mat(rnd(), e(-10), wl.TENSOR)
+        Rz = ie.Mat(rnd(0, 128), e(-5), wl.TENSOR)
+        Z = ie.Mat.empty(M, N, wl.TENSOR)
+        n = float(M * N)
+        for inst in range(L.count):
+            calls.append(Call(f"{L.name}#{inst}:relu", lambda Y=Y: ie.ie_relu_fwd(Y, Y), 0.0, 2 * n))
+            calls.append(Call(f"{L.name}#{inst}:relu_bwd", lambda dY=dY, Y=Y: ie.ie_relu_bwd(dY, Y, dY), 0.0, 3 * n))
+            calls.append(Call(f"{L.name}#{inst}:add", lambda Y=Y, Rz=Rz, Z=Z: ie.ie_add(Y, Rz, Z, ws), 0.0, 3 * n))
+        meta["layers"].append({"name": L.name, "count": L.count, "elements": M * N})
+    return calls, meta
+
+
 WORKLOADS = {
     "resnet18": ("resnet18_cifar_conv3x3_batch128", "ResNet-18 3x3 convolutions on 32x32x3 inputs, batch 128"),
     "vitb": ("vit_b_block_linears_128x197_plus_update_85M", "ViT-B block linears (128 x 197 tokens) + update of 84.9M params"),
     "vitti": ("vit_ti_block_linears_256x197", "ViT-Ti block linears (256 x 197 tokens)"),
     "resnet50": ("resnet50_bottleneck_convs_batch128", "ResNet-50 bottleneck convolutions on 224x224x3 inputs, batch 128"),
     "linear_small": ("linear_64x256x128", "single linear layer 64x256 -> 128"),
+    "pointwise": ("resnet18_pointwise_batch128",
+                  "ReLU forward and backward masks and the residual Sum on the ResNet-18 conv outputs, batch 128"),
 }
 
 
@@ -248,6 +278,8 @@ def build_workload(name, torch, ie, ws):
         return build_vit(torch, ie, ws, wl.vit_ti_linears(256), False)
     if name == "linear_small":
         return build_linear_small(torch, ie, ws)
+    if name == "pointwise":
+        return build_pointwise(torch, ie, ws, 128)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -264,6 +296,23 @@ def cpu_baseline(name: str):
         threads = 1
     t0 = time.perf_counter()
     ops = 0.0
+    if name == "pointwise":
+        # the three steps on every layer's output once, at batch 16
+        rng = np.random.default_rng(7)
+        nbytes = 0.0
+        for L in wl.resnet18_cifar_layers(16):
+            M, N, _ = L.gemm_mnk()
+            Y = o.QT(rng.integers(-127, 128, (M, N)).astype(np.int8), np.array([-6], np.int8), o.TENSOR)
+            dY = o.QT(rng.integers(-127, 128, (M, N)).astype(np.int8), np.array([-10], np.int8), o.TENSOR)
+            Rz = o.QT(rng.integers(0, 128, (M, N)).astype(np.int8), np.array([-5], np.int8), o.TENSOR)
+            Y = o.QT(o.relu_fwd(Y.mant).astype(np.int8), Y.exp, Y.group)
+            o.relu_bwd(dY.mant, Y.mant)
+            o.sum_op(Y, Rz, o.TENSOR)
+            nbytes += 8.0 * M * N
+        dt = time.perf_counter() - t0
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "ReLU, ReLU mask and Sum on every ResNet-18 conv output once at batch 16",
+                "seconds": round(dt, 3)}
     if name in ("resnet18", "resnet50"):
         batch = 128
         layers = wl.resnet18_cifar_layers(batch) if name == "resnet18" else wl.resnet50_layers(2)
@@ -389,6 +438,7 @@ def main():
             for c in calls:
                 n_gemm = sum(1 for k in c.kinds if is_gemm(k))
                 n_upd = sum(1 for k in c.kinds if 2000 <= k < 3000)
+                n_pw = sum(1 for k in c.kinds if 3500 <= k < 3600)
                 prod = -1  # index of the last contraction launched
                 fin = 0    # index of the contraction the next finalize belongs to
                 for k in c.kinds:
@@ -408,6 +458,9 @@ def main():
                         a["bytes"] += c.io
                     elif 2000 <= kind < 3000 and c.bytes:
                         a["bytes"] += c.bytes / n_upd
+                    elif 3500 <= kind < 3600:
+                        # pointwise step: the call's algorithmic bytes over its launches
+                        a["bytes"] += c.bytes / n_pw
                     elif kind == 3400:
                         # both finalizes of a convolution's backward pass
                         a["bytes"] += sum(c.outs)
@@ -456,6 +509,11 @@ def main():
 
     step_ops = sum(c.ops for c in calls)
     value = step_ops / (ms_per_step * 1e-3) / 1e12
+    unit = "TOPS"
+    if step_ops == 0:
+        # a pointwise workload: algorithmic bytes per second
+        value = sum(c.bytes for c in calls) / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
     if is_gemm(dom):
         achieved = A["ops"] / (A["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
@@ -471,12 +529,12 @@ def main():
     roof.update(measured_traffic(args.workload, roof["kernel"]))
     agg = breakdown
     upd_ms = sum(v["ms"] for k, v in agg.items() if 2000 <= k < 3000) / n_bd
-    upd_bytes = sum(c.bytes for c in calls)
+    upd_bytes = sum(c.bytes for c in calls if any(2000 <= k < 3000 for k in c.kinds))
     gemm_ms = sum(v["ms"] for k, v in agg.items() if is_gemm(k)) / n_bd
     out = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "TOPS",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -488,7 +546,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl_id, "description": wl_desc, "step_gop": round(step_ops / 1e9, 3),
                    "params_updated": meta["params"]},
-        "frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "frac_int8_peak": round(value / PEAK_INT8_TOPS, 4) if step_ops else None,
+        "frac_hbm": round(value / PEAK_HBM_GBS, 4) if not step_ops else None,
         "contraction_tops": round(step_ops / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
         "update": ({"gbps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(upd_bytes / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

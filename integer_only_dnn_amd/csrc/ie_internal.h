@@ -139,6 +139,11 @@ constexpr int PROF_ROUND_SUMS = 3150;
 constexpr int PROF_ALIGN = 3200;
 constexpr int PROF_SPLIT_ROUND = 3300;
 constexpr int PROF_FIN_PAIR = 3400;
+constexpr int PROF_RELU_FWD = 3500;
+constexpr int PROF_RELU_BWD = 3510;
+constexpr int PROF_ADD_NEED = 3520;
+constexpr int PROF_ADD_ROUND = 3521;
+constexpr int PROF_ADD_ROWS = 3530;
 
 // Auxiliary kernels (ie_aux.hip).
 hipError_t launch_fill_i32(int *p, long long n, int v, hipStream_t st);

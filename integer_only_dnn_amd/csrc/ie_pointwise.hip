@@ -199,11 +199,56 @@ __device__ __forceinline__ int block_max_256(int v, int *sh) {
     return max(max(sh[0], sh[1]), max(sh[2], sh[3]));
 }
 
+// Both operands with one exponent each and at most 22 bits apart: every
+// sum is exact in int32 at the smaller exponent (|n| < 2^30), and the
+// largest |n| gives the need.
+struct Uni {
+    bool on;
+    int sa, sb, base;
+};
+
+__device__ __forceinline__ Uni uni_of(const AddArgs &p) {
+    Uni u{false, 0, 0, 0};
+    if (p.a_row || p.b_row) return u;
+    const int ea = p.ae[0], eb = p.be[0];
+    if (abs(ea - eb) > 22) return u;
+    u.on = true;
+    u.base = min(ea, eb);
+    u.sa = ea - u.base;
+    u.sb = eb - u.base;
+    return u;
+}
+
+__device__ __forceinline__ int sum_uni(const Uni &u, const v4i &va, const v4i &vb, int j) {
+    return (byte_at(va, j) << u.sa) + (byte_at(vb, j) << u.sb);
+}
+
 // Whole-tensor output, pass 1: every block's largest need.
 __global__ __launch_bounds__(256) void add_need_kernel(AddArgs p) {
     __shared__ int sh[4];
     const long long total = p.rows * p.cols;
     int m = NEED_NONE;
+    const Uni u = uni_of(p);
+    if (u.on) {
+        int hi = 0, lo = 0;
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
+             i += (long long)gridDim.x * blockDim.x) {
+            const long long f0 = i * 16;
+            const v4i va = load16(p.a, f0, total, p.vec), vb = load16(p.b, f0, total, p.vec);
+            // bytes past the end load as zeros and add nothing
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int n = sum_uni(u, va, vb, j);
+                hi = max(hi, n);
+                lo = min(lo, n);
+            }
+        }
+        const uint32_t mx = max((uint32_t)hi, 0u - (uint32_t)lo);
+        m = mx ? u.base + mant_shift32(mx) : NEED_NONE;
+        m = block_max_256(m, sh);
+        if (threadIdx.x == 0) p.bmax[blockIdx.x] = m;
+        return;
+    }
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
          i += (long long)gridDim.x * blockDim.x) {
         const long long f0 = i * 16;
@@ -231,6 +276,22 @@ __global__ __launch_bounds__(256) void add_round_kernel(AddArgs p) {
     m = block_max_256(m, sh);
     const int e = clamp_exp_flag(max(E_MIN, m), p.flags);
     const long long total = p.rows * p.cols;
+    const Uni u = uni_of(p);
+    if (u.on) {
+        // one shift for every element: n * 2^-(e - base), half to even
+        const int s = e - u.base;
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
+             i += (long long)gridDim.x * blockDim.x) {
+            const long long f0 = i * 16;
+            const v4i va = load16(p.a, f0, total, p.vec), vb = load16(p.b, f0, total, p.vec);
+            v4i out = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) set_byte(out, j, rne_shift32(sum_uni(u, va, vb, j), s));
+            store16(p.z, f0, total, p.vec, out);
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) p.ze[0] = (int8_t)e;
+        return;
+    }
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
          i += (long long)gridDim.x * blockDim.x) {
         const long long f0 = i * 16;
@@ -293,8 +354,10 @@ hipError_t launch_relu_fwd(const int8_t *x, const int8_t *xe, int x_row, int8_t 
     const long long chunks = (rows * cols + 15) / 16;
     const int n_e = x_row ? (int)rows : 1;
     if (chunks == 0 && n_e == 0) return hipSuccess;
+    prof_begin(st, PROF_RELU_FWD);
     hipLaunchKernelGGL(relu_fwd_kernel, dim3(grid_for(chunks, 4096)), dim3(256), 0, st, x, xe, x_row, y, ye, rows,
                        cols, relu6, vec16(x, y, y));
+    prof_end(st, PROF_RELU_FWD);
     return hipGetLastError();
 }
 
@@ -304,8 +367,10 @@ hipError_t launch_relu_bwd(const int8_t *dy, const int8_t *dye, int dy_row, cons
     const long long chunks = (rows * cols + 15) / 16;
     const int n_e = dy_row ? (int)rows : 1;
     if (chunks == 0 && n_e == 0) return hipSuccess;
+    prof_begin(st, PROF_RELU_BWD);
     hipLaunchKernelGGL(relu_bwd_kernel, dim3(grid_for(chunks, 4096)), dim3(256), 0, st, dy, dye, dy_row, yc, ye,
                        y_row, dx, dxe, rows, cols, relu6, vec16(dy, yc, dx));
+    prof_end(st, PROF_RELU_BWD);
     return hipGetLastError();
 }
 
@@ -315,14 +380,20 @@ hipError_t launch_add(const int8_t *a, const int8_t *ae, int a_row, const int8_t
     AddArgs p{a, ae, b, be, z, ze, a_row, b_row, rows, cols, bmax, flags, vec16(a, b, z)};
     if (z_row) {
         if (rows == 0) return hipSuccess;
+        prof_begin(st, PROF_ADD_ROWS);
         hipLaunchKernelGGL(add_rows_kernel, dim3((int)(rows < 8192 ? rows : 8192)), dim3(256), 0, st, p);
+        prof_end(st, PROF_ADD_ROWS);
         return hipGetLastError();
     }
     const int g = grid_for((rows * cols + 15) / 16, ADD_MAX_BLOCKS);
+    prof_begin(st, PROF_ADD_NEED);
     hipLaunchKernelGGL(add_need_kernel, dim3(g), dim3(256), 0, st, p);
+    prof_end(st, PROF_ADD_NEED);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    prof_begin(st, PROF_ADD_ROUND);
     hipLaunchKernelGGL(add_round_kernel, dim3(g), dim3(256), 0, st, p);
+    prof_end(st, PROF_ADD_ROUND);
     return hipGetLastError();
 }
 

@@ -128,6 +128,21 @@ def test_add_gap_sweep(ws):
     assert ws.status() == 0
 
 
+def test_add_tensor_gaps(ws):
+    """Whole-tensor operands at every exponent gap from -30 to 30 (the int32
+    form covers gaps up to 22), into both output group kinds."""
+    announce("add whole-tensor gaps")
+    rng = np.random.default_rng(5)
+    for gap in range(-30, 31):
+        A = o.QT(rng.integers(-128, 128, size=(37, 45)).astype(np.int8), np.array([-40], np.int8), T)
+        B = o.QT(rng.integers(-128, 128, size=(37, 45)).astype(np.int8), np.array([-40 - gap], np.int8), T)
+        for gz in (T, R):
+            Z = ie.Mat.empty(37, 45, gz)
+            ie.ie_add(qt_to_dev(A), qt_to_dev(B), Z, ws)
+            assert_same(Z, o.sum_op(A, B, gz), f"gap {gap} out group={gz}")
+    assert ws.status() == 0
+
+
 def test_add_zero_and_overflow(ws):
     """All-zero sums give E_MIN; a sum whose exponent would pass 127 raises
     the sticky range flag."""
