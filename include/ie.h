@@ -178,6 +178,20 @@ ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const
                               void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Forward products with the activation fused into their output (Table 7:
+ * the clip acts on the rounded mantissas, the exponents are those of the
+ * plain product).  act: IE_ACT_NONE (same as ie_linear_fwd / ie_conv_fwd) or
+ * IE_ACT_RELU; other values return IE_ERR_UNSUPPORTED.  Arguments, limits
+ * and workspace sizes as for the plain entry points.
+ */
+#define IE_ACT_NONE 0
+#define IE_ACT_RELU 1
+ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act,
+                            void *ws, size_t ws_bytes, void *stream);
+ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
+                          const ie_mat *Y, int act, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * ReLU and ReLU6 of a (C, e) tensor (Table 7, "Clip activations"), on the
  * mantissas; the exponents are copied:
  *   relu:  Y.C = max(X.C, 0)

@@ -204,7 +204,7 @@ ProductWs carve_product(Carve &c, long long M, long long N, long long K, int fam
 // A(m,k) . B(n,k) over K into an int8 output with the planned epilogue.
 ie_status run_product(const Operand &A, const Operand &B, long long M, long long N, long long K, ExpSrc ea,
                       ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, int family,
-                      hipStream_t st) {
+                      hipStream_t st, int relu = 0) {
     if (M == 0 || N == 0) {
         return hip_status(launch_fill_i8(out->exp, out->group == IE_GROUP_ROW ? M : 1, E_MIN, st));
     }
@@ -224,6 +224,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     ep.out = out->mant;
     ep.out_exp = out->exp;
     ep.flags = flags;
+    ep.relu = relu;
     if (pl.mode == PLAN_DIRECT) {
         ep.mode = EPI_DIRECT;
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
@@ -234,7 +235,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
         ep.v16 = pw.v16;
         ep.p16 = pw.p16;
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
-        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st));
+        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st, relu));
         return IE_OK;
     }
     ep.partial = pw.partial;
@@ -242,7 +243,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     if (rg && split_round_rows_fits((int)N, 1, 1)) {
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
         IE_TRY(launch_split_round_rows(pw.partial, pl.splits, M * N, (int)M, (int)N, (int)N, 1, 1, ea, eb, out->mant,
-                                       out->exp, flags, st));
+                                       out->exp, flags, st, relu));
         return IE_OK;
     }
     ep.gneed = pw.gneed;
@@ -250,7 +251,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
     IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed, st));
     IE_TRY(launch_round_sums(pw.sums, (int)M, (int)N, (int)N, 1, 1, ea, eb, rg, pw.gneed, out->mant, out->exp, flags,
-                             st));
+                             st, relu));
     return IE_OK;
 }
 
@@ -592,8 +593,8 @@ ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     return hip_status(launch_zero_flags(ws, (hipStream_t)stream));
 }
 
-ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
-                        void *stream) {
+static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
+                            void *stream, int relu) {
     IE_CHECK(check_mat(X));
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(Y));
@@ -620,7 +621,18 @@ ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void 
     Operand B{LD_K, wsrc, Kp, (int)N, {}};
     ExpSrc ea{X->exp, nullptr, X->group == IE_GROUP_ROW};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, M, N, Kp, ea, eb, Y, pw, flags, 0, st);
+    return run_product(A, B, M, N, Kp, ea, eb, Y, pw, flags, 0, st, relu);
+}
+
+ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
+                        void *stream) {
+    return linear_fwd(X, W, Y, ws, ws_bytes, stream, 0);
+}
+
+ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act, void *ws, size_t ws_bytes,
+                            void *stream) {
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    return linear_fwd(X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
 ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
@@ -700,8 +712,8 @@ ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, 
     return run_wgrad(A, B, N, K, K, 1, 1, M, ea, eb, dW, w, flags, st);
 }
 
-ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
-                      size_t ws_bytes, void *stream) {
+static ie_status conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
+                          size_t ws_bytes, void *stream, int relu) {
     IE_CHECK(check_conv(d));
     IE_CHECK(check_mat(X));
     IE_CHECK(check_mat(W));
@@ -735,7 +747,18 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     Operand B{LD_K, wsrc, kg, g.k, {}};
     ExpSrc ea{X->exp, nullptr, 0};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, npq, g.k, kg, ea, eb, Y, pw, flags, 1, st);
+    return run_product(A, B, npq, g.k, kg, ea, eb, Y, pw, flags, 1, st, relu);
+}
+
+ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
+                      size_t ws_bytes, void *stream) {
+    return conv_fwd(d, X, W, Y, ws, ws_bytes, stream, 0);
+}
+
+ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act,
+                          void *ws, size_t ws_bytes, void *stream) {
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    return conv_fwd(d, X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
 ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,

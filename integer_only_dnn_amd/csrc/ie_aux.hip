@@ -297,7 +297,7 @@ constexpr int FIN_NEEDS = 2048;
 __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int16_t *p16, int M, int N,
                                                            int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
-                                                           FastDiv dper, int bid, int nblk) {
+                                                           FastDiv dper, int relu, int bid, int nblk) {
     __shared__ int sh[4];
     __shared__ int16_t needs[FIN_NEEDS];
     __shared__ int rowe[256];
@@ -312,6 +312,10 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
             if (j < 2) lo |= b << (16 * j);
             else hi |= b << (16 * (j - 2));
         }
+        if (relu) {
+            lo = relu4(lo);
+            hi = relu4(hi);
+        }
         *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
     };
     auto round8 = [&](long long o, int sh_) {
@@ -325,9 +329,14 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
                 if (j < 2) lo |= b << (16 * j);
                 else hi |= b << (16 * (j - 2));
             }
+            if (relu) {
+                lo = relu4(lo);
+                hi = relu4(hi);
+            }
             *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
         } else {
-            out[o] = (int8_t)rne_shift32(v16[o], sh_);
+            const int c = rne_shift32(v16[o], sh_);
+            out[o] = (int8_t)(relu && c < 0 ? 0 : c);
         }
     };
     if (!row_group) {
@@ -425,8 +434,9 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
 __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
                                                            int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
-                                                           FastDiv dper) {
-    rto_finalize_body(v16, p16, M, N, lbm, lbn, TM, n_ct, row_group, rb, out, out_exp, flags, vw, dper, blockIdx.x, gridDim.x);
+                                                           FastDiv dper, int relu) {
+    rto_finalize_body(v16, p16, M, N, lbm, lbn, TM, n_ct, row_group, rb, out, out_exp, flags, vw, dper, relu,
+                      blockIdx.x, gridDim.x);
 }
 
 // Arguments of a round-to-odd finalize and its grid.
@@ -438,6 +448,7 @@ struct RtoFin {
     int vw;
     FastDiv dper;
     int blocks;
+    int relu;
 };
 
 static RtoFin rto_fin(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group, int8_t *out,
@@ -463,16 +474,17 @@ static RtoFin rto_fin(const int16_t *v16, const int16_t *p16, int M, int N, Tile
     f.out_exp = out_exp;
     f.flags = flags;
     f.dper = make_fastdiv((uint32_t)(N / f.vw));
+    f.relu = 0;
     return f;
 }
 
 hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
-                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st) {
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const RtoFin f = rto_fin(v16, p16, M, N, t, row_group, out, out_exp, flags);
     prof_begin(st, PROF_RTO_FINALIZE);
     hipLaunchKernelGGL(rto_finalize_kernel, dim3(f.blocks), dim3(256), 0, st, f.v16, f.p16, f.M, f.N, f.lbm, f.lbn,
-                       f.TM, f.n_ct, f.row_group, f.rb, f.out, f.out_exp, f.flags, f.vw, f.dper);
+                       f.TM, f.n_ct, f.row_group, f.rb, f.out, f.out_exp, f.flags, f.vw, f.dper, relu);
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
@@ -575,7 +587,8 @@ __global__ __launch_bounds__(256) void partial_reduce_kernel(const int *partial,
 __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, int M, int N, int src_pitch,
                                                          int mc, int mcp, FastDiv dmc, ExpSrc ea, ExpSrc eb,
                                                          int row_group, const int *gneed, int8_t *out,
-                                                         int8_t *out_exp, uint32_t *flags, int vw, FastDiv dper) {
+                                                         int8_t *out_exp, uint32_t *flags, int vw, FastDiv dper,
+                                                         int relu) {
     const uint32_t per_row = N / vw;
     const uint32_t total = (uint32_t)M * per_row;
     const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
@@ -604,6 +617,7 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
         }
         uint32_t w = 0;
         for (int j = 0; j < vw; ++j) w |= (uint32_t)(uint8_t)rne_shift64(sv[j], e - ev[j]) << (8 * j);
+        if (relu) w = relu4(w);
         if (vw == 4) *(uint32_t *)(out + o) = w;
         else out[o] = (int8_t)w;
         if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
@@ -677,7 +691,8 @@ template <int THR>
 __device__ __forceinline__ void split_round_body(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q, int bid, int nblk) {
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q, int relu,
+                                                                 int bid, int nblk) {
     // short rows (THR == SR_THR_SHORT) hold at most one chunk per thread
     constexpr int MAXV = THR == SR_THR_SHORT ? 1 : SR_MAXV;
     __shared__ int sh[THR / 64];
@@ -786,9 +801,10 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - eps(4 * c + j)) << (8 * j);
-                *(uint32_t *)(orow + 4 * c) = w;
+                *(uint32_t *)(orow + 4 * c) = relu ? relu4(w) : w;
             } else {
-                orow[c] = (int8_t)rne_shift64(v[k][0], e - eps(c));
+                const int cv = (int)rne_shift64(v[k][0], e - eps(c));
+                orow[c] = (int8_t)(relu && cv < 0 ? 0 : cv);
             }
         }
         __syncthreads();
@@ -799,9 +815,10 @@ template <int THR>
 __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void split_round_rows_kernel(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q) {
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q,
+                                                                 int relu) {
     split_round_body<THR>(partial, splits, stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q,
-                          blockIdx.x, gridDim.x);
+                          relu, blockIdx.x, gridDim.x);
 }
 
 bool split_round_rows_fits(int Nout, int mc, int mcp) {
@@ -821,6 +838,7 @@ struct SplitFin {
     uint32_t *flags;
     int vw, Q, blocks;
     bool shortrow;
+    int relu;
 };
 
 static SplitFin split_fin(const int *partial, int splits, long long split_stride, int M, int Nout, int src_pitch,
@@ -850,12 +868,13 @@ static SplitFin split_fin(const int *partial, int splits, long long split_stride
     }
     f.blocks = blocks_for(M, 1, 16384);
     f.dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
+    f.relu = 0;
     return f;
 }
 
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, hipStream_t st) {
+                                   int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu) {
     if (M <= 0 || Nout <= 0) return hipSuccess;
     const SplitFin f = split_fin(partial, splits, split_stride, M, Nout, src_pitch, mc, mcp, ea, eb, out, out_exp,
                                  flags);
@@ -863,11 +882,11 @@ hipError_t launch_split_round_rows(const int *partial, int splits, long long spl
     if (f.shortrow)
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, dim3(f.blocks), dim3(SR_THR_SHORT), 0, st,
                            f.partial, f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb,
-                           f.out, f.out_exp, f.flags, f.vw, f.Q);
+                           f.out, f.out_exp, f.flags, f.vw, f.Q, relu);
     else
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, dim3(f.blocks), dim3(SR_THR), 0, st, f.partial,
                            f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb, f.out,
-                           f.out_exp, f.flags, f.vw, f.Q);
+                           f.out_exp, f.flags, f.vw, f.Q, relu);
     prof_end(st, PROF_SPLIT_ROUND);
     return hipGetLastError();
 }
@@ -882,10 +901,10 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void f
     if ((int)blockIdx.x < r.blocks) {
         if (threadIdx.x >= 256) return;
         rto_finalize_body(r.v16, r.p16, r.M, r.N, r.lbm, r.lbn, r.TM, r.n_ct, r.row_group, r.rb, r.out, r.out_exp,
-                          r.flags, r.vw, r.dper, blockIdx.x, r.blocks);
+                          r.flags, r.vw, r.dper, r.relu, blockIdx.x, r.blocks);
     } else {
         split_round_body<THR>(q.partial, q.splits, q.stride, q.M, q.Nout, q.src_pitch, q.mc, q.mcp, q.dmc, q.ea,
-                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, blockIdx.x - r.blocks,
+                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, q.relu, blockIdx.x - r.blocks,
                               gridDim.x - r.blocks);
     }
 }
@@ -929,14 +948,14 @@ hipError_t launch_partial_reduce(const int *partial, int splits, long long split
 
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
-                             uint32_t *flags, hipStream_t st) {
+                             uint32_t *flags, hipStream_t st, int relu) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int vw = (N % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
     const long long total = (long long)M * (N / vw);
     prof_begin(st, PROF_ROUND_SUMS);
     hipLaunchKernelGGL(round_sums_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, sums, M, N,
                        src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb, row_group, gneed,
-                       out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)));
+                       out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)), relu);
     prof_end(st, PROF_ROUND_SUMS);
     return hipGetLastError();
 }

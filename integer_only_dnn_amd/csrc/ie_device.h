@@ -76,6 +76,13 @@ __device__ __forceinline__ int rto_shift32(int a, int t) {
     return q | sticky;
 }
 
+// ReLU of four packed int8 mantissas (Table 7: the exponent is kept): the
+// negative bytes become zero.
+__device__ __forceinline__ uint32_t relu4(uint32_t w) {
+    const uint32_t neg = (w & 0x80808080u) >> 7;
+    return w & ~(neg * 0xffu);
+}
+
 __device__ __forceinline__ int clamp_exp_flag(int e, uint32_t *flags) {
     if (e < E_MIN) e = E_MIN;
     if (e > E_MAX) {

@@ -837,7 +837,13 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             const int row = q / CPR, cb = (q % CPR) * 16;
             const int grow = m0 + row, gcol = n0 + cb / ES;
             if (grow >= M || gcol >= N) continue;
-            const v4i v = *(const v4i *)(lds + row * PITCH + cb);
+            v4i v = *(const v4i *)(lds + row * PITCH + cb);
+            if constexpr (ES == 1) {
+                if (ep.relu) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[k] = (int)relu4((uint32_t)v[k]);
+                }
+            }
             int8_t *g = (int8_t *)dst + ((long long)grow * ld + gcol) * ES;
             if (vec && gcol + EPC <= N) {
                 *(v4i *)g = v;

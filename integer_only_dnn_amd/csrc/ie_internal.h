@@ -46,6 +46,7 @@ struct Epi {
     int *partial;     // PARTIAL: int32 [splits][M][N]
     long long split_stride;
     uint32_t *flags;
+    int relu;         // int8 results pass through ReLU (forward products)
 };
 
 enum LoaderKind {
@@ -163,7 +164,7 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, i
 // maximum of the tile needs in p16 (ROW groups: per (row, column tile);
 // whole-tensor groups: per tile, tile_m + TM * tile_n).
 hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
-                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st);
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu = 0);
 // Split-contraction finalize: sum int32 partials into int64 and raise the
 // group maxima (set empty by the split kernel, or by launch_fill_i32 when no
 // split kernel ran); then round the sums into int8.
@@ -172,14 +173,14 @@ hipError_t launch_partial_reduce(const int *partial, int splits, long long split
                                  hipStream_t st);
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
-                             uint32_t *flags, hipStream_t st);
+                             uint32_t *flags, hipStream_t st, int relu = 0);
 // Split finalize of row groups in one pass (sums never stored): output
 // [M x Nout] from partials [splits][M][src_pitch] with the column map of
 // launch_round_sums.  Requires split_round_rows_fits(Nout, mc, mcp).
 bool split_round_rows_fits(int Nout, int mc, int mcp);
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, hipStream_t st);
+                                   int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu = 0);
 // A round-to-odd finalize (whole-tensor group, M1 x N1 from tile t1) and a
 // split finalize by rows (the arguments of launch_split_round_rows) in one
 // launch.

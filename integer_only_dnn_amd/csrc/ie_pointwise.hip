@@ -65,12 +65,6 @@ __device__ __forceinline__ void set_byte(v4i &v, int j, int c) {
     v[j >> 2] = (int)(((uint32_t)v[j >> 2] & ~(0xffu << sh)) | ((uint32_t)(uint8_t)c << sh));
 }
 
-// Zero the negative bytes of four packed int8 values.
-__device__ __forceinline__ uint32_t relu4(uint32_t w) {
-    const uint32_t neg = (w & 0x80808080u) >> 7;
-    return w & ~(neg * 0xffu);
-}
-
 // Copy of `n` exponent bytes (grid-stride), skipped when in place.
 __device__ __forceinline__ void copy_exps(const int8_t *src, int8_t *dst, long long n) {
     if (src == dst) return;

@@ -61,6 +61,8 @@ EXPORTS = [
     ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update_multi", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_fwd_act", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
+    ("ie_conv_fwd_act", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
     ("ie_relu_fwd", c_int, [POINTER(ie_mat)] * 2 + [c_int, c_void_p]),
     ("ie_relu_bwd", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p]),
     ("ie_add_workspace", c_size_t, [c_int64, c_int64]),
@@ -243,6 +245,29 @@ def ie_sgd_update_multi(Ws, Vs, Gs, lr, momentum, weight_decay=(0, 0), ws: Works
     p, b = ws.get(_ws_size("ie_sgd_update_multi_workspace", n))
     _check(lib().ie_sgd_update_multi(n, w, v, g, ie_scalar(*lr), ie_scalar(*momentum), ie_scalar(*weight_decay),
                                      p, b, _stream(ws.device)), "ie_sgd_update_multi")
+
+
+ACT_NONE, ACT_RELU = 0, 1
+
+
+def ie_linear_fwd_act(X: Mat, W: Mat, Y: Mat, act: int, ws: Workspace) -> None:
+    """ie_linear_fwd with the activation fused into the output."""
+    x, w, y = X.c(), W.c(), Y.c()
+    p, b = ws.get(_ws_size("ie_linear_fwd_workspace", x.rows, w.rows, x.cols))
+    _check(lib().ie_linear_fwd_act(byref(x), byref(w), byref(y), int(act), p, b, _stream(ws.device)),
+           "ie_linear_fwd_act")
+
+
+def ie_conv_fwd_act(d: ie_conv_desc, X: Mat, W: Mat, Y: Mat, act: int, ws: Workspace) -> None:
+    """ie_conv_fwd with the activation fused into the output."""
+    x = X.c(d.n * d.h * d.w, d.c)
+    w = W.c(d.k, d.r * d.s * d.c)
+    P = (d.h + 2 * d.pad - d.r) // d.stride + 1
+    Q = (d.w + 2 * d.pad - d.s) // d.stride + 1
+    y = Y.c(d.n * P * Q, d.k)
+    p, b = ws.get(_ws_size("ie_conv_fwd_workspace", d))
+    _check(lib().ie_conv_fwd_act(byref(d), byref(x), byref(w), byref(y), int(act), p, b, _stream(ws.device)),
+           "ie_conv_fwd_act")
 
 
 def ie_relu_fwd(X: Mat, Y: Mat, relu6: bool = False) -> None:

@@ -108,3 +108,9 @@ def test_pointwise_argument_errors():
     assert L.ie_add(by(A), by(B), by(_mat(4, 8)), 1, 16, None) == 4
     assert L.ie_add(by(A), by(_mat(4, 7)), by(_mat(4, 8)), 1, 1 << 20, None) == 2
     assert L.ie_add_workspace(4, 8) >= 256
+    # fused activations: only none and ReLU
+    X, W, Y = _mat(4, 8), _mat(3, 8), _mat(4, 3)
+    assert L.ie_linear_fwd_act(by(X), by(W), by(Y), 2, 1, 1 << 20, None) == 6
+    d = ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 1, 1)
+    assert L.ie_conv_fwd_act(by(d), by(_mat(128, 16)), by(_mat(32, 144)), by(_mat(128, 32)), 5, 1, 1 << 30,
+                             None) == 6

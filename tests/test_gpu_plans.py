@@ -78,6 +78,42 @@ def test_dense_direct(tile, ws, plan):
         assert_same(Y, o.linear_fwd(X, W, gy), f"direct group {gy}")
 
 
+def _relu(t: o.QT) -> o.QT:
+    return o.QT(o.relu_fwd(t.mant).astype(np.int8), t.exp, t.group)
+
+
+@pytest.mark.parametrize("tile", [(2, 2), (1, 1), (2, 1)], ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
+@pytest.mark.parametrize("mode", [(0, 1)] + MODES, ids=lambda m: f"m{m[0]}s{m[1]}")
+def test_fused_relu_plans(tile, mode, ws, plan):
+    """The forward products with ReLU fused into their output equal the
+    oracle's ReLU of the plain product, through every epilogue (direct,
+    round-to-odd, split with the row finalize or the whole-tensor one)."""
+    direct = mode[0] == 0
+    M, N, K = (64 * tile[0] - 3, 64 * tile[1] - 5, 200) if direct else (200, 150, 392)
+    announce(f"fused relu tile={tile} mode={mode} M={M} N={N} K={K}")
+    rng = np.random.default_rng(3 * tile[0] + tile[1] + 17 * mode[0] + mode[1])
+    X = rand_qt(rng, (M, K), R)
+    W = rand_qt(rng, (N, K), R)
+    Xd, Wd = qt_to_dev(X), qt_to_dev(W)
+    plan(tile, *mode)
+    for gy in (T, R):
+        Y = ie.Mat.empty(M, N, gy)
+        ie.ie_linear_fwd_act(Xd, Wd, Y, ie.ACT_RELU, ws)
+        assert_same(Y, _relu(o.linear_fwd(X, W, gy)), f"linear relu group {gy}")
+    if not direct:
+        shape = (2, 10, 10, 32, 40, 3, 3, 1, 1)
+        d, dd = o.ConvShape(*shape), ie.conv_desc(*shape)
+        Xc = rand_qt(rng, (2, 10, 10, 32), T, zero_frac=0.2)
+        Wc = rand_qt(rng, (40, 288), T)
+        Y = ie.Mat.empty(2 * d.p * d.q, 40, T)
+        ie.ie_conv_fwd_act(dd, qt_to_dev(Xc, rows=200), qt_to_dev(Wc), Y, ie.ACT_RELU, ws)
+        assert_same(Y, _relu(o.conv_fwd(d, Xc, Wc, T)), "conv relu")
+        Y0 = ie.Mat.empty(2 * d.p * d.q, 40, T)
+        ie.ie_conv_fwd_act(dd, qt_to_dev(Xc, rows=200), qt_to_dev(Wc), Y0, ie.ACT_NONE, ws)
+        assert_same(Y0, o.conv_fwd(d, Xc, Wc, T), "conv act none")
+    assert ws.status() == 0
+
+
 # 24 channels: the input gradient reads a transposed, aligned copy of W;
 # 32 / 48 channels with a whole-tensor W: it reads W in place
 CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1),
