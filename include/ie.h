@@ -157,10 +157,11 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
 /*
  * Integer SGD with momentum and per-group velocity (Figure 1b; Table 5),
  * in place on W and V:
- *   V <- R_V(momentum * V + G),  W <- R_W(W - lr * V)
- * where R_x requantises into x's groups and the weight step uses the stored,
- * rounded V.  W, V, G: [rows x cols], each TENSOR or ROW.
- * weight_decay must have mant == 0 in this build.
+ *   V <- R_V(momentum * V + G + weight_decay * W),  W <- R_W(W - lr * V)
+ * where R_x requantises into x's groups, the velocity sum is exact (the
+ * decay term uses W before the step; Table 10 lists weight decay 1e-4, e.g.
+ * (1, -13)), and the weight step uses the stored, rounded V.  W, V, G:
+ * [rows x cols], each TENSOR or ROW.  weight_decay.mant == 0: no decay term.
  */
 ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G,
                         ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,

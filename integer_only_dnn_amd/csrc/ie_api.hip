@@ -520,18 +520,18 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const ie_mat *W, con
 }
 
 ie_status check_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar weight_decay) {
+    (void)weight_decay;  // any (C, e) scalar
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(V));
     IE_CHECK(check_mat(G));
     if (V->rows != W->rows || V->cols != W->cols || G->rows != W->rows || G->cols != W->cols)
         return IE_ERR_SHAPE;
-    if (weight_decay.mant != 0) return IE_ERR_UNSUPPORTED;
     if (W->cols > 64 * 4 * 32) return IE_ERR_UNSUPPORTED;
     return IE_OK;
 }
 
 UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar lr, ie_scalar momentum,
-                       int *tmp, void *ws) {
+                       ie_scalar weight_decay, int *tmp, void *ws) {
     UpdateArgs a;
     a.w = W->mant;
     a.w_exp = W->exp;
@@ -548,6 +548,8 @@ UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
     a.lr_e = lr.exp;
     a.mom_m = momentum.mant;
     a.mom_e = momentum.exp;
+    a.wd_m = weight_decay.mant;
+    a.wd_e = weight_decay.exp;
     a.tmp = tmp;
     a.flags = (uint32_t *)ws;
     return a;
@@ -853,7 +855,7 @@ ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sc
     if (!ws) return IE_ERR_WORKSPACE;
     if (ws_bytes < ie_sgd_update_workspace(W->rows, W->cols)) return IE_ERR_WORKSPACE;
     Carve c{(char *)ws, HEADER};
-    UpdateArgs a = update_args(W, V, G, lr, momentum, c.take<int>(UPD_WS_INTS), ws);
+    UpdateArgs a = update_args(W, V, G, lr, momentum, weight_decay, c.take<int>(UPD_WS_INTS), ws);
     return hip_status(launch_sgd_update(a, (hipStream_t)stream));
 }
 
@@ -867,7 +869,8 @@ ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const
     if (ws_bytes < ie_sgd_update_multi_workspace(n)) return IE_ERR_WORKSPACE;
     Carve c{(char *)ws, HEADER};
     std::vector<UpdateArgs> a((size_t)n);
-    for (int i = 0; i < n; ++i) a[i] = update_args(W + i, V + i, G + i, lr, momentum, c.take<int>(UPD_WS_INTS), ws);
+    for (int i = 0; i < n; ++i)
+        a[i] = update_args(W + i, V + i, G + i, lr, momentum, weight_decay, c.take<int>(UPD_WS_INTS), ws);
     return hip_status(launch_sgd_update_multi(a.data(), n, (hipStream_t)stream));
 }
 

@@ -198,6 +198,7 @@ struct UpdateArgs {
     int w_row, v_row, g_row;
     long long rows, cols;
     int lr_m, lr_e, mom_m, mom_e;
+    int wd_m, wd_e;    // weight decay (C, e); wd_m == 0: none
     int *tmp;          // [UPD_WS_INTS]: exponent snapshots, per-block maxima
     uint32_t *flags;
 };

@@ -91,6 +91,97 @@ __device__ __forceinline__ int sum_round(bool narrow, int X, int pa, int Y, int 
     return sum_round_wide(X, pa, Y, pb, e);
 }
 
+// ---------------------------------------------------------------------------
+// Weight decay adds a third term: v = momentum*V + G + wd*W.  Exact sums of
+// three terms X*2^p (|X| < 2^15) as n * 2^base in 128 bits, terms sorted by
+// exponent pa >= pb >= pc:
+//   - pa - pb > 60: b and c lie below 2^(pa-45) while the sum exceeds
+//     2^(pa-1), so every exponent the group can take is at least pa - 8 and
+//     they only decide ties and sticky bits: a * 2^24 + sign(b 2^pb + c 2^pc)
+//     at pa - 24 rounds identically;
+//   - else S = a 2^(pa-pb) + b exactly (|S| < 2^75); if pb - pc > 40 and
+//     S != 0, c (below 2^(pb-25) against a sum above 2^(pb-1)) is replaced
+//     the same way: S * 2^24 + sign(c) at pb - 24; S == 0 leaves c exactly;
+//   - otherwise S * 2^(pb-pc) + c exactly (|.| < 2^116).
+// ---------------------------------------------------------------------------
+
+struct Ex128 {
+    __int128 n;
+    int base;
+};
+
+__device__ __noinline__ Ex128 combine3(int X1, int p1, int X2, int p2, int X3, int p3) {
+    int x[3] = {X1, X2, X3}, p[3] = {p1, p2, p3};
+    // sort by exponent, descending (three compare-exchanges)
+    auto cx = [&](int i, int j) {
+        if (p[i] < p[j]) {
+            int t = p[i]; p[i] = p[j]; p[j] = t;
+            t = x[i]; x[i] = x[j]; x[j] = t;
+        }
+    };
+    cx(0, 1);
+    cx(1, 2);
+    cx(0, 1);
+    // zero terms drop out: the two-term form covers what is left
+    if (x[0] == 0 || x[1] == 0 || x[2] == 0) {
+        int k = 0, y[3], q[3];
+        for (int i = 0; i < 3; ++i)
+            if (x[i] != 0) {
+                y[k] = x[i];
+                q[k] = p[i];
+                ++k;
+            }
+        if (k == 0) return {0, p[2]};
+        if (k == 1) return {(__int128)y[0], q[0]};
+        const Ex64 s = combine64(y[0], q[0], y[1], q[1]);
+        return {(__int128)s.n, s.base};
+    }
+    const int a = x[0], b = x[1], c = x[2], pa = p[0], pb = p[1], pc = p[2];
+    if (pa - pb > 60) {
+        const Ex64 bc = combine64(b, pb, c, pc);
+        if (bc.n == 0) return {(__int128)a, pa};
+        return {((__int128)a << 24) + (bc.n > 0 ? 1 : -1), pa - 24};
+    }
+    const __int128 S = ((__int128)a << (pa - pb)) + b;
+    if (pb - pc > 40) {
+        if (S == 0) return {(__int128)c, pc};
+        return {(S << 24) + (c > 0 ? 1 : -1), pb - 24};
+    }
+    return {(S << (pb - pc)) + c, pc};
+}
+
+// Smallest exponent of n * 2^base (NEED_NONE for n == 0): bit length - 7,
+// plus one when the top eight bits are all ones.
+__device__ __forceinline__ int need128(__int128 n, int base) {
+    if (n == 0) return NEED_NONE;
+    const unsigned __int128 m = (unsigned __int128)(n < 0 ? -n : n);
+    const uint64_t hi = (uint64_t)(m >> 64), lo = (uint64_t)m;
+    const int z = hi ? __clzll(hi) : 64 + __clzll(lo);  // leading zeros of m (m != 0)
+    const uint32_t top = (uint32_t)((m << z) >> 120);
+    return base + (128 - z) - 7 + (top == 255u ? 1 : 0);
+}
+
+// n * 2^-s rounded half to even (s <= 0: exact left shift; the result is a
+// mantissa, so callers only reach it for values that fit).
+__device__ __forceinline__ int rne128(__int128 n, int s) {
+    if (s <= 0) return (int)(n << (-s > 126 ? 126 : -s));
+    if (s >= 126) return 0;
+    __int128 q = n >> s;
+    const __int128 r = n - (q << s), half = (__int128)1 << (s - 1);
+    if (r > half || (r == half && (q & 1))) ++q;
+    return (int)q;
+}
+
+__device__ __noinline__ int sum3_need_wide(int X1, int p1, int X2, int p2, int X3, int p3) {
+    const Ex128 s = combine3(X1, p1, X2, p2, X3, p3);
+    return need128(s.n, s.base);
+}
+
+__device__ __noinline__ int sum3_round_wide(int X1, int p1, int X2, int p2, int X3, int p3, int e) {
+    const Ex128 s = combine3(X1, p1, X2, p2, X3, p3);
+    return rne128(s.n, e - s.base);
+}
+
 // Rounding of a row with one uniform shift: n * 2^-sh, half to even
 // (sh <= 0: exact left shift); |n| < 2^30.
 struct RneU {
@@ -158,7 +249,7 @@ __device__ __forceinline__ uint32_t umax_wave(uint32_t v) { return wave_umax_dpp
 // by the pass before (tmp[0]: old velocity exponent, tmp[1]: old weight
 // exponent).  All passes run on the same grid of nblk blocks (this block is
 // blk of them).
-template <int D, int WPR>
+template <int D, int WPR, bool WD = false>
 __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int vec, int blk, int nblk) {
     constexpr int RPB = 4 / WPR;  // rows per block
     const int lane = threadIdx.x & 63;
@@ -197,6 +288,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     int ev_t = 0, ew_t = 0, evn_t = 0, ewn_t = 0;
     if (pass == 0) {
         ev_t = a.v_exp[0];
+        if (WD && w_tensor) ew_t = a.w_exp[0];  // the decay term reads W before it changes
         if (blk == 0 && threadIdx.x == 0) a.tmp[0] = ev_t;
     } else if (pass == 1) {
         if (v_tensor) {
@@ -226,7 +318,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const long long col = 4ll * (lane + 64 * (sub + WPR * j));
-            x.W[j] = (pass != 0) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
+            x.W[j] = (pass != 0 || WD) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
             x.V[j] = load_dw(a.v + off, col, a.cols, vec);
             x.G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
         }
@@ -274,29 +366,41 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
                 return;
             }
 
-            // ---- velocity: v = momentum * V + G ----
+            // ---- velocity: v = momentum * V + G (+ weight_decay * W) ----
             const int ev = x.ev;
             const int eg = x.eg;
             const int pa = ev + a.mom_e, pb = eg;
-            const bool nv = abs(pa - pb) <= 15;
+            const int pc = WD ? ew + a.wd_e : pa;
+            const int vbase = WD ? min(min(pa, pb), pc) : min(pa, pb);
+            // narrow: exact in int32 at vbase (three terms: each below 2^28)
+            const bool nv = WD ? max(max(pa, pb), pc) - vbase <= 14 : abs(pa - pb) <= 15;
             int vn[D][4];
             int needv;
             if (nv) {
                 // |factors| <= 2^22 and mantissas are bytes: exact 24-bit products
-                const int base = min(pa, pb);
-                const int fa = a.mom_m * (1 << (pa - base)), fb = 1 << (pb - base);
+                const int fa = a.mom_m * (1 << (pa - vbase)), fb = 1 << (pb - vbase);
+                const int fc = WD ? a.wd_m * (1 << (pc - vbase)) : 0;
     #pragma unroll
                 for (int j = 0; j < D; ++j)
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(V[j], t), fa) + __mul24(sbyte(G[j], t), fb);
+                    for (int t = 0; t < 4; ++t) {
+                        vn[j][t] = __mul24(sbyte(V[j], t), fa) + __mul24(sbyte(G[j], t), fb);
+                        if constexpr (WD) vn[j][t] += __mul24(sbyte(W[j], t), fc);
+                    }
                 const uint32_t mx = row_umax(absmax_rows<D>(vn));
-                needv = mx ? base + mant_shift32(mx) : NEED_NONE;
+                needv = mx ? vbase + mant_shift32(mx) : NEED_NONE;
             } else {
                 int m = NEED_NONE;
     #pragma unroll
                 for (int j = 0; j < D; ++j)
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+                    for (int t = 0; t < 4; ++t) {
+                        if constexpr (WD)
+                            m = max(m, sum3_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb,
+                                                      a.wd_m * sbyte(W[j], t), pc));
+                        else
+                            m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+                    }
                 needv = row_imax(m);
             }
             if (pass == 0) {
@@ -306,13 +410,18 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
             const int evn = v_tensor ? evn_t : clamp_exp_flag(max(E_MIN, needv), a.flags);
             int c[D][4];
             if (nv) {
-                rne_rows<D>(vn, rne_u(evn - min(pa, pb)), c);
+                rne_rows<D>(vn, rne_u(evn - vbase), c);
             } else {
     #pragma unroll
                 for (int j = 0; j < D; ++j)
     #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
+                    for (int t = 0; t < 4; ++t) {
+                        if constexpr (WD)
+                            c[j][t] = sum3_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb,
+                                                      a.wd_m * sbyte(W[j], t), pc, evn);
+                        else
+                            c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
+                    }
             }
     #pragma unroll
             for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
@@ -384,9 +493,9 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     }
 }
 
-template <int D, int WPR>
+template <int D, int WPR, bool WD>
 __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec) {
-    update_rows<D, WPR>(a, pass, vec, blockIdx.x, gridDim.x);
+    update_rows<D, WPR, WD>(a, pass, vec, blockIdx.x, gridDim.x);
 }
 
 // Several tensors of one (D, WPR) class in one launch: segment i owns blocks
@@ -452,7 +561,7 @@ static int update_blocks(const UpdateArgs &a, int wpr) {
     return (int)blocks;
 }
 
-template <int D, int WPR>
+template <int D, int WPR, bool WD = false>
 static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
     const int blocks = update_blocks(a, WPR);
     hipError_t err;
@@ -460,7 +569,7 @@ static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
         if (pass == 0 && a.v_row) continue;
         if (pass == 2 && a.w_row) continue;
         prof_begin(st, 2000 + pass);
-        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR>), dim3((int)blocks), dim3(256), 0, st, a, pass, vec);
+        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR, WD>), dim3((int)blocks), dim3(256), 0, st, a, pass, vec);
         prof_end(st, 2000 + pass);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -511,8 +620,26 @@ static int update_vec(const UpdateArgs &a) {
            ((uintptr_t)a.g % 4 == 0);
 }
 
+// One tensor with weight decay: a launch per pass of its class's kernel.
+static hipError_t run_class_wd(int c, const UpdateArgs &a, int vec, hipStream_t st) {
+    switch (c) {
+        case 0: return run_passes<1, 1, true>(a, vec, st);
+        case 1: return run_passes<2, 1, true>(a, vec, st);
+        case 2: return run_passes<3, 1, true>(a, vec, st);
+        case 3: return run_passes<4, 1, true>(a, vec, st);
+        case 4: return run_passes<1, 4, true>(a, vec, st);
+        case 5: return run_passes<2, 4, true>(a, vec, st);
+        case 6: return run_passes<3, 4, true>(a, vec, st);
+        case 7: return run_passes<4, 4, true>(a, vec, st);
+        case 8: return run_passes<6, 4, true>(a, vec, st);
+        case 9: return run_passes<8, 4, true>(a, vec, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 // One tensor: a launch per pass of its class's kernel.
 static hipError_t run_class(int c, const UpdateArgs &a, int vec, hipStream_t st) {
+    if (a.wd_m != 0) return run_class_wd(c, a, vec, st);
     switch (c) {
         case 0: return run_passes<1, 1>(a, vec, st);
         case 1: return run_passes<2, 1>(a, vec, st);
@@ -601,6 +728,14 @@ hipError_t launch_sgd_update(const UpdateArgs &a, hipStream_t st) {
 hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st) {
     for (int i = 0; i < n; ++i)
         if (a[i].rows > 0 && update_class(a[i]) < 0) return hipErrorInvalidValue;
+    if (n > 0 && a[0].wd_m != 0) {
+        // weight decay (one scalar for all): tensor by tensor
+        for (int i = 0; i < n; ++i) {
+            hipError_t err = launch_sgd_update(a[i], st);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
     // small tensors of the narrow classes: all together, one launch per pass
     {
         UpdateArgs seg[UPD_MIX];

@@ -72,7 +72,7 @@ def test_conv_and_update_argument_errors():
     S = ie.ie_scalar
     assert L.ie_sgd_update(by(W), by(_mat(32, 144)), by(_mat(31, 144)), S(1, -7), S(7, -3), S(0, 0),
                            1, 4096, None) == 2
-    assert L.ie_sgd_update(by(W), by(W), by(W), S(1, -7), S(7, -3), S(1, -13), 1, 4096, None) == 6
+    assert L.ie_sgd_update(by(W), by(W), by(_mat(31, 144)), S(1, -7), S(7, -3), S(1, -13), 1, 4096, None) == 2
     arr = ie.ie_mat * 2
     Ws, Vs, Gs = arr(W, W), arr(W, W), arr(W, _mat(31, 144))
     big = 1 << 20
