@@ -30,6 +30,10 @@ R6  products are exact integer sums of int8 x int8 terms, exponent e_a + e_b.
 R7  the optimizer is SGD with momentum in the PyTorch form
     v <- beta*v + g,  w <- w - lr*v  (no dampening), the velocity rounded
     first and the weight update using the stored, rounded velocity.
+R8  mantissa width B (Table 4, B in 8..4): a B-bit result has
+    |C| <= 2**(B-1) - 1 in R1 and R3, stored in the same int8 container;
+    the velocity stays INT8 whatever B the weights use.  Every requantising
+    function takes ``bits`` (default 8).
 
 Integer contractions use float64 matrix products: every partial sum is an
 integer of magnitude < 2**53 (asserted), where float64 addition is exact in
@@ -156,8 +160,14 @@ def rne_np(a: np.ndarray, s) -> np.ndarray:
 # Smallest exponent for one exact value (reading R3)
 # ---------------------------------------------------------------------------
 
-def need_int(a: int, eps: int):
-    """Smallest e with |rne(a * 2**eps, at exponent e)| <= Q_MAX; None if a == 0.
+def q_max(bits: int = Q_BITS) -> int:
+    """Largest output mantissa magnitude of a B-bit tensor (reading R8)."""
+    assert 2 <= bits <= 8
+    return (1 << (bits - 1)) - 1
+
+
+def need_int(a: int, eps: int, bits: int = Q_BITS):
+    """Smallest e with |rne(a * 2**eps, at exponent e)| <= q_max(bits); None if a == 0.
 
     Walks e upward from a point where the bound certainly fails; |rne| is
     non-increasing in the shift, so the first e that satisfies it is the
@@ -166,9 +176,10 @@ def need_int(a: int, eps: int):
     a, eps = int(a), int(eps)
     if a == 0:
         return None
-    s = abs(a).bit_length() - Q_BITS - 1   # |a| / 2**s >= 2**Q_BITS > Q_MAX
-    assert abs(rne_int(a, s)) > Q_MAX
-    while abs(rne_int(a, s)) > Q_MAX:
+    qm = q_max(bits)
+    s = abs(a).bit_length() - bits - 1   # |a| / 2**s >= 2**bits > qm
+    assert abs(rne_int(a, s)) > qm
+    while abs(rne_int(a, s)) > qm:
         s += 1
     return eps + s
 
@@ -181,17 +192,18 @@ def _bitlen_np(m: np.ndarray) -> np.ndarray:
     return np.where(m == 0, 0, ex).astype(np.int64)
 
 
-def need_np(a: np.ndarray, eps) -> np.ndarray:
+def need_np(a: np.ndarray, eps, bits: int = Q_BITS) -> np.ndarray:
     """Vectorised need_int; entries with a == 0 get a very small sentinel."""
     a = np.asarray(a, dtype=np.int64)
     eps = np.broadcast_to(np.asarray(eps, dtype=np.int64), a.shape)
-    s = _bitlen_np(np.abs(a)) - Q_BITS - 1
+    qm = q_max(bits)
+    s = _bitlen_np(np.abs(a)) - bits - 1
     nz = a != 0
-    assert np.all(np.abs(rne_np(a[nz], s[nz])) > Q_MAX)
+    assert np.all(np.abs(rne_np(a[nz], s[nz])) > qm)
     bad = nz.copy()
     while np.any(bad):
         s = np.where(bad, s + 1, s)
-        bad = nz & (np.abs(rne_np(a, s)) > Q_MAX)
+        bad = nz & (np.abs(rne_np(a, s)) > qm)
     return np.where(nz, eps + s, np.int64(-(1 << 40)))
 
 
@@ -208,7 +220,7 @@ def group_exponent(needs) -> int:
     return e
 
 
-def requant_np(acc: np.ndarray, eps: np.ndarray, group: int) -> QT:
+def requant_np(acc: np.ndarray, eps: np.ndarray, group: int, bits: int = Q_BITS) -> QT:
     """Requantise exact values acc * 2**eps (int64, 2-D [rows x cols]).
 
     ROW: one exponent per row; TENSOR: one for the whole array.
@@ -216,7 +228,7 @@ def requant_np(acc: np.ndarray, eps: np.ndarray, group: int) -> QT:
     acc = np.asarray(acc, dtype=np.int64)
     eps = np.broadcast_to(np.asarray(eps, dtype=np.int64), acc.shape)
     assert acc.ndim == 2
-    nd = need_np(acc, eps)
+    nd = need_np(acc, eps, bits)
     if group == ROW:
         gmax = nd.max(axis=1) if acc.shape[1] else np.full(acc.shape[0], -(1 << 40))
         e = np.maximum(gmax, E_MIN)
@@ -231,11 +243,11 @@ def requant_np(acc: np.ndarray, eps: np.ndarray, group: int) -> QT:
             raise ExpRangeError(f"tensor exponent {e} > {E_MAX}")
         c = rne_np(acc, e - eps)
         eo = np.array([e])
-    assert np.all(np.abs(c) <= Q_MAX)
+    assert np.all(np.abs(c) <= q_max(bits))
     return QT(c.astype(np.int8), eo.astype(np.int8), group)
 
 
-def requant_frac(vals: list, group: int) -> tuple:
+def requant_frac(vals: list, group: int, bits: int = Q_BITS) -> tuple:
     """Requantise nested lists of exact Fractions (small inputs, reading R3).
 
     Returns (mantissa rows as lists of int, exponent list).  The group
@@ -244,7 +256,7 @@ def requant_frac(vals: list, group: int) -> tuple:
     groups = vals if group == ROW else [[v for row in vals for v in row]]
 
     def fits(g, e):
-        return all(abs(rne_frac(v / Fraction(2) ** e)) <= Q_MAX for v in g)
+        return all(abs(rne_frac(v / Fraction(2) ** e)) <= q_max(bits) for v in g)
 
     exps = []
     for g in groups:
@@ -308,10 +320,10 @@ def linear_fwd_acc(X: QT, W: QT):
     return acc, eps
 
 
-def linear_fwd(X: QT, W: QT, y_group: int) -> QT:
+def linear_fwd(X: QT, W: QT, y_group: int, bits: int = Q_BITS) -> QT:
     """Forward product Y = X . W^T requantised into y_group (Figure 1a)."""
     acc, eps = linear_fwd_acc(X, W)
-    return requant_np(acc, eps, y_group)
+    return requant_np(acc, eps, y_group, bits)
 
 
 def linear_bwd_dx_acc(dY: QT, W: QT):
@@ -322,10 +334,10 @@ def linear_bwd_dx_acc(dY: QT, W: QT):
     return acc, eps
 
 
-def linear_bwd_dx(dY: QT, W: QT, dx_group: int) -> QT:
+def linear_bwd_dx(dY: QT, W: QT, dx_group: int, bits: int = Q_BITS) -> QT:
     """Backward input gradient dX = dY . W (Figure 1a)."""
     acc, eps = linear_bwd_dx_acc(dY, W)
-    return requant_np(acc, eps, dx_group)
+    return requant_np(acc, eps, dx_group, bits)
 
 
 def linear_bwd_dw_acc(dY: QT, X: QT):
@@ -336,11 +348,11 @@ def linear_bwd_dw_acc(dY: QT, X: QT):
     return acc, np.full(acc.shape, e_dy + e_x, dtype=np.int64)
 
 
-def linear_bwd_dw(dY: QT, X: QT, dw_group: int) -> QT:
+def linear_bwd_dw(dY: QT, X: QT, dw_group: int, bits: int = Q_BITS) -> QT:
     """Backward weight gradient dW = dY^T . X (Figure 1a); per output channel
     groups for ROW (Table 5)."""
     acc, eps = linear_bwd_dw_acc(dY, X)
-    return requant_np(acc, eps, dw_group)
+    return requant_np(acc, eps, dw_group, bits)
 
 
 # ---------------------------------------------------------------------------
@@ -409,33 +421,33 @@ def conv_wgrad_acc(d: ConvShape, dy: np.ndarray, x: np.ndarray) -> np.ndarray:
     return acc
 
 
-def conv_fwd(d: ConvShape, X: QT, W: QT, y_group: int = TENSOR) -> QT:
+def conv_fwd(d: ConvShape, X: QT, W: QT, y_group: int = TENSOR, bits: int = Q_BITS) -> QT:
     """Y = conv(X, W): X NHWC TENSOR-grouped, W [K x RSC] TENSOR or ROW."""
     assert X.group == TENSOR
     acc = conv_fwd_acc(d, X.mant.reshape(d.n, d.h, d.w, d.c).astype(np.int64),
                        W.mant.reshape(d.k, d.r, d.s, d.c))
     eps = int(X.row_exp()[0]) + W.row_exp()[None, :]
-    out = requant_np(acc.reshape(-1, d.k), np.broadcast_to(eps, (acc.size // d.k, d.k)), y_group)
+    out = requant_np(acc.reshape(-1, d.k), np.broadcast_to(eps, (acc.size // d.k, d.k)), y_group, bits)
     return QT(out.mant.reshape(d.n, d.p, d.q, d.k), out.exp, y_group)
 
 
-def conv_dgrad(d: ConvShape, dY: QT, W: QT, dx_group: int = TENSOR) -> QT:
+def conv_dgrad(d: ConvShape, dY: QT, W: QT, dx_group: int = TENSOR, bits: int = Q_BITS) -> QT:
     """dX: W aligned over output channels (R5), then the exact adjoint."""
     assert dY.group == TENSOR
     w_al, e_w = align_rows(QT(W.mant.reshape(d.k, -1), W.exp, W.group))
     acc = conv_dgrad_acc(d, dY.mant.reshape(d.n, d.p, d.q, d.k), w_al.reshape(d.k, d.r, d.s, d.c))
     eps = int(dY.row_exp()[0]) + e_w
-    out = requant_np(acc.reshape(-1, d.c), np.full((acc.size // d.c, d.c), eps), dx_group)
+    out = requant_np(acc.reshape(-1, d.c), np.full((acc.size // d.c, d.c), eps), dx_group, bits)
     return QT(out.mant.reshape(d.n, d.h, d.w, d.c), out.exp, dx_group)
 
 
-def conv_wgrad(d: ConvShape, dY: QT, X: QT, dw_group: int = ROW) -> QT:
+def conv_wgrad(d: ConvShape, dY: QT, X: QT, dw_group: int = ROW, bits: int = Q_BITS) -> QT:
     """dW [K x RSC]: exact adjoint, per output channel groups (Table 5)."""
     assert dY.group == TENSOR and X.group == TENSOR
     acc = conv_wgrad_acc(d, dY.mant.reshape(d.n, d.p, d.q, d.k),
                          X.mant.reshape(d.n, d.h, d.w, d.c).astype(np.int64))
     eps = int(dY.row_exp()[0]) + int(X.row_exp()[0])
-    return requant_np(acc.reshape(d.k, -1), np.full((d.k, d.r * d.s * d.c), eps), dw_group)
+    return requant_np(acc.reshape(d.k, -1), np.full((d.k, d.r * d.s * d.c), eps), dw_group, bits)
 
 
 # ---------------------------------------------------------------------------
@@ -473,14 +485,14 @@ def exact_sum(terms):
     return num, base
 
 
-def requant_exact(num, base, group_of: np.ndarray, n_groups: int):
+def requant_exact(num, base, group_of: np.ndarray, n_groups: int, bits: int = Q_BITS):
     """Requantise exact values num * 2**base into groups (reading R3).
 
     group_of gives each element's group index.  Returns (int8 mantissas,
     int8 exponents per group).
     """
     if num.dtype != object:
-        nd = need_np(num, base)
+        nd = need_np(num, base, bits)
         gmax = np.full(n_groups, -(1 << 40), dtype=np.int64)
         np.maximum.at(gmax, group_of.reshape(-1), nd.reshape(-1))
         e = np.maximum(gmax, E_MIN)
@@ -493,7 +505,7 @@ def requant_exact(num, base, group_of: np.ndarray, n_groups: int):
         flat_g = group_of.reshape(-1)
         gmax = [E_MIN] * n_groups
         for i in range(flat_n.size):
-            nd = need_int(flat_n[i], flat_b[i])
+            nd = need_int(flat_n[i], flat_b[i], bits)
             if nd is not None and nd > gmax[flat_g[i]]:
                 gmax[flat_g[i]] = nd
         if max(gmax) > E_MAX:
@@ -501,7 +513,7 @@ def requant_exact(num, base, group_of: np.ndarray, n_groups: int):
         e = np.array(gmax, dtype=np.int64)
         c = np.array([rne_int(flat_n[i], int(e[flat_g[i]]) - int(flat_b[i]))
                       for i in range(flat_n.size)], dtype=np.int64).reshape(num.shape)
-    assert np.all(np.abs(c) <= Q_MAX)
+    assert np.all(np.abs(c) <= q_max(bits))
     return c.astype(np.int8), e.astype(np.int8)
 
 
@@ -518,7 +530,7 @@ def _group_index(t: QT) -> tuple:
 # Sum (Table 6 "Residual add, gradient merge -> Sum")
 # ---------------------------------------------------------------------------
 
-def sum_op(A: QT, B: QT, out_group: int) -> QT:
+def sum_op(A: QT, B: QT, out_group: int, bits: int = Q_BITS) -> QT:
     """Exact elementwise A + B, requantised once into out_group."""
     rows = A.mant.shape[0]
     per_row = int(np.prod(A.mant.shape[1:], dtype=np.int64))
@@ -531,7 +543,7 @@ def sum_op(A: QT, B: QT, out_group: int) -> QT:
         g, ng = np.repeat(np.arange(rows), ma.shape[1]).reshape(ma.shape), rows
     else:
         g, ng = np.zeros(ma.shape, dtype=np.int64), 1
-    c, e = requant_exact(num, base, g, ng)
+    c, e = requant_exact(num, base, g, ng, bits)
     return QT(c.reshape(A.mant.shape), e, out_group)
 
 
@@ -579,11 +591,12 @@ class Scalar:
 
 
 def sgd_update(W: QT, V: QT, G: QT, lr: Scalar, beta: Scalar,
-               wd: Scalar = Scalar(0, 0)) -> tuple:
+               wd: Scalar = Scalar(0, 0), w_bits: int = Q_BITS) -> tuple:
     """One integer SGD-with-momentum step on a [N x K] weight (reading R7).
 
     v_exact = beta*V + G (+ wd*W)        -> V' = requant over V's groups
     w_exact = W - lr*V'                  -> W' = requant over W's groups
+    W' takes w_bits of mantissa; V' is always INT8 (reading R8).
     Returns (W', V') as QT.
     """
     rows = W.mant.shape[0]
@@ -606,7 +619,7 @@ def sgd_update(W: QT, V: QT, G: QT, lr: Scalar, beta: Scalar,
     ev_new = np.broadcast_to(V_new.row_exp()[:, None], shp)
     num_w, base_w = exact_sum([(mw, ew), (-lr.mant * cv.astype(np.int64), ev_new + lr.exp)])
     gw, ngw = _group_index(QT(mw, W.exp, W.group))
-    cw, e_w = requant_exact(num_w, base_w, gw, ngw)
+    cw, e_w = requant_exact(num_w, base_w, gw, ngw, w_bits)
     W_new = QT(cw.reshape(W.mant.shape), e_w, W.group)
     return W_new, V_new
 
@@ -625,22 +638,23 @@ def relu_bwd(dY: np.ndarray, C: np.ndarray) -> np.ndarray:
     return np.where(np.asarray(C) > 0, np.asarray(dY, dtype=np.int64), 0)
 
 
-def relu6_cap(e: int) -> int:
+def relu6_cap(e: int, bits: int = Q_BITS) -> int:
     """c = min(6 >> e, q_max), reading 6 >> e as 6 * 2**-e rounded down
-    (a right shift for e > 0, a left shift for e < 0)."""
-    v = 6 >> e if e >= 0 else 6 << (-e)
-    return min(v, Q_MAX)
+    (a right shift for e > 0, a left shift for e < 0); q_max is that of the
+    activation's mantissa width (reading R8)."""
+    v = 6 >> e if e >= 0 else 6 << min(-e, 8)
+    return min(v, q_max(bits))
 
 
-def relu6_fwd(C: np.ndarray, e: int) -> np.ndarray:
-    """clip(C, 0, c) with c = relu6_cap(e) (Table 7)."""
-    return np.clip(np.asarray(C, dtype=np.int64), 0, relu6_cap(e))
+def relu6_fwd(C: np.ndarray, e: int, bits: int = Q_BITS) -> np.ndarray:
+    """clip(C, 0, c) with c = relu6_cap(e, bits) (Table 7)."""
+    return np.clip(np.asarray(C, dtype=np.int64), 0, relu6_cap(e, bits))
 
 
-def relu6_bwd(dY: np.ndarray, C: np.ndarray, e: int) -> np.ndarray:
+def relu6_bwd(dY: np.ndarray, C: np.ndarray, e: int, bits: int = Q_BITS) -> np.ndarray:
     """dY * 1[0 < C < c] (Table 7)."""
     C = np.asarray(C)
-    c = relu6_cap(e)
+    c = relu6_cap(e, bits)
     return np.where((C > 0) & (C < c), np.asarray(dY, dtype=np.int64), 0)
 
 
