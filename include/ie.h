@@ -55,7 +55,8 @@ typedef enum {
     IE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     IE_ERR_EXP_RANGE = 5,   /* reported by ie_device_status callers */
     IE_ERR_UNSUPPORTED = 6, /* valid but outside what this build supports */
-    IE_ERR_HIP = 7          /* a HIP runtime call failed */
+    IE_ERR_HIP = 7,         /* a HIP runtime call failed */
+    IE_ERR_BITS = 8         /* ie_mat.bits outside {0, 2..8}, or a velocity not INT8 */
 } ie_status;
 
 typedef enum { IE_GROUP_TENSOR = 0, IE_GROUP_ROW = 1 } ie_group;
@@ -63,13 +64,22 @@ typedef enum { IE_GROUP_TENSOR = 0, IE_GROUP_ROW = 1 } ie_group;
 #define IE_FLAG_EXP_RANGE 1u
 
 /* A (C, e) matrix.  mant: rows*cols bytes, row-major.  exp: 1 byte (TENSOR)
- * or `rows` bytes (ROW). */
+ * or `rows` bytes (ROW).
+ * bits: the mantissa width B ("Memory-Efficient Integer-Only Training of Deep
+ * Neural Networks", Table 4: INT8 down to INT4), 2..8, with 0 read as 8.
+ * Every step that rounds into this matrix rounds to |C| <= 2^(B-1) - 1
+ * (its group exponent is the smallest that fits), and ReLU6's cap on an
+ * activation is at most 2^(B-1) - 1.  Mantissas are stored one per byte
+ * whatever B is, and inputs are read as the bytes they hold, so B matters
+ * only on outputs and on ReLU6's activation.  The velocity of
+ * ie_sgd_update must be INT8 (0 or 8). */
 typedef struct {
     int8_t *mant;
     int8_t *exp;
     int64_t rows;
     int64_t cols;
     int32_t group;
+    int32_t bits;
 } ie_mat;
 
 /* Convolution shape: input NHWC [n, h, w, c], weight [k, r, s, c], zero
@@ -162,6 +172,8 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
  * decay term uses W before the step; Table 10 lists weight decay 1e-4, e.g.
  * (1, -13)), and the weight step uses the stored, rounded V.  W, V, G:
  * [rows x cols], each TENSOR or ROW.  weight_decay.mant == 0: no decay term.
+ * W' rounds to W's mantissa width (W->bits); V is always INT8 (Table 4's
+ * B-bit variants keep the velocity INT8), else IE_ERR_BITS.
  */
 ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G,
                         ie_scalar lr, ie_scalar momentum, ie_scalar weight_decay,
@@ -196,15 +208,17 @@ ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *
  * ReLU and ReLU6 of a (C, e) tensor (Table 7, "Clip activations"), on the
  * mantissas; the exponents are copied:
  *   relu:  Y.C = max(X.C, 0)
- *   relu6: Y.C = min(max(X.C, 0), c6),  c6 = min(floor(6 * 2^-e), 127)
- * with e the element's group exponent (6 expressed in the group's units).
- * X, Y: same shape and group.  Y may be X (in place).  relu6: 0 or 1.
+ *   relu6: Y.C = min(max(X.C, 0), c6),  c6 = min(floor(6 * 2^-e), 2^(B-1) - 1)
+ * with e the element's group exponent (6 expressed in the group's units) and
+ * B the width of Y.  X, Y: same shape and group.  Y may be X (in place).
+ * relu6: 0 or 1.
  */
 ie_status ie_relu_fwd(const ie_mat *X, const ie_mat *Y, int relu6, void *stream);
 
 /*
  * Backward of ie_relu_fwd (Table 7): dX.C = dY.C where the forward output
- * Y.C > 0 (and Y.C < c6 of Y's group for relu6), else 0; dX.exp = dY.exp.
+ * Y.C > 0 (and Y.C < c6 of Y's group and width for relu6), else 0;
+ * dX.exp = dY.exp.
  * dY, Y, dX: same shape; dX has dY's group.  dX may be dY (in place).
  */
 ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int relu6, void *stream);

@@ -43,8 +43,12 @@ ie_status check_mat(const ie_mat *t) {
     if (t->rows < 0 || t->cols < 0 || t->rows > DIM_MAX || t->cols > DIM_MAX) return IE_ERR_SHAPE;
     if (t->rows * t->cols > 0 && !t->mant) return IE_ERR_NULL;
     if ((t->group == IE_GROUP_TENSOR || t->rows > 0) && !t->exp) return IE_ERR_NULL;
+    if (t->bits != 0 && (t->bits < 2 || t->bits > 8)) return IE_ERR_BITS;
     return IE_OK;
 }
+
+// Mantissa width as q: a result of t has |C| <= 2^q - 1 (bits 0 reads as 8).
+int mat_q(const ie_mat *t) { return (t->bits ? t->bits : 8) - 1; }
 
 ie_status hip_status(hipError_t e) { return e == hipSuccess ? IE_OK : IE_ERR_HIP; }
 
@@ -225,6 +229,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     ep.out_exp = out->exp;
     ep.flags = flags;
     ep.relu = relu;
+    ep.q = mat_q(out);
     if (pl.mode == PLAN_DIRECT) {
         ep.mode = EPI_DIRECT;
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
@@ -243,13 +248,14 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     if (rg && split_round_rows_fits((int)N, 1, 1)) {
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
         IE_TRY(launch_split_round_rows(pw.partial, pl.splits, M * N, (int)M, (int)N, (int)N, 1, 1, ea, eb, out->mant,
-                                       out->exp, flags, st, relu));
+                                       out->exp, flags, mat_q(out), st, relu));
         return IE_OK;
     }
     ep.gneed = pw.gneed;
     ep.gneed_n = rg ? (int)M : 1;
     IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
-    IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed, st));
+    IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed,
+                                 mat_q(out), st));
     IE_TRY(launch_round_sums(pw.sums, (int)M, (int)N, (int)N, 1, 1, ea, eb, rg, pw.gneed, out->mant, out->exp, flags,
                              st, relu));
     return IE_OK;
@@ -290,6 +296,7 @@ ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K
     ep.partial = w.partial;
     ep.split_stride = N * Kg;
     ep.flags = flags;
+    ep.q = mat_q(dW);
     ep.gneed = w.gneed;
     ep.gneed_n = fused ? 0 : rg ? (int)N : 1;
     int splits = pl.splits;
@@ -302,10 +309,11 @@ ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K
     }
     if (fused) {
         IE_TRY(launch_split_round_rows(w.partial, splits, N * Kg, (int)N, (int)Kout, (int)Kg, mc, mcp, ea, eb,
-                                       dW->mant, dW->exp, flags, st));
+                                       dW->mant, dW->exp, flags, mat_q(dW), st));
         return IE_OK;
     }
-    IE_TRY(launch_partial_reduce(w.partial, splits, N * Kg, (int)N, (int)Kg, ea, eb, rg, w.sums, w.gneed, st));
+    IE_TRY(launch_partial_reduce(w.partial, splits, N * Kg, (int)N, (int)Kg, ea, eb, rg, w.sums, w.gneed,
+                                 mat_q(dW), st));
     IE_TRY(launch_round_sums(w.sums, (int)N, (int)Kout, (int)Kg, mc, mcp, ea, eb, rg, w.gneed, dW->mant, dW->exp,
                              flags, st));
     return IE_OK;
@@ -504,6 +512,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const ie_mat *W, con
     e1.mode = EPI_RTO;
     e1.v16 = pw.v16;
     e1.p16 = pw.p16;
+    e1.q = mat_q(dX);
     Epi e2;
     memset(&e2, 0, sizeof e2);
     e2.partial = w.partial;
@@ -511,11 +520,12 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const ie_mat *W, con
     e2.flags = flags;
     e2.gneed = w.gneed;
     e2.gneed_n = 0;
+    e2.q = mat_q(dW);
     IE_TRY(launch_gemm_pair(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
                             (int)npq, p2.t, p2.splits, p2.k_chunk, e2, st));
     IE_TRY(launch_finalize_pair(pw.v16, pw.p16, (int)nhw, g.c, p1.t, dX->mant, dX->exp, w.partial, p2.splits,
                                 g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex, dW->mant, dW->exp, flags,
-                                st));
+                                mat_q(dW), st));
     return IE_OK;
 }
 
@@ -524,6 +534,7 @@ ie_status check_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(V));
     IE_CHECK(check_mat(G));
+    if (mat_q(V) != 7) return IE_ERR_BITS;  // the velocity is INT8 at every weight width
     if (V->rows != W->rows || V->cols != W->cols || G->rows != W->rows || G->cols != W->cols)
         return IE_ERR_SHAPE;
     if (W->cols > 64 * 4 * 32) return IE_ERR_UNSUPPORTED;
@@ -550,6 +561,7 @@ UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
     a.mom_e = momentum.exp;
     a.wd_m = weight_decay.mant;
     a.wd_e = weight_decay.exp;
+    a.w_q = mat_q(W);
     a.tmp = tmp;
     a.flags = (uint32_t *)ws;
     return a;
@@ -888,7 +900,7 @@ ie_status ie_relu_fwd(const ie_mat *X, const ie_mat *Y, int relu6, void *stream)
     if (X->group != Y->group) return IE_ERR_GROUP;
     if (relu6 != 0 && relu6 != 1) return IE_ERR_SHAPE;
     return hip_status(launch_relu_fwd(X->mant, X->exp, X->group == IE_GROUP_ROW, Y->mant, Y->exp, X->rows, X->cols,
-                                      relu6, (hipStream_t)stream));
+                                      relu6, mat_q(Y), (hipStream_t)stream));
 }
 
 ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int relu6, void *stream) {
@@ -900,7 +912,7 @@ ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int r
     if (relu6 != 0 && relu6 != 1) return IE_ERR_SHAPE;
     return hip_status(launch_relu_bwd(dY->mant, dY->exp, dY->group == IE_GROUP_ROW, Y->mant, Y->exp,
                                       Y->group == IE_GROUP_ROW, dX->mant, dX->exp, dY->rows, dY->cols, relu6,
-                                      (hipStream_t)stream));
+                                      mat_q(Y), (hipStream_t)stream));
 }
 
 size_t ie_add_workspace(int64_t rows, int64_t cols) {
@@ -920,7 +932,7 @@ ie_status ie_add(const ie_mat *A, const ie_mat *B, const ie_mat *Z, void *ws, si
     int *bmax = c.take<int>(ADD_MAX_BLOCKS);
     return hip_status(launch_add(A->mant, A->exp, A->group == IE_GROUP_ROW, B->mant, B->exp,
                                  B->group == IE_GROUP_ROW, Z->mant, Z->exp, Z->group == IE_GROUP_ROW, A->rows,
-                                 A->cols, bmax, (uint32_t *)ws, (hipStream_t)stream));
+                                 A->cols, bmax, (uint32_t *)ws, mat_q(Z), (hipStream_t)stream));
 }
 
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {
@@ -957,6 +969,7 @@ const char *ie_status_str(ie_status s) {
         case IE_ERR_EXP_RANGE: return "IE_ERR_EXP_RANGE";
         case IE_ERR_UNSUPPORTED: return "IE_ERR_UNSUPPORTED";
         case IE_ERR_HIP: return "IE_ERR_HIP";
+        case IE_ERR_BITS: return "IE_ERR_BITS";
     }
     return "IE_ERR_UNKNOWN";
 }

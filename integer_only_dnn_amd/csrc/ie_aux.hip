@@ -499,7 +499,7 @@ hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, in
 __global__ __launch_bounds__(256) void partial_reduce_kernel(const int *partial, int splits, long long stride,
                                                              int M, int N, ExpSrc ea, ExpSrc eb, int row_group,
                                                              long long *sums, int *gneed, int vw,
-                                                             FastDiv dper) {
+                                                             FastDiv dper, int wq) {
     __shared__ long long sh[3][64][4];
     const uint32_t per_row = N / vw;
     const uint32_t total = (uint32_t)M * per_row;
@@ -552,11 +552,11 @@ __global__ __launch_bounds__(256) void partial_reduce_kernel(const int *partial,
                     so[1] = s1;
                     so[2] = s2;
                     so[3] = s3;
-                    m = max(max(need64(s0, er + exp_at(eb, c0)), need64(s1, er + exp_at(eb, c0 + 1))),
-                            max(need64(s2, er + exp_at(eb, c0 + 2)), need64(s3, er + exp_at(eb, c0 + 3))));
+                    m = max(max(need64(s0, er + exp_at(eb, c0), wq), need64(s1, er + exp_at(eb, c0 + 1), wq)),
+                            max(need64(s2, er + exp_at(eb, c0 + 2), wq), need64(s3, er + exp_at(eb, c0 + 3), wq)));
                 } else {
                     sums[o] = s0;
-                    m = need64(s0, er + exp_at(eb, c0));
+                    m = need64(s0, er + exp_at(eb, c0), wq);
                 }
             }
             // wave 0 (all 64 lanes) reduces its chunks: rows of consecutive
@@ -692,7 +692,7 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
                                                                  int8_t *out_exp, uint32_t *flags, int vw, int Q, int relu,
-                                                                 int bid, int nblk) {
+                                                                 int wq, int bid, int nblk) {
     // short rows (THR == SR_THR_SHORT) hold at most one chunk per thread
     constexpr int MAXV = THR == SR_THR_SHORT ? 1 : SR_MAXV;
     __shared__ int sh[THR / 64];
@@ -746,7 +746,7 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
                 v[0][3] = a3;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (j < vw) need = max(need, need64(v[0][j], eps(vw * tid + j)));
+                    if (j < vw) need = max(need, need64(v[0][j], eps(vw * tid + j), wq));
             }
         } else {
             if (vw == 4 && splits <= SR_FEW) {
@@ -769,7 +769,7 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
 #pragma unroll
                         for (int z = 0; z < SR_FEW; ++z) a += x[k][z][j];
                         v[k][j] = a;
-                        if (c < nch) need = max(need, need64(a, eps(4 * c + j)));
+                        if (c < nch) need = max(need, need64(a, eps(4 * c + j), wq));
                     }
                 }
             } else {
@@ -782,7 +782,7 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
                         else sum_splits<1>(prow + src_col(c), stride, 0, 1, splits, v[k]);
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            if (j < vw) need = max(need, need64(v[k][j], eps(vw * c + j)));
+                            if (j < vw) need = max(need, need64(v[k][j], eps(vw * c + j), wq));
                     }
                 }
             }
@@ -816,9 +816,9 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void s
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
                                                                  int8_t *out_exp, uint32_t *flags, int vw, int Q,
-                                                                 int relu) {
+                                                                 int relu, int wq) {
     split_round_body<THR>(partial, splits, stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q,
-                          relu, blockIdx.x, gridDim.x);
+                          relu, wq, blockIdx.x, gridDim.x);
 }
 
 bool split_round_rows_fits(int Nout, int mc, int mcp) {
@@ -839,10 +839,12 @@ struct SplitFin {
     int vw, Q, blocks;
     bool shortrow;
     int relu;
+    int wq;  // results have |C| <= 2^wq - 1
 };
 
 static SplitFin split_fin(const int *partial, int splits, long long split_stride, int M, int Nout, int src_pitch,
-                          int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out, int8_t *out_exp, uint32_t *flags) {
+                          int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out, int8_t *out_exp, uint32_t *flags,
+                          int wq) {
     SplitFin f;
     f.partial = partial;
     f.splits = splits;
@@ -869,24 +871,25 @@ static SplitFin split_fin(const int *partial, int splits, long long split_stride
     f.blocks = blocks_for(M, 1, 16384);
     f.dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
     f.relu = 0;
+    f.wq = wq;
     return f;
 }
 
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu) {
+                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, int relu) {
     if (M <= 0 || Nout <= 0) return hipSuccess;
     const SplitFin f = split_fin(partial, splits, split_stride, M, Nout, src_pitch, mc, mcp, ea, eb, out, out_exp,
-                                 flags);
+                                 flags, q);
     prof_begin(st, PROF_SPLIT_ROUND);
     if (f.shortrow)
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, dim3(f.blocks), dim3(SR_THR_SHORT), 0, st,
                            f.partial, f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb,
-                           f.out, f.out_exp, f.flags, f.vw, f.Q, relu);
+                           f.out, f.out_exp, f.flags, f.vw, f.Q, relu, f.wq);
     else
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, dim3(f.blocks), dim3(SR_THR), 0, st, f.partial,
                            f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb, f.out,
-                           f.out_exp, f.flags, f.vw, f.Q, relu);
+                           f.out_exp, f.flags, f.vw, f.Q, relu, f.wq);
     prof_end(st, PROF_SPLIT_ROUND);
     return hipGetLastError();
 }
@@ -904,7 +907,7 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void f
                           r.flags, r.vw, r.dper, r.relu, blockIdx.x, r.blocks);
     } else {
         split_round_body<THR>(q.partial, q.splits, q.stride, q.M, q.Nout, q.src_pitch, q.mc, q.mcp, q.dmc, q.ea,
-                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, q.relu, blockIdx.x - r.blocks,
+                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, q.relu, q.wq, blockIdx.x - r.blocks,
                               gridDim.x - r.blocks);
     }
 }
@@ -912,16 +915,16 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void f
 hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
                                 int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
                                 int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
-                                int8_t *out2_exp, uint32_t *flags, hipStream_t st) {
+                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st) {
     if (M1 <= 0 || N1 <= 0 || M2 <= 0 || Nout <= 0) {
         hipError_t e = launch_rto_finalize(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags, st);
         if (e != hipSuccess) return e;
         return launch_split_round_rows(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2,
-                                       out2_exp, flags, st);
+                                       out2_exp, flags, q2, st);
     }
     const RtoFin r = rto_fin(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags);
     const SplitFin q = split_fin(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2, out2_exp,
-                                 flags);
+                                 flags, q2);
     const dim3 grid(r.blocks + q.blocks);
     prof_begin(st, PROF_FIN_PAIR);
     if (q.shortrow)
@@ -933,7 +936,7 @@ hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, 
 }
 
 hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
-                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
+                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed, int q,
                                  hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int vw = (N % 4 == 0) ? 4 : 1;
@@ -941,7 +944,7 @@ hipError_t launch_partial_reduce(const int *partial, int splits, long long split
     prof_begin(st, PROF_PARTIAL_REDUCE);
     hipLaunchKernelGGL(partial_reduce_kernel, dim3(blocks_for(total, 64, 8192)), dim3(256), 0, st, partial,
                        splits, split_stride, M, N, ea, eb, row_group, sums, gneed, vw,
-                       make_fastdiv((uint32_t)(N / vw)));
+                       make_fastdiv((uint32_t)(N / vw)), q);
     prof_end(st, PROF_PARTIAL_REDUCE);
     return hipGetLastError();
 }

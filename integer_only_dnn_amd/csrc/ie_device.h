@@ -22,30 +22,31 @@ constexpr int NEED_NONE = -(1 << 28);
 // Sentinel provisional exponent of an all-zero row tile (fits int16).
 constexpr int P_NONE = -30000;
 
-// Smallest s with |rne(m / 2^s)| <= 127, for m = |a| > 0 (32-bit).
-// With b the bit length of m and t the top 8 bits of m (m normalised), the
-// answer is b - 7, plus one when t == 255 (m / 2^(b-7) >= 127.5 rounds to 128).
-__device__ __forceinline__ int mant_shift32(uint32_t m) {
+// Smallest s with |rne(m / 2^s)| <= 2^q - 1 (q = B - 1 for a B-bit mantissa,
+// 7 for INT8), for m = |a| > 0 (32-bit).  With b the bit length of m, the
+// answer is b - q, plus one when the top q + 1 bits of m are all ones
+// (m / 2^(b-q) >= 2^q - 0.5 rounds up to 2^q).
+__device__ __forceinline__ int mant_shift32(uint32_t m, int q = 7) {
     int z = __clz(m);
-    uint32_t top = (m << z) >> 24;
-    return 25 - z + (top == 255u ? 1 : 0);
+    uint32_t top = (m << z) >> (31 - q);
+    return 32 - z - q + (top == (2u << q) - 1u ? 1 : 0);
 }
 
-__device__ __forceinline__ int mant_shift64(uint64_t m) {
+__device__ __forceinline__ int mant_shift64(uint64_t m, int q = 7) {
     int z = __clzll(m);
-    uint32_t top = (uint32_t)((m << z) >> 56);
-    return 57 - z + (top == 255u ? 1 : 0);
+    uint32_t top = (uint32_t)((m << z) >> (63 - q));
+    return 64 - z - q + (top == (2u << q) - 1u ? 1 : 0);
 }
 
 // Smallest exponent for the exact value a * 2^eps; NEED_NONE when a == 0.
-__device__ __forceinline__ int need32(int a, int eps) {
+__device__ __forceinline__ int need32(int a, int eps, int q = 7) {
     uint32_t m = (uint32_t)(a < 0 ? -a : a);
-    return m ? eps + mant_shift32(m) : NEED_NONE;
+    return m ? eps + mant_shift32(m, q) : NEED_NONE;
 }
 
-__device__ __forceinline__ int need64(long long a, int eps) {
+__device__ __forceinline__ int need64(long long a, int eps, int q = 7) {
     uint64_t m = (uint64_t)(a < 0 ? -a : a);
-    return m ? eps + mant_shift64(m) : NEED_NONE;
+    return m ? eps + mant_shift64(m, q) : NEED_NONE;
 }
 
 // a * 2^-s rounded half to even, |a| < 2^30.  s <= 0 is an exact left shift

@@ -885,6 +885,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
 #pragma unroll
         for (int b = 0; b < NI; ++b) ebv[b] = seB[TC(b)];
         const bool uni = !ep.ea.row && !ep.eb.row;
+        const int wq = ep.q;  // results have |C| <= 2^wq - 1
         const int ea0 = seA[0];
         const int eb0 = seB[0];
         const bool direct = ep.mode == EPI_DIRECT;
@@ -906,7 +907,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                             lo = min(lo, min(acc[a][b][r], acc[a][b][r + 1]));
                         }
                 const uint32_t mx = max((uint32_t)hi, 0u - (uint32_t)lo);
-                tmax = mx ? ea0 + eb0 + mant_shift32(mx) : NEED_NONE;
+                tmax = mx ? ea0 + eb0 + mant_shift32(mx, wq) : NEED_NONE;
             } else {
                 tmax = NEED_NONE;
 #pragma unroll
@@ -915,7 +916,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                     for (int r = 0; r < 16; ++r) {
                         const int eav = seA[TR(a, r)];
 #pragma unroll
-                        for (int b = 0; b < NI; ++b) tmax = max(tmax, need32(acc[a][b][r], eav + ebv[b]));
+                        for (int b = 0; b < NI; ++b) tmax = max(tmax, need32(acc[a][b][r], eav + ebv[b], wq));
                     }
             }
             tmax = wave_max(tmax);
@@ -1039,7 +1040,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                         const int eav = seA[TR(a, r)];
                         int m = NEED_NONE;
 #pragma unroll
-                        for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b]));
+                        for (int b = 0; b < NI; ++b) m = max(m, need32(acc[a][b][r], eav + ebv[b], wq));
                         key[r] = m;
                     }
                 }
@@ -1061,8 +1062,10 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                 int rm, s = 0;
                 if (fpath) {
                     // need of m = |acc| 2^(eb - ebmin) from its fp32 exponent and top
-                    // mantissa bits: bit length - 7, plus one at 255 * 2^(len - 8)
-                    s = ((kmax >> 23) - 127) - 6 + (((kmax >> 16) & 0x7f) == 0x7f);
+                    // mantissa bits: bit length - wq, plus one when the top wq + 1
+                    // bits are all ones (m at or above (2^(wq+1) - 1) 2^(len - wq - 1))
+                    const int ones = (1 << wq) - 1;
+                    s = ((kmax >> 23) - 127) - (wq - 1) + (((kmax >> (23 - wq)) & ones) == ones);
                     rm = kmax == 0 ? NEED_NONE : eav + ebmin + s;
                 } else {
                     rm = kmax;

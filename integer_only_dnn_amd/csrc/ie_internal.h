@@ -47,6 +47,7 @@ struct Epi {
     long long split_stride;
     uint32_t *flags;
     int relu;         // int8 results pass through ReLU (forward products)
+    int q;            // results have |C| <= 2^q - 1 (mantissa width q + 1 bits)
 };
 
 enum LoaderKind {
@@ -169,7 +170,7 @@ hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, in
 // group maxima (set empty by the split kernel, or by launch_fill_i32 when no
 // split kernel ran); then round the sums into int8.
 hipError_t launch_partial_reduce(const int *partial, int splits, long long split_stride, int M, int N,
-                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed,
+                                 ExpSrc ea, ExpSrc eb, int row_group, long long *sums, int *gneed, int q,
                                  hipStream_t st);
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
@@ -180,14 +181,14 @@ hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch,
 bool split_round_rows_fits(int Nout, int mc, int mcp);
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu = 0);
+                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, int relu = 0);
 // A round-to-odd finalize (whole-tensor group, M1 x N1 from tile t1) and a
 // split finalize by rows (the arguments of launch_split_round_rows) in one
 // launch.
 hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
                                 int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
                                 int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
-                                int8_t *out2_exp, uint32_t *flags, hipStream_t st);
+                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st);
 hipError_t launch_zero_flags(void *ws, hipStream_t st);
 
 // Integer SGD update (ie_update.hip).
@@ -199,6 +200,7 @@ struct UpdateArgs {
     long long rows, cols;
     int lr_m, lr_e, mom_m, mom_e;
     int wd_m, wd_e;    // weight decay (C, e); wd_m == 0: none
+    int w_q;           // new weights have |C| <= 2^w_q - 1 (the velocity: 127)
     int *tmp;          // [UPD_WS_INTS]: exponent snapshots, per-block maxima
     uint32_t *flags;
 };
@@ -211,13 +213,14 @@ hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st);
 // Pointwise steps (ie_pointwise.hip).  Whole-tensor sums keep one int per
 // block in `bmax` (at most ADD_MAX_BLOCKS).
 constexpr int ADD_MAX_BLOCKS = 1024;
+// relu6: the cap is min(6 * 2^-e, 2^q - 1) with q from the activation's width.
 hipError_t launch_relu_fwd(const int8_t *x, const int8_t *xe, int x_row, int8_t *y, int8_t *ye, long long rows,
-                           long long cols, int relu6, hipStream_t st);
+                           long long cols, int relu6, int q, hipStream_t st);
 hipError_t launch_relu_bwd(const int8_t *dy, const int8_t *dye, int dy_row, const int8_t *yc, const int8_t *ye,
-                           int y_row, int8_t *dx, int8_t *dxe, long long rows, long long cols, int relu6,
+                           int y_row, int8_t *dx, int8_t *dxe, long long rows, long long cols, int relu6, int q,
                            hipStream_t st);
 hipError_t launch_add(const int8_t *a, const int8_t *ae, int a_row, const int8_t *b, const int8_t *be, int b_row,
                       int8_t *z, int8_t *ze, int z_row, long long rows, long long cols, int *bmax, uint32_t *flags,
-                      hipStream_t st);
+                      int q, hipStream_t st);
 
 }  // namespace ie

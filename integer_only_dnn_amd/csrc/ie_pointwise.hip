@@ -3,22 +3,23 @@
 // activations"):
 //   - ReLU / ReLU6 forward act on the mantissas alone (the exponent is kept):
 //     max(C, 0), and for ReLU6 min(., c6) with c6 = floor(6 * 2^-e) capped at
-//     127 for the element's group exponent e;
+//     the activation's largest mantissa 2^q - 1 (127 for INT8), e the
+//     element's group exponent;
 //   - their backward passes mask the incoming gradient's mantissas where the
 //     forward output was clipped (dY's exponents are kept);
 //   - Sum is the exact elementwise A + B, rounded once (half to even) into
-//     the output's groups.
+//     the output's groups and its mantissa width (|C| <= 2^q - 1).
 // All three are HBM-bound streams: one 16-byte chunk per thread and trip.
 #include "ie_device.h"
 #include "ie_internal.h"
 
 namespace ie {
 
-// floor(6 * 2^-e), at most 127
-__device__ __forceinline__ int relu6_cap(int e) {
+// floor(6 * 2^-e), at most 2^q - 1 (q <= 7)
+__device__ __forceinline__ int relu6_cap(int e, int q) {
     if (e >= 3) return 0;
-    if (e >= 0) return 6 >> e;
-    return -e >= 5 ? 127 : (6 << -e);
+    const int c = e >= 0 ? 6 >> e : (-e >= 5 ? 192 : 6 << -e);
+    return min(c, (1 << q) - 1);
 }
 
 // Walks the bytes of one 16-byte chunk of a row-major [rows x cols] buffer
@@ -74,7 +75,7 @@ __device__ __forceinline__ void copy_exps(const int8_t *src, int8_t *dst, long l
 
 __global__ __launch_bounds__(256) void relu_fwd_kernel(const int8_t *x, const int8_t *xe, int x_row, int8_t *y,
                                                        int8_t *ye, long long rows, long long cols, int relu6,
-                                                       int vec) {
+                                                       int q, int vec) {
     const long long total = rows * cols;
     copy_exps(xe, ye, x_row ? rows : 1);
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
@@ -87,9 +88,9 @@ __global__ __launch_bounds__(256) void relu_fwd_kernel(const int8_t *x, const in
         } else {
             RowWalk rw;
             rw.start(f0, cols);
-            const int cap_t = relu6_cap(xe[0]);
+            const int cap_t = relu6_cap(xe[0], q);
             for (int j = 0; j < 16 && f0 + j < total; ++j) {
-                const int cap = x_row ? relu6_cap(xe[rw.at(f0 + j)]) : cap_t;
+                const int cap = x_row ? relu6_cap(xe[rw.at(f0 + j)], q) : cap_t;
                 set_byte(v, j, min(max(byte_at(v, j), 0), cap));
             }
         }
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void relu_fwd_kernel(const int8_t *x, const in
 __global__ __launch_bounds__(256) void relu_bwd_kernel(const int8_t *dy, const int8_t *dye, int dy_row,
                                                        const int8_t *yc, const int8_t *ye, int y_row, int8_t *dx,
                                                        int8_t *dxe, long long rows, long long cols, int relu6,
-                                                       int vec) {
+                                                       int q, int vec) {
     const long long total = rows * cols;
     copy_exps(dye, dxe, dy_row ? rows : 1);
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i * 16 < total;
@@ -122,9 +123,9 @@ __global__ __launch_bounds__(256) void relu_bwd_kernel(const int8_t *dy, const i
         } else {
             RowWalk rw;
             rw.start(f0, cols);
-            const int cap_t = relu6_cap(ye[0]);
+            const int cap_t = relu6_cap(ye[0], q);
             for (int j = 0; j < 16 && f0 + j < total; ++j) {
-                const int cap = y_row ? relu6_cap(ye[rw.at(f0 + j)]) : cap_t;
+                const int cap = y_row ? relu6_cap(ye[rw.at(f0 + j)], q) : cap_t;
                 const int cv = byte_at(c, j);
                 if (!(cv > 0 && cv < cap)) set_byte(g, j, 0);
             }
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void relu_bwd_kernel(const int8_t *dy, const i
 // Sum.  X * 2^pa + Y * 2^pb with |X|, |Y| <= 128 as n * 2^base: exact for
 // exponent gaps up to 30; above, the smaller term (below 2^(P-23), P the
 // larger exponent) only decides ties and sticky bits at every exponent the
-// result can take (at least P - 7), so it is replaced by its sign at
+// result can take (at least P - 7 at any width), so it is replaced by its sign at
 // 2^(P-23), which rounds identically.
 // ---------------------------------------------------------------------------
 
@@ -181,6 +182,7 @@ struct AddArgs {
     long long rows, cols;
     int *bmax;  // [gridDim.x] block maxima (whole-tensor output)
     uint32_t *flags;
+    int q;      // results have |C| <= 2^q - 1
     int vec;
 };
 
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(256) void add_need_kernel(AddArgs p) {
             }
         }
         const uint32_t mx = max((uint32_t)hi, 0u - (uint32_t)lo);
-        m = mx ? u.base + mant_shift32(mx) : NEED_NONE;
+        m = mx ? u.base + mant_shift32(mx, p.q) : NEED_NONE;
         m = block_max_256(m, sh);
         if (threadIdx.x == 0) p.bmax[blockIdx.x] = m;
         return;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void add_need_kernel(AddArgs p) {
             long long n;
             int base;
             sum2(byte_at(va, j), p.ae[p.a_row ? r : 0], byte_at(vb, j), p.be[p.b_row ? r : 0], n, base);
-            m = max(m, need64(n, base));
+            m = max(m, need64(n, base, p.q));
         }
     }
     m = block_max_256(m, sh);
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(256) void add_rows_kernel(AddArgs p) {
             long long n;
             int base;
             sum2(ra[c], ea, rb[c], eb, n, base);
-            m = max(m, need64(n, base));
+            m = max(m, need64(n, base, p.q));
         }
         m = block_max_256(m, sh);
         const int e = clamp_exp_flag(max(E_MIN, m), p.flags);
@@ -344,34 +346,34 @@ static int vec16(const void *a, const void *b, const void *c) {
 }
 
 hipError_t launch_relu_fwd(const int8_t *x, const int8_t *xe, int x_row, int8_t *y, int8_t *ye, long long rows,
-                           long long cols, int relu6, hipStream_t st) {
+                           long long cols, int relu6, int q, hipStream_t st) {
     const long long chunks = (rows * cols + 15) / 16;
     const int n_e = x_row ? (int)rows : 1;
     if (chunks == 0 && n_e == 0) return hipSuccess;
     prof_begin(st, PROF_RELU_FWD);
     hipLaunchKernelGGL(relu_fwd_kernel, dim3(grid_for(chunks, 4096)), dim3(256), 0, st, x, xe, x_row, y, ye, rows,
-                       cols, relu6, vec16(x, y, y));
+                       cols, relu6, q, vec16(x, y, y));
     prof_end(st, PROF_RELU_FWD);
     return hipGetLastError();
 }
 
 hipError_t launch_relu_bwd(const int8_t *dy, const int8_t *dye, int dy_row, const int8_t *yc, const int8_t *ye,
-                           int y_row, int8_t *dx, int8_t *dxe, long long rows, long long cols, int relu6,
+                           int y_row, int8_t *dx, int8_t *dxe, long long rows, long long cols, int relu6, int q,
                            hipStream_t st) {
     const long long chunks = (rows * cols + 15) / 16;
     const int n_e = dy_row ? (int)rows : 1;
     if (chunks == 0 && n_e == 0) return hipSuccess;
     prof_begin(st, PROF_RELU_BWD);
     hipLaunchKernelGGL(relu_bwd_kernel, dim3(grid_for(chunks, 4096)), dim3(256), 0, st, dy, dye, dy_row, yc, ye,
-                       y_row, dx, dxe, rows, cols, relu6, vec16(dy, yc, dx));
+                       y_row, dx, dxe, rows, cols, relu6, q, vec16(dy, yc, dx));
     prof_end(st, PROF_RELU_BWD);
     return hipGetLastError();
 }
 
 hipError_t launch_add(const int8_t *a, const int8_t *ae, int a_row, const int8_t *b, const int8_t *be, int b_row,
                       int8_t *z, int8_t *ze, int z_row, long long rows, long long cols, int *bmax, uint32_t *flags,
-                      hipStream_t st) {
-    AddArgs p{a, ae, b, be, z, ze, a_row, b_row, rows, cols, bmax, flags, vec16(a, b, z)};
+                      int q, hipStream_t st) {
+    AddArgs p{a, ae, b, be, z, ze, a_row, b_row, rows, cols, bmax, flags, q, vec16(a, b, z)};
     if (z_row) {
         if (rows == 0) return hipSuccess;
         prof_begin(st, PROF_ADD_ROWS);

@@ -4,6 +4,8 @@
 // For every velocity group (one row = one output channel):
 //   v = momentum * V + G          exact, then V' = requantised into V's group
 //   w = W - lr * V'               exact, then W' = requantised into W's group
+// W' takes the weights' mantissa width (|C| <= 2^w_q - 1, Table 4's B-bit
+// variants); the velocity is always INT8.
 // momentum and lr are (C, e) scalars.  One wave owns one row; the row's
 // bytes of W, V and G stay in registers between the two steps.
 //
@@ -13,7 +15,7 @@
 // magnitude, P the larger term's exponent) can only decide a rounding tie
 // or a sticky bit, so it is replaced by sign(Y) * 2^(P-24), which rounds
 // identically at every exponent the group can take (every such exponent is
-// at least P - 7, where the larger term dominates).
+// at least P - 7 at any width, where the larger term dominates).
 #include "ie_device.h"
 #include "ie_internal.h"
 
@@ -61,9 +63,9 @@ __device__ __forceinline__ void store_dw(int8_t *row, long long col, long long c
 // The wide (int64) forms are out of line: rows with exponent gaps above 15
 // are rare, and inlined they raise the register pressure of every row's path
 // (measured: spills and half the throughput).
-__device__ __noinline__ int sum_need_wide(int X, int pa, int Y, int pb) {
+__device__ __noinline__ int sum_need_wide(int X, int pa, int Y, int pb, int q) {
     Ex64 s = combine64(X, pa, Y, pb);
-    return need64(s.n, s.base);
+    return need64(s.n, s.base, q);
 }
 
 __device__ __noinline__ int sum_round_wide(int X, int pa, int Y, int pb, int e) {
@@ -79,7 +81,7 @@ __device__ __forceinline__ int sum_need(bool narrow, int X, int pa, int Y, int p
         int n = (X << (pa - base)) + (Y << (pb - base));
         return need32(n, base);
     }
-    return sum_need_wide(X, pa, Y, pb);
+    return sum_need_wide(X, pa, Y, pb, 7);
 }
 
 __device__ __forceinline__ int sum_round(bool narrow, int X, int pa, int Y, int pb, int e) {
@@ -399,7 +401,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
                             m = max(m, sum3_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb,
                                                       a.wd_m * sbyte(W[j], t), pc));
                         else
-                            m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb));
+                            m = max(m, sum_need_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, 7));
                     }
                 needv = row_imax(m);
             }
@@ -442,13 +444,14 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     #pragma unroll
                     for (int t = 0; t < 4; ++t) vn[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(c[j][t], fb);
                 const uint32_t mx = row_umax(absmax_rows<D>(vn));
-                needw = mx ? base + mant_shift32(mx) : NEED_NONE;
+                needw = mx ? base + mant_shift32(mx, a.w_q) : NEED_NONE;
             } else {
                 int m = NEED_NONE;
     #pragma unroll
                 for (int j = 0; j < D; ++j)
     #pragma unroll
-                    for (int t = 0; t < 4; ++t) m = max(m, sum_need_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw));
+                    for (int t = 0; t < 4; ++t)
+                        m = max(m, sum_need_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, a.w_q));
                 needw = row_imax(m);
             }
             if (w_tensor) {

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libie.so")
 
 STATUS = {0: "IE_OK", 1: "IE_ERR_NULL", 2: "IE_ERR_SHAPE", 3: "IE_ERR_GROUP", 4: "IE_ERR_WORKSPACE",
-          5: "IE_ERR_EXP_RANGE", 6: "IE_ERR_UNSUPPORTED", 7: "IE_ERR_HIP"}
+          5: "IE_ERR_EXP_RANGE", 6: "IE_ERR_UNSUPPORTED", 7: "IE_ERR_HIP", 8: "IE_ERR_BITS"}
 
 
 class IeError(RuntimeError):
@@ -34,7 +34,7 @@ class IeError(RuntimeError):
 
 class ie_mat(ctypes.Structure):
     _fields_ = [("mant", c_void_p), ("exp", c_void_p), ("rows", c_int64), ("cols", c_int64),
-                ("group", c_int32)]
+                ("group", c_int32), ("bits", c_int32)]
 
 
 class ie_conv_desc(ctypes.Structure):
@@ -103,35 +103,38 @@ def _stream(dev: torch.device) -> int:
 
 class Mat:
     """A (C, e) matrix in device memory: int8 mantissas [rows, cols],
-    int8 exponents (1 entry for TENSOR, `rows` for ROW)."""
+    int8 exponents (1 entry for TENSOR, `rows` for ROW), and the mantissa
+    width `bits` (2..8) that results rounded into it take."""
 
-    def __init__(self, mant: torch.Tensor, exp: torch.Tensor, group: int):
+    def __init__(self, mant: torch.Tensor, exp: torch.Tensor, group: int, bits: int = 8):
         assert mant.dtype == torch.int8 and exp.dtype == torch.int8
         assert mant.is_contiguous() and exp.is_contiguous()
         self.mant = mant
         self.exp = exp
         self.group = int(group)
-        self._desc = {}  # (rows, cols) -> (mant, exp, ie_mat): descriptors built once per view
+        self.bits = int(bits)
+        self._desc = {}  # (rows, cols, bits) -> (mant, exp, ie_mat): descriptors built once per view
 
     @staticmethod
-    def empty(rows: int, cols: int, group: int, device="cuda") -> "Mat":
+    def empty(rows: int, cols: int, group: int, device="cuda", bits: int = 8) -> "Mat":
         m = torch.empty((rows, cols), dtype=torch.int8, device=device)
         e = torch.empty((rows if group == ROW else 1,), dtype=torch.int8, device=device)
-        return Mat(m, e, group)
+        return Mat(m, e, group, bits)
 
     def c(self, rows=None, cols=None) -> ie_mat:
         """The C descriptor; `rows`/`cols` view an NHWC tensor as [N*H*W x C].
         Built once per view and reused while `mant` and `exp` are the same
         tensors."""
-        hit = self._desc.get((rows, cols))
+        key = (rows, cols, self.bits)
+        hit = self._desc.get(key)
         if hit is not None and hit[0] is self.mant and hit[1] is self.exp:
             return hit[2]
         r, c = rows, cols
         if r is None:
             assert self.mant.dim() == 2
             r, c = self.mant.shape
-        d = ie_mat(self.mant.data_ptr(), self.exp.data_ptr(), r, c, self.group)
-        self._desc[(rows, cols)] = (self.mant, self.exp, d)
+        d = ie_mat(self.mant.data_ptr(), self.exp.data_ptr(), r, c, self.group, self.bits)
+        self._desc[key] = (self.mant, self.exp, d)
         return d
 
 

@@ -32,8 +32,28 @@ def test_status_strings():
         assert L.ie_status_str(code).decode() == name
 
 
-def _mat(rows, cols, group=0, mant=256, exp=256):
-    return ie.ie_mat(mant, exp, rows, cols, group)
+def _mat(rows, cols, group=0, mant=256, exp=256, bits=0):
+    return ie.ie_mat(mant, exp, rows, cols, group, bits)
+
+
+def test_mat_layout():
+    # 40 bytes: two pointers, two int64 sizes, group and mantissa width
+    assert ctypes.sizeof(ie.ie_mat) == 40 and ie.ie_mat.bits.offset == 36
+
+
+def test_bits_argument_errors():
+    """Mantissa widths outside 2..8 (0 reads as 8), and a velocity that is
+    not INT8, are refused before anything is enqueued."""
+    L = ie.lib()
+    by = ctypes.byref
+    X, W = _mat(4, 8), _mat(3, 8)
+    for bad in (1, 9, -1, 16):
+        assert L.ie_linear_fwd(by(X), by(W), by(_mat(4, 3, bits=bad)), 1, 1 << 20, None) == 8
+        assert L.ie_relu_fwd(by(_mat(4, 3, bits=bad)), by(_mat(4, 3)), 0, None) == 8
+    S = ie.ie_scalar
+    for vb in (2, 4, 7):
+        assert L.ie_sgd_update(by(W), by(_mat(3, 8, bits=vb)), by(W), S(1, -7), S(7, -3), S(0, 0),
+                               1, 4096, None) == 8
 
 
 def test_linear_argument_errors():
