@@ -107,7 +107,7 @@ def test_sum_bits_matches_fraction(bits):
 
 @pytest.mark.parametrize("bits", [4, 5, 6, 7])
 def test_update_bits_matches_fraction(bits):
-    """The weight takes B bits, the velocity INT8 (Table 4's "velocity INT8")."""
+    """The weight takes B bits, the velocity INT8 (Table 4)."""
     rng = np.random.default_rng(400 + bits)
     qa = (1 << (bits - 1)) - 1
     for trial in range(6):
