@@ -356,6 +356,51 @@ def linear_bwd_dw(dY: QT, X: QT, dw_group: int, bits: int = Q_BITS) -> QT:
 
 
 # ---------------------------------------------------------------------------
+# Batched products: the Product primitive applied independently to a stack of
+# matrices, e.g. a ViT's attention per (image, head): scores Q . K^T, context
+# P . V and their gradients (ViT-Ti / ViT-B in the Abstract and Table 11 use
+# them; the page names no other primitive for them).  Every operand is a
+# stack [batch * rows x cols]; slice z is rows z*rows .. (z+1)*rows - 1.  The
+# result's groups are ROW (one exponent per row of every slice).
+# ---------------------------------------------------------------------------
+
+def _slice(t: QT, batch: int, z: int) -> QT:
+    rows = t.mant.shape[0] // batch
+    m = t.mant[z * rows:(z + 1) * rows]
+    e = t.exp if t.group == TENSOR else t.exp[z * rows:(z + 1) * rows]
+    return QT(m, e, t.group)
+
+
+def _stack(parts: list, cols: int) -> QT:
+    mant = np.concatenate([p.mant for p in parts]) if parts else np.zeros((0, cols), np.int8)
+    exp = np.concatenate([p.exp for p in parts]) if parts else np.zeros(0, np.int8)
+    return QT(mant.astype(np.int8), exp.astype(np.int8), ROW)
+
+
+def bmm_nt(A: QT, B: QT, batch: int, bits: int = Q_BITS) -> QT:
+    """C_z = A_z . B_z^T for every slice (A_z [M x K], B_z [N x K]): the
+    linear forward product per slice; ROW groups."""
+    n = B.mant.shape[0] // batch if batch else 0
+    return _stack([linear_fwd(_slice(A, batch, z), _slice(B, batch, z), ROW, bits) for z in range(batch)], n)
+
+
+def bmm_nn(A: QT, B: QT, batch: int, bits: int = Q_BITS) -> QT:
+    """C_z = A_z . B_z (A_z [M x K], B_z [K x N]): the contraction runs over
+    B_z's rows, so a row-grouped B_z is first re-expressed at the largest of
+    its own row exponents (reading R5), as in the linear input gradient."""
+    n = B.mant.shape[1]
+    return _stack([linear_bwd_dx(_slice(A, batch, z), _slice(B, batch, z), ROW, bits) for z in range(batch)], n)
+
+
+def bmm_tn(A: QT, B: QT, batch: int, bits: int = Q_BITS) -> QT:
+    """C_z = A_z^T . B_z (A_z [K x M], B_z [K x N]): both contracted over
+    their rows, each slice aligned at its own largest row exponent (R5), as
+    in the linear weight gradient."""
+    n = B.mant.shape[1]
+    return _stack([linear_bwd_dw(_slice(A, batch, z), _slice(B, batch, z), ROW, bits) for z in range(batch)], n)
+
+
+# ---------------------------------------------------------------------------
 # Convolution: Table 6 "Convolution (incl. 1x1, depthwise) -> Product"
 # Activations NHWC, weights [K, R, S, C]; zero padding; cross-correlation.
 # ---------------------------------------------------------------------------
