@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 METRIC = "int8 layer fwd+bwd TOPS & % INT8 MFMA peak; SGD-update GB/s & % HBM"
 
 LOADER = {0: "K", 1: "T", 2: "im2col", 3: "dgrad", 4: "im2colT", 5: "WT"}
-EPI = {0: "direct", 1: "rto", 2: "partial"}
+EPI = {0: "direct", 1: "rto", 2: "partial", 4: "bmm_direct", 5: "bmm_rto"}
 OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_kernel"),
          2002: ("sgd_pass2", "sgd_rows_kernel"), 3000: ("rto_finalize", "rto_finalize_kernel"),
          3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
@@ -87,6 +87,8 @@ def kind_symbol(kind: int) -> str:
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
+    if epi in (4, 5):
+        return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}>"
     return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}>"
 
 
@@ -256,12 +258,39 @@ def build_pointwise(torch, ie, ws, batch):
     return calls, meta
 
 
+def build_vit_attention(torch, ie, ws, batch, heads=12, seq=197, dim=64):
+    """ViT-B attention products per (image, head), forward and backward:
+    scores Q.K^T, context P.V, dP = dO.V^T, dV = P^T.dO, dQ = dS.K and
+    dK = dS^T.Q (softmax and its backward are not products: P and dS are
+    synthetic inputs), every result one exponent per row."""
+    inp = wl.vit_attention_inputs(batch, heads, seq, dim, 8000)
+    Z, S, D = inp.z, seq, dim
+    Q, K, V, dO, P, dS = (_dev(torch, ie, c) for c in (inp.Q, inp.K, inp.V, inp.dO, inp.P, inp.dS))
+    outs = {n: ie.Mat.empty(Z * S, c, wl.ROW) for n, c in
+            (("scores", S), ("context", D), ("dP", S), ("dV", D), ("dQ", D), ("dK", D))}
+    ops = 2.0 * Z * S * S * D
+    sd, ss = float(Z * S * D), float(Z * S * S)
+    calls = [
+        Call("scores", lambda: ie.ie_bmm_nt(Z, Q, K, outs["scores"], ws), ops, io=2 * sd + ss, outs=[ss]),
+        Call("context", lambda: ie.ie_bmm_nn(Z, P, V, outs["context"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+        Call("dP", lambda: ie.ie_bmm_nt(Z, dO, V, outs["dP"], ws), ops, io=2 * sd + ss, outs=[ss]),
+        Call("dV", lambda: ie.ie_bmm_tn(Z, P, dO, outs["dV"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+        Call("dQ", lambda: ie.ie_bmm_nn(Z, dS, K, outs["dQ"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+        Call("dK", lambda: ie.ie_bmm_tn(Z, dS, Q, outs["dK"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+    ]
+    meta = {"layers": [{"name": "attention", "slices": Z, "seq": S, "head_dim": D}], "params": 0}
+    return calls, meta
+
+
 WORKLOADS = {
     "resnet18": ("resnet18_cifar_conv3x3_batch128", "ResNet-18 3x3 convolutions on 32x32x3 inputs, batch 128"),
     "vitb": ("vit_b_block_linears_128x197_plus_update_85M", "ViT-B block linears (128 x 197 tokens) + update of 84.9M params"),
     "vitti": ("vit_ti_block_linears_256x197", "ViT-Ti block linears (256 x 197 tokens)"),
     "resnet50": ("resnet50_bottleneck_convs_batch128", "ResNet-50 bottleneck convolutions on 224x224x3 inputs, batch 128"),
     "linear_small": ("linear_64x256x128", "single linear layer 64x256 -> 128"),
+    "vitb_attn": ("vit_b_attention_products_128x12_heads",
+                  "ViT-B attention products per (image, head), forward and backward, batch 128, 12 heads, "
+                  "197 tokens, head size 64"),
     "pointwise": ("resnet18_pointwise_batch128",
                   "ReLU forward and backward masks and the residual Sum on the ResNet-18 conv outputs, batch 128"),
 }
@@ -280,6 +309,8 @@ def build_workload(name, torch, ie, ws):
         return build_linear_small(torch, ie, ws)
     if name == "pointwise":
         return build_pointwise(torch, ie, ws, 128)
+    if name == "vitb_attn":
+        return build_vit_attention(torch, ie, ws, 128)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -313,7 +344,21 @@ def cpu_baseline(name: str):
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": "ReLU, ReLU mask and Sum on every ResNet-18 conv output once at batch 16",
                 "seconds": round(dt, 3)}
-    if name in ("resnet18", "resnet50"):
+    if name == "vitb_attn":
+        # the six products on 576 (image, head) slices (48 images)
+        inp = wl.vit_attention_inputs(128, 12, 197, 64, 9100, slices=576)
+        q = {n: o.QT(c.mant, c.exp, c.group) for n, c in
+             (("Q", inp.Q), ("K", inp.K), ("V", inp.V), ("dO", inp.dO), ("P", inp.P), ("dS", inp.dS))}
+        t0 = time.perf_counter()
+        o.bmm_nt(q["Q"], q["K"], inp.z)
+        o.bmm_nn(q["P"], q["V"], inp.z)
+        o.bmm_nt(q["dO"], q["V"], inp.z)
+        o.bmm_tn(q["P"], q["dO"], inp.z)
+        o.bmm_nn(q["dS"], q["K"], inp.z)
+        o.bmm_tn(q["dS"], q["Q"], inp.z)
+        ops = 6 * 2.0 * inp.z * inp.s * inp.s * inp.d
+        sample = "the six attention products on 576 of the 1536 (image, head) slices"
+    elif name in ("resnet18", "resnet50"):
         batch = 128
         layers = wl.resnet18_cifar_layers(batch) if name == "resnet18" else wl.resnet50_layers(2)
         sample = (f"every layer once at batch {batch if name == 'resnet18' else 2} "

@@ -231,6 +231,36 @@ ie_status ie_relu_bwd(const ie_mat *dY, const ie_mat *Y, const ie_mat *dX, int r
 size_t ie_add_workspace(int64_t rows, int64_t cols);
 ie_status ie_add(const ie_mat *A, const ie_mat *B, const ie_mat *Z, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Batched products: one independent Product (Table 6: the same primitive as
+ * the linear layer) per slice z of stacked operands, e.g. a ViT's attention
+ * per (image, head) with batch = images * heads:
+ *   ie_bmm_nt: C_z = A_z . B_z^T   A [batch*M x K], B [batch*N x K]
+ *              (scores Q.K^T; dP = dO.V^T)
+ *   ie_bmm_nn: C_z = A_z . B_z     A [batch*M x K], B [batch*K x N]
+ *              (context P.V; dQ = dS.K)
+ *   ie_bmm_tn: C_z = A_z^T . B_z   A [batch*K x M], B [batch*K x N]
+ *              (dK = dS^T.Q; dV = P^T.dO)
+ * C [batch*M x N]; slice z of a stack is its rows z*rows .. (z+1)*rows - 1.
+ * Operands may be TENSOR (one exponent for the stack) or ROW (one per row).
+ * An operand contracted over its rows (B of nn, A and B of tn) that is
+ * ROW-grouped is first re-expressed, slice by slice, at the largest of that
+ * slice's row exponents (round half to even), as the linear input and
+ * weight gradients do.  Sums are exact (contraction K <= 65536); C must be
+ * ROW (one exponent per row of every slice), else IE_ERR_UNSUPPORTED; it is
+ * rounded to C->bits.  batch >= 1 (0: every stack empty), batch <= 65535,
+ * and every stack's rows a multiple of batch, else IE_ERR_SHAPE.  A and B of
+ * nt (A of nn) with K a multiple of 16 must be 16-byte aligned.  Workspace:
+ * ie_bmm_workspace(batch, M, N, K) bytes, the same for all three forms.
+ */
+size_t ie_bmm_workspace(int32_t batch, int64_t M, int64_t N, int64_t K);
+ie_status ie_bmm_nt(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C,
+                    void *ws, size_t ws_bytes, void *stream);
+ie_status ie_bmm_nn(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C,
+                    void *ws, size_t ws_bytes, void *stream);
+ie_status ie_bmm_tn(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C,
+                    void *ws, size_t ws_bytes, void *stream);
+
 /* Wait for `stream`, then copy the workspace's sticky flags to *flags and,
  * if clear != 0, zero them. */
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
@@ -243,7 +273,9 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * recorded events, writes up to `max` records in launch order (elapsed
  * milliseconds and a kernel-kind code: 10000*(10*mi + ni) + 1000 +
  * 100*epilogue + 10*loader_A + loader_B for contractions with a
- * (64 mi) x (64 ni) tile, 2000 + pass for the update, 3000 round-to-odd
+ * (64 mi) x (64 ni) tile (epilogue 0 direct, 1 round-to-odd, 2 split, 3 the
+ * paired convolution backward, 4 / 5 batched direct / round-to-odd),
+ * 2000 + pass for the update, 3000 round-to-odd
  * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
  * alignment copies, 3300 split rounding by rows, 3400 the paired finalize of
  * a convolution's backward pass, 3500 / 3510 ReLU forward / backward, 3520 /

@@ -15,7 +15,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libie.so")
 SOURCES = ["ie_api.hip", "ie_aux.hip", "ie_update.hip", "ie_gemm_kk.hip", "ie_gemm_im2col.hip",
            "ie_gemm_dgrad.hip", "ie_gemm_dgrad_wt.hip", "ie_gemm_wgrad.hip", "ie_gemm_pair.hip",
-           "ie_pointwise.hip"]
+           "ie_pointwise.hip", "ie_gemm_batched.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -567,6 +567,184 @@ UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
     return a;
 }
 
+// ---------------------------------------------------------------------------
+// Batched products: C_z = op(A_z) . op(B_z) over stacks of slices, row groups
+// ---------------------------------------------------------------------------
+
+enum BmmForm { BMM_NT = 0, BMM_NN = 1, BMM_TN = 2 };
+
+// Tiles instantiated for the batched kernel: 128x128, 64x256, 128x64, 64x64
+// (the 64x256 one for A . B^T only).  A row group fits one tile (direct
+// epilogue, no second pass) when N <= the tile width, so rows up to 256
+// wide take the 64x256 tile when there is work enough for it.
+Plan plan_batched(long long Z, long long M, long long N, bool kk) {
+    Plan f;
+    auto known = [&](Tile t) {
+        return (t.mi == 2 && (t.ni == 2 || t.ni == 1)) || (t.mi == 1 && t.ni == 1) || (kk && t.mi == 1 && t.ni == 4);
+    };
+    if (forced_plan(BK, f) && known(f.t)) {
+        f.mode = f.mode == PLAN_DIRECT && N <= f.t.bn() ? PLAN_DIRECT : PLAN_RTO;
+        f.splits = 1;
+        return f;
+    }
+    auto tiles = [&](Tile t) { return Z * cdiv(M, t.bm()) * cdiv(N, t.bn()); };
+    Tile t{1, 1};
+    if (kk && N > 128 && N <= 256 && tiles(Tile{1, 4}) >= 2ll * NCU) t = Tile{1, 4};
+    else if (N > 64 && tiles(Tile{2, 2}) >= 2ll * NCU) t = Tile{2, 2};
+    else if (tiles(Tile{2, 1}) >= 2ll * NCU) t = Tile{2, 1};
+    return Plan{t, N <= t.bn() ? PLAN_DIRECT : PLAN_RTO, 1, BK};
+}
+
+struct BmmWs {
+    int8_t *a, *b;   // padded / aligned operand copies
+    int *ea, *eb;    // per-slice common exponents of aligned operands
+    int16_t *p16, *v16;
+};
+
+BmmWs carve_bmm(Carve &c, int form, long long Z, long long M, long long N, long long K) {
+    BmmWs w{};
+    const long long Kp = r16(K);
+    if (form == BMM_NT) {
+        if (Kp != K) {
+            w.a = c.take<int8_t>((size_t)(Z * M * Kp));
+            w.b = c.take<int8_t>((size_t)(Z * N * Kp));
+        }
+    } else if (form == BMM_NN) {
+        if (Kp != K) w.a = c.take<int8_t>((size_t)(Z * M * Kp));
+        w.b = c.take<int8_t>((size_t)(Z * N * Kp));
+        w.eb = c.take<int>((size_t)(Z > 0 ? Z : 1));
+    } else {
+        w.a = c.take<int8_t>((size_t)(Z * K * r16(M)));
+        w.b = c.take<int8_t>((size_t)(Z * K * r16(N)));
+        w.ea = c.take<int>((size_t)(Z > 0 ? Z : 1));
+        w.eb = c.take<int>((size_t)(Z > 0 ? Z : 1));
+    }
+    if (N > 64) {
+        // round-to-odd: per (row, 64-wide column tile) needs and int16 values
+        w.p16 = c.take<int16_t>((size_t)(Z * M * cdiv(N, 64)));
+        w.v16 = c.take<int16_t>((size_t)(Z * M * N));
+    }
+    return w;
+}
+
+size_t bmm_ws(long long Z, long long M, long long N, long long K) {
+    size_t best = HEADER;
+    for (int form = 0; form < 3; ++form) {
+        Carve c{nullptr, HEADER};
+        carve_bmm(c, form, Z, M, N, K);
+        best = best > align256(c.off) ? best : align256(c.off);
+    }
+    return best;
+}
+
+ie_status bmm(int form, int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C, void *ws, size_t ws_bytes,
+              void *stream) {
+    IE_CHECK(check_mat(A));
+    IE_CHECK(check_mat(B));
+    IE_CHECK(check_mat(C));
+    if (batch < 0) return IE_ERR_SHAPE;
+    if (batch == 0) return A->rows == 0 && B->rows == 0 && C->rows == 0 ? IE_OK : IE_ERR_SHAPE;
+    if (A->rows % batch || B->rows % batch || C->rows % batch) return IE_ERR_SHAPE;
+    const long long Z = batch, ra = A->rows / Z, rb = B->rows / Z;
+    long long M, N, K;
+    if (form == BMM_NT) {
+        M = ra, K = A->cols, N = rb;
+        if (B->cols != K) return IE_ERR_SHAPE;
+    } else if (form == BMM_NN) {
+        M = ra, K = A->cols, N = B->cols;
+        if (rb != K) return IE_ERR_SHAPE;
+    } else {
+        K = ra, M = A->cols, N = B->cols;
+        if (rb != K) return IE_ERR_SHAPE;
+    }
+    if (C->rows != Z * M || C->cols != N) return IE_ERR_SHAPE;
+    if (C->group != IE_GROUP_ROW) return IE_ERR_UNSUPPORTED;
+    if (K > MAX_CONTRACT || Z > 65535) return IE_ERR_UNSUPPORTED;
+    if (form != BMM_TN && r16(K) == K && (!aligned(A->mant, 16) || (form == BMM_NT && !aligned(B->mant, 16))))
+        return IE_ERR_UNSUPPORTED;
+    if (form == BMM_TN && ((long long)BK * r16(M) > WINDOW || (long long)BK * r16(N) > WINDOW))
+        return IE_ERR_UNSUPPORTED;
+    if (!ws) return IE_ERR_WORKSPACE;
+    if (ws_bytes < bmm_ws(Z, M, N, K)) return IE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *flags = (uint32_t *)ws;
+    Carve c{(char *)ws, HEADER};
+    const BmmWs w = carve_bmm(c, form, Z, M, N, K);
+    if (M == 0 || N == 0) return hip_status(launch_fill_i8(C->exp, Z * M, E_MIN, st));
+    if (K == 0) {
+        IE_TRY(launch_fill_i8(C->mant, Z * M * N, 0, st));
+        return hip_status(launch_fill_i8(C->exp, Z * M, E_MIN, st));
+    }
+    const Plan pl = plan_batched(Z, M, N, form != BMM_TN);
+    log_plan(form == BMM_NT ? "bmm_nt" : form == BMM_NN ? "bmm_nn" : "bmm_tn", Z * M, N, K, pl);
+    Epi ep;
+    memset(&ep, 0, sizeof ep);
+    ep.row_group = 1;
+    ep.out = C->mant;
+    ep.out_exp = C->exp;
+    ep.flags = flags;
+    ep.q = mat_q(C);
+    ep.mode = pl.mode == PLAN_DIRECT ? EPI_DIRECT : EPI_RTO;
+    if (ep.mode == EPI_RTO) {
+        ep.v16 = w.v16;
+        ep.p16 = w.p16;
+    }
+    BatchArgs ba;
+    memset(&ba, 0, sizeof ba);
+    ba.Z = batch;
+    ba.out = M * N;
+    ba.out_exp = M;
+    ba.p16 = M * cdiv(N, pl.t.bn());
+    const int a_row = A->group == IE_GROUP_ROW, b_row = B->group == IE_GROUP_ROW;
+    Operand Aop{}, Bop{};
+    long long Kc = r16(K);
+    if (form == BMM_NT || form == BMM_NN) {
+        const int8_t *as = A->mant;
+        if (Kc != K) {
+            IE_TRY(launch_pad_rows(A->mant, Z * M, K, nullptr, 0, nullptr, Kc, w.a, st));
+            as = w.a;
+        }
+        Aop = Operand{LD_K, as, Kc, (int)M, {}};
+        ba.a = M * Kc;
+        ep.ea = ExpSrc{A->exp, nullptr, a_row};
+        ba.ea8 = a_row ? M : 0;
+        if (form == BMM_NT) {
+            const int8_t *bs = B->mant;
+            if (Kc != K) {
+                IE_TRY(launch_pad_rows(B->mant, Z * N, K, nullptr, 0, nullptr, Kc, w.b, st));
+                bs = w.b;
+            }
+            Bop = Operand{LD_K, bs, Kc, (int)N, {}};
+            ep.eb = ExpSrc{B->exp, nullptr, b_row};
+            ba.eb8 = b_row ? N : 0;
+        } else {
+            // B_z [K x N] contracted over its rows: aligned per slice, transposed to [N x Kc]
+            IE_TRY(launch_align_transpose_z(B->mant, B->exp, b_row, batch, (int)K, (int)N, (int)Kc, w.b, w.eb, st));
+            Bop = Operand{LD_K, w.b, Kc, (int)N, {}};
+            ep.eb = ExpSrc{nullptr, w.eb, 0};
+            ba.eb32 = 1;
+        }
+        ba.b = N * Kc;
+    } else {
+        // both contracted over their rows: aligned per slice, rows padded to 16
+        const long long Mp = r16(M), Np = r16(N);
+        IE_TRY(launch_pad_rows_z(A->mant, A->exp, a_row, batch, (int)K, (int)M, (int)Mp, w.a, w.ea, st));
+        IE_TRY(launch_pad_rows_z(B->mant, B->exp, b_row, batch, (int)K, (int)N, (int)Np, w.b, w.eb, st));
+        Aop = Operand{LD_T, w.a, Mp, (int)M, {}};
+        Bop = Operand{LD_T, w.b, Np, (int)N, {}};
+        ba.a = K * Mp;
+        ba.b = K * Np;
+        ep.ea = ExpSrc{nullptr, w.ea, 0};
+        ep.eb = ExpSrc{nullptr, w.eb, 0};
+        ba.ea32 = ba.eb32 = 1;
+        Kc = K;
+    }
+    IE_TRY(launch_gemm_batched(Aop, Bop, (int)M, (int)N, (int)Kc, pl.t, ep, ba, st));
+    if (ep.mode == EPI_RTO)
+        IE_TRY(launch_rto_finalize(w.v16, w.p16, (int)(Z * M), (int)N, pl.t, 1, C->mant, C->exp, flags, st));
+    return IE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -933,6 +1111,26 @@ ie_status ie_add(const ie_mat *A, const ie_mat *B, const ie_mat *Z, void *ws, si
     return hip_status(launch_add(A->mant, A->exp, A->group == IE_GROUP_ROW, B->mant, B->exp,
                                  B->group == IE_GROUP_ROW, Z->mant, Z->exp, Z->group == IE_GROUP_ROW, A->rows,
                                  A->cols, bmax, (uint32_t *)ws, mat_q(Z), (hipStream_t)stream));
+}
+
+size_t ie_bmm_workspace(int32_t batch, int64_t M, int64_t N, int64_t K) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return 0;
+    return bmm_ws(batch, M, N, K);
+}
+
+ie_status ie_bmm_nt(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C, void *ws, size_t ws_bytes,
+                    void *stream) {
+    return bmm(BMM_NT, batch, A, B, C, ws, ws_bytes, stream);
+}
+
+ie_status ie_bmm_nn(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C, void *ws, size_t ws_bytes,
+                    void *stream) {
+    return bmm(BMM_NN, batch, A, B, C, ws, ws_bytes, stream);
+}
+
+ie_status ie_bmm_tn(int32_t batch, const ie_mat *A, const ie_mat *B, const ie_mat *C, void *ws, size_t ws_bytes,
+                    void *stream) {
+    return bmm(BMM_TN, batch, A, B, C, ws, ws_bytes, stream);
 }
 
 ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear) {

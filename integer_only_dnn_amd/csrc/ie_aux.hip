@@ -95,6 +95,8 @@ __global__ void fill_i8_kernel(int8_t *p, long long n, int v) {
         p[i] = (int8_t)v;
 }
 
+__device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.s); }
+
 static int blocks_for(long long n, int per_block, int cap = 4096) {
     long long b = (n + per_block - 1) / per_block;
     if (b < 1) b = 1;
@@ -176,6 +178,37 @@ __device__ __forceinline__ uint32_t rne_bytes4(uint32_t w, int sh) {
     return o;
 }
 
+// 16 bytes of a row at byte offset p of a 4-byte aligned buffer of `total`
+// bytes, any alignment of p: five aligned dword loads, funnel-shifted (a
+// dword reaching past `total` is read byte by byte); bytes of the row past
+// `valid` (< 16) are zeroed.
+__device__ __forceinline__ v4i load16_row(const int8_t *base, long long p, long long total, int valid) {
+    const long long a0 = p & ~3ll;
+    const int sh = (int)(p - a0) * 8;
+    uint32_t d[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const long long a = a0 + 4 * k;
+        if (a + 4 <= total) {
+            d[k] = *(const uint32_t *)(base + a);
+        } else {
+            uint32_t w = 0;
+            for (int j = 0; j < 4; ++j)
+                if (a + j < total) w |= (uint32_t)(uint8_t)base[a + j] << (8 * j);
+            d[k] = w;
+        }
+    }
+    v4i v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t w = sh ? (d[k] >> sh) | (d[k + 1] << (32 - sh)) : d[k];
+        const int nb = valid - 4 * k;
+        if (nb < 4) w = nb <= 0 ? 0u : w & ((1u << (8 * nb)) - 1u);
+        v[k] = (int)w;
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(256) void pad_rows_kernel(const int8_t *in, long long rows, long long cols,
                                                        const int8_t *e, int e_row, const int *estar, long long cols_p,
                                                        int8_t *out, int vec_in, FastDiv dcpr) {
@@ -189,6 +222,8 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const int8_t *in, long lo
         v4i v;
         if (vec_in && c0 + 16 <= cols) {
             v = *(const v4i *)src;
+        } else if (((uintptr_t)in & 3) == 0) {
+            v = load16_row(in, r * cols + c0, rows * cols, (int)min(cols - c0, 16ll));
         } else {
             uint32_t w[4] = {0, 0, 0, 0};
             for (int j = 0; j < 16; ++j)
@@ -257,6 +292,96 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, i
     return hipGetLastError();
 }
 
+// Batched form of align_transpose: slice z = blockIdx.z, w [Z][A][C] ->
+// out [Z][C][Ap] at the slice's largest row exponent (block (0, 0, z) stores
+// it in estar[z]).
+__global__ __launch_bounds__(256) void align_transpose_z_kernel(const int8_t *w, const int8_t *e, int e_row, int A,
+                                                                int C, int Ap, int8_t *out, int *estar) {
+    __shared__ int8_t tile[64][65];
+    __shared__ int sh[4];
+    const int z = blockIdx.z;
+    const int8_t *ez = e_row ? e + (long long)z * A : e;
+    const int8_t *wz = w + (long long)z * A * C;
+    int8_t *oz = out + (long long)z * C * Ap;
+    const int es = e_row ? exp_max_block(ez, A, sh) : (int)e[0];
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) estar[z] = es;
+    const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int la = i >> 6, lc = i & 63;
+        const int a = a0 + la, c = c0 + lc;
+        int8_t v = 0;
+        if (a < A && c < C) v = (int8_t)rne_shift32(wz[(long long)a * C + c], es - (e_row ? (int)ez[a] : es));
+        tile[la][lc] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int lc = i >> 6, la = i & 63;
+        const int a = a0 + la, c = c0 + lc;
+        if (a < Ap && c < C) oz[(long long)c * Ap + a] = tile[la][lc];
+    }
+}
+
+hipError_t launch_align_transpose_z(const int8_t *w, const int8_t *e, int e_row, int Z, int A, int C, int Ap,
+                                    int8_t *out, int *estar, hipStream_t st) {
+    if (Z <= 0 || Ap <= 0 || C <= 0) return hipSuccess;
+    if (Z > 65535 || (Ap + 63) / 64 > 65535) return hipErrorInvalidValue;
+    dim3 grid((C + 63) / 64, (Ap + 63) / 64, Z);
+    prof_begin(st, PROF_ALIGN);
+    hipLaunchKernelGGL(align_transpose_z_kernel, grid, dim3(256), 0, st, w, e, e_row, A, C, Ap, out, estar);
+    prof_end(st, PROF_ALIGN);
+    return hipGetLastError();
+}
+
+// Batched row alignment with padding: slice z = blockIdx.y; every block finds
+// the slice's largest row exponent itself (R bytes) and block (0, z) stores
+// it; each thread writes 16 output bytes of one row.
+__global__ __launch_bounds__(256) void pad_rows_z_kernel(const int8_t *in, const int8_t *e, int e_row, int R,
+                                                         int cols, int cols_p, int8_t *out, int *estar,
+                                                         FastDiv dcpr) {
+    __shared__ int sh[4];
+    const int z = blockIdx.y;
+    const int8_t *ez = e_row ? e + (long long)z * R : e;
+    const int es = e_row ? exp_max_block(ez, R, sh) : (int)e[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) estar[z] = es;
+    const int8_t *iz = in + (long long)z * R * cols;
+    int8_t *oz = out + (long long)z * R * cols_p;
+    const uint32_t cpr = (uint32_t)(cols_p >> 4);
+    const uint32_t n = (uint32_t)R * cpr;
+    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+        const uint32_t r = fdiv32(i, dcpr);
+        const int c0 = (int)(i - r * cpr) << 4;
+        const int sh_ = e_row ? es - (int)ez[r] : 0;
+        const int valid = min(cols - c0, 16);
+        v4i v;
+        if (((uintptr_t)in & 3) == 0) {
+            v = load16_row(in, ((long long)z * R + r) * cols + c0, (long long)gridDim.y * R * cols, valid);
+        } else {
+            const int8_t *src = iz + (long long)r * cols + c0;
+            uint32_t wv[4] = {0, 0, 0, 0};
+            for (int j = 0; j < valid; ++j) wv[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+            v = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+        }
+        if (sh_ != 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (int)rne_bytes4((uint32_t)v[j], sh_);
+        }
+        *(v4i *)(oz + (long long)r * cols_p + c0) = v;
+    }
+}
+
+hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z, int R, int cols, int cols_p,
+                             int8_t *out, int *estar, hipStream_t st) {
+    if (Z <= 0) return hipSuccess;
+    if (Z > 65535) return hipErrorInvalidValue;
+    const long long n = (long long)R * (cols_p >> 4);
+    if (n >= (1ll << 31)) return hipErrorInvalidValue;
+    prof_begin(st, PROF_ALIGN);
+    hipLaunchKernelGGL(pad_rows_z_kernel, dim3(blocks_for(n > 0 ? n : 1, 256, 64), Z), dim3(256), 0, st, in, e,
+                       e_row, R, cols, cols_p, out, estar, make_fastdiv((uint32_t)(cols_p >> 4 > 0 ? cols_p >> 4 : 1)));
+    prof_end(st, PROF_ALIGN);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Host helpers
 // ---------------------------------------------------------------------------
@@ -287,7 +412,6 @@ hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, 
 // length is not a multiple of 8).
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t fdiv32(uint32_t n, FastDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.s); }
 
 // Whole-tensor groups: every block first takes the maximum of all tile
 // needs (T values).  Row groups: a block walks runs of RB rows; the needs of

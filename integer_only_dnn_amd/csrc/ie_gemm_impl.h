@@ -1195,6 +1195,61 @@ hipError_t launch_pair(const PairPart &p1, const PairPart &p2, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The block index that work_of (one split) maps to logical tile L of T: its
+// inverse, so that a caller can pick the tile and still run gemm_tile.
+__device__ __forceinline__ int block_of_tile(int L, int T) {
+    const int q = T / 8, r = T % 8;
+    int x, j;
+    if (L < r * (q + 1)) {
+        x = L / (q + 1);
+        j = L - x * (q + 1);
+    } else {
+        const int L2 = L - r * (q + 1);  // q >= 1 here: L < T
+        x = r + L2 / q;
+        j = L2 - (x - r) * q;
+    }
+    return x + 8 * j;
+}
+
+// A stack of independent products (slice z = the batch index): the work of
+// all slices is spread over the XCDs as one grid of Z * TM * TN tiles (a
+// slice's tiles stay together), each workgroup shifts the operands, exponent
+// sources and outputs to its slice and runs the plain tile.
+template <int KA, int KB, int MI, int NI>
+__global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_batched_kernel(Operand A, Operand B, int M, int N,
+                                                                                int K, int TM, Epi ep, BatchArgs ba) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
+    const int TN = (N + 64 * NI - 1) / (64 * NI), T = TM * TN;
+    int tm, tn, z;
+    work_of(blockIdx.x, TM, TN, ba.Z, tm, tn, z);
+    A.base += z * ba.a;
+    B.base += z * ba.b;
+    if (ep.ea.e8) ep.ea.e8 += z * ba.ea8;
+    if (ep.ea.e32) ep.ea.e32 += z * ba.ea32;
+    if (ep.eb.e8) ep.eb.e8 += z * ba.eb8;
+    if (ep.eb.e32) ep.eb.e32 += z * ba.eb32;
+    if (ep.out) ep.out += z * ba.out;
+    if (ep.v16) ep.v16 += z * ba.out;
+    if (ep.out_exp) ep.out_exp += z * ba.out_exp;
+    if (ep.p16) ep.p16 += z * ba.p16;
+    gemm_tile<KA, KB, MI, NI, false>(A, B, M, N, K, K, TM, 1, ep, block_of_tile(tm * TN + tn, T), T, lds);
+}
+
+template <int KA, int KB, int MI, int NI>
+hipError_t launch_batched_one(const Operand &A, const Operand &B, int M, int N, int K, const Epi &ep,
+                              const BatchArgs &ba, hipStream_t st) {
+    const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
+    const long long blocks = (long long)TM * TN * ba.Z;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (4 + ep.mode) + 10 * KA + KB;
+    prof_begin(st, kind);
+    hipLaunchKernelGGL((gemm_batched_kernel<KA, KB, MI, NI>), dim3((int)blocks), dim3(NTHR), 0, st, A, B, M, N, K, TM,
+                       ep, ba);
+    prof_end(st, kind);
+    return hipGetLastError();
+}
+
 template <int KA, int KB, int MI, int NI, bool PARTIAL>
 hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, int splits, int k_chunk,
                       const Epi &ep, hipStream_t st) {

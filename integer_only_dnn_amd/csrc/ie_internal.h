@@ -129,6 +129,21 @@ hipError_t launch_gemm_pair(const Operand &A1, const Operand &B1, int M1, int N1
                             const Epi &ep1, const Operand &A2, const Operand &B2, int M2, int N2, int K2, Tile t2,
                             int splits2, int k_chunk2, const Epi &ep2, hipStream_t st);
 
+// Batched products (ie_gemm_batched.hip): slice z of a stack reads A at
+// A.base + z * a, B at B.base + z * b, exponents at e8 + z * e*8 or
+// e32 + z * e*32, and writes its [M x N] result (row groups) at out +
+// z * out (mantissas and round-to-odd values), out_exp + z * out_exp and
+// p16 + z * p16.  mode: EPI_DIRECT (N within one tile) or EPI_RTO.
+struct BatchArgs {
+    long long a, b;
+    long long ea8, eb8;
+    int ea32, eb32;
+    long long out, out_exp, p16;
+    int Z;
+};
+hipError_t launch_gemm_batched(const Operand &A, const Operand &B, int M, int N, int K, Tile t, const Epi &ep,
+                               const BatchArgs &ba, hipStream_t st);
+
 // Optional kernel timing (ie_aux.hip): bracket a launch with HIP events.
 void prof_begin(hipStream_t st, int kind);
 void prof_end(hipStream_t st, int kind);
@@ -213,6 +228,16 @@ hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st);
 // Pointwise steps (ie_pointwise.hip).  Whole-tensor sums keep one int per
 // block in `bmax` (at most ADD_MAX_BLOCKS).
 constexpr int ADD_MAX_BLOCKS = 1024;
+// Batched alignment (reading R5 per slice).  align_transpose_z: w [Z][A][C]
+// (row exponents e[z*A + a], or e[0]) -> out [Z][C][Ap], every slice at its
+// largest row exponent estar[z], zero for A <= a < Ap.  pad_rows_z: in
+// [Z][R][cols] -> out [Z][R][cols_p] re-expressed at estar[z] (the slice's
+// largest row exponent; e[0] when e_row is 0), zero past cols.
+hipError_t launch_align_transpose_z(const int8_t *w, const int8_t *e, int e_row, int Z, int A, int C, int Ap,
+                                    int8_t *out, int *estar, hipStream_t st);
+hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z, int R, int cols, int cols_p,
+                             int8_t *out, int *estar, hipStream_t st);
+
 // relu6: the cap is min(6 * 2^-e, 2^q - 1) with q from the activation's width.
 hipError_t launch_relu_fwd(const int8_t *x, const int8_t *xe, int x_row, int8_t *y, int8_t *ye, long long rows,
                            long long cols, int relu6, int q, hipStream_t st);

@@ -60,6 +60,10 @@ EXPORTS = [
     ("ie_conv_fwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_conv_bwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update", c_int, [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_bmm_workspace", c_size_t, [c_int32, c_int64, c_int64, c_int64]),
+    ("ie_bmm_nt", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_bmm_nn", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_bmm_tn", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_sgd_update_multi", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_fwd_act", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
     ("ie_conv_fwd_act", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
@@ -248,6 +252,33 @@ def ie_sgd_update_multi(Ws, Vs, Gs, lr, momentum, weight_decay=(0, 0), ws: Works
     p, b = ws.get(_ws_size("ie_sgd_update_multi_workspace", n))
     _check(lib().ie_sgd_update_multi(n, w, v, g, ie_scalar(*lr), ie_scalar(*momentum), ie_scalar(*weight_decay),
                                      p, b, _stream(ws.device)), "ie_sgd_update_multi")
+
+
+def _bmm(name: str, batch: int, A: Mat, B: Mat, C: Mat, ws: Workspace) -> None:
+    a, b, c = A.c(), B.c(), C.c()
+    if name == "ie_bmm_nt":
+        m, n, k = a.rows // max(batch, 1), b.rows // max(batch, 1), a.cols
+    elif name == "ie_bmm_nn":
+        m, n, k = a.rows // max(batch, 1), b.cols, a.cols
+    else:
+        m, n, k = a.cols, b.cols, a.rows // max(batch, 1)
+    p, nb = ws.get(lib().ie_bmm_workspace(batch, m, n, k))
+    _check(getattr(lib(), name)(batch, byref(a), byref(b), byref(c), p, nb, _stream(ws.device)), name)
+
+
+def ie_bmm_nt(batch: int, A: Mat, B: Mat, C: Mat, ws: Workspace) -> None:
+    """C_z = A_z . B_z^T for every slice z of the stacks (attention scores)."""
+    _bmm("ie_bmm_nt", batch, A, B, C, ws)
+
+
+def ie_bmm_nn(batch: int, A: Mat, B: Mat, C: Mat, ws: Workspace) -> None:
+    """C_z = A_z . B_z (attention context P . V)."""
+    _bmm("ie_bmm_nn", batch, A, B, C, ws)
+
+
+def ie_bmm_tn(batch: int, A: Mat, B: Mat, C: Mat, ws: Workspace) -> None:
+    """C_z = A_z^T . B_z (attention's key and value gradients)."""
+    _bmm("ie_bmm_tn", batch, A, B, C, ws)
 
 
 ACT_NONE, ACT_RELU = 0, 1

@@ -287,7 +287,7 @@ def align_rows(t: QT) -> tuple:
     groups whose exponents are all equal, this is the identity.
     """
     re = t.row_exp()
-    m = t.mant.astype(np.int64).reshape(t.mant.shape[0], -1)
+    m = t.mant.astype(np.int64).reshape(t.mant.shape[0], int(np.prod(t.mant.shape[1:], dtype=np.int64)))
     if re.size == 0:
         return m.reshape(t.mant.shape), E_MIN
     e_star = int(re.max())

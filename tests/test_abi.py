@@ -72,6 +72,28 @@ def test_linear_argument_errors():
     assert L.ie_linear_bwd_dw(by(Y), by(X), by(_mat(3, 9)), 1, 1 << 20, None) == 2
 
 
+def test_bmm_argument_errors():
+    """Batched products: stacks not divisible by the batch, mismatched
+    slices, a whole-tensor result, and a short workspace are refused before
+    anything is enqueued."""
+    L = ie.lib()
+    by = ctypes.byref
+    nt, nn, tn = L.ie_bmm_nt, L.ie_bmm_nn, L.ie_bmm_tn
+    A, B, C = _mat(3 * 5, 16), _mat(3 * 7, 16), _mat(3 * 5, 7, group=1)
+    big = 1 << 30
+    assert nt(3, by(A), by(_mat(20, 16)), by(C), 1, big, None) == 2      # 20 rows, batch 3
+    assert nt(3, by(A), by(_mat(21, 17)), by(C), 1, big, None) == 2      # K differs
+    assert nt(3, by(A), by(B), by(_mat(15, 8, group=1)), 1, big, None) == 2
+    assert nt(-1, by(A), by(B), by(C), 1, big, None) == 2
+    assert nt(3, by(A), by(B), by(_mat(15, 7, group=0)), 1, big, None) == 6
+    assert nt(3, by(A), by(B), by(C), None, big, None) == 4
+    assert nt(3, by(A), by(B), by(C), 1, 64, None) == 4
+    assert nn(3, by(A), by(_mat(3 * 15, 7)), by(C), 1, big, None) == 2   # B slices of 15 rows, K = 16
+    assert tn(3, by(_mat(3 * 16, 5)), by(_mat(3 * 15, 7)), by(C), 1, big, None) == 2
+    assert tn(3, by(_mat(3 * 16, 5)), by(_mat(3 * 16, 7)), by(_mat(15, 7, group=0)), 1, big, None) == 6
+    assert L.ie_bmm_workspace(3, 5, 7, 16) >= 256 and L.ie_bmm_workspace(-1, 5, 7, 16) == 0
+
+
 def test_conv_and_update_argument_errors():
     L = ie.lib()
     by = ctypes.byref

@@ -281,3 +281,43 @@ def update_inputs(rows: int, cols: int, seed: int, w_group: int = ROW,
 # Learning rate 2**-7 and momentum 7/8 as (C, e) scalars.
 LR = (1, -7)
 MOMENTUM = (7, -3)
+
+
+# ---------------------------------------------------------------------------
+# ViT attention products per (image, head): stacks of slices
+# ---------------------------------------------------------------------------
+
+@dataclass
+class AttentionInputs:
+    """Stacked per-(image, head) operands: Q, K, V, dO [Z*S x D] and P, dS
+    [Z*S x S], every row its own group (one exponent per token and head)."""
+    z: int
+    s: int
+    d: int
+    Q: Code
+    K: Code
+    V: Code
+    dO: Code
+    P: Code
+    dS: Code
+
+
+def vit_attention_inputs(batch: int, heads: int, seq: int, dim: int, seed: int,
+                         slices: int = None) -> AttentionInputs:
+    """Q, K, V, dO and dS from normal draws; P as attention probabilities
+    (every row the softmax of normal logits: non-negative, summing to one).
+    `slices` draws only the first that many (image, head) slices."""
+    rng = np.random.default_rng(seed)
+    z = batch * heads if slices is None else slices
+    f = np.float32
+
+    def normal(rows, cols):
+        return rng.standard_normal((rows, cols), dtype=f)
+
+    q, k, v, do = (max127_code(normal(z * seq, dim), ROW) for _ in range(4))
+    logits = normal(z * seq, seq)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    P = max127_code(p, ROW)
+    dS = max127_code(normal(z * seq, seq), ROW)
+    return AttentionInputs(z, seq, dim, q, k, v, do, P, dS)
