@@ -574,19 +574,12 @@ UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
 enum BmmForm { BMM_NT = 0, BMM_NN = 1, BMM_TN = 2 };
 
 // Tiles instantiated for the batched kernel: 128x128, 64x256, 128x64, 64x64
-// (the 64x256 one for A . B^T only).  A row group fits one tile (direct
+// (the 64x256 one for A . B^T and A . B).  A row group fits one tile (direct
 // epilogue, no second pass) when N <= the tile width, so rows up to 256
-// wide take the 64x256 tile when there is work enough for it.
+// wide take the 64x256 tile when there is work enough for it.  The tuning
+// override of the other products does not apply here: only these choices
+// are run.
 Plan plan_batched(long long Z, long long M, long long N, bool kk) {
-    Plan f;
-    auto known = [&](Tile t) {
-        return (t.mi == 2 && (t.ni == 2 || t.ni == 1)) || (t.mi == 1 && t.ni == 1) || (kk && t.mi == 1 && t.ni == 4);
-    };
-    if (forced_plan(BK, f) && known(f.t)) {
-        f.mode = f.mode == PLAN_DIRECT && N <= f.t.bn() ? PLAN_DIRECT : PLAN_RTO;
-        f.splits = 1;
-        return f;
-    }
     auto tiles = [&](Tile t) { return Z * cdiv(M, t.bm()) * cdiv(N, t.bn()); };
     Tile t{1, 1};
     if (kk && N > 128 && N <= 256 && tiles(Tile{1, 4}) >= 2ll * NCU) t = Tile{1, 4};

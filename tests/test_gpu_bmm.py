@@ -1,7 +1,7 @@
 """GPU parity of the batched products (attention's Q.K^T, P.V and their
 gradients as one Product per slice), through the C ABI, bit for bit against
 the oracle: the three forms over ragged shapes, both input group kinds, both
-epilogues and every instantiated tile, narrower result widths, empty and
+epilogues and every tile the planner picks, narrower result widths, empty and
 degenerate stacks, and ViT-B's attention at batch 64 with sampled slices."""
 
 import numpy as np
@@ -20,17 +20,6 @@ FORMS = {"nt": (o.bmm_nt, ie.ie_bmm_nt), "nn": (o.bmm_nn, ie.ie_bmm_nn), "tn": (
 @pytest.fixture(scope="module")
 def ws():
     return ie.Workspace("cuda")
-
-
-@pytest.fixture
-def plan(monkeypatch):
-    def force(tile=None, mode=None):
-        if tile is None:
-            monkeypatch.delenv("IE_TILE", raising=False)
-        else:
-            monkeypatch.setenv("IE_TILE", f"{tile[0]},{tile[1]},{mode},1")
-    yield force
-    monkeypatch.delenv("IE_TILE", raising=False)
 
 
 def _qt(rng, rows, cols, group, elo=-14, ehi=-2, zero_frac=0.05, bits=8):
@@ -75,17 +64,23 @@ def test_bmm(form, shape, groups, ws):
     assert ws.status() == 0
 
 
+# Shapes that lead the planner to each tile and epilogue of the batched
+# kernel (512 work items fill the chip): 64x256 direct (A . B^T and A . B,
+# rows of 129..256), 128x128 direct (rows of 65..128) and round-to-odd (rows
+# past 256), 128x64 direct (rows up to 64), 64x64 direct and round-to-odd
+# (few slices).
+PLAN_SHAPES = [(128, 260, 200, 40), (256, 200, 100, 40), (100, 200, 300, 24), (256, 200, 50, 40),
+               (3, 150, 60, 90), (3, 150, 150, 90)]
+
+
 @pytest.mark.parametrize("form", list(FORMS))
-@pytest.mark.parametrize("tile", [(2, 2), (1, 4), (2, 1), (1, 1)], ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
-@pytest.mark.parametrize("mode", [0, 1], ids=["direct", "rto"])
-def test_bmm_plans(form, tile, mode, ws, plan):
-    """Every instantiated tile with either epilogue (direct only where a row
-    fits the tile: the planner falls back to round-to-odd otherwise)."""
-    batch, M, N, K = 3, 150, 60 if mode == 0 else 150, 90
-    announce(f"bmm plans {form} tile={tile} mode={mode} M={M} N={N} K={K}")
-    rng = np.random.default_rng(11 * tile[0] + 5 * tile[1] + mode + ord(form[1]))
+@pytest.mark.parametrize("shape", PLAN_SHAPES, ids=lambda s: "b{}m{}n{}k{}".format(*s))
+def test_bmm_plans(form, shape, ws):
+    """Every tile and epilogue the planner picks, reached through the shape."""
+    batch, M, N, K = shape
+    announce(f"bmm plans {form} batch={batch} M={M} N={N} K={K}")
+    rng = np.random.default_rng(sum(shape) + ord(form[1]))
     A, B = _operands(rng, form, batch, M, N, K, R, R)
-    plan(tile, mode)
     C = _run(form, batch, A, B, M, N, ws)
     assert_same(C, FORMS[form][0](A, B, batch), f"bmm {form} plan")
     assert ws.status() == 0
