@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 METRIC = "int8 layer fwd+bwd TOPS & % INT8 MFMA peak; SGD-update GB/s & % HBM"
 
 LOADER = {0: "K", 1: "T", 2: "im2col", 3: "dgrad", 4: "im2colT", 5: "WT"}
-EPI = {0: "direct", 1: "rto", 2: "partial", 4: "bmm_direct", 5: "bmm_rto"}
+EPI = {0: "direct", 1: "rto", 2: "partial", 4: "bmm_direct", 5: "bmm_rto", 6: "bmm1_direct", 7: "bmm1_rto"}
 OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_kernel"),
          2002: ("sgd_pass2", "sgd_rows_kernel"), 3000: ("rto_finalize", "rto_finalize_kernel"),
          3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
@@ -87,8 +87,8 @@ def kind_symbol(kind: int) -> str:
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
-    if epi in (4, 5):
-        return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}>"
+    if epi in (4, 5, 6, 7):
+        return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi >= 6 else 'false'}>"
     return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}>"
 
 

@@ -274,7 +274,8 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * milliseconds and a kernel-kind code: 10000*(10*mi + ni) + 1000 +
  * 100*epilogue + 10*loader_A + loader_B for contractions with a
  * (64 mi) x (64 ni) tile (epilogue 0 direct, 1 round-to-odd, 2 split, 3 the
- * paired convolution backward, 4 / 5 batched direct / round-to-odd),
+ * paired convolution backward, 4 / 5 batched direct / round-to-odd, 6 / 7
+ * the same with a one-step contraction),
  * 2000 + pass for the update, 3000 round-to-odd
  * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
  * alignment copies, 3300 split rounding by rows, 3400 the paired finalize of

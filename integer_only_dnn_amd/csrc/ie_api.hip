@@ -574,7 +574,7 @@ UpdateArgs update_args(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_sca
 enum BmmForm { BMM_NT = 0, BMM_NN = 1, BMM_TN = 2 };
 
 // Tiles instantiated for the batched kernel: 128x128, 64x256, 128x64, 64x64
-// (the 64x256 one for A . B^T and A . B).  A row group fits one tile (direct
+// (the 64x256 one for A . B^T only).  A row group fits one tile (direct
 // epilogue, no second pass) when N <= the tile width, so rows up to 256
 // wide take the 64x256 tile when there is work enough for it.  The tuning
 // override of the other products does not apply here: only these choices
@@ -604,7 +604,7 @@ BmmWs carve_bmm(Carve &c, int form, long long Z, long long M, long long N, long 
         }
     } else if (form == BMM_NN) {
         if (Kp != K) w.a = c.take<int8_t>((size_t)(Z * M * Kp));
-        w.b = c.take<int8_t>((size_t)(Z * N * Kp));
+        w.b = c.take<int8_t>((size_t)(Z * K * r16(N)));
         w.eb = c.take<int>((size_t)(Z > 0 ? Z : 1));
     } else {
         w.a = c.take<int8_t>((size_t)(Z * K * r16(M)));
@@ -668,7 +668,7 @@ ie_status bmm(int form, int32_t batch, const ie_mat *A, const ie_mat *B, const i
         IE_TRY(launch_fill_i8(C->mant, Z * M * N, 0, st));
         return hip_status(launch_fill_i8(C->exp, Z * M, E_MIN, st));
     }
-    const Plan pl = plan_batched(Z, M, N, form != BMM_TN);
+    const Plan pl = plan_batched(Z, M, N, form == BMM_NT);
     log_plan(form == BMM_NT ? "bmm_nt" : form == BMM_NN ? "bmm_nn" : "bmm_tn", Z * M, N, K, pl);
     Epi ep;
     memset(&ep, 0, sizeof ep);
@@ -710,14 +710,19 @@ ie_status bmm(int form, int32_t batch, const ie_mat *A, const ie_mat *B, const i
             Bop = Operand{LD_K, bs, Kc, (int)N, {}};
             ep.eb = ExpSrc{B->exp, nullptr, b_row};
             ba.eb8 = b_row ? N : 0;
+            ba.b = N * Kc;
         } else {
-            // B_z [K x N] contracted over its rows: aligned per slice, transposed to [N x Kc]
-            IE_TRY(launch_align_transpose_z(B->mant, B->exp, b_row, batch, (int)K, (int)N, (int)Kc, w.b, w.eb, st));
-            Bop = Operand{LD_K, w.b, Kc, (int)N, {}};
+            // B_z [K x N] contracted over its rows: aligned per slice, rows
+            // padded to 16 bytes, read row-contiguous; A's padding columns
+            // are zeroed by its loader (contraction K, not Kc)
+            const long long Np = r16(N);
+            IE_TRY(launch_pad_rows_z(B->mant, B->exp, b_row, batch, (int)K, (int)N, (int)Np, w.b, w.eb, st));
+            Bop = Operand{LD_T, w.b, Np, (int)N, {}};
             ep.eb = ExpSrc{nullptr, w.eb, 0};
             ba.eb32 = 1;
+            ba.b = K * Np;
+            Kc = K;
         }
-        ba.b = N * Kc;
     } else {
         // both contracted over their rows: aligned per slice, rows padded to 16
         const long long Mp = r16(M), Np = r16(N);

@@ -292,46 +292,6 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, i
     return hipGetLastError();
 }
 
-// Batched form of align_transpose: slice z = blockIdx.z, w [Z][A][C] ->
-// out [Z][C][Ap] at the slice's largest row exponent (block (0, 0, z) stores
-// it in estar[z]).
-__global__ __launch_bounds__(256) void align_transpose_z_kernel(const int8_t *w, const int8_t *e, int e_row, int A,
-                                                                int C, int Ap, int8_t *out, int *estar) {
-    __shared__ int8_t tile[64][65];
-    __shared__ int sh[4];
-    const int z = blockIdx.z;
-    const int8_t *ez = e_row ? e + (long long)z * A : e;
-    const int8_t *wz = w + (long long)z * A * C;
-    int8_t *oz = out + (long long)z * C * Ap;
-    const int es = e_row ? exp_max_block(ez, A, sh) : (int)e[0];
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) estar[z] = es;
-    const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int la = i >> 6, lc = i & 63;
-        const int a = a0 + la, c = c0 + lc;
-        int8_t v = 0;
-        if (a < A && c < C) v = (int8_t)rne_shift32(wz[(long long)a * C + c], es - (e_row ? (int)ez[a] : es));
-        tile[la][lc] = v;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int lc = i >> 6, la = i & 63;
-        const int a = a0 + la, c = c0 + lc;
-        if (a < Ap && c < C) oz[(long long)c * Ap + a] = tile[la][lc];
-    }
-}
-
-hipError_t launch_align_transpose_z(const int8_t *w, const int8_t *e, int e_row, int Z, int A, int C, int Ap,
-                                    int8_t *out, int *estar, hipStream_t st) {
-    if (Z <= 0 || Ap <= 0 || C <= 0) return hipSuccess;
-    if (Z > 65535 || (Ap + 63) / 64 > 65535) return hipErrorInvalidValue;
-    dim3 grid((C + 63) / 64, (Ap + 63) / 64, Z);
-    prof_begin(st, PROF_ALIGN);
-    hipLaunchKernelGGL(align_transpose_z_kernel, grid, dim3(256), 0, st, w, e, e_row, A, C, Ap, out, estar);
-    prof_end(st, PROF_ALIGN);
-    return hipGetLastError();
-}
-
 // Batched row alignment with padding: slice z = blockIdx.y; every block finds
 // the slice's largest row exponent itself (R bytes) and block (0, z) stores
 // it; each thread writes 16 output bytes of one row.

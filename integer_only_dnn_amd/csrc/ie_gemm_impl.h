@@ -640,17 +640,28 @@ struct TileLds {
     static constexpr int value = stages > partial ? stages : partial;
 };
 
+// LDS of a tile whose contraction is one step (K <= BK): one stage, or the
+// epilogue's staging and maxima if larger (no split products).
+template <int KA, int KB, int MI, int NI>
+struct TileLds1 {
+    static constexpr int stage = Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES;
+    static constexpr int epi = 64 * MI * (64 * NI * 2 + 16) + 4 * 64 * MI * 4 + 64;
+    static constexpr int value = stage > epi ? stage : epi;
+};
+
 // One workgroup's work item: bid and nblk are its index and the number of
 // workgroups of its grid (or of its part of a paired grid); lds points to
-// TileLds bytes of shared memory.
-template <int KA, int KB, int MI, int NI, bool PARTIAL>
+// TileLds bytes of shared memory (TileLds1 when ONE: a contraction of at
+// most one step, loaded once, with no pipeline and no second buffer).
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false>
 __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, int M, int N, int K, int k_chunk,
                                           int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
+    static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
     using LA = Lds<KA, BMt>;
     using LB = Lds<KB, BNt>;
     constexpr int STAGE = LA::BYTES + LB::BYTES;
-    constexpr int LDSB = TileLds<KA, KB, MI, NI>::value;  // bytes at lds
+    constexpr int LDSB = ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value;  // bytes at lds
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -694,7 +705,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
     // NS register stages in flight: stage s is loaded into register set
     // s % NS at step s - NS, written to LDS buffer s % 2 at the end of step
     // s - 1 and computed at step s, so a load has NS - 1 steps to land.
-    constexpr int NS = Stages<MI, NI>::value;
+    constexpr int NS = ONE ? 1 : Stages<MI, NI>::value;
     v4i ra[NS][CA], rb[NS][CB];
     // An empty chunk issues no load at all: with an empty contraction the
     // operand pointers need not address any memory.
@@ -743,7 +754,10 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
     // Trips of NU steps with no exit inside: the loads of the next stages stay
     // in flight across the back edge (an exit inside the trip would make the
     // loop head wait for all of them).  The last nk % NU steps follow the loop.
-    {
+    if constexpr (ONE) {
+        // nk <= 1: the stage loaded above is the whole contraction
+        if (nk > 0) compute(lds);
+    } else {
         auto step = [&](const int uu, const int s) {
             const int u = uu % NS;
             // set u held stage s, already in LDS: refill it with stage s + NS
@@ -1214,11 +1228,14 @@ __device__ __forceinline__ int block_of_tile(int L, int T) {
 // A stack of independent products (slice z = the batch index): the work of
 // all slices is spread over the XCDs as one grid of Z * TM * TN tiles (a
 // slice's tiles stay together), each workgroup shifts the operands, exponent
-// sources and outputs to its slice and runs the plain tile.
-template <int KA, int KB, int MI, int NI>
+// sources and outputs to its slice and runs the plain tile.  ONE: the
+// contraction is one step (K <= BK), so the tile needs half the LDS and twice
+// the workgroups fit a CU.
+template <int KA, int KB, int MI, int NI, bool ONE>
 __global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_batched_kernel(Operand A, Operand B, int M, int N,
                                                                                 int K, int TM, Epi ep, BatchArgs ba) {
-    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
+    __shared__ __attribute__((aligned(16)))
+    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value];
     const int TN = (N + 64 * NI - 1) / (64 * NI), T = TM * TN;
     int tm, tn, z;
     work_of(blockIdx.x, TM, TN, ba.Z, tm, tn, z);
@@ -1232,20 +1249,21 @@ __global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_batched_kerne
     if (ep.v16) ep.v16 += z * ba.out;
     if (ep.out_exp) ep.out_exp += z * ba.out_exp;
     if (ep.p16) ep.p16 += z * ba.p16;
-    gemm_tile<KA, KB, MI, NI, false>(A, B, M, N, K, K, TM, 1, ep, block_of_tile(tm * TN + tn, T), T, lds);
+    gemm_tile<KA, KB, MI, NI, false, ONE>(A, B, M, N, K, K, TM, 1, ep, block_of_tile(tm * TN + tn, T), T, lds);
 }
 
-template <int KA, int KB, int MI, int NI>
+template <int KA, int KB, int MI, int NI, bool ONE = false>
 hipError_t launch_batched_one(const Operand &A, const Operand &B, int M, int N, int K, const Epi &ep,
                               const BatchArgs &ba, hipStream_t st) {
+    if (ONE && K > BK) return hipErrorInvalidValue;
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     const long long blocks = (long long)TM * TN * ba.Z;
     if (blocks <= 0) return hipSuccess;
     if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
-    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (4 + ep.mode) + 10 * KA + KB;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * ((ONE ? 6 : 4) + ep.mode) + 10 * KA + KB;
     prof_begin(st, kind);
-    hipLaunchKernelGGL((gemm_batched_kernel<KA, KB, MI, NI>), dim3((int)blocks), dim3(NTHR), 0, st, A, B, M, N, K, TM,
-                       ep, ba);
+    hipLaunchKernelGGL((gemm_batched_kernel<KA, KB, MI, NI, ONE>), dim3((int)blocks), dim3(NTHR), 0, st, A, B, M, N,
+                       K, TM, ep, ba);
     prof_end(st, kind);
     return hipGetLastError();
 }

@@ -228,13 +228,9 @@ hipError_t launch_sgd_update_multi(const UpdateArgs *a, int n, hipStream_t st);
 // Pointwise steps (ie_pointwise.hip).  Whole-tensor sums keep one int per
 // block in `bmax` (at most ADD_MAX_BLOCKS).
 constexpr int ADD_MAX_BLOCKS = 1024;
-// Batched alignment (reading R5 per slice).  align_transpose_z: w [Z][A][C]
-// (row exponents e[z*A + a], or e[0]) -> out [Z][C][Ap], every slice at its
-// largest row exponent estar[z], zero for A <= a < Ap.  pad_rows_z: in
-// [Z][R][cols] -> out [Z][R][cols_p] re-expressed at estar[z] (the slice's
-// largest row exponent; e[0] when e_row is 0), zero past cols.
-hipError_t launch_align_transpose_z(const int8_t *w, const int8_t *e, int e_row, int Z, int A, int C, int Ap,
-                                    int8_t *out, int *estar, hipStream_t st);
+// Batched alignment (reading R5 per slice): in [Z][R][cols] -> out
+// [Z][R][cols_p] re-expressed at estar[z] (the slice's largest row exponent;
+// e[0] when e_row is 0), zero past cols.
 hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z, int R, int cols, int cols_p,
                              int8_t *out, int *estar, hipStream_t st);
 
