@@ -54,7 +54,7 @@ typedef enum {
     IE_ERR_GROUP = 3,       /* unknown group kind */
     IE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     IE_ERR_EXP_RANGE = 5,   /* reported by ie_device_status callers */
-    IE_ERR_UNSUPPORTED = 6, /* valid but outside what this build supports */
+    IE_ERR_UNSUPPORTED = 6, /* valid but outside what this library supports */
     IE_ERR_HIP = 7,         /* a HIP runtime call failed */
     IE_ERR_BITS = 8         /* ie_mat.bits outside {0, 2..8}, or a velocity not INT8 */
 } ie_status;
