@@ -861,6 +861,27 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             int8_t *g = (int8_t *)dst + ((long long)grow * ld + gcol) * ES;
             if (vec && gcol + EPC <= N) {
                 *(v4i *)g = v;
+            } else if constexpr (ES == 1) {
+                // rows not 16-byte aligned (or a row's last chunk): bytes up to
+                // the first 4-byte boundary, then whole dwords, then the rest
+                const int n = min(16, N - gcol);
+                auto sel = [&](int i) -> uint32_t {
+                    return (uint32_t)(i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : i == 3 ? v[3] : 0);
+                };
+                auto byte_at_ = [&](int j) { return (int8_t)(sel(j >> 2) >> (8 * (j & 3))); };
+                const int j0 = min((int)((4u - ((uint32_t)(uintptr_t)g & 3u)) & 3u), n);
+                for (int j = 0; j < 3; ++j)
+                    if (j < j0) g[j] = byte_at_(j);
+                const int nd = (n - j0) >> 2, sh = 8 * j0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (k < nd) {
+                        const int p = j0 + 4 * k;
+                        const uint32_t lo = sel(p >> 2), hi = sel((p >> 2) + 1);
+                        *(uint32_t *)(g + p) = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+                    }
+                }
+                for (int j = j0 + 4 * nd; j < n; ++j) g[j] = byte_at_(j);
             } else {
                 const int8_t *b8 = (const int8_t *)&v;
                 for (int j = 0; j < EPC && gcol + j < N; ++j)
