@@ -50,6 +50,7 @@ OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_k
          2002: ("sgd_pass2", "sgd_rows_kernel"), 3000: ("rto_finalize", "rto_finalize_kernel"),
          3100: ("partial_reduce", "partial_reduce_kernel"), 3150: ("round_sums", "round_sums_kernel"),
          3200: ("pad_align", "pad_rows_kernel / align_transpose_kernel"),
+         3210: ("pad_align_z", "pad_rows_z_kernel"),
          3300: ("split_round", "split_round_rows_kernel"),
          3400: ("finalize_pair", "finalize_pair_kernel"),
          3500: ("relu_fwd", "relu_fwd_kernel"), 3510: ("relu_bwd", "relu_bwd_kernel"),
@@ -100,13 +101,14 @@ def kind_symbol(kind: int) -> str:
 class Call:
     """One library call of the step: a closure plus what it computes."""
 
-    def __init__(self, label, fn, ops=0.0, bytes_=0.0, io=0.0, outs=()):
+    def __init__(self, label, fn, ops=0.0, bytes_=0.0, io=0.0, outs=(), prep=()):
         self.label = label
         self.fn = fn
         self.ops = ops          # algorithmic int8 ops of its contraction(s)
         self.bytes = bytes_     # algorithmic HBM bytes (update)
         self.io = io            # algorithmic bytes of each contraction: operands read once, result written once
         self.outs = list(outs)  # int8 result bytes of each contraction, in launch order
+        self.prep = list(prep)  # algorithmic bytes of each padding / alignment copy, in launch order
         self.kinds = None
 
 
@@ -271,13 +273,21 @@ def build_vit_attention(torch, ie, ws, batch, heads=12, seq=197, dim=64):
             (("scores", S), ("context", D), ("dP", S), ("dV", D), ("dQ", D), ("dK", D))}
     ops = 2.0 * Z * S * S * D
     sd, ss = float(Z * S * D), float(Z * S * S)
+    # copies: an S x S stack padded to rows of 16 (read S, write S rounded up)
+    # and a D-wide stack aligned (read and write D)
+    sp = 16 * ((S + 15) // 16)
+    pad_ss, pad_sd = ss + float(Z * S * sp), 2 * sd
     calls = [
         Call("scores", lambda: ie.ie_bmm_nt(Z, Q, K, outs["scores"], ws), ops, io=2 * sd + ss, outs=[ss]),
-        Call("context", lambda: ie.ie_bmm_nn(Z, P, V, outs["context"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+        Call("context", lambda: ie.ie_bmm_nn(Z, P, V, outs["context"], ws), ops, io=ss + 2 * sd, outs=[sd],
+             prep=[pad_ss, pad_sd]),
         Call("dP", lambda: ie.ie_bmm_nt(Z, dO, V, outs["dP"], ws), ops, io=2 * sd + ss, outs=[ss]),
-        Call("dV", lambda: ie.ie_bmm_tn(Z, P, dO, outs["dV"], ws), ops, io=ss + 2 * sd, outs=[sd]),
-        Call("dQ", lambda: ie.ie_bmm_nn(Z, dS, K, outs["dQ"], ws), ops, io=ss + 2 * sd, outs=[sd]),
-        Call("dK", lambda: ie.ie_bmm_tn(Z, dS, Q, outs["dK"], ws), ops, io=ss + 2 * sd, outs=[sd]),
+        Call("dV", lambda: ie.ie_bmm_tn(Z, P, dO, outs["dV"], ws), ops, io=ss + 2 * sd, outs=[sd],
+             prep=[pad_ss, pad_sd]),
+        Call("dQ", lambda: ie.ie_bmm_nn(Z, dS, K, outs["dQ"], ws), ops, io=ss + 2 * sd, outs=[sd],
+             prep=[pad_ss, pad_sd]),
+        Call("dK", lambda: ie.ie_bmm_tn(Z, dS, Q, outs["dK"], ws), ops, io=ss + 2 * sd, outs=[sd],
+             prep=[pad_ss, pad_sd]),
     ]
     meta = {"layers": [{"name": "attention", "slices": Z, "seq": S, "head_dim": D}], "params": 0}
     return calls, meta
@@ -487,10 +497,14 @@ def main():
                 n_pw = sum(1 for k in c.kinds if 3500 <= k < 3600)
                 prod = -1  # index of the last contraction launched
                 fin = 0    # index of the contraction the next finalize belongs to
+                npre = 0   # padding / alignment copies of this call so far
                 for k in c.kinds:
                     if is_gemm(k):
                         prod += 2 if is_pair(k) else 1
                         fin = prod - 1 if is_pair(k) else prod
+                    pre = -1
+                    if k in (3200, 3210):
+                        pre, npre = npre, npre + 1
                     if only is not None and k != only:
                         continue
                     ms, kind = recs[pos]
@@ -507,6 +521,9 @@ def main():
                     elif 3500 <= kind < 3600:
                         # pointwise step: the call's algorithmic bytes over its launches
                         a["bytes"] += c.bytes / n_pw
+                    elif pre >= 0 and c.prep:
+                        # a padding / alignment copy with its own byte count
+                        a["bytes"] += c.prep[min(pre, len(c.prep) - 1)]
                     elif kind == 3400:
                         # both finalizes of a convolution's backward pass
                         a["bytes"] += sum(c.outs)

@@ -278,7 +278,8 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * the same with a one-step contraction),
  * 2000 + pass for the update, 3000 round-to-odd
  * finalize, 3100 split-sum reduction, 3150 rounding of sums, 3200 padding /
- * alignment copies, 3300 split rounding by rows, 3400 the paired finalize of
+ * alignment copies, 3210 the per-slice alignment copies of batched products,
+ * 3300 split rounding by rows, 3400 the paired finalize of
  * a convolution's backward pass, 3500 / 3510 ReLU forward / backward, 3520 /
  * 3521 / 3530 the Sum's maximum, rounding and row-grouped passes) and returns how
  * many were recorded since the last read; the records are then cleared.

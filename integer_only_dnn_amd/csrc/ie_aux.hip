@@ -335,10 +335,10 @@ hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z
     if (Z > 65535) return hipErrorInvalidValue;
     const long long n = (long long)R * (cols_p >> 4);
     if (n >= (1ll << 31)) return hipErrorInvalidValue;
-    prof_begin(st, PROF_ALIGN);
+    prof_begin(st, PROF_ALIGN_Z);
     hipLaunchKernelGGL(pad_rows_z_kernel, dim3(blocks_for(n > 0 ? n : 1, 256, 64), Z), dim3(256), 0, st, in, e,
                        e_row, R, cols, cols_p, out, estar, make_fastdiv((uint32_t)(cols_p >> 4 > 0 ? cols_p >> 4 : 1)));
-    prof_end(st, PROF_ALIGN);
+    prof_end(st, PROF_ALIGN_Z);
     return hipGetLastError();
 }
 

@@ -154,6 +154,7 @@ constexpr int PROF_RTO_FINALIZE = 3000;
 constexpr int PROF_PARTIAL_REDUCE = 3100;
 constexpr int PROF_ROUND_SUMS = 3150;
 constexpr int PROF_ALIGN = 3200;
+constexpr int PROF_ALIGN_Z = 3210;  // per-slice alignment of batched products
 constexpr int PROF_SPLIT_ROUND = 3300;
 constexpr int PROF_FIN_PAIR = 3400;
 constexpr int PROF_RELU_FWD = 3500;
