@@ -224,12 +224,13 @@ def test_update_bits(bits, shape, ws):
     assert ws.status() == 0
 
 
-def test_update_multi_mixed_widths(ws):
+@pytest.mark.parametrize("wd", [(0, 0), (1, -13)], ids=["nowd", "wd"])
+def test_update_multi_mixed_widths(wd, ws):
     """One multi-tensor call over tensors of different widths (8 down to 4,
-    small ones in the shared launch and a large one on its own): each weight
-    takes its own width."""
-    announce("sgd_update_multi mixed widths")
-    rng = np.random.default_rng(4242)
+    small ones in the shared launch and a large one on its own), with and
+    without weight decay: each weight takes its own width."""
+    announce(f"sgd_update_multi mixed widths wd={wd}")
+    rng = np.random.default_rng(4242 + wd[0])
     shapes = [(3, 17), (64, 64), (10, 300), (5, 1000), (128, 96), (1025, 2048)]
     widths = [8, 7, 6, 5, 4, 6]
     lr, mom = (3, -5), (115, -7)
@@ -240,9 +241,9 @@ def test_update_multi_mixed_widths(ws):
         Wd, Vd, Gd = qt_to_dev(W), qt_to_dev(V), qt_to_dev(G)
         Wd.bits = b
         devs.append((Wd, Vd, Gd))
-    ie.ie_sgd_update_multi([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], lr, mom, ws=ws)
+    ie.ie_sgd_update_multi([d[0] for d in devs], [d[1] for d in devs], [d[2] for d in devs], lr, mom, wd, ws=ws)
     for (W, V, G, b), (Wd, Vd, Gd) in zip(cases, devs):
-        W2, V2 = o.sgd_update(W, V, G, o.Scalar(*lr), o.Scalar(*mom), w_bits=b)
+        W2, V2 = o.sgd_update(W, V, G, o.Scalar(*lr), o.Scalar(*mom), o.Scalar(*wd), w_bits=b)
         assert_same(Vd, V2, f"velocity {W.mant.shape} bits={b}")
         assert_same(Wd, W2, f"weight {W.mant.shape} bits={b}")
     assert ws.status() == 0
