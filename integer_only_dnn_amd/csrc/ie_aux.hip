@@ -301,26 +301,38 @@ __global__ __launch_bounds__(256) void pad_rows_z_kernel(const int8_t *in, const
     __shared__ int sh[4];
     const int z = blockIdx.y;
     const int8_t *ez = e_row ? e + (long long)z * R : e;
-    const int es = e_row ? exp_max_block(ez, R, sh) : (int)e[0];
-    if (blockIdx.x == 0 && threadIdx.x == 0) estar[z] = es;
     const int8_t *iz = in + (long long)z * R * cols;
     int8_t *oz = out + (long long)z * R * cols_p;
     const uint32_t cpr = (uint32_t)(cols_p >> 4);
     const uint32_t n = (uint32_t)R * cpr;
-    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-        const uint32_t r = fdiv32(i, dcpr);
-        const int c0 = (int)(i - r * cpr) << 4;
-        const int sh_ = e_row ? es - (int)ez[r] : 0;
+    const bool vec = (cols & 15) == 0 && ((uintptr_t)in & 15) == 0;
+    // chunk i: its row, first column and 16 bytes (zeros past the row)
+    auto fetch = [&](uint32_t i, uint32_t &r, int &c0) -> v4i {
+        r = fdiv32(i, dcpr);
+        c0 = (int)(i - r * cpr) << 4;
         const int valid = min(cols - c0, 16);
-        v4i v;
-        if (((uintptr_t)in & 3) == 0) {
-            v = load16_row(in, ((long long)z * R + r) * cols + c0, (long long)gridDim.y * R * cols, valid);
-        } else {
-            const int8_t *src = iz + (long long)r * cols + c0;
-            uint32_t wv[4] = {0, 0, 0, 0};
-            for (int j = 0; j < valid; ++j) wv[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
-            v = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
-        }
+        if (vec && valid == 16) return *(const v4i *)(iz + (long long)r * cols + c0);
+        if (((uintptr_t)in & 3) == 0)
+            return load16_row(in, ((long long)z * R + r) * cols + c0, (long long)gridDim.y * R * cols, valid);
+        const int8_t *src = iz + (long long)r * cols + c0;
+        uint32_t wv[4] = {0, 0, 0, 0};
+        for (int j = 0; j < valid; ++j) wv[j >> 2] |= (uint32_t)(uint8_t)src[j] << (8 * (j & 3));
+        return v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    };
+    // the first chunk's load goes out before the slice's largest exponent is
+    // reduced, so the two memory round trips overlap
+    const uint32_t i0 = blockIdx.x * 256 + threadIdx.x;
+    uint32_t r0 = 0;
+    int c00 = 0;
+    v4i v0 = v4i{0, 0, 0, 0};
+    if (i0 < n) v0 = fetch(i0, r0, c00);
+    const int es = e_row ? exp_max_block(ez, R, sh) : (int)e[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) estar[z] = es;
+    for (uint32_t i = i0; i < n; i += gridDim.x * 256) {
+        uint32_t r = r0;
+        int c0 = c00;
+        v4i v = i == i0 ? v0 : fetch(i, r, c0);
+        const int sh_ = e_row ? es - (int)ez[r] : 0;
         if (sh_ != 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = (int)rne_bytes4((uint32_t)v[j], sh_);
@@ -336,7 +348,7 @@ hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z
     const long long n = (long long)R * (cols_p >> 4);
     if (n >= (1ll << 31)) return hipErrorInvalidValue;
     prof_begin(st, PROF_ALIGN_Z);
-    hipLaunchKernelGGL(pad_rows_z_kernel, dim3(blocks_for(n > 0 ? n : 1, 256, 64), Z), dim3(256), 0, st, in, e,
+    hipLaunchKernelGGL(pad_rows_z_kernel, dim3(blocks_for(n > 0 ? n : 1, 1024, 64), Z), dim3(256), 0, st, in, e,
                        e_row, R, cols, cols_p, out, estar, make_fastdiv((uint32_t)(cols_p >> 4 > 0 ? cols_p >> 4 : 1)));
     prof_end(st, PROF_ALIGN_Z);
     return hipGetLastError();
