@@ -653,6 +653,7 @@ ie_status bmm(int form, int32_t batch, const ie_mat *A, const ie_mat *B, const i
     if (C->rows != Z * M || C->cols != N) return IE_ERR_SHAPE;
     if (C->group != IE_GROUP_ROW) return IE_ERR_UNSUPPORTED;
     if (K > MAX_CONTRACT || Z > 65535) return IE_ERR_UNSUPPORTED;
+    if (r16(M) > DIM_MAX || r16(N) > DIM_MAX) return IE_ERR_UNSUPPORTED;  // padded pitches stay int
     if (form != BMM_TN && r16(K) == K && (!aligned(A->mant, 16) || (form == BMM_NT && !aligned(B->mant, 16))))
         return IE_ERR_UNSUPPORTED;
     if (form == BMM_TN && ((long long)BK * r16(M) > WINDOW || (long long)BK * r16(N) > WINDOW))
