@@ -65,12 +65,12 @@ def test_bmm(form, shape, groups, ws):
 
 
 # Shapes that lead the planner to each tile and epilogue of the batched
-# kernel (512 work items fill the chip): 64x256 direct (A . B^T and A . B,
-# rows of 129..256), 128x128 direct (rows of 65..128) and round-to-odd (rows
-# past 256), 128x64 direct (rows up to 64), 64x64 direct and round-to-odd
-# (few slices).
-PLAN_SHAPES = [(128, 260, 200, 40), (256, 200, 100, 40), (100, 200, 300, 24), (256, 200, 50, 40),
-               (3, 150, 60, 90), (3, 150, 150, 90)]
+# kernel (512 work items fill the chip): 64x256 direct for A . B^T (rows of
+# 129..256; its one-step form when K <= 128), 128x128 direct (rows of
+# 65..128) and round-to-odd (rows past 256), 128x64 direct (rows up to 64),
+# 64x64 direct and round-to-odd (few slices).
+PLAN_SHAPES = [(128, 260, 200, 40), (128, 260, 200, 200), (256, 200, 100, 40), (100, 200, 300, 24),
+               (256, 200, 50, 40), (3, 150, 60, 90), (3, 150, 150, 90)]
 
 
 @pytest.mark.parametrize("form", list(FORMS))
