@@ -5,11 +5,13 @@ for every layer, the forward product, the input gradient and the weight
 gradient, then one integer SGD-momentum update of every layer's weights (a
 single multi-tensor call, as an optimiser step runs after the backward pass).
 
-Default workload: the 3x3 convolutions of a ResNet-18 on 32x32x3 inputs at
-batch 128 (NHWC, per-tensor activation exponents, per-output-channel weight
-gradient / velocity groups).  Other workloads (--workload) are the ViT-B and
-ViT-Ti block linears, the ResNet-50 bottleneck convolutions, the single
-small linear layer, the pointwise steps and the ViT-B attention products.
+Default workload: the bottleneck convolutions of a ResNet-50 on 224x224x3
+inputs at batch 128 (23 layer shapes, 52 instances, each with its own
+tensors; NHWC, per-tensor activation exponents, per-output-channel weight,
+weight-gradient and velocity exponents), the largest of the workloads.
+Other workloads (--workload) are the ResNet-18 3x3 convolutions on 32x32x3
+inputs, the ViT-B and ViT-Ti block linears, the single small linear layer,
+the pointwise steps and the ViT-B attention products.
 
 Output: one JSON line (rank 0).  `value` is the step's algorithmic int8 ops
 (2*M*N*K per product; the input gradient counted at the forward MAC count)
@@ -109,6 +111,8 @@ class Call:
         self.io = io            # algorithmic bytes of each contraction: operands read once, result written once
         self.outs = list(outs)  # int8 result bytes of each contraction, in launch order
         self.prep = list(prep)  # algorithmic bytes of each padding / alignment copy, in launch order
+        self.ios = None         # per-contraction algorithmic bytes, in launch order (default: io each)
+        self.pair_io = io       # a paired launch of two products: operands read once, both results written
         self.kinds = None
 
 
@@ -139,14 +143,17 @@ def build_resnet18(torch, ie, ws, batch):
             upd = wl.update_inputs(N, K, seed + 50000, w_group=wl.TENSOR)
             V = _dev(torch, ie, upd.V)
             ops = 2.0 * M * N * K
-            io = float(L.n * L.h * L.w * L.c + N * K + M * N)
+            io = _conv_ios(L, M, N, K)
             name = f"{L.name}#{inst}"
-            calls.append(Call(f"{name}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops, io=io,
-                              outs=[M * N]))
+            calls.append(Call(f"{name}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops,
+                              io=io["fwd"], outs=[M * N]))
             bwd_ops = ops * (1 if L.first else 2)
-            calls.append(Call(f"{name}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
-                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), bwd_ops, io=io,
-                              outs=([] if L.first else [L.n * L.h * L.w * L.c]) + [N * K]))
+            c = Call(f"{name}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
+                     ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), bwd_ops, io=io["wgrad"] if L.first else io["dgrad"],
+                     outs=([] if L.first else [L.n * L.h * L.w * L.c]) + [N * K])
+            c.ios = [io["wgrad"]] if L.first else [io["dgrad"], io["wgrad"]]
+            c.pair_io = io["pair"]
+            calls.append(c)
             params = N * K
             # read W, V, G and write W, V (1 byte each) + group exponents
             upd_bytes += 5.0 * params + 3.0 * N + 2.0
@@ -161,29 +168,57 @@ def build_resnet18(torch, ie, ws, batch):
     return calls, meta
 
 
+def _conv_ios(L, M, N, K):
+    """Algorithmic bytes of a convolution's products: forward (X, W read, Y
+    written), input gradient (dY, W read, dX written), weight gradient (dY, X
+    read, dW written), and the paired backward launch (dY, W, X read once, dX
+    and dW written)."""
+    x, w, y = float(L.n * L.h * L.w * L.c), float(N * K), float(M * N)
+    return {"fwd": x + w + y, "dgrad": y + w + x, "wgrad": y + x + w, "pair": y + w + x + x + w}
+
+
 def build_resnet50(torch, ie, ws, batch):
+    """Every bottleneck convolution instance of a ResNet-50 at batch 128 with
+    its own device tensors (the step's working set is several GB, far beyond
+    the 256 MB last-level cache), then one SGD-momentum update of every conv
+    weight (per-output-channel weight, velocity and gradient exponents)."""
     calls, meta = [], {"layers": [], "params": 0}
+    upd_w, upd_v, upd_g, upd_bytes = [], [], [], 0.0
     seed = 4000
     for L in wl.resnet50_layers(batch):
         seed += 1
         inp = wl.resnet50_conv_inputs(L, seed)
+        upd = wl.update_inputs(L.k, L.r * L.s * L.c, seed + 50000)
         d = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
         M, N, K = L.gemm_mnk()
-        X = _dev(torch, ie, inp.X, rows=L.n * L.h * L.w)
-        W = _dev(torch, ie, inp.W)
-        dY = _dev(torch, ie, inp.dY, rows=M)
-        Y = ie.Mat.empty(M, N, wl.TENSOR)
-        dX = ie.Mat.empty(L.n * L.h * L.w, L.c, wl.TENSOR)
-        dW = ie.Mat.empty(N, K, wl.ROW)
         ops = 2.0 * M * N * K
-        io = float(L.n * L.h * L.w * L.c + N * K + M * N)
-        for inst in range(L.count):   # identical shapes: reuse the tensors
+        io = _conv_ios(L, M, N, K)
+        for inst in range(L.count):
+            # distinct device copies per instance: no instance reads another's
+            # data from cache
+            X = _dev(torch, ie, inp.X, rows=L.n * L.h * L.w)
+            W = _dev(torch, ie, inp.W)
+            dY = _dev(torch, ie, inp.dY, rows=M)
+            V = _dev(torch, ie, upd.V)
+            Y = ie.Mat.empty(M, N, wl.TENSOR)
+            dX = ie.Mat.empty(L.n * L.h * L.w, L.c, wl.TENSOR)
+            dW = ie.Mat.empty(N, K, wl.ROW)
             calls.append(Call(f"{L.name}#{inst}:fwd", lambda d=d, X=X, W=W, Y=Y: ie.ie_conv_fwd(d, X, W, Y, ws), ops,
-                              io=io, outs=[M * N]))
-            calls.append(Call(f"{L.name}#{inst}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
-                              ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), 2 * ops, io=io,
-                              outs=[L.n * L.h * L.w * L.c, N * K]))
+                              io=io["fwd"], outs=[M * N]))
+            c = Call(f"{L.name}#{inst}:bwd", lambda d=d, X=X, W=W, dY=dY, dX=dX, dW=dW:
+                     ie.ie_conv_bwd(d, X, W, dY, dX, dW, ws), 2 * ops, io=io["dgrad"],
+                     outs=[L.n * L.h * L.w * L.c, N * K])
+            c.ios = [io["dgrad"], io["wgrad"]]
+            c.pair_io = io["pair"]
+            calls.append(c)
+            upd_bytes += 5.0 * N * K + 5.0 * N
+            upd_w.append(W)
+            upd_v.append(V)
+            upd_g.append(dW)
+            meta["params"] += N * K
         meta["layers"].append({"name": L.name, "count": L.count, "gemm_mnk": [M, N, K]})
+    calls.append(Call("update_all", lambda: ie.ie_sgd_update_multi(upd_w, upd_v, upd_g, wl.LR, wl.MOMENTUM, ws=ws),
+                      0.0, upd_bytes))
     return calls, meta
 
 
@@ -297,7 +332,8 @@ WORKLOADS = {
     "resnet18": ("resnet18_cifar_conv3x3_batch128", "ResNet-18 3x3 convolutions on 32x32x3 inputs, batch 128"),
     "vitb": ("vit_b_block_linears_128x197_plus_update_85M", "ViT-B block linears (128 x 197 tokens) + update of 84.9M params"),
     "vitti": ("vit_ti_block_linears_256x197", "ViT-Ti block linears (256 x 197 tokens)"),
-    "resnet50": ("resnet50_bottleneck_convs_batch128", "ResNet-50 bottleneck convolutions on 224x224x3 inputs, batch 128"),
+    "resnet50": ("resnet50_bottleneck_convs_batch128",
+                 "ResNet-50 bottleneck convolutions on 224x224x3 inputs, batch 128, + update of their 23.4M weights"),
     "linear_small": ("linear_64x256x128", "single linear layer 64x256 -> 128"),
     "vitb_attn": ("vit_b_attention_products_128x12_heads",
                   "ViT-B attention products per (image, head), forward and backward, batch 128, 12 heads, "
@@ -329,7 +365,25 @@ def build_workload(name, torch, ie, ws):
 # CPU baseline: the oracle on a bounded sample of the workload
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str):
+    out = _cpu_baseline(name)
+    out["cpu_model"] = cpu_model()
+    out["host_cpus"] = len(os.sched_getaffinity(0))
+    return out
+
+
+def _cpu_baseline(name: str):
     import oracle as o
     try:
         from threadpoolctl import threadpool_info
@@ -444,7 +498,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="resnet18", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="resnet50", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="also print the per-kernel breakdown")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -515,7 +569,12 @@ def main():
                     a["launches"] += 1
                     if is_gemm(kind):
                         a["ops"] += c.ops / n_gemm
-                        a["bytes"] += c.io
+                        if is_pair(kind):
+                            a["bytes"] += c.pair_io
+                        elif c.ios:
+                            a["bytes"] += c.ios[min(max(prod, 0), len(c.ios) - 1)]
+                        else:
+                            a["bytes"] += c.io
                     elif 2000 <= kind < 3000 and c.bytes:
                         a["bytes"] += c.bytes / n_upd
                     elif 3500 <= kind < 3600:

@@ -22,8 +22,9 @@
  *
  * Memory and execution:
  *   - every mantissa/exponent/workspace pointer is a DEVICE pointer owned by
- *     the caller; the library allocates no device memory and keeps no global
- *     state apart from the optional kernel timing below;
+ *     the caller; the library allocates no device memory, creates no stream
+ *     or event (the optional kernel timing below aside) and keeps no global
+ *     state apart from that timing;
  *   - matrices are row-major and contiguous; activations of convolutions are
  *     NHWC, viewed as a matrix [N*H*W x C]; weights are [K x R*S*C] (KRSC);
  *   - outputs are fully overwritten, mantissas and exponents; outputs must not
@@ -35,7 +36,15 @@
  *     runs asynchronously; calls sharing one workspace must be ordered on one
  *     stream;
  *   - argument errors are detected on the host and returned before anything
- *     is enqueued; launch failures return IE_ERR_HIP.
+ *     is enqueued; launch failures return IE_ERR_HIP;
+ *   - each product's execution plan (workgroup tile, epilogue, contraction
+ *     split) is chosen from its shape.  For tests and tuning only, the
+ *     environment variables IE_TILE="mi,ni[,mode[,splits]]" and
+ *     IE_WTILE="mi,ni,splits" force the plans of products and of weight
+ *     gradients; a forced plan without a built kernel, or one whose direct
+ *     epilogue would split a group across workgroups, returns
+ *     IE_ERR_UNSUPPORTED before anything is enqueued (as does any plan whose
+ *     buffers the carved workspace does not hold).
  */
 #ifndef IE_H
 #define IE_H
@@ -149,16 +158,18 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
                       const ie_mat *Y, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Backward convolution: input gradient dX (the exact adjoint of ie_conv_fwd
- * in X, W aligned over output channels when ROW-grouped) and weight gradient
- * dW (its adjoint in W, per output channel groups when ROW).  dX or dW may be
- * NULL to skip that output.  dX: TENSOR; dW: TENSOR or ROW.
- * With both outputs requested, the two products run as one grid where a
- * paired kernel covers their plans (16-channel multiples, row-grouped dW);
- * otherwise the weight gradient runs on a second stream that the library
- * keeps per device (default priority, created on first use), forked from
- * `stream` and joined back into it with events before the call returns.
- * Either way all work stays ordered on `stream` for the caller.
+ * Backward convolution ("Memory-Efficient Integer-Only Training of Deep
+ * Neural Networks", Figure 1a: the backward pass of every layer; Table 6:
+ * "Convolution -> Product"): the input gradient dX, the exact adjoint of
+ * ie_conv_fwd in X (W aligned over its output channels first when
+ * ROW-grouped), and the weight gradient dW, its adjoint in W (one exponent
+ * per output channel when ROW, Table 5).  dX or dW may be NULL to skip that
+ * output.  X, dY, dX: TENSOR; W, dW: TENSOR or ROW.
+ * With both outputs requested the two products run as one grid where a
+ * paired kernel covers their plans (round-to-odd input gradient, row-grouped
+ * weight gradient), else one after the other; all work is enqueued on
+ * `stream`, and the library creates no stream or event of its own.
+ * Limits as for ie_conv_fwd, with the contraction k*r*s <= 65536.
  */
 ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
                       const ie_mat *dY, const ie_mat *dX, const ie_mat *dW,
@@ -283,8 +294,8 @@ ie_status ie_device_status(void *ws, void *stream, uint32_t *flags, int clear);
  * a convolution's backward pass, 3500 / 3510 ReLU forward / backward, 3520 /
  * 3521 / 3530 the Sum's maximum, rounding and row-grouped passes) and returns how
  * many were recorded since the last read; the records are then cleared.
- * The timing records and the per-device second stream of ie_conv_bwd are the
- * library's only process-wide state; the timing records are not thread-safe.
+ * The timing records (and their events) are the library's only process-wide
+ * state; they are not thread-safe.
  */
 ie_status ie_profile_enable(int on);
 ie_status ie_profile_select(int kind);

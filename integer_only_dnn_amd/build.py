@@ -15,7 +15,11 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libie.so")
 SOURCES = ["ie_api.hip", "ie_aux.hip", "ie_update.hip", "ie_gemm_kk.hip", "ie_gemm_im2col.hip",
            "ie_gemm_dgrad.hip", "ie_gemm_dgrad_wt.hip", "ie_gemm_wgrad.hip", "ie_gemm_pair.hip",
-           "ie_pointwise.hip", "ie_gemm_batched.hip"]
+           "ie_gemm_pair_al.hip", "ie_pointwise.hip", "ie_gemm_batched.hip"]
+# host-only C++ (planner, argument checks, workspace layout): no GPU code
+HOST_SOURCES = ["ie_plan.cpp"]
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -47,6 +51,9 @@ def build(verbose: bool = False) -> str:
     for s in SOURCES:
         obj = os.path.join(OBJ, s.replace(".hip", ".o"))
         jobs.append(([HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], obj))
+    for s in HOST_SOURCES:
+        obj = os.path.join(OBJ, s.replace(".cpp", ".o"))
+        jobs.append(([CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], obj))
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
     tmp = LIB + ".tmp"

@@ -358,13 +358,6 @@ hipError_t launch_pad_rows_z(const int8_t *in, const int8_t *e, int e_row, int Z
 // Host helpers
 // ---------------------------------------------------------------------------
 
-FastDiv make_fastdiv(uint32_t d) {
-    int l = 0;
-    while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
-    int s = 31 + l;
-    uint64_t m = ((1ull << s) + d - 1) / d;
-    return FastDiv{(uint32_t)m, s};
-}
 
 hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                        int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
@@ -728,9 +721,6 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
 // largest need, and the row is rounded and stored.
 // Short rows (at most 512 chunks) take 1024 threads, so more split subsets
 // load at once; long rows take 512 threads with up to SR_MAXV chunks each.
-constexpr int SR_THR = 512;
-constexpr int SR_THR_SHORT = 1024;
-constexpr int SR_MAXV = 4;  // chunks per thread when Q == 1
 constexpr int SR_FEW = 2;   // up to this many splits, a thread loads all of its chunks before summing
 
 __device__ __forceinline__ int block_max_n(int v, int *sh) {
@@ -917,10 +907,6 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void s
                           relu, wq, blockIdx.x, gridDim.x);
 }
 
-bool split_round_rows_fits(int Nout, int mc, int mcp) {
-    const int vw = (mc == mcp && Nout % 4 == 0) ? 4 : 1;
-    return Nout / vw <= SR_THR * SR_MAXV;
-}
 
 // Arguments of a split finalize by rows and its grid.
 struct SplitFin {

@@ -7,10 +7,9 @@ namespace ie {
 hipError_t launch_gemm_dgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
     if (B.kind == LD_WT) return launch_gemm_dgrad_wt(A, B, M, N, K, t, splits, k_chunk, partial, ep, st);
-    IE_TILE_CASE(LD_DGRAD, LD_K, 2, 2)
-    IE_TILE_CASE(LD_DGRAD, LD_K, 4, 1)
-    IE_TILE_CASE(LD_DGRAD, LD_K, 2, 1)
-    IE_TILE_CASE(LD_DGRAD, LD_K, 1, 1)
+#define IE_CASE(a, b) IE_TILE_CASE(LD_DGRAD, LD_K, a, b)
+    IE_TILES_CONV(IE_CASE)
+#undef IE_CASE
     return hipErrorInvalidValue;
 }
 

@@ -6,10 +6,9 @@ namespace ie {
 
 hipError_t launch_gemm_dgrad_wt(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                                 int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
-    IE_TILE_CASE(LD_DGRAD, LD_WT, 2, 2)
-    IE_TILE_CASE(LD_DGRAD, LD_WT, 4, 1)
-    IE_TILE_CASE(LD_DGRAD, LD_WT, 2, 1)
-    IE_TILE_CASE(LD_DGRAD, LD_WT, 1, 1)
+#define IE_CASE(a, b) IE_TILE_CASE(LD_DGRAD, LD_WT, a, b)
+    IE_TILES_CONV(IE_CASE)
+#undef IE_CASE
     return hipErrorInvalidValue;
 }
 

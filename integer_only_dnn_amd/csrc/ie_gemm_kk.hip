@@ -6,12 +6,9 @@ namespace ie {
 
 hipError_t launch_gemm_kk(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                           int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
-    IE_TILE_CASE(LD_K, LD_K, 2, 2)
-    IE_TILE_CASE(LD_K, LD_K, 4, 1)
-    IE_TILE_CASE(LD_K, LD_K, 1, 4)
-    IE_TILE_CASE(LD_K, LD_K, 2, 1)
-    IE_TILE_CASE(LD_K, LD_K, 1, 2)
-    IE_TILE_CASE(LD_K, LD_K, 1, 1)
+#define IE_CASE(a, b) IE_TILE_CASE(LD_K, LD_K, a, b)
+    IE_TILES_DENSE(IE_CASE)
+#undef IE_CASE
     return hipErrorInvalidValue;
 }
 

@@ -12,17 +12,15 @@ namespace ie {
 hipError_t launch_gemm_wgrad(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                              int k_chunk, bool partial, const Epi &ep, hipStream_t st) {
     if (!partial) return hipErrorInvalidValue;
+#define IE_CASE_T(a, b) IE_WG_CASE(LD_T, a, b)
+#define IE_CASE_I(a, b) IE_WG_CASE(LD_IM2COL_T, a, b)
     if (B.kind == LD_T) {
-        IE_WG_CASE(LD_T, 2, 2)
-        IE_WG_CASE(LD_T, 1, 4)
-        IE_WG_CASE(LD_T, 4, 1)
-        IE_WG_CASE(LD_T, 1, 1)
+        IE_TILES_WGRAD(IE_CASE_T)
     } else {
-        IE_WG_CASE(LD_IM2COL_T, 2, 2)
-        IE_WG_CASE(LD_IM2COL_T, 1, 4)
-        IE_WG_CASE(LD_IM2COL_T, 4, 1)
-        IE_WG_CASE(LD_IM2COL_T, 1, 1)
+        IE_TILES_WGRAD(IE_CASE_I)
     }
+#undef IE_CASE_T
+#undef IE_CASE_I
     return hipErrorInvalidValue;
 }
 

@@ -5,10 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace ie {
+#include "ie_plan.h"
 
-constexpr int BK = 128;   // contraction step of a workgroup tile (bytes)
-constexpr int NCU = 256;  // compute units of an MI355X
+namespace ie {
 
 // Exponent of operand rows: per-row int8 array (row != 0), one int8 for the
 // whole tensor (row == 0), or, when e32 is set, one int32 computed on the
@@ -60,48 +59,12 @@ enum LoaderKind {
                       // k = (r, s, k_out) over kp; weight read in place [k_out][r][s][c]
 };
 
-// n / d = (n * m) >> s for 0 <= n < 2^31 (m = ceil(2^s / d), s = 31 + ceil(log2 d)).
-struct FastDiv {
-    uint32_t m;
-    int s;
-};
-FastDiv make_fastdiv(uint32_t d);
-
-// Convolution geometry.  cp / kp: input / output channel counts as stored in
-// the operands the kernels read (rounded up to multiples of 16 with zeros);
-// dc divides by cp, dk by kp, dst by the stride.
-struct ConvGeom {
-    int n, h, w, c, k, r, s, stride, pad, p, q, cp, kp;
-    FastDiv dpq, dq, dhw, dw, dc, ds, dk, dst;
-    // Advance of the contraction index by one BK step, for the loaders:
-    //   (r, s, c) over cp:  im_dc = BK % cp, im_ds = (BK / cp) % s, im_dr = BK / (cp s);
-    //                       the tap offset (r w + s) cp + c moves by im_d0, plus im_d1
-    //                       when s wraps;
-    //   (r, s, ko) over kp: dg_dc, dg_ds, dg_dr likewise; ko r s c + (r s_ + s) c moves
-    //                       by wt_d0, plus wt_d1 when ko wraps;
-    //   output pixels:      px_dq = BK % q, px_dp = (BK / q) % p; the NHWC offset of
-    //                       tap (0, 0) moves by px_d0, plus px_d1 when q wraps and px_d2
-    //                       when p wraps; px_nw images cover any BK consecutive pixels;
-    //   st_inv = ceil(2^16 / stride).
-    int im_dc, im_ds, im_dr, im_d0, im_d1;
-    int dg_dc, dg_ds, dg_dr, wt_d0, wt_d1;
-    int px_dq, px_dp, px_d0, px_d1, px_d2, px_nw;
-    int st_inv;
-};
-
 struct Operand {
     int kind;
     const int8_t *base;
     long long ld;
     int rows;         // valid rows of this operand (GEMM M or N)
     ConvGeom g;
-};
-
-// Workgroup tile: 4 waves (2 x 2), each 32*mi x 32*ni; workgroup 64*mi x 64*ni.
-struct Tile {
-    int mi, ni;
-    int bm() const { return 64 * mi; }
-    int bn() const { return 64 * ni; }
 };
 
 // C[m][n] = sum_k A(m, k) B(n, k) over k in [0, K), split into `splits`
@@ -194,7 +157,6 @@ hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch,
 // Split finalize of row groups in one pass (sums never stored): output
 // [M x Nout] from partials [splits][M][src_pitch] with the column map of
 // launch_round_sums.  Requires split_round_rows_fits(Nout, mc, mcp).
-bool split_round_rows_fits(int Nout, int mc, int mcp);
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
                                    int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, int relu = 0);

@@ -182,15 +182,18 @@ def test_vit_b_update(arena, ws):
 # ResNet-50 bottleneck convolutions (per-channel weight exponents)
 # ---------------------------------------------------------------------------
 
-R50 = {L.name: L for L in wl.resnet50_layers(128)}
-R50_PICK = ["s1_3x3_64@56", "s2_3x3_128_s2@56", "s3_1x1_1024_256@14", "s4_1x1_512_2048@7", "s4_sc_1024_2048_s2@14"]
+R50 = wl.resnet50_layers(128)
 
 
-@pytest.mark.parametrize("name", R50_PICK)
-def test_resnet50_layer(name, ws):
-    L = R50[name]
-    announce(f"config resnet50 {name} batch 128: fwd, dgrad, wgrad")
-    inp = wl.resnet50_conv_inputs(L, 4001 + R50_PICK.index(name))
+@pytest.mark.parametrize("li", range(len(R50)), ids=[L.name for L in R50])
+def test_resnet50_layer(li, ws):
+    """Every distinct bottleneck convolution of a ResNet-50 at batch 128:
+    forward, input gradient and weight gradient compared in full, then the
+    SGD update of the per-output-channel weight."""
+    L = R50[li]
+    name = L.name
+    announce(f"config resnet50 {name} batch 128: fwd, dgrad, wgrad, update")
+    inp = wl.resnet50_conv_inputs(L, 4001 + li)
     d = o.ConvShape(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
     dd = ie.conv_desc(L.n, L.h, L.w, L.c, L.k, L.r, L.s, L.stride, L.pad)
     X, W, dY = _qt(inp.X), _qt(inp.W), _qt(inp.dY)
@@ -201,9 +204,19 @@ def test_resnet50_layer(name, ws):
     Y = ie.Mat.empty(M, N, o.TENSOR)
     ie.ie_conv_fwd(dd, Xd, Wd, Y, ws)
     assert_same(Y, o.conv_fwd(d, X, W, o.TENSOR), "conv fwd")
+    del Y
     dX = ie.Mat.empty(L.n * L.h * L.w, L.c, o.TENSOR)
     dW = ie.Mat.empty(N, K, o.ROW)
     ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, dW, ws)
     assert_same(dX, o.conv_dgrad(d, dY, W, o.TENSOR), "conv dgrad")
-    assert_same(dW, o.conv_wgrad(d, dY, X, o.ROW), "conv wgrad")
+    del dX
+    wdW = o.conv_wgrad(d, dY, X, o.ROW)
+    assert_same(dW, wdW, "conv wgrad")
+    upd = wl.update_inputs(N, K, 54001 + li)
+    V = _qt(upd.V)
+    Vd = to_dev(V.mant, V.exp, V.group)
+    ie.ie_sgd_update(Wd, Vd, dW, wl.LR, wl.MOMENTUM, ws=ws)
+    W2, V2 = o.sgd_update(W, V, wdW, o.Scalar(*wl.LR), o.Scalar(*wl.MOMENTUM))
+    assert_same(Vd, V2, "velocity")
+    assert_same(Wd, W2, "weight")
     assert ws.status() == 0
