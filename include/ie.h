@@ -65,7 +65,8 @@ typedef enum {
     IE_ERR_EXP_RANGE = 5,   /* reported by ie_device_status callers */
     IE_ERR_UNSUPPORTED = 6, /* valid but outside what this library supports */
     IE_ERR_HIP = 7,         /* a HIP runtime call failed */
-    IE_ERR_BITS = 8         /* ie_mat.bits outside {0, 2..8}, or a velocity not INT8 */
+    IE_ERR_BITS = 8,        /* ie_mat.bits outside {0, 2..8}, or a velocity not INT8 */
+    IE_ERR_SCRATCH = 9      /* the call needs more than the fixed scratch of ie_linear_fwd_noalloc */
 } ie_status;
 
 typedef enum { IE_GROUP_TENSOR = 0, IE_GROUP_ROW = 1 } ie_group;
@@ -124,6 +125,26 @@ ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream);
  */
 ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y,
                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ie_linear_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * There is no workspace argument: the call uses a fixed scratch array of
+ * IE_NOALLOC_SCRATCH_BYTES that the library keeps in device memory (one copy
+ * per GPU, held until the process ends, its address looked up on the first
+ * call on each device), and calls no allocating routine.  Results, limits and
+ * errors are those of ie_linear_fwd, plus IE_ERR_SCRATCH (nothing enqueued)
+ * when the shape needs more scratch than that (ie_linear_fwd_workspace(M, N,
+ * K) > IE_NOALLOC_SCRATCH_BYTES).  flags: a device word into which the
+ * exponent-range flag (IE_FLAG_EXP_RANGE) is ORed, or NULL to drop it.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind (nothing in it needs to start at any value): calls that may overlap
+ * on one GPU (different streams, different host threads) race and must be
+ * ordered by the caller.
+ */
+#define IE_NOALLOC_SCRATCH_BYTES (64u << 20)
+ie_status ie_linear_fwd_noalloc(const ie_mat *X, const ie_mat *W, const ie_mat *Y,
+                                uint32_t *flags, void *stream);
 
 /*
  * Input gradient of a linear layer, dX = dY . W (Figure 1a, backward).

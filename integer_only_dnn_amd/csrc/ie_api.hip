@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/ie.h"
@@ -13,7 +14,27 @@
 
 using namespace ie;
 
+// Fixed device scratch of ie_linear_fwd_noalloc (one copy per GPU, held until
+// the process ends).  Host code never uses this name as an address: each
+// device's copy is found once with hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[IE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> g_scratch[MAX_DEVICES];
+
+// The current device's copy of `scratch` (looked up on the first call on that
+// device; the lookup is idempotent, so racing first calls agree), or nullptr.
+void *scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+    return p;
+}
 
 ie_status hip_status(hipError_t e) { return e == hipSuccess ? IE_OK : IE_ERR_HIP; }
 
@@ -419,7 +440,7 @@ ie_status ie_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 }
 
 static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
-                            void *stream, int relu) {
+                            void *stream, int relu, uint32_t *flags_out = nullptr) {
     IE_CHECK(check_mat(X));
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(Y));
@@ -431,7 +452,7 @@ static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, v
     const Force f = force_product();
     if (ws_bytes < linear_fwd_ws(M, N, K, f)) return IE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    uint32_t *flags = (uint32_t *)ws;
+    uint32_t *flags = flags_out ? flags_out : (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
     const LinearFwdWs w = carve_linear_fwd(c, M, N, K, f);
     const long long Kp = r16(K);
@@ -452,6 +473,19 @@ static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, v
 ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
                         void *stream) {
     return linear_fwd(X, W, Y, ws, ws_bytes, stream, 0);
+}
+
+ie_status ie_linear_fwd_noalloc(const ie_mat *X, const ie_mat *W, const ie_mat *Y, uint32_t *flags, void *stream) {
+    IE_CHECK(check_mat(X));
+    IE_CHECK(check_mat(W));
+    IE_CHECK(check_mat(Y));
+    if (W->cols != X->cols || Y->rows != X->rows || Y->cols != W->rows) return IE_ERR_SHAPE;
+    if (linear_fwd_ws(X->rows, W->rows, X->cols, force_product()) > IE_NOALLOC_SCRATCH_BYTES) return IE_ERR_SCRATCH;
+    void *p = scratch_ptr();
+    if (!p) return IE_ERR_HIP;
+    // the scratch's flag header stands in for the caller's flag word when
+    // none is given (nothing reads it then)
+    return linear_fwd(X, W, Y, p, IE_NOALLOC_SCRATCH_BYTES, stream, 0, flags);
 }
 
 ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act, void *ws, size_t ws_bytes,
@@ -780,6 +814,7 @@ const char *ie_status_str(ie_status s) {
         case IE_ERR_UNSUPPORTED: return "IE_ERR_UNSUPPORTED";
         case IE_ERR_HIP: return "IE_ERR_HIP";
         case IE_ERR_BITS: return "IE_ERR_BITS";
+        case IE_ERR_SCRATCH: return "IE_ERR_SCRATCH";
     }
     return "IE_ERR_UNKNOWN";
 }

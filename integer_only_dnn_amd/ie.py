@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libie.so")
 
 STATUS = {0: "IE_OK", 1: "IE_ERR_NULL", 2: "IE_ERR_SHAPE", 3: "IE_ERR_GROUP", 4: "IE_ERR_WORKSPACE",
-          5: "IE_ERR_EXP_RANGE", 6: "IE_ERR_UNSUPPORTED", 7: "IE_ERR_HIP", 8: "IE_ERR_BITS"}
+          5: "IE_ERR_EXP_RANGE", 6: "IE_ERR_UNSUPPORTED", 7: "IE_ERR_HIP", 8: "IE_ERR_BITS", 9: "IE_ERR_SCRATCH"}
 
 
 class IeError(RuntimeError):
@@ -55,6 +55,7 @@ EXPORTS = [
     ("ie_sgd_update_multi_workspace", c_size_t, [c_int32]),
     ("ie_workspace_init", c_int, [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_fwd", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_fwd_noalloc", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_void_p]),
     ("ie_linear_bwd_dx", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_bwd_dw", c_int, [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_conv_fwd", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_void_p, c_size_t, c_void_p]),
@@ -194,6 +195,15 @@ def ie_linear_fwd(X: Mat, W: Mat, Y: Mat, ws: Workspace) -> None:
     x, w, y = X.c(), W.c(), Y.c()
     p, b = ws.get(_ws_size("ie_linear_fwd_workspace", x.rows, w.rows, x.cols))
     _check(lib().ie_linear_fwd(byref(x), byref(w), byref(y), p, b, _stream(ws.device)), "ie_linear_fwd")
+
+
+def ie_linear_fwd_noalloc(X: Mat, W: Mat, Y: Mat, flags: torch.Tensor | None = None) -> None:
+    """ie_linear_fwd on the library's fixed device scratch (no workspace);
+    flags: an int32 device tensor receiving the exponent-range flag, or None."""
+    x, w, y = X.c(), W.c(), Y.c()
+    fp = c_void_p(flags.data_ptr()) if flags is not None else None
+    _check(lib().ie_linear_fwd_noalloc(byref(x), byref(w), byref(y), fp, _stream(X.mant.device)),
+           "ie_linear_fwd_noalloc")
 
 
 def ie_linear_bwd_dx(dY: Mat, W: Mat, dX: Mat, ws: Workspace) -> None:
