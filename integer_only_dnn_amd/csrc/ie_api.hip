@@ -122,6 +122,16 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
         IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st, relu));
         return IE_OK;
     }
+    if (pl.mode == PLAN_RECOMP) {
+        // group maxima first, then the product again, rounded straight to int8
+        ep.tneed = pw.tneed;
+        ep.tneed_n = rg ? 0 : recomp_grid(M, N, pl.t);
+        ep.mode = EPI_MAX;
+        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
+        ep.mode = EPI_GIVEN;
+        IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
+        return IE_OK;
+    }
     ep.partial = pw.partial;
     ep.split_stride = M * N;
     if (rg && split_round_rows_fits((int)N, 1, 1)) {
@@ -184,10 +194,11 @@ ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K
 }
 
 // Input and weight gradient of a convolution in one paired launch, when both
-// plans allow it: the input gradient as a round-to-odd product (B1: the
-// weight read in place, or its aligned transposed copy, already written), the
-// weight gradient as a split contraction with the fused row finalize.
-// IE_ERR_UNSUPPORTED, with nothing launched, otherwise.
+// plans allow it: the input gradient as a round-to-odd product, or as the
+// second pass of a recomputed one (its first pass launched just before), B1
+// being the weight read in place or its aligned transposed copy, already
+// written; the weight gradient as a split contraction with the fused row
+// finalize.  IE_ERR_UNSUPPORTED, with nothing launched, otherwise.
 ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, ExpSrc ew, const ie_mat *dY,
                         const ie_mat *dX, const ie_mat *dW, const int8_t *dys, int8_t *xp, const ConvBwdWs &cw,
                         uint32_t *flags, hipStream_t st) {
@@ -201,7 +212,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     const Operand B2{LD_IM2COL_T, xp ? xp : X->mant, g.cp, (int)rscp, g};
     const int fam1 = family_of(A1, B1);
     const Plan p1 = plan_product(nhw, g.c, rskp, 0, fam1, force_product());
-    if (p1.mode != PLAN_RTO) return IE_ERR_UNSUPPORTED;
+    if (p1.mode != PLAN_RTO && p1.mode != PLAN_RECOMP) return IE_ERR_UNSUPPORTED;
     const Plan p2 = plan_wgrad(g.k, rscp, npq, FAM_WGRAD_CONV, force_wgrad());
     if (!gemm_pair_supported(A1, B1, p1.t, A2, B2, p2.t)) return IE_ERR_UNSUPPORTED;
     if (checked_plan(p1, nhw, g.c, rskp, 0, fam1, cw.pw.n, product_needs(p1, nhw, g.c, 0)) != IE_OK ||
@@ -223,6 +234,13 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     e1.v16 = cw.pw.v16;
     e1.p16 = cw.pw.p16;
     e1.q = mat_q(dX);
+    if (p1.mode == PLAN_RECOMP) {
+        e1.tneed = cw.pw.tneed;
+        e1.tneed_n = recomp_grid(nhw, g.c, p1.t);
+        e1.mode = EPI_MAX;
+        IE_TRY(launch_gemm(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, 1, p1.k_chunk, false, e1, st));
+        e1.mode = EPI_GIVEN;
+    }
     Epi e2;
     memset(&e2, 0, sizeof e2);
     e2.partial = cw.w.partial;
@@ -233,6 +251,11 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     e2.q = mat_q(dW);
     IE_TRY(launch_gemm_pair(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
                             (int)npq, p2.t, p2.splits, p2.k_chunk, e2, st));
+    if (p1.mode == PLAN_RECOMP) {
+        IE_TRY(launch_split_round_rows(cw.w.partial, p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy,
+                                       ex, dW->mant, dW->exp, flags, mat_q(dW), st));
+        return IE_OK;
+    }
     IE_TRY(launch_finalize_pair(cw.pw.v16, cw.pw.p16, (int)nhw, g.c, p1.t, dX->mant, dX->exp, cw.w.partial,
                                 p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex, dW->mant, dW->exp,
                                 flags, mat_q(dW), st));

@@ -256,15 +256,45 @@ hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, con
 
 // w viewed as [A][B][C] (row exponent e[a], or e[0]): out[c][b][a] =
 // w[a][b][c] at the largest row exponent e*, zero for A <= a < Ap (output
-// pitch Ap).  Every block finds e* itself (A bytes); block 0 stores it.
+// pitch Ap, a multiple of 16).  Every block finds e* itself (A bytes); block
+// 0 stores it.  A block moves a 64 x 64 tile through LDS: with C a multiple
+// of 16 (vec), each thread loads 16 bytes of one row a and stores 16 bytes
+// of one output row c; otherwise bytes one at a time.
 __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, const int8_t *e, int e_row, int A,
-                                                              int B, int C, int Ap, int8_t *out, int *estar_out) {
-    __shared__ int8_t tile[64][65];
+                                                              int B, int C, int Ap, int8_t *out, int *estar_out,
+                                                              int vec) {
+    constexpr int TP = 64 + 16;  // tile pitch
+    __shared__ __attribute__((aligned(16))) int8_t tile[64 * TP];
     __shared__ int sh[4];
     const int es = e_row ? exp_max_block(e, A, sh) : (int)e[0];
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) estar_out[0] = es;
-    int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
+    const int t = threadIdx.x;
+    if (vec) {
+        const int la = t >> 2, lc = (t & 3) * 16;
+        const int a = a0 + la, c = c0 + lc;
+        v4i v = v4i{0, 0, 0, 0};
+        if (a < A && c < C) {
+            v = *(const v4i *)(w + ((long long)a * B + b) * C + c);
+            const int s = es - (e_row ? (int)e[a] : es);
+            if (s != 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = (int)rne_bytes4((uint32_t)v[k], s);
+            }
+        }
+        *(v4i *)(tile + la * TP + lc) = v;
+        __syncthreads();
+        const int oc = t >> 2, oa = (t & 3) * 16;
+        if (c0 + oc < C && a0 + oa < Ap) {
+            uint32_t d[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) d[j >> 2] |= (uint32_t)(uint8_t)tile[(oa + j) * TP + oc] << (8 * (j & 3));
+            *(v4i *)(out + ((long long)(c0 + oc) * B + b) * Ap + a0 + oa) =
+                v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+        }
+        return;
+    }
+    for (int i = t; i < 64 * 64; i += 256) {
         int la = i >> 6, lc = i & 63;
         int a = a0 + la, c = c0 + lc;
         int8_t v = 0;
@@ -272,13 +302,13 @@ __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, c
             int ea = e_row ? (int)e[a] : es;
             v = (int8_t)rne_shift32(w[((long long)a * B + b) * C + c], es - ea);
         }
-        tile[la][lc] = v;
+        tile[la * TP + lc] = v;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    for (int i = t; i < 64 * 64; i += 256) {
         int lc = i >> 6, la = i & 63;
         int a = a0 + la, c = c0 + lc;
-        if (a < Ap && c < C) out[((long long)c * B + b) * Ap + a] = tile[la][lc];
+        if (a < Ap && c < C) out[((long long)c * B + b) * Ap + a] = tile[la * TP + lc];
     }
 }
 
@@ -286,8 +316,10 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, i
                                   int8_t *out, int *estar_out, hipStream_t st) {
     if (Ap <= 0 || B <= 0 || C <= 0) return hipSuccess;
     dim3 grid((C + 63) / 64, (Ap + 63) / 64, B);
+    const int vec = C % 16 == 0 && Ap % 16 == 0 && ((uintptr_t)w % 16) == 0 && ((uintptr_t)out % 16) == 0;
     prof_begin(st, PROF_ALIGN);
-    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, A, B, C, Ap, out, estar_out);
+    hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, A, B, C, Ap, out, estar_out,
+                       vec);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }

@@ -653,8 +653,10 @@ struct TileLds1 {
 // workgroups of its grid (or of its part of a paired grid); lds points to
 // TileLds bytes of shared memory (TileLds1 when ONE: a contraction of at
 // most one step, loaded once, with no pipeline and no second buffer).
+// Returns the tile's group maximum in the first pass of a recomputed
+// whole-tensor product (EPI_MAX), NEED_NONE otherwise.
 template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false>
-__device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, int M, int N, int K, int k_chunk,
+__device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int M, int N, int K, int k_chunk,
                                           int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
@@ -690,6 +692,13 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
     } else {
         // group maxima of the split finalize start empty (it runs after this grid)
         for (int i = bid * NTHR + tid; i < ep.gneed_n; i += nblk * NTHR) ep.gneed[i] = NEED_NONE;
+    }
+    // second pass of a recomputed whole-tensor product: the first pass's
+    // maxima, loaded now so that they land during the main loop
+    int given = NEED_NONE;
+    if constexpr (!PARTIAL) {
+        if (ep.mode == EPI_GIVEN && !ep.row_group)
+            for (int i = tid; i < ep.tneed_n; i += NTHR) given = max(given, ep.tneed[i]);
     }
 
     constexpr bool KS = KSlice<MI, NI>::value;
@@ -911,7 +920,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                 for (int r = 0; r < 16; ++r) stage(ES4{}, a, b, r, acc[a][b][r]);
         __syncthreads();
         flush(ES4{}, ep.partial + (long long)z * ep.split_stride, N, (N & 3) == 0);
-        return;
+        return NEED_NONE;
     } else {
         int *red = (int *)(lds + LDSB) - 2 * BMt;  // maxima, at the top of LDS
         int *scr = red - 16;                             // block reductions
@@ -923,12 +932,16 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
         const int wq = ep.q;  // results have |C| <= 2^wq - 1
         const int ea0 = seA[0];
         const int eb0 = seB[0];
-        const bool direct = ep.mode == EPI_DIRECT;
+        const int mode = ep.mode;
+        const bool direct = mode == EPI_DIRECT || mode == EPI_GIVEN;  // int8 results from this pass
 
         if (!ep.row_group) {
-            // whole-tensor group: one maximum for the tile
+            // whole-tensor group: one maximum for the tile (or, in the second
+            // pass of a recomputed product, the first pass's maxima)
             int tmax;
-            if (uni) {
+            if (mode == EPI_GIVEN) {
+                tmax = given;
+            } else if (uni) {
                 // largest |acc| from the signed maximum and minimum, two
                 // values per three-input max / min
                 int hi = 0, lo = 0;
@@ -958,6 +971,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             if (lane == 0) red[wave] = tmax;
             __syncthreads();
             const int gmax = max(max(red[0], red[1]), max(red[2], red[3]));
+            if (mode == EPI_MAX) return gmax;  // nothing stored in the first pass
             // the result's exponent (direct) or the round-to-odd position
             int e = 0, p = 0;
             if (direct) {
@@ -1105,12 +1119,23 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
                 } else {
                     rm = kmax;
                 }
+                if (mode == EPI_MAX) {
+                    // first pass: this (row, column tile)'s need only
+                    if (row < M) ep.tneed[(long long)row * n_ct + tile_n] = rm;
+                    continue;
+                }
+                if (mode == EPI_GIVEN) {
+                    // second pass: the row's exponent from every column tile's need
+                    rm = NEED_NONE;
+                    if (row < M)
+                        for (int j = 0; j < n_ct; ++j) rm = max(rm, ep.tneed[(long long)row * n_ct + j]);
+                }
                 int tgt;
                 if (direct) {
                     tgt = max(E_MIN, rm);
                     ovf |= tgt > E_MAX;
                     tgt = min(tgt, E_MAX);
-                    if (row < M) ep.out_exp[row] = (int8_t)tgt;
+                    if (row < M && tile_n == 0) ep.out_exp[row] = (int8_t)tgt;
                     rowf[tr] = __builtin_ldexpf(1.0f, eav + ebmin - tgt);
                 } else {
                     tgt = rm == NEED_NONE ? P_NONE : rm - 2;
@@ -1121,6 +1146,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
             }
             if (ovf) atomicOr(ep.flags, 1u);
             __syncthreads();
+            if (mode == EPI_MAX) return NEED_NONE;  // nothing stored in the first pass
             // 3. the elements, with the mode and the path fixed per instance
             auto elems = [&](auto dir_tag, auto fp_tag) {
                 constexpr bool DIR = decltype(dir_tag)::value, FP = decltype(fp_tag)::value;
@@ -1164,6 +1190,7 @@ __device__ __forceinline__ void gemm_tile(const Operand &A, const Operand &B, in
         __syncthreads();
         if (direct) flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0);
         else flush(ES2{}, ep.v16, N, (N & 7) == 0);
+        return NEED_NONE;
     }
 }
 
@@ -1172,6 +1199,38 @@ __global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_i8_kernel(Ope
                                                                          int k_chunk, int TM, int S, Epi ep) {
     __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
     gemm_tile<KA, KB, MI, NI, PARTIAL>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
+}
+
+// First pass of a recomputed product (EPI_MAX): a persistent grid walks the
+// tiles (item = blockIdx.x + j * gridDim.x; gridDim.x a multiple of 8 keeps
+// item % 8 on the workgroup's XCD), finding group maxima without storing
+// values.  Whole-tensor groups: each workgroup writes its running maximum to
+// tneed[blockIdx.x]; row groups: the tiles write tneed[row][column tile].
+template <int KA, int KB, int MI, int NI>
+__global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_max_kernel(Operand A, Operand B, int M, int N,
+                                                                            int K, int TM, int items, Epi ep) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
+    int run = NEED_NONE;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        run = max(run, gemm_tile<KA, KB, MI, NI, false>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
+        __syncthreads();  // the next item's stages reuse the LDS
+    }
+    if (!ep.row_group && threadIdx.x == 0) ep.tneed[blockIdx.x] = run;
+}
+
+template <int KA, int KB, int MI, int NI>
+hipError_t launch_max(const Operand &A, const Operand &B, int M, int N, int K, const Epi &ep, hipStream_t st) {
+    const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
+    const int items = TM * TN;
+    const int grid = recomp_grid(M, N, Tile{MI, NI});
+    if (grid <= 0) return hipSuccess;
+    if (!ep.row_group && ep.tneed_n != grid) return hipErrorInvalidValue;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * EPI_MAX + 10 * KA + KB;
+    prof_begin(st, kind);
+    hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K, TM, items,
+                       ep);
+    prof_end(st, kind);
+    return hipGetLastError();
 }
 
 // Two independent products in one grid: the first part's workgroups (a
@@ -1307,6 +1366,7 @@ hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, i
 // Dispatch over a tile list inside one translation unit.
 #define IE_TILE_CASE(KA, KB, MI_, NI_)                                                                   \
     if (t.mi == MI_ && t.ni == NI_) {                                                                    \
+        if (!partial && ep.mode == EPI_MAX) return launch_max<KA, KB, MI_, NI_>(A, B, M, N, K, ep, st);   \
         return partial ? launch_one<KA, KB, MI_, NI_, true>(A, B, M, N, K, splits, k_chunk, ep, st)       \
                        : launch_one<KA, KB, MI_, NI_, false>(A, B, M, N, K, splits, k_chunk, ep, st);     \
     }

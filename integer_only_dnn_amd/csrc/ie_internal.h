@@ -29,7 +29,12 @@ __device__ __forceinline__ int exp_at(const ExpSrc &e, int idx) {
 //   DIRECT  - every result group lies inside the workgroup tile
 //   RTO     - round-to-odd int16 values at a provisional exponent + group maxima
 //   PARTIAL - exact int32 partial sums of one contraction chunk
-enum EpiKind { EPI_DIRECT = 0, EPI_RTO = 1, EPI_PARTIAL = 2 };
+//   MAX     - first pass of a recomputed product: group maxima only, no
+//             values stored (whole tensor: one running maximum per workgroup
+//             of a persistent grid; rows: one per (row, column tile))
+//   GIVEN   - second pass: the product again, rounded straight to int8 at the
+//             group exponents reduced from the first pass's maxima
+enum EpiKind { EPI_DIRECT = 0, EPI_RTO = 1, EPI_PARTIAL = 2, EPI_MAX = 8, EPI_GIVEN = 9 };
 
 struct Epi {
     ExpSrc ea;        // exponent of GEMM row m
@@ -47,6 +52,8 @@ struct Epi {
     uint32_t *flags;
     int relu;         // int8 results pass through ReLU (forward products)
     int q;            // results have |C| <= 2^q - 1 (mantissa width q + 1 bits)
+    int *tneed;       // MAX writes / GIVEN reads: group maxima of the first pass
+    int tneed_n;      //   whole tensor: the first pass's grid size (entries)
 };
 
 enum LoaderKind {
@@ -71,6 +78,8 @@ struct Operand {
 // chunks of `k_chunk` (a multiple of BK), then the epilogue.
 hipError_t launch_gemm(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,
                        int k_chunk, bool partial, const Epi &ep, hipStream_t st);
+// ep.mode == EPI_MAX: the first pass of a recomputed product, on a persistent
+// grid of recomp_grid(M, N, t) workgroups.
 // Per-translation-unit launchers (return hipErrorInvalidValue if the
 // loader / tile combination is not instantiated there).
 hipError_t launch_gemm_kk(const Operand &A, const Operand &B, int M, int N, int K, Tile t, int splits,

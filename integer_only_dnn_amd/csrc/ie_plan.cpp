@@ -250,7 +250,7 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
     if (N > 64 && tiles(Tile{2, 2}) >= 4ll * NCU) t = Tile{2, 2};
     else if (tiles(Tile{2, 1}) >= 2ll * NCU) t = Tile{2, 1};
     const bool direct = row_group ? N <= t.bn() : tiles(t) == 1;
-    Plan best{t, direct ? PLAN_DIRECT : PLAN_RTO, 1, chunk_for(K, 1)};
+    Plan best{t, direct ? PLAN_DIRECT : K <= RECOMP_KMAX ? PLAN_RECOMP : PLAN_RTO, 1, chunk_for(K, 1)};
     if (!direct && tiles(Tile{1, 1}) < NCU / 2 && K >= 8 * BK) {
         const long long n11 = tiles(Tile{1, 1});
         int sp = 1;
@@ -295,9 +295,18 @@ Plan plan_batched(long long Z, long long M, long long N, bool kk) {
     return Plan{t, N <= t.bn() ? PLAN_DIRECT : PLAN_RTO, 1, BK};
 }
 
+int recomp_grid(long long M, long long N, Tile t) {
+    const long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+    const long long per_cu = t.mi * t.ni == 1 ? 3 : t.mi * t.ni <= 4 ? 2 : 1;
+    long long g = NCU * per_cu;
+    if (tiles < g) g = tiles;
+    return (int)(g > 8 ? g / 8 * 8 : g);  // a multiple of 8: item % 8 stays the XCD
+}
+
 bool plan_valid(const Plan &pl, long long M, long long N, long long K, int row_group, int family) {
     if (pl.t.mi < 1 || pl.t.ni < 1) return false;
-    if (pl.mode != PLAN_DIRECT && pl.mode != PLAN_RTO && pl.mode != PLAN_SPLIT) return false;
+    if (pl.mode != PLAN_DIRECT && pl.mode != PLAN_RTO && pl.mode != PLAN_SPLIT && pl.mode != PLAN_RECOMP)
+        return false;
     const bool wg = family == FAM_WGRAD || family == FAM_WGRAD_CONV;
     if (wg && pl.mode != PLAN_SPLIT) return false;
     if (!tile_built(family, pl.t, pl.mode == PLAN_SPLIT)) return false;
@@ -339,9 +348,11 @@ bool split_round_rows_fits(int Nout, int mc, int mcp) {
 static size_t mx(size_t a, size_t b) { return a > b ? a : b; }
 
 Needs product_needs(const Plan &pl, long long M, long long N, int row_group) {
-    Needs n{0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, 0};
     if (pl.t.mi < 1 || pl.t.ni < 1) return n;
-    if (pl.mode == PLAN_RTO) {
+    if (pl.mode == PLAN_RECOMP) {
+        n.tneed = row_group ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)recomp_grid(M, N, pl.t);
+    } else if (pl.mode == PLAN_RTO) {
         n.p16 = row_group ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)cdiv(M, pl.t.bm()) * cdiv(N, pl.t.bn());
         n.v16 = (size_t)M * N;
     } else if (pl.mode == PLAN_SPLIT) {
@@ -355,7 +366,7 @@ Needs product_needs(const Plan &pl, long long M, long long N, int row_group) {
 }
 
 Needs wgrad_needs(const Plan &pl, long long N, long long Kg, long long Kout, int mc, int mcp, int row_group) {
-    Needs n{0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, 0};
     n.partial = (size_t)(pl.splits < 1 ? 1 : pl.splits) * N * Kg;
     n.gneed = row_group ? (size_t)N : 1;
     if (!(row_group && split_round_rows_fits((int)Kout, mc, mcp))) n.sums = (size_t)N * Kg;
@@ -363,7 +374,7 @@ Needs wgrad_needs(const Plan &pl, long long N, long long Kg, long long Kout, int
 }
 
 Needs batched_needs(const Plan &pl, long long Z, long long M, long long N) {
-    Needs n{0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, 0};
     if (pl.mode == PLAN_RTO && pl.t.ni >= 1) {
         n.p16 = (size_t)Z * M * cdiv(N, pl.t.bn());
         n.v16 = (size_t)Z * M * N;
@@ -373,12 +384,12 @@ Needs batched_needs(const Plan &pl, long long Z, long long M, long long N) {
 
 bool covers(const Needs &have, const Needs &need) {
     return need.gneed <= have.gneed && need.p16 <= have.p16 && need.v16 <= have.v16 &&
-           need.partial <= have.partial && need.sums <= have.sums;
+           need.partial <= have.partial && need.sums <= have.sums && need.tneed <= have.tneed;
 }
 
 ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f) {
     ProductWs w{};
-    Needs n{0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, 0};
     for (int rg = 0; rg < 2; ++rg) {
         const Needs r = product_needs(plan_product(M, N, K, rg, family, f), M, N, rg);
         n.gneed = mx(n.gneed, r.gneed);
@@ -386,6 +397,7 @@ ProductWs carve_product(Carve &c, long long M, long long N, long long K, int fam
         n.v16 = mx(n.v16, r.v16);
         n.partial = mx(n.partial, r.partial);
         n.sums = mx(n.sums, r.sums);
+        n.tneed = mx(n.tneed, r.tneed);
     }
     n.gneed = mx(n.gneed, M > 0 ? (size_t)M : 1);
     w.gneed = c.take<int>(n.gneed);
@@ -393,6 +405,7 @@ ProductWs carve_product(Carve &c, long long M, long long N, long long K, int fam
     w.v16 = c.take<int16_t>(n.v16);
     w.partial = c.take<int>(n.partial);
     w.sums = c.take<long long>(n.sums);
+    w.tneed = c.take<int>(n.tneed);
     w.n = n;
     return w;
 }
@@ -400,7 +413,7 @@ ProductWs carve_product(Carve &c, long long M, long long N, long long K, int fam
 WgradWs carve_wgrad(Carve &c, long long N, long long Kg, long long L, int family, const Force &f) {
     WgradWs w{};
     const Plan pl = plan_wgrad(N, Kg, L, family, f);
-    Needs n{0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, 0};
     n.gneed = N > 0 ? (size_t)N : 1;
     n.partial = (size_t)(pl.splits < 1 ? 1 : pl.splits) * N * Kg;
     n.sums = (size_t)N * Kg;

@@ -116,7 +116,18 @@ bool pair_tiles_built(Tile t1, Tile t2);
 //         then a rounding pass.
 // SPLIT:  the contraction is split into chunks of exact int32 partial sums,
 //         merged and rounded by a finalize pass.
-enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2 };
+// RECOMP: two passes of the product: the first finds the group maxima only
+//         (nothing stored), the second recomputes and rounds straight to int8.
+//         Cheaper than RTO when the contraction is short (the extra pass
+//         reads the operands again but saves 4 bytes per output element).
+enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2, PLAN_RECOMP = 3 };
+
+// Contractions of at most this many bytes recompute instead of two-pass
+// rounding (RECOMP instead of RTO).
+constexpr long long RECOMP_KMAX = 512;
+// Workgroups of the first pass of a recomputed whole-tensor product (a
+// persistent grid; each writes one maximum).
+int recomp_grid(long long M, long long N, Tile t);
 
 struct Plan {
     Tile t;
@@ -177,7 +188,7 @@ constexpr int SR_MAXV = 4;
 
 // Element counts of the buffers a plan's kernels write besides the output.
 struct Needs {
-    size_t gneed, p16, v16, partial, sums;
+    size_t gneed, p16, v16, partial, sums, tneed;
 };
 bool split_round_rows_fits(int Nout, int mc, int mcp);
 Needs product_needs(const Plan &pl, long long M, long long N, int row_group);
@@ -192,6 +203,7 @@ struct ProductWs {
     int16_t *v16;
     int *partial;
     long long *sums;
+    int *tneed;
     Needs n;  // element counts reserved
 };
 ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f);

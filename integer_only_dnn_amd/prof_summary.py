@@ -11,11 +11,17 @@ Two products:
   records a digest of the library sources, so a reader can tell whether the
   kernels have changed since the counters were taken.
 
+* several counter runs (``rocprofv3 --pmc <SQ counters>``, one pass each) ->
+  per-kernel averages per dispatch and derived ratios (instructions per wave,
+  the share of wave lifetime spent waiting or issuing, LDS bank conflicts).
+
 Usage::
 
     python -m integer_only_dnn_amd.prof_summary stats  --dir D --out profiles/x.md --cmd "..."
     python -m integer_only_dnn_amd.prof_summary traffic --fetch D1 --write D2 --copy-mib 256 \\
         --workload resnet18 --out profiles/y.txt --cmd "..." --cmd "..."
+    python -m integer_only_dnn_amd.prof_summary counters --dir D1 --dir D2 --dir D3 \\
+        --workload resnet50 --out profiles/z.md --cmd "..." --cmd "..."
 """
 
 from __future__ import annotations
@@ -35,7 +41,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 def source_digest() -> str:
     """sha256 over the library's kernel sources (name and content, sorted)."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))):
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip")) +
+                       glob.glob(os.path.join(CSRC, "*.cpp"))):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
@@ -146,6 +153,69 @@ def read_traffic(path: str):
     return digest, table
 
 
+def counters_per_kernel(dirs):
+    """{kernel: {counter: mean value per dispatch}} over several --pmc runs,
+    and {kernel: dispatches}."""
+    acc = defaultdict(lambda: defaultdict(lambda: [0, 0.0]))
+    disp = defaultdict(set)
+    for d in dirs:
+        path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                a = acc[k][r["Counter_Name"]]
+                a[0] += 1
+                a[1] += float(r["Counter_Value"])
+                disp[k].add((d, r.get("Dispatch_Id", r.get("Correlation_Id", ""))))
+    return ({k: {c: v / n for c, (n, v) in cs.items()} for k, cs in acc.items()},
+            {k: len(v) // max(1, len(dirs)) for k, v in disp.items()})
+
+
+def write_counters(dirs, workload: str, out: str, cmds, top: int = 16) -> None:
+    per, ndisp = counters_per_kernel(dirs)
+
+    def g(cs, name):
+        return cs.get(name)
+
+    def ratio(a, b, scale=1.0):
+        return f"{100.0 * scale * a / b:.1f}" if a is not None and b else "-"
+
+    def per_wave(cs, name):
+        v, w = g(cs, name), g(cs, "SQ_WAVES")
+        return f"{v / w:.0f}" if v is not None and w else "-"
+
+    rows = sorted(per.items(), key=lambda kv: -(kv[1].get("SQ_WAVE_CYCLES", 0.0) * ndisp.get(kv[0], 1)))
+    lines = [f"# Hardware counters per kernel: {workload}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; bench.py at the repository root; one pass per counter "
+             "set):", "", "```"] + list(cmds) + ["```", "",
+             f"Library source digest: {source_digest()}", "",
+             "Per dispatch, averaged over dispatches.  Columns: waves; instructions per wave (VALU, MFMA, LDS, "
+             "vector-memory reads); `wait%` = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave lifetime waiting on a memory "
+             "or LDS counter); `valu%`, `lds%` = SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_LDS over SQ_WAVE_CYCLES "
+             "(lifetime issuing); `mfma%` = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES x 4 SIMDs), the "
+             "share of busy-CU cycles the matrix cores work; `bank%` = SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | disp | waves | VALU/w | MFMA/w | LDS/w | VMEMrd/w | wait% | valu% | lds% | mfma% | bank% |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k, cs in rows[:top]:
+        wc = g(cs, "SQ_WAVE_CYCLES")
+        lines.append(
+            f"| `{k}` | {ndisp.get(k, 0)} | {g(cs, 'SQ_WAVES') or 0:.0f} | {per_wave(cs, 'SQ_INSTS_VALU')} | "
+            f"{per_wave(cs, 'SQ_INSTS_MFMA')} | {per_wave(cs, 'SQ_INSTS_LDS')} | {per_wave(cs, 'SQ_INSTS_VMEM_RD')} | "
+            f"{ratio(g(cs, 'SQ_WAIT_ANY'), wc)} | {ratio(g(cs, 'SQ_ACTIVE_INST_VALU'), wc)} | "
+            f"{ratio(g(cs, 'SQ_ACTIVE_INST_LDS'), wc)} | "
+            f"{ratio(g(cs, 'SQ_VALU_MFMA_BUSY_CYCLES'), g(cs, 'SQ_BUSY_CU_CYCLES'), 0.25)} | "
+            f"{ratio(g(cs, 'SQ_LDS_BANK_CONFLICT'), g(cs, 'SQ_LDS_IDX_ACTIVE'))} |")
+    lines += ["", "Raw means per dispatch:", ""]
+    names = sorted({c for cs in per.values() for c in cs})
+    lines.append("| kernel | " + " | ".join(names) + " |")
+    lines.append("|---|" + "---:|" * len(names))
+    for k, cs in rows[:top]:
+        lines.append(f"| `{k}` | " + " | ".join(f"{cs[c]:.4g}" if c in cs else "-" for c in names) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -160,9 +230,17 @@ def main() -> None:
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", action="append", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", action="append", default=[])
+    c.add_argument("--top", type=int, default=16)
     a = ap.parse_args()
     if a.what == "stats":
         write_stats(a.dir, a.out, a.cmd)
+    elif a.what == "counters":
+        write_counters(a.dir, a.workload, a.out, a.cmd, a.top)
     else:
         write_traffic(a.fetch, a.write, a.copy_mib, a.workload, a.out, a.cmd)
 

@@ -73,7 +73,15 @@ static void touch(T *p, size_t idx) {
 static void product_writes(const Plan &pl, long long M, long long N, int rg, const ProductWs &w) {
     const int bm = pl.t.bm(), bn = pl.t.bn();
     const long long TM = (M + bm - 1) / bm, TN = (N + bn - 1) / bn;
-    if (pl.mode == PLAN_RTO) {
+    if (pl.mode == PLAN_RECOMP) {
+        if (!rg) {
+            // one running maximum per workgroup of the persistent first pass
+            for (int b = 0; b < recomp_grid(M, N, pl.t); ++b) touch(w.tneed, (size_t)b);
+        } else {
+            for (long long r = 0; r < M; ++r)
+                for (long long tn = 0; tn < TN; ++tn) touch(w.tneed, (size_t)(r * TN + tn));
+        }
+    } else if (pl.mode == PLAN_RTO) {
         for (long long tn = 0; tn < TN; ++tn)
             for (long long tm = 0; tm < TM; ++tm) {
                 if (!rg) {
@@ -124,6 +132,7 @@ static void open_product(Arena &a, const ProductWs &w) {
     a.open(w.v16, w.n.v16);
     a.open(w.partial, w.n.partial);
     a.open(w.sums, w.n.sums);
+    a.open(w.tneed, w.n.tneed);
 }
 
 static void open_wgrad(Arena &a, const WgradWs &w) {
@@ -179,7 +188,7 @@ static void check_products() {
             for (long long N : EDGES_FORCED)
                 for (long long K : Ks) {
                     for (const Tile &t : TRY_TILES)
-                        for (int mode = 0; mode < 4; ++mode)
+                        for (int mode = 0; mode < 5; ++mode)
                             for (int sp : {1, 2, 3, 7}) {
                                 if (mode != PLAN_SPLIT && sp != 1 && sp != 2) continue;
                                 check_product_case(M, N, K, fam, Force{1, t.mi, t.ni, mode, sp}, false);

@@ -156,3 +156,21 @@ def test_pointwise_argument_errors():
     d = ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 1, 1)
     assert L.ie_conv_fwd_act(by(d), by(_mat(128, 16)), by(_mat(32, 144)), by(_mat(128, 32)), 5, 1, 1 << 30,
                              None) == 6
+
+
+@pytest.mark.parametrize("force", ["1,1,0,1", "2,2,0", "0,1", "1,0,1", "3,1,1", "4,4,1", "1,1,7"])
+def test_forced_plans_without_kernel_are_refused(force, monkeypatch):
+    """A forced plan (tests and tuning only) is validated like any other: a
+    direct epilogue on groups spanning several tiles, a zero or unbuilt tile
+    or an unknown mode returns IE_ERR_UNSUPPORTED before anything is
+    enqueued (the pointers here are never dereferenced)."""
+    L = ie.lib()
+    by = ctypes.byref
+    monkeypatch.setenv("IE_TILE", force)
+    M, N, K = 200, 150, 64
+    X, W = _mat(M, K), _mat(N, K)
+    ws_bytes = L.ie_linear_fwd_workspace(M, N, K)
+    assert ws_bytes >= 256
+    for group in (0, 1):
+        st = L.ie_linear_fwd(by(X), by(W), by(_mat(M, N, group)), 256, ws_bytes, None)
+        assert st == 6, (force, group, st)

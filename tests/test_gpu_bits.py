@@ -59,8 +59,8 @@ def _relu(t: o.QT) -> o.QT:
 
 
 # (mode, splits): 0 = direct (one tile holds every group), 1 = round-to-odd
-# two-pass, 2 = split contraction
-MODES = [(0, 1), (1, 1), (2, 2), (2, 3)]
+# two-pass, 2 = split contraction, 3 = recomputed
+MODES = [(0, 1), (1, 1), (2, 2), (2, 3), (3, 1)]
 
 
 @pytest.mark.parametrize("bits", BITS)

@@ -17,8 +17,9 @@ T, R = o.TENSOR, o.ROW
 DENSE_TILES = [(2, 2), (4, 1), (1, 4), (2, 1), (1, 2), (1, 1)]
 CONV_TILES = [(2, 2), (4, 1), (2, 1), (1, 1)]
 WGRAD_TILES = [(2, 2), (1, 4), (4, 1), (1, 1)]
-# (mode, splits): 1 = round-to-odd two-pass, 2 = split contraction
-MODES = [(1, 1), (2, 2), (2, 3)]
+# (mode, splits): 1 = round-to-odd two-pass, 2 = split contraction,
+# 3 = recomputed (group maxima first, then the product rounded directly)
+MODES = [(1, 1), (2, 2), (2, 3), (3, 1)]
 
 
 @pytest.fixture(scope="module")
@@ -122,7 +123,7 @@ CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1),
 
 @pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"c{s[3]}st{s[7]}")
 @pytest.mark.parametrize("tile", CONV_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
-@pytest.mark.parametrize("mode", MODES[:2], ids=lambda m: f"m{m[0]}s{m[1]}")
+@pytest.mark.parametrize("mode", [(1, 1), (2, 2), (3, 1)], ids=lambda m: f"m{m[0]}s{m[1]}")
 @pytest.mark.parametrize("wg", [T, R], ids=["WT", "WR"])
 def test_conv_plans(shape, tile, mode, wg, ws, plan):
     n, h, w, c, k, r, s, st, pad = shape
@@ -140,7 +141,15 @@ def test_conv_plans(shape, tile, mode, wg, ws, plan):
     assert_same(Y, o.conv_fwd(d, X, W, T), "conv fwd")
     dX = ie.Mat.empty(n * h * w, c, T)
     ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, None, ws)
-    assert_same(dX, o.conv_dgrad(d, dY, W, T), "conv dgrad")
+    want_dx = o.conv_dgrad(d, dY, W, T)
+    assert_same(dX, want_dx, "conv dgrad")
+    # both gradients in one call: the paired grid where its kernels cover
+    # the plans (round-to-odd or recomputed input gradient)
+    dX2 = ie.Mat.empty(n * h * w, c, T)
+    dW = ie.Mat.empty(k, r * s * c, R)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX2, dW, ws)
+    assert_same(dX2, want_dx, "conv dgrad (paired)")
+    assert_same(dW, o.conv_wgrad(d, dY, X, R), "conv wgrad (paired)")
     assert ws.status() == 0
 
 
