@@ -61,8 +61,15 @@ OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_k
          3530: ("add_rows", "add_rows_kernel")}
 
 
+ONE_KIND = 99000000  # added to the code of a one-step (K <= 128) contraction kernel
+
+
 def is_gemm(kind: int) -> bool:
     return kind >= 10000 and 1000 <= kind % 10000 < 2000
+
+
+def is_one(kind: int) -> bool:
+    return kind >= ONE_KIND
 
 
 def is_pair(kind: int) -> bool:
@@ -79,6 +86,8 @@ def _decode(kind: int):
 def kind_name(kind: int) -> str:
     if not is_gemm(kind):
         return OTHER.get(kind, (str(kind), ""))[0]
+    if is_one(kind):
+        return kind_name(kind - ONE_KIND) + "_1step"
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_{LOADER[ka]}_{LOADER[kb]}_rto_{64 * mi}x{64 * ni}+T_im2colT_partial_{64 * mi2}x{64 * ni2}"
@@ -89,13 +98,18 @@ def kind_symbol(kind: int) -> str:
     """The kernel's name as rocprofv3 reports it."""
     if not is_gemm(kind):
         return OTHER.get(kind, ("", str(kind)))[1]
+    if is_one(kind):
+        mi, ni, _, _, ka, kb, epi = _decode(kind - ONE_KIND)
+        if epi == 8:
+            return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, true>"
+        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, true>"
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
     if epi in (4, 5, 6, 7):
         return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi >= 6 else 'false'}>"
     if epi == 8:
-        return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}>"
+        return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, false>"
     return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}>"
 
 

@@ -97,7 +97,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     }
     const int family = family_of(A, B);
     const Plan pl = plan_product(M, N, K, rg, family, force_product());
-    IE_CHECK(checked_plan(pl, M, N, K, rg, family, pw.n, product_needs(pl, M, N, rg)));
+    IE_CHECK(checked_plan(pl, M, N, K, rg, family, pw.n, product_needs(pl, M, N, K, rg)));
     log_plan(family == FAM_DENSE ? "dense" : "conv", M, N, K, pl);
     Epi ep;
     memset(&ep, 0, sizeof ep);
@@ -125,7 +125,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     if (pl.mode == PLAN_RECOMP) {
         // group maxima first, then the product again, rounded straight to int8
         ep.tneed = pw.tneed;
-        ep.tneed_n = rg ? 0 : recomp_grid(M, N, pl.t);
+        ep.tneed_n = rg ? 0 : recomp_grid(M, N, K, pl.t);
         ep.mode = EPI_MAX;
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
         ep.mode = EPI_GIVEN;
@@ -215,7 +215,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     if (p1.mode != PLAN_RTO && p1.mode != PLAN_RECOMP) return IE_ERR_UNSUPPORTED;
     const Plan p2 = plan_wgrad(g.k, rscp, npq, FAM_WGRAD_CONV, force_wgrad());
     if (!gemm_pair_supported(A1, B1, p1.t, A2, B2, p2.t)) return IE_ERR_UNSUPPORTED;
-    if (checked_plan(p1, nhw, g.c, rskp, 0, fam1, cw.pw.n, product_needs(p1, nhw, g.c, 0)) != IE_OK ||
+    if (checked_plan(p1, nhw, g.c, rskp, 0, fam1, cw.pw.n, product_needs(p1, nhw, g.c, rskp, 0)) != IE_OK ||
         checked_plan(p2, g.k, rscp, npq, 1, FAM_WGRAD_CONV, cw.w.n, wgrad_needs(p2, g.k, rscp, rsc, g.c, g.cp, 1)) !=
             IE_OK)
         return IE_ERR_UNSUPPORTED;
@@ -236,7 +236,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     e1.q = mat_q(dX);
     if (p1.mode == PLAN_RECOMP) {
         e1.tneed = cw.pw.tneed;
-        e1.tneed_n = recomp_grid(nhw, g.c, p1.t);
+        e1.tneed_n = recomp_grid(nhw, g.c, rskp, p1.t);
         e1.mode = EPI_MAX;
         IE_TRY(launch_gemm(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, 1, p1.k_chunk, false, e1, st));
         e1.mode = EPI_GIVEN;

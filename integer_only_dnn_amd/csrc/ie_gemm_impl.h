@@ -583,6 +583,56 @@ __device__ __forceinline__ int rto_bf(int a, int t) {
     return (x >> R) | (int)((((uint32_t)x & mask) + mask) >> R);
 }
 
+// The same roundings with the shift-dependent part computed once: a value
+// shared by a column (or row) of the tile then costs four operations (shift,
+// bit extract, three-input add, shift) for rne, five for rto.
+struct RneP {
+    int L, R, hm1, w;  // left shift, right shift, 2^(R-1) - 1, extract width (1 when R > 0)
+};
+__device__ __forceinline__ RneP rne_prep(int s) {
+    s = min(max(s, -31), 31);
+    RneP p;
+    p.L = max(-s, 0);
+    p.R = max(s, 0);
+    p.hm1 = p.R > 0 ? (1 << (p.R - 1)) - 1 : 0;
+    p.w = p.R > 0 ? 1 : 0;
+    return p;
+}
+__device__ __forceinline__ int rne_apply(int a, const RneP &p) {
+    const int x = a << p.L;
+    const int bit = (int)__builtin_amdgcn_ubfe((uint32_t)x, (uint32_t)p.R, (uint32_t)p.w);
+    return (x + p.hm1 + bit) >> p.R;
+}
+struct RtoP {
+    int L, R;
+    uint32_t mask;  // the R bits shifted out
+};
+__device__ __forceinline__ RtoP rto_prep(int t) {
+    t = min(max(t, -31), 31);
+    RtoP p;
+    p.L = max(-t, 0);
+    p.R = max(t, 0);
+    p.mask = (1u << p.R) - 1u;
+    return p;
+}
+__device__ __forceinline__ int rto_apply(int a, const RtoP &p) {
+    const int x = a << p.L;
+    return (x >> p.R) | (int)min((uint32_t)x & p.mask, 1u);
+}
+
+// Largest |v| over a run of values as an unsigned magnitude, from the signed
+// maximum and minimum (two values per three-input max / min).
+template <int N>
+__device__ __forceinline__ uint32_t max_mag(const int (&v)[N]) {
+    int hi = 0, lo = 0;
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+        hi = max(hi, max(v[i], v[i + 1]));
+        lo = min(lo, min(v[i], v[i + 1]));
+    }
+    return max((uint32_t)hi, 0u - (uint32_t)lo);
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -631,6 +681,12 @@ template <int MI, int NI>
 struct Occ {
     static constexpr int value = MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI <= 4 ? 2 : 1;
 };
+// The same for the one-step form of a tile (one LDS stage, no register
+// pipeline): up to four workgroups per CU.
+template <int MI, int NI>
+struct Occ1 {
+    static constexpr int value = MI * NI <= 2 ? 4 : MI * NI == 4 ? 3 : 2;
+};
 
 // LDS of a tile: two stages of both operands (also the epilogue's staging).
 template <int KA, int KB, int MI, int NI>
@@ -646,7 +702,10 @@ template <int KA, int KB, int MI, int NI>
 struct TileLds1 {
     static constexpr int stage = Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES;
     static constexpr int epi = 64 * MI * (64 * NI * 2 + 16) + 4 * 64 * MI * 4 + 64;
-    static constexpr int value = stage > epi ? stage : epi;
+    // the contraction-sliced 64 x 64 tile sums four partial tiles through LDS
+    static constexpr int slices = KSlice<MI, NI>::value ? 8 * 4096 : 0;
+    static constexpr int v0 = stage > epi ? stage : epi;
+    static constexpr int value = v0 > slices ? v0 : slices;
 };
 
 // One workgroup's work item: bid and nblk are its index and the number of
@@ -956,6 +1015,33 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
                         }
                 const uint32_t mx = max((uint32_t)hi, 0u - (uint32_t)lo);
                 tmax = mx ? ea0 + eb0 + mant_shift32(mx, wq) : NEED_NONE;
+            } else if (!ep.ea.row) {
+                // one row exponent, per-column ones: a column's largest |acc|
+                // decides its need
+                tmax = NEED_NONE;
+#pragma unroll
+                for (int b = 0; b < NI; ++b) {
+                    int v[16 * MI];
+#pragma unroll
+                    for (int a = 0; a < MI; ++a)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) v[16 * a + r] = acc[a][b][r];
+                    const uint32_t mx = max_mag(v);
+                    tmax = max(tmax, mx ? ea0 + ebv[b] + mant_shift32(mx, wq) : NEED_NONE);
+                }
+            } else if (!ep.eb.row) {
+                // per-row exponents, one column exponent: a row's largest |acc|
+                tmax = NEED_NONE;
+#pragma unroll
+                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        int v[2 * NI];
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) v[2 * b] = v[2 * b + 1] = acc[a][b][r];
+                        const uint32_t mx = max_mag(v);
+                        tmax = max(tmax, mx ? seA[TR(a, r)] + eb0 + mant_shift32(mx, wq) : NEED_NONE);
+                    }
             } else {
                 tmax = NEED_NONE;
 #pragma unroll
@@ -1024,21 +1110,58 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
                             }
                 }
             } else {
-                // per-element exponents: every shift computed, branch free
+                // the shift of a value depends on its column (one row
+                // exponent), on its row (one column exponent), or on both
                 auto elems = [&](auto dir_tag) {
                     constexpr bool DIR = decltype(dir_tag)::value;
                     const int tgt = DIR ? e : p;
+                    if (!ep.ea.row) {
 #pragma unroll
-                    for (int a = 0; a < MI; ++a)
+                        for (int b = 0; b < NI; ++b) {
+                            const int sh = tgt - ea0 - ebv[b];
+                            if constexpr (DIR) {
+                                const RneP q = rne_prep(sh);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int off = tgt - seA[TR(a, r)];
+                                for (int a = 0; a < MI; ++a)
 #pragma unroll
-                            for (int b = 0; b < NI; ++b) {
-                                if constexpr (DIR) stage(ES1{}, a, b, r, rne_bf(acc[a][b][r], off - ebv[b]));
-                                else stage(ES2{}, a, b, r, rto_bf(acc[a][b][r], off - ebv[b]));
+                                    for (int r = 0; r < 16; ++r) stage(ES1{}, a, b, r, rne_apply(acc[a][b][r], q));
+                            } else {
+                                const RtoP q = rto_prep(sh);
+#pragma unroll
+                                for (int a = 0; a < MI; ++a)
+#pragma unroll
+                                    for (int r = 0; r < 16; ++r) stage(ES2{}, a, b, r, rto_apply(acc[a][b][r], q));
                             }
                         }
+                    } else if (!ep.eb.row) {
+#pragma unroll
+                        for (int a = 0; a < MI; ++a)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int sh = tgt - seA[TR(a, r)] - eb0;
+                                if constexpr (DIR) {
+                                    const RneP q = rne_prep(sh);
+#pragma unroll
+                                    for (int b = 0; b < NI; ++b) stage(ES1{}, a, b, r, rne_apply(acc[a][b][r], q));
+                                } else {
+                                    const RtoP q = rto_prep(sh);
+#pragma unroll
+                                    for (int b = 0; b < NI; ++b) stage(ES2{}, a, b, r, rto_apply(acc[a][b][r], q));
+                                }
+                            }
+                    } else {
+#pragma unroll
+                        for (int a = 0; a < MI; ++a)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int off = tgt - seA[TR(a, r)];
+#pragma unroll
+                                for (int b = 0; b < NI; ++b) {
+                                    if constexpr (DIR) stage(ES1{}, a, b, r, rne_bf(acc[a][b][r], off - ebv[b]));
+                                    else stage(ES2{}, a, b, r, rto_bf(acc[a][b][r], off - ebv[b]));
+                                }
+                            }
+                    }
                 };
                 if (direct) elems(std::true_type{});
                 else elems(std::false_type{});
@@ -1082,6 +1205,16 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
 #pragma unroll
                         for (int b = 0; b < NI; ++b) m = fmaxf(m, fabsf((float)acc[a][b][r] * cs[b]));
                         key[r] = __float_as_int(m);
+                    }
+                } else if (!ep.eb.row) {
+                    // one column exponent: the row's largest |acc| decides
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        int v[2 * NI];
+#pragma unroll
+                        for (int b = 0; b < NI; ++b) v[2 * b] = v[2 * b + 1] = acc[a][b][r];
+                        const uint32_t mx = max_mag(v);
+                        key[r] = mx ? seA[TR(a, r)] + eb0 + mant_shift32(mx, wq) : NEED_NONE;
                     }
                 } else {
 #pragma unroll
@@ -1169,6 +1302,17 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
                                     stage(ES2{}, a, b, r, (int)q | (int)(y != q));
                                 }
                             }
+                        } else if (!ep.eb.row) {
+                            // one column exponent: one shift for the row
+                            if constexpr (DIR) {
+                                const RneP q = rne_prep(rowi[tr] - eb0);
+#pragma unroll
+                                for (int b = 0; b < NI; ++b) stage(ES1{}, a, b, r, rne_apply(acc[a][b][r], q));
+                            } else {
+                                const RtoP q = rto_prep(rowi[tr] - eb0);
+#pragma unroll
+                                for (int b = 0; b < NI; ++b) stage(ES2{}, a, b, r, rto_apply(acc[a][b][r], q));
+                            }
                         } else {
                             const int off = rowi[tr];
 #pragma unroll
@@ -1194,25 +1338,35 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
     }
 }
 
-template <int KA, int KB, int MI, int NI, bool PARTIAL>
-__global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_i8_kernel(Operand A, Operand B, int M, int N, int K,
-                                                                         int k_chunk, int TM, int S, Epi ep) {
-    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
-    gemm_tile<KA, KB, MI, NI, PARTIAL>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
+// ONE: the contraction is at most one step (K <= BK; not for split
+// contractions), so the tile loads it once into a single LDS stage and more
+// workgroups fit a CU.
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false>
+__global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_i8_kernel(
+    Operand A, Operand B, int M, int N, int K, int k_chunk, int TM, int S, Epi ep) {
+    static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
+    __shared__ __attribute__((aligned(16)))
+    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value];
+    gemm_tile<KA, KB, MI, NI, PARTIAL, ONE>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
 }
+
+// Kind codes of one-step kernels for the timing records: the code of the
+// plain kernel plus ONE_KIND.
+constexpr int ONE_KIND = 99000000;
 
 // First pass of a recomputed product (EPI_MAX): a persistent grid walks the
 // tiles (item = blockIdx.x + j * gridDim.x; gridDim.x a multiple of 8 keeps
 // item % 8 on the workgroup's XCD), finding group maxima without storing
 // values.  Whole-tensor groups: each workgroup writes its running maximum to
 // tneed[blockIdx.x]; row groups: the tiles write tneed[row][column tile].
-template <int KA, int KB, int MI, int NI>
-__global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_max_kernel(Operand A, Operand B, int M, int N,
-                                                                            int K, int TM, int items, Epi ep) {
-    __shared__ __attribute__((aligned(16))) int8_t lds[TileLds<KA, KB, MI, NI>::value];
+template <int KA, int KB, int MI, int NI, bool ONE>
+__global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_max_kernel(
+    Operand A, Operand B, int M, int N, int K, int TM, int items, Epi ep) {
+    __shared__ __attribute__((aligned(16)))
+    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value];
     int run = NEED_NONE;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        run = max(run, gemm_tile<KA, KB, MI, NI, false>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
+        run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
         __syncthreads();  // the next item's stages reuse the LDS
     }
     if (!ep.row_group && threadIdx.x == 0) ep.tneed[blockIdx.x] = run;
@@ -1222,13 +1376,18 @@ template <int KA, int KB, int MI, int NI>
 hipError_t launch_max(const Operand &A, const Operand &B, int M, int N, int K, const Epi &ep, hipStream_t st) {
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     const int items = TM * TN;
-    const int grid = recomp_grid(M, N, Tile{MI, NI});
+    const int grid = recomp_grid(M, N, K, Tile{MI, NI});
     if (grid <= 0) return hipSuccess;
     if (!ep.row_group && ep.tneed_n != grid) return hipErrorInvalidValue;
-    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * EPI_MAX + 10 * KA + KB;
+    const bool one = K <= BK;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * EPI_MAX + 10 * KA + KB + (one ? ONE_KIND : 0);
     prof_begin(st, kind);
-    hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K, TM, items,
-                       ep);
+    if (one)
+        hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI, true>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K,
+                           TM, items, ep);
+    else
+        hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI, false>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K,
+                           TM, items, ep);
     prof_end(st, kind);
     return hipGetLastError();
 }
@@ -1353,8 +1512,17 @@ hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, i
                       const Epi &ep, hipStream_t st) {
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     dim3 grid(TM * TN * splits, 1, 1);
-    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB;
+    const bool one = !PARTIAL && K <= BK;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB + (one ? ONE_KIND : 0);
     prof_begin(st, kind);
+    if constexpr (!PARTIAL) {
+        if (one) {
+            hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, false, true>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
+                               k_chunk, TM, splits, ep);
+            prof_end(st, kind);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, PARTIAL>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
                        k_chunk, TM, splits, ep);
     prof_end(st, kind);

@@ -295,9 +295,11 @@ Plan plan_batched(long long Z, long long M, long long N, bool kk) {
     return Plan{t, N <= t.bn() ? PLAN_DIRECT : PLAN_RTO, 1, BK};
 }
 
-int recomp_grid(long long M, long long N, Tile t) {
+int recomp_grid(long long M, long long N, long long K, Tile t) {
     const long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
-    const long long per_cu = t.mi * t.ni == 1 ? 3 : t.mi * t.ni <= 4 ? 2 : 1;
+    // workgroups per CU of the tile's kernel (its one-step form for K <= BK)
+    const long long per_cu = K <= BK ? (t.mi * t.ni <= 2 ? 4 : t.mi * t.ni == 4 ? 3 : 2)
+                                     : (t.mi * t.ni == 1 ? 3 : t.mi * t.ni <= 4 ? 2 : 1);
     long long g = NCU * per_cu;
     if (tiles < g) g = tiles;
     return (int)(g > 8 ? g / 8 * 8 : g);  // a multiple of 8: item % 8 stays the XCD
@@ -347,11 +349,11 @@ bool split_round_rows_fits(int Nout, int mc, int mcp) {
 
 static size_t mx(size_t a, size_t b) { return a > b ? a : b; }
 
-Needs product_needs(const Plan &pl, long long M, long long N, int row_group) {
+Needs product_needs(const Plan &pl, long long M, long long N, long long K, int row_group) {
     Needs n{0, 0, 0, 0, 0, 0};
     if (pl.t.mi < 1 || pl.t.ni < 1) return n;
     if (pl.mode == PLAN_RECOMP) {
-        n.tneed = row_group ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)recomp_grid(M, N, pl.t);
+        n.tneed = row_group ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)recomp_grid(M, N, K, pl.t);
     } else if (pl.mode == PLAN_RTO) {
         n.p16 = row_group ? (size_t)M * cdiv(N, pl.t.bn()) : (size_t)cdiv(M, pl.t.bm()) * cdiv(N, pl.t.bn());
         n.v16 = (size_t)M * N;
@@ -391,7 +393,7 @@ ProductWs carve_product(Carve &c, long long M, long long N, long long K, int fam
     ProductWs w{};
     Needs n{0, 0, 0, 0, 0, 0};
     for (int rg = 0; rg < 2; ++rg) {
-        const Needs r = product_needs(plan_product(M, N, K, rg, family, f), M, N, rg);
+        const Needs r = product_needs(plan_product(M, N, K, rg, family, f), M, N, K, rg);
         n.gneed = mx(n.gneed, r.gneed);
         n.p16 = mx(n.p16, r.p16);
         n.v16 = mx(n.v16, r.v16);

@@ -127,7 +127,7 @@ enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2, PLAN_RECOMP = 3 }
 constexpr long long RECOMP_KMAX = 512;
 // Workgroups of the first pass of a recomputed whole-tensor product (a
 // persistent grid; each writes one maximum).
-int recomp_grid(long long M, long long N, Tile t);
+int recomp_grid(long long M, long long N, long long K, Tile t);
 
 struct Plan {
     Tile t;
@@ -191,7 +191,7 @@ struct Needs {
     size_t gneed, p16, v16, partial, sums, tneed;
 };
 bool split_round_rows_fits(int Nout, int mc, int mcp);
-Needs product_needs(const Plan &pl, long long M, long long N, int row_group);
+Needs product_needs(const Plan &pl, long long M, long long N, long long K, int row_group);
 Needs wgrad_needs(const Plan &pl, long long N, long long Kg, long long Kout, int mc, int mcp, int row_group);
 Needs batched_needs(const Plan &pl, long long Z, long long M, long long N);
 bool covers(const Needs &have, const Needs &need);

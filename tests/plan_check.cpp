@@ -70,13 +70,13 @@ static void touch(T *p, size_t idx) {
 // ---------------------------------------------------------------------------
 
 // The product epilogues and finalizes of plan pl on an M x N output.
-static void product_writes(const Plan &pl, long long M, long long N, int rg, const ProductWs &w) {
+static void product_writes(const Plan &pl, long long M, long long N, long long K, int rg, const ProductWs &w) {
     const int bm = pl.t.bm(), bn = pl.t.bn();
     const long long TM = (M + bm - 1) / bm, TN = (N + bn - 1) / bn;
     if (pl.mode == PLAN_RECOMP) {
         if (!rg) {
             // one running maximum per workgroup of the persistent first pass
-            for (int b = 0; b < recomp_grid(M, N, pl.t); ++b) touch(w.tneed, (size_t)b);
+            for (int b = 0; b < recomp_grid(M, N, K, pl.t); ++b) touch(w.tneed, (size_t)b);
         } else {
             for (long long r = 0; r < M; ++r)
                 for (long long tn = 0; tn < TN; ++tn) touch(w.tneed, (size_t)(r * TN + tn));
@@ -156,7 +156,7 @@ static void check_product_case(long long M, long long N, long long K, int family
         const bool valid = plan_valid(pl, M, N, K, rg, family);
         Carve c0{nullptr, HEADER};
         const ProductWs q = carve_product(c0, M, N, K, family, f);
-        const bool cov = covers(q.n, product_needs(pl, M, N, rg));
+        const bool cov = covers(q.n, product_needs(pl, M, N, K, rg));
         if (unforced) {
             REQUIRE(valid, "planner plan invalid: fam %d M %lld N %lld K %lld rg %d tile %dx%d mode %d", family, M, N,
                     K, rg, pl.t.mi, pl.t.ni, pl.mode);
@@ -171,7 +171,7 @@ static void check_product_case(long long M, long long N, long long K, int family
         Carve c{a.base, HEADER};
         const ProductWs w = carve_product(c, M, N, K, family, f);
         open_product(a, w);
-        product_writes(pl, M, N, rg, w);
+        product_writes(pl, M, N, K, rg, w);
         ++g_runs;
     }
 }
@@ -344,7 +344,7 @@ static void conv_layouts(const ie_conv_desc &d) {
         if (w.dyp) touch(w.dyp, (size_t)npq * g.kp - 1);
         if (w.xp) touch(w.xp, (size_t)nhw * g.cp - 1);
         const long long rskp = (long long)g.r * g.s * g.kp, rscp = (long long)g.r * g.s * g.cp;
-        product_writes(plan_product(nhw, g.c, rskp, 0, FAM_DGRAD, off), nhw, g.c, 0, w.pw);
+        product_writes(plan_product(nhw, g.c, rskp, 0, FAM_DGRAD, off), nhw, g.c, rskp, 0, w.pw);
         const Plan pw = plan_wgrad(g.k, rscp, npq, FAM_WGRAD_CONV, off);
         wgrad_writes(pw, g.k, rscp, (long long)g.r * g.s * g.c, g.c, g.cp, 1, npq, w.w);
     }
@@ -357,7 +357,8 @@ static void conv_layouts(const ie_conv_desc &d) {
         open_product(a, w.pw);
         if (w.xp) touch(w.xp, (size_t)nhw * g.cp - 1);
         if (w.wp) touch(w.wp, (size_t)g.k * g.r * g.s * g.cp - 1);
-        product_writes(plan_product(npq, g.k, (long long)g.r * g.s * g.cp, 0, FAM_IM2COL, off), npq, g.k, 0, w.pw);
+        product_writes(plan_product(npq, g.k, (long long)g.r * g.s * g.cp, 0, FAM_IM2COL, off), npq, g.k,
+                       (long long)g.r * g.s * g.cp, 0, w.pw);
     }
     ++g_runs;
 }
@@ -382,7 +383,8 @@ static void check_layouts() {
         if (w.xp) a.open(w.xp, (size_t)M * r16(K));
         if (w.wp) a.open(w.wp, (size_t)N * r16(K));
         open_product(a, w.pw);
-        for (int rg = 0; rg < 2; ++rg) product_writes(plan_product(M, N, r16(K), rg, FAM_DENSE, off), M, N, rg, w.pw);
+        for (int rg = 0; rg < 2; ++rg)
+            product_writes(plan_product(M, N, r16(K), rg, FAM_DENSE, off), M, N, r16(K), rg, w.pw);
         Arena b(linear_dw_ws(M, N, K, off));
         Carve cb{b.base, HEADER};
         const LinearDwWs v = carve_linear_dw(cb, M, N, K, off);
