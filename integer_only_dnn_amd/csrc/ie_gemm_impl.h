@@ -660,7 +660,7 @@ __device__ __forceinline__ void work_of(int bid, int TM, int TN, int S, int &tm,
 // per CU and would spill at 4, and for the 64 x 64 tile.
 template <int MI, int NI>
 struct Stages {
-    static constexpr int value = (MI == 2 && NI == 2) || MI * NI == 1 ? 3 : IE_STAGES;
+    static constexpr int value = MI * NI >= 8 ? 2 : (MI == 2 && NI == 2) || MI * NI == 1 ? 3 : IE_STAGES;
 };
 
 // Contraction slicing of the 64 x 64 tile: wave w takes the w-th 32-byte
@@ -685,15 +685,17 @@ struct Occ {
 // pipeline): up to four workgroups per CU.
 template <int MI, int NI>
 struct Occ1 {
-    static constexpr int value = MI * NI <= 2 ? 4 : MI * NI == 4 ? 3 : 2;
+    static constexpr int value = MI * NI <= 2 ? 4 : MI * NI == 4 ? 3 : MI * NI <= 8 ? 2 : 1;
 };
 
 // LDS of a tile: two stages of both operands (also the epilogue's staging).
-template <int KA, int KB, int MI, int NI>
+template <int KA, int KB, int MI, int NI, bool PARTIAL = true>
 struct TileLds {
     static constexpr int stages = 2 * (Lds<KA, 64 * MI>::BYTES + Lds<KB, 64 * NI>::BYTES);
     static constexpr int partial = 64 * MI * (64 * NI * 4 + 32);  // int32 staging of a split product
-    static constexpr int value = stages > partial ? stages : partial;
+    static constexpr int epi = 64 * MI * (64 * NI * 2 + 16) + 4 * 64 * MI * 4 + 64;  // int16 staging + maxima
+    static constexpr int out = PARTIAL ? partial : epi;
+    static constexpr int value = stages > out ? stages : out;
 };
 
 // LDS of a tile whose contraction is one step (K <= BK): one stage, or the
@@ -722,7 +724,7 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
     using LA = Lds<KA, BMt>;
     using LB = Lds<KB, BNt>;
     constexpr int STAGE = LA::BYTES + LB::BYTES;
-    constexpr int LDSB = ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value;  // bytes at lds
+    constexpr int LDSB = ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, PARTIAL>::value;  // bytes at lds
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1346,7 +1348,7 @@ __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::val
     Operand A, Operand B, int M, int N, int K, int k_chunk, int TM, int S, Epi ep) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     __shared__ __attribute__((aligned(16)))
-    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value];
+    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, PARTIAL>::value];
     gemm_tile<KA, KB, MI, NI, PARTIAL, ONE>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
 }
 
@@ -1363,7 +1365,7 @@ template <int KA, int KB, int MI, int NI, bool ONE>
 __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_max_kernel(
     Operand A, Operand B, int M, int N, int K, int TM, int items, Epi ep) {
     __shared__ __attribute__((aligned(16)))
-    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI>::value];
+    int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, false>::value];
     int run = NEED_NONE;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));

@@ -298,7 +298,7 @@ Plan plan_batched(long long Z, long long M, long long N, bool kk) {
 int recomp_grid(long long M, long long N, long long K, Tile t) {
     const long long tiles = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
     // workgroups per CU of the tile's kernel (its one-step form for K <= BK)
-    const long long per_cu = K <= BK ? (t.mi * t.ni <= 2 ? 4 : t.mi * t.ni == 4 ? 3 : 2)
+    const long long per_cu = K <= BK ? (t.mi * t.ni <= 2 ? 4 : t.mi * t.ni == 4 ? 3 : t.mi * t.ni <= 8 ? 2 : 1)
                                      : (t.mi * t.ni == 1 ? 3 : t.mi * t.ni <= 4 ? 2 : 1);
     long long g = NCU * per_cu;
     if (tiles < g) g = tiles;

@@ -158,7 +158,7 @@ def test_pointwise_argument_errors():
                              None) == 6
 
 
-@pytest.mark.parametrize("force", ["1,1,0,1", "2,2,0", "0,1", "1,0,1", "3,1,1", "4,4,1", "1,1,7"])
+@pytest.mark.parametrize("force", ["1,1,0,1", "2,2,0", "0,1", "1,0,1", "3,1,1", "4,4,1", "8,8,1", "1,1,7"])
 def test_forced_plans_without_kernel_are_refused(force, monkeypatch):
     """A forced plan (tests and tuning only) is validated like any other: a
     direct epilogue on groups spanning several tiles, a zero or unbuilt tile

@@ -43,8 +43,11 @@ def plan(monkeypatch):
     monkeypatch.delenv("IE_WTILE", raising=False)
 
 
-@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
-@pytest.mark.parametrize("mode", MODES, ids=lambda m: f"m{m[0]}s{m[1]}")
+DENSE_CASES = [(t, m) for t in DENSE_TILES for m in MODES]
+
+
+@pytest.mark.parametrize("tile,mode", DENSE_CASES,
+                         ids=[f"{64 * t[0]}x{64 * t[1]}-m{m[0]}s{m[1]}" for t, m in DENSE_CASES])
 def test_dense_plans(tile, mode, ws, plan):
     M, N, K = 200, 150, 392
     announce(f"dense plans tile={tile} mode={mode} M={M} N={N} K={K}")
