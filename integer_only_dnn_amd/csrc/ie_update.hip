@@ -60,6 +60,64 @@ __device__ __forceinline__ void store_dw(int8_t *row, long long col, long long c
         if (col + j < cols) row[col + j] = (int8_t)(w >> (8 * j));
 }
 
+// The D dwords a lane owns in a row are contiguous (bytes col0 .. col0 +
+// 4 D): one vector access per four dwords when the row holds them all and is
+// 4-byte aligned, else dword by dword with bounds checks.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int D>
+__device__ __forceinline__ void load_dws(const int8_t *row, long long col0, long long cols, int vec, uint32_t (&w)[D]) {
+    if (vec && col0 + 4 * D <= cols) {
+#pragma unroll
+        for (int j = 0; j < D; j += 4) {
+            const int8_t *p = row + col0 + 4 * j;
+            const int n = D - j < 4 ? D - j : 4;  // a compile-time constant once unrolled
+            // (indices clamped so that every branch compiles for any D)
+            if (n == 4) {
+                const u32x4 v = *(const u32x4 *)p;
+                w[j] = v.x, w[j + 1 < D ? j + 1 : j] = v.y, w[j + 2 < D ? j + 2 : j] = v.z,
+                w[j + 3 < D ? j + 3 : j] = v.w;
+            } else if (n == 3) {
+                const u32x3 v = *(const u32x3 *)p;
+                w[j] = v.x, w[j + 1 < D ? j + 1 : j] = v.y, w[j + 2 < D ? j + 2 : j] = v.z;
+            } else if (n == 2) {
+                const u32x2 v = *(const u32x2 *)p;
+                w[j] = v.x, w[j + 1 < D ? j + 1 : j] = v.y;
+            } else {
+                w[j] = *(const uint32_t *)p;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) w[j] = load_dw(row, col0 + 4 * j, cols, vec);
+}
+
+template <int D>
+__device__ __forceinline__ void store_dws(int8_t *row, long long col0, long long cols, int vec, const uint32_t (&w)[D]) {
+    if (vec && col0 + 4 * D <= cols) {
+#pragma unroll
+        for (int j = 0; j < D; j += 4) {
+            int8_t *p = row + col0 + 4 * j;
+            const int n = D - j < 4 ? D - j : 4;
+            if (n == 4) {
+                *(u32x4 *)p = u32x4{w[j], w[j + 1 < D ? j + 1 : j], w[j + 2 < D ? j + 2 : j], w[j + 3 < D ? j + 3 : j]};
+            } else if (n == 3) {
+                *(u32x3 *)p = u32x3{w[j], w[j + 1 < D ? j + 1 : j], w[j + 2 < D ? j + 2 : j]};
+            } else if (n == 2) {
+                *(u32x2 *)p = u32x2{w[j], w[j + 1 < D ? j + 1 : j]};
+            } else {
+                *(uint32_t *)p = w[j];
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) store_dw(row, col0 + 4 * j, cols, vec, w[j]);
+}
+
 // The wide (int64) forms are out of line: rows with exponent gaps above 15
 // are rare, and inlined they raise the register pressure of every row's path
 // (measured: spills and half the throughput).
@@ -257,6 +315,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = wave % WPR;
+    const long long col0 = 4ll * D * (lane + 64 * sub);  // this lane's first byte of a row
     __shared__ uint32_t red[2][4];
     __shared__ int bred[4];
     int parity = 0;
@@ -317,12 +376,18 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     };
     auto load_row = [&](long long row, RowIn &x) {
         const long long off = row * a.cols;
+        if (pass != 0 || WD) {
+            load_dws<D>(a.w + off, col0, a.cols, vec, x.W);
+        } else {
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const long long col = 4ll * (lane + 64 * (sub + WPR * j));
-            x.W[j] = (pass != 0 || WD) ? load_dw(a.w + off, col, a.cols, vec) : 0u;
-            x.V[j] = load_dw(a.v + off, col, a.cols, vec);
-            x.G[j] = (pass != 2) ? load_dw(a.g + off, col, a.cols, vec) : 0u;
+            for (int j = 0; j < D; ++j) x.W[j] = 0u;
+        }
+        load_dws<D>(a.v + off, col0, a.cols, vec, x.V);
+        if (pass != 2) {
+            load_dws<D>(a.g + off, col0, a.cols, vec, x.G);
+        } else {
+#pragma unroll
+            for (int j = 0; j < D; ++j) x.G[j] = 0u;
         }
         x.ew = w_tensor ? ew_t : (int)a.w_exp[row];
         x.ev = pass == 2 ? (int)a.v_exp[v_tensor ? 0 : row] : v_tensor ? ev_t : (int)a.v_exp[row];
@@ -350,19 +415,22 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     #pragma unroll
                         for (int t = 0; t < 4; ++t) n[j][t] = __mul24(sbyte(W[j], t), fa) + __mul24(sbyte(V[j], t), fb);
                     rne_rows<D>(n, rne_u(e - base), c);
+                    uint32_t o[D];
     #pragma unroll
-                    for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
+                    for (int j = 0; j < D; ++j) o[j] = pack4(c[j]);
+                    store_dws<D>(a.w + off, col0, a.cols, vec, o);
                 } else {
+                    uint32_t o[D];
     #pragma unroll
                     for (int j = 0; j < D; ++j) {
-                        uint32_t o = 0;
+                        o[j] = 0;
     #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             const int c = sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * sbyte(V[j], t), pw, e);
-                            o |= (uint32_t)(uint8_t)c << (8 * t);
+                            o[j] |= (uint32_t)(uint8_t)c << (8 * t);
                         }
-                        store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
                     }
+                    store_dws<D>(a.w + off, col0, a.cols, vec, o);
                 }
                 if (row == 0 && lane == 0 && sub == 0) a.w_exp[0] = (int8_t)e;
                 return;
@@ -425,8 +493,12 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
                             c[j][t] = sum_round_wide(a.mom_m * sbyte(V[j], t), pa, sbyte(G[j], t), pb, evn);
                     }
             }
+            {
+                uint32_t o[D];
     #pragma unroll
-            for (int j = 0; j < D; ++j) store_dw(a.v + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(c[j]));
+                for (int j = 0; j < D; ++j) o[j] = pack4(c[j]);
+                store_dws<D>(a.v + off, col0, a.cols, vec, o);
+            }
             if (lane == 0 && sub == 0) {
                 if (!v_tensor) a.v_exp[row] = (int8_t)evn;
                 else if (row == 0) a.v_exp[0] = (int8_t)evn;
@@ -462,17 +534,20 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
             if (nw) {
                 int cw[D][4];
                 rne_rows<D>(vn, rne_u(ewn - min(ew, pw)), cw);
+                uint32_t o[D];
     #pragma unroll
-                for (int j = 0; j < D; ++j) store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, pack4(cw[j]));
+                for (int j = 0; j < D; ++j) o[j] = pack4(cw[j]);
+                store_dws<D>(a.w + off, col0, a.cols, vec, o);
             } else {
+                uint32_t o[D];
     #pragma unroll
                 for (int j = 0; j < D; ++j) {
-                    uint32_t o = 0;
+                    o[j] = 0;
     #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        o |= (uint32_t)(uint8_t)sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, ewn) << (8 * t);
-                    store_dw(a.w + off, 4ll * (lane + 64 * (sub + WPR * j)), a.cols, vec, o);
+                        o[j] |= (uint32_t)(uint8_t)sum_round_wide(sbyte(W[j], t), ew, -a.lr_m * c[j][t], pw, ewn) << (8 * t);
                 }
+                store_dws<D>(a.w + off, col0, a.cols, vec, o);
             }
             if (lane == 0 && sub == 0) a.w_exp[row] = (int8_t)ewn;
     };
