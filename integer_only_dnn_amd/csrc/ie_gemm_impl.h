@@ -1271,7 +1271,9 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
                     ovf |= tgt > E_MAX;
                     tgt = min(tgt, E_MAX);
                     if (row < M && tile_n == 0) ep.out_exp[row] = (int8_t)tgt;
-                    rowf[tr] = __builtin_ldexpf(1.0f, eav + ebmin - tgt);
+                    // an all-zero row would otherwise scale by up to 2^254
+                    // (inf, and 0 * inf is NaN); its results are 0
+                    rowf[tr] = rm == NEED_NONE ? 0.0f : __builtin_ldexpf(1.0f, eav + ebmin - tgt);
                 } else {
                     tgt = rm == NEED_NONE ? P_NONE : rm - 2;
                     if (row < M) ep.p16[(long long)row * n_ct + tile_n] = (int16_t)(rm == NEED_NONE ? P_NONE : rm);
