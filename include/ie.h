@@ -185,9 +185,13 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,
  * ie_conv_fwd in X (W aligned over its output channels first when
  * ROW-grouped), and the weight gradient dW, its adjoint in W (one exponent
  * per output channel when ROW, Table 5).  dX or dW may be NULL to skip that
- * output.  X, dY, dX: TENSOR; W, dW: TENSOR or ROW.
+ * output.  X, dY: TENSOR; dX: TENSOR, or ROW (one exponent per input
+ * pixel); W, dW: TENSOR or ROW.
+ * A stride-2 input gradient with one exponent is computed in stride phases
+ * (each input pixel only meets the filter taps of its phase), so no tap that
+ * misses an output pixel is multiplied.
  * With both outputs requested the two products run as one grid where a
- * paired kernel covers their plans (round-to-odd input gradient, row-grouped
+ * paired kernel covers their plans (whole-tensor input gradient, row-grouped
  * weight gradient), else one after the other; all work is enqueued on
  * `stream`, and the library creates no stream or event of its own.
  * Limits as for ie_conv_fwd, with the contraction k*r*s <= 65536.

@@ -150,6 +150,32 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     return IE_OK;
 }
 
+// Input gradient of a strided convolution in stride phases (the recomputed
+// epilogue: group maximum over every phase, then each phase rounded
+// straight to int8 at its input pixels).
+ie_status run_dgrad_phased(const DgradPlan &dp, const Operand &A, const Operand &B, long long N, ExpSrc ea,
+                           ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, hipStream_t st) {
+    IE_CHECK(checked_plan(dp.pl, dp.M, N, dp.K, 0, FAM_DGRAD, pw.n, product_needs(dp.pl, dp.M, N, dp.K, 0)));
+    if (dp.pl.mode != PLAN_RECOMP || out->group != IE_GROUP_TENSOR || dp.ps.n == 0) return IE_ERR_UNSUPPORTED;
+    log_plan("conv phased", dp.M, N, dp.K, dp.pl);
+    Epi ep;
+    memset(&ep, 0, sizeof ep);
+    ep.ea = ea;
+    ep.eb = eb;
+    ep.out = out->mant;
+    ep.out_exp = out->exp;
+    ep.flags = flags;
+    ep.q = mat_q(out);
+    ep.ph = dp.ps;
+    ep.tneed = pw.tneed;
+    ep.tneed_n = recomp_grid(dp.M, N, dp.K, dp.pl.t);
+    ep.mode = EPI_MAX;
+    IE_TRY(launch_gemm(A, B, (int)dp.M, (int)N, (int)dp.K, dp.pl.t, 1, dp.pl.k_chunk, false, ep, st));
+    ep.mode = EPI_GIVEN;
+    IE_TRY(launch_gemm(A, B, (int)dp.M, (int)N, (int)dp.K, dp.pl.t, 1, dp.pl.k_chunk, false, ep, st));
+    return IE_OK;
+}
+
 // Weight gradient [N x Kg] contracted over L rows; the stored output is
 // [N x Kout] with column j taken from (j / mc) * mcp + j % mc of the GEMM
 // columns (mc == mcp: identity).
@@ -199,27 +225,29 @@ ie_status run_wgrad(const Operand &A, const Operand &B, long long N, long long K
 // being the weight read in place or its aligned transposed copy, already
 // written; the weight gradient as a split contraction with the fused row
 // finalize.  IE_ERR_UNSUPPORTED, with nothing launched, otherwise.
-ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, ExpSrc ew, const ie_mat *dY,
-                        const ie_mat *dX, const ie_mat *dW, const int8_t *dys, int8_t *xp, const ConvBwdWs &cw,
-                        uint32_t *flags, hipStream_t st) {
+ie_status conv_bwd_pair(const ConvGeom &g, const DgradPlan &dp, const ie_mat *X, const Operand &B1, ExpSrc ew,
+                        const ie_mat *dY, const ie_mat *dX, const ie_mat *dW, const int8_t *dys, int8_t *xp,
+                        const ConvBwdWs &cw, uint32_t *flags, hipStream_t st) {
     const long long nhw = (long long)g.n * g.h * g.w, npq = (long long)g.n * g.p * g.q;
-    const long long rskp = (long long)g.r * g.s * g.kp, rscp = (long long)g.r * g.s * g.cp;
+    const long long rscp = (long long)g.r * g.s * g.cp;
     const long long rsc = (long long)g.r * g.s * g.c;
-    if (nhw == 0 || npq == 0 || dW->group != IE_GROUP_ROW || !split_round_rows_fits((int)rsc, g.c, g.cp))
+    if (nhw == 0 || npq == 0 || dX->group != IE_GROUP_TENSOR || dW->group != IE_GROUP_ROW ||
+        !split_round_rows_fits((int)rsc, g.c, g.cp))
         return IE_ERR_UNSUPPORTED;
     const Operand A1{LD_DGRAD, dys, g.kp, (int)nhw, g};
     const Operand A2{LD_T, dys, g.kp, g.k, {}};
     const Operand B2{LD_IM2COL_T, xp ? xp : X->mant, g.cp, (int)rscp, g};
     const int fam1 = family_of(A1, B1);
-    const Plan p1 = plan_product(nhw, g.c, rskp, 0, fam1, force_product());
+    const Plan p1 = dp.pl;
+    const long long M1 = dp.M, K1 = dp.K;
     if (p1.mode != PLAN_RTO && p1.mode != PLAN_RECOMP) return IE_ERR_UNSUPPORTED;
     const Plan p2 = plan_wgrad(g.k, rscp, npq, FAM_WGRAD_CONV, force_wgrad());
     if (!gemm_pair_supported(A1, B1, p1.t, A2, B2, p2.t)) return IE_ERR_UNSUPPORTED;
-    if (checked_plan(p1, nhw, g.c, rskp, 0, fam1, cw.pw.n, product_needs(p1, nhw, g.c, rskp, 0)) != IE_OK ||
+    if (checked_plan(p1, M1, g.c, K1, 0, fam1, cw.pw.n, product_needs(p1, M1, g.c, K1, 0)) != IE_OK ||
         checked_plan(p2, g.k, rscp, npq, 1, FAM_WGRAD_CONV, cw.w.n, wgrad_needs(p2, g.k, rscp, rsc, g.c, g.cp, 1)) !=
             IE_OK)
         return IE_ERR_UNSUPPORTED;
-    log_plan("conv", nhw, g.c, rskp, p1);
+    log_plan(dp.ps.n ? "conv phased" : "conv", M1, g.c, K1, p1);
     log_plan("wgrad", g.k, rscp, npq, p2);
     if (xp) IE_TRY(launch_pad_rows(X->mant, nhw, g.c, nullptr, 0, nullptr, g.cp, xp, st));
     const ExpSrc edy{dY->exp, nullptr, 0}, ex{X->exp, nullptr, 0};
@@ -234,11 +262,12 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     e1.v16 = cw.pw.v16;
     e1.p16 = cw.pw.p16;
     e1.q = mat_q(dX);
+    e1.ph = dp.ps;
     if (p1.mode == PLAN_RECOMP) {
         e1.tneed = cw.pw.tneed;
-        e1.tneed_n = recomp_grid(nhw, g.c, rskp, p1.t);
+        e1.tneed_n = recomp_grid(M1, g.c, K1, p1.t);
         e1.mode = EPI_MAX;
-        IE_TRY(launch_gemm(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, 1, p1.k_chunk, false, e1, st));
+        IE_TRY(launch_gemm(A1, B1, (int)M1, g.c, (int)K1, p1.t, 1, p1.k_chunk, false, e1, st));
         e1.mode = EPI_GIVEN;
     }
     Epi e2;
@@ -249,7 +278,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const ie_mat *X, const Operand &B1, E
     e2.gneed = cw.w.gneed;
     e2.gneed_n = 0;
     e2.q = mat_q(dW);
-    IE_TRY(launch_gemm_pair(A1, B1, (int)nhw, g.c, (int)rskp, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
+    IE_TRY(launch_gemm_pair(A1, B1, (int)M1, g.c, (int)K1, p1.t, p1.k_chunk, e1, A2, B2, g.k, (int)rscp,
                             (int)npq, p2.t, p2.splits, p2.k_chunk, e2, st));
     if (p1.mode == PLAN_RECOMP) {
         IE_TRY(launch_split_round_rows(cw.w.partial, p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy,
@@ -675,25 +704,43 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
         dys = cw.dyp;
     }
     // B side of the input gradient: the weight read in place (one exponent,
-    // 16-channel multiples), else its copy aligned over the output channels
-    // and transposed to [c][r][s][kp]
-    const bool in_place = W->group == IE_GROUP_TENSOR && g.c % 16 == 0 && aligned(W->mant, 16) &&
-                          weight_window_fits(g);
+    // 16-channel multiples, no phases), else its copy aligned over the
+    // output channels and transposed to [c][r][s][kp].  The input gradient's
+    // plan: stride 2 with one exponent for dX runs in stride phases, which
+    // read the copy with its taps sorted by phase.
+    const bool in_place_ok = W->group == IE_GROUP_TENSOR && g.c % 16 == 0 && aligned(W->mant, 16) &&
+                             weight_window_fits(g);
+    const DgradPlan dp = plan_dgrad(g, dX && dX->group == IE_GROUP_ROW, f, in_place_ok);
+    const bool phased = dX && dp.ps.n > 0;
+    const bool in_place = !phased && in_place_ok;
     const Operand B1 = in_place ? Operand{LD_WT, W->mant, 0, g.c, g} : Operand{LD_K, cw.wt, rskp, g.c, {}};
     const ExpSrc ew = in_place ? ExpSrc{W->exp, nullptr, 0} : ExpSrc{nullptr, cw.estar, 0};
     if (dX && !in_place && nhw > 0) {
+        TapOrder to{};
+        if (phased) {
+            to.st = dp.ps.st;
+            to.pad = g.pad;
+            to.s = g.s;
+            for (int t = 0; t < dp.ps.n; ++t) {
+                to.tap0[t] = dp.ps.r[t].tap0;
+                to.sb[t] = dp.ps.r[t].sb;
+            }
+        }
         IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, g.k, g.r * g.s, g.c, g.kp, cw.wt,
-                                      cw.estar, st));
+                                      cw.estar, st, to));
     }
     if (dX && dW) {
         // the two products are independent: one grid runs both when a paired
         // kernel covers their plans, else they run one after the other
-        const ie_status sp = conv_bwd_pair(g, X, B1, ew, dY, dX, dW, dys, cw.xp, cw, flags, st);
+        const ie_status sp = conv_bwd_pair(g, dp, X, B1, ew, dY, dX, dW, dys, cw.xp, cw, flags, st);
         if (sp != IE_ERR_UNSUPPORTED) return sp;
     }
     if (dX) {
         const Operand A{LD_DGRAD, dys, g.kp, (int)nhw, g};
-        IE_CHECK(run_product(A, B1, nhw, g.c, rskp, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st));
+        if (phased)
+            IE_CHECK(run_dgrad_phased(dp, A, B1, g.c, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st));
+        else
+            IE_CHECK(run_product(A, B1, nhw, g.c, rskp, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st));
     }
     if (dW) {
         const int8_t *xs = X->mant;

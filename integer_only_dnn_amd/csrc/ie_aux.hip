@@ -254,28 +254,39 @@ hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, con
     return hipGetLastError();
 }
 
-// w viewed as [A][B][C] (row exponent e[a], or e[0]): out[c][b][a] =
+// w viewed as [A][B][C] (row exponent e[a], or e[0]): out[c][b'][a] =
 // w[a][b][c] at the largest row exponent e*, zero for A <= a < Ap (output
-// pitch Ap, a multiple of 16).  Every block finds e* itself (A bytes); block
-// 0 stores it.  A block moves a 64 x 64 tile through LDS: with C a multiple
-// of 16 (vec), each thread loads 16 bytes of one row a and stores 16 bytes
-// of one output row c; otherwise bytes one at a time.
+// pitch Ap, a multiple of 16); b' = b, or with to.st the position of filter
+// tap b = (r, s) among the taps sorted by stride phase.  Every block finds
+// e* itself (A bytes); block 0 stores it.  A block moves a 64 x 64 tile
+// through LDS: with C a multiple of 16 (vec), each thread loads 16 bytes of
+// one row a and stores 16 bytes of one output row c; otherwise bytes one at
+// a time.
 __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, const int8_t *e, int e_row, int A,
                                                               int B, int C, int Ap, int8_t *out, int *estar_out,
-                                                              int vec) {
+                                                              int vec, TapOrder to) {
     constexpr int TP = 64 + 16;  // tile pitch
     __shared__ __attribute__((aligned(16))) int8_t tile[64 * TP];
     __shared__ int sh[4];
     const int es = e_row ? exp_max_block(e, A, sh) : (int)e[0];
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) estar_out[0] = es;
-    const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64, b = blockIdx.z;
+    const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 64, bi = blockIdx.z;
+    int b = bi;
+    if (to.st) {
+        // tap (r, s) of phase (ph, pw), ph = (r - pad) mod st: its (r / st, s / st)
+        // in that phase's row-major block
+        const int r = bi / to.s, s_ = bi - r * to.s;
+        const int ph = ((r - to.pad) % to.st + to.st) % to.st, pw = ((s_ - to.pad) % to.st + to.st) % to.st;
+        const int t = ph * to.st + pw;
+        b = to.tap0[t] + (r / to.st) * to.sb[t] + s_ / to.st;
+    }
     const int t = threadIdx.x;
     if (vec) {
         const int la = t >> 2, lc = (t & 3) * 16;
         const int a = a0 + la, c = c0 + lc;
         v4i v = v4i{0, 0, 0, 0};
         if (a < A && c < C) {
-            v = *(const v4i *)(w + ((long long)a * B + b) * C + c);
+            v = *(const v4i *)(w + ((long long)a * B + bi) * C + c);
             const int s = es - (e_row ? (int)e[a] : es);
             if (s != 0) {
 #pragma unroll
@@ -300,7 +311,7 @@ __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, c
         int8_t v = 0;
         if (a < A && c < C) {
             int ea = e_row ? (int)e[a] : es;
-            v = (int8_t)rne_shift32(w[((long long)a * B + b) * C + c], es - ea);
+            v = (int8_t)rne_shift32(w[((long long)a * B + bi) * C + c], es - ea);
         }
         tile[la * TP + lc] = v;
     }
@@ -313,13 +324,13 @@ __global__ __launch_bounds__(256) void align_transpose_kernel(const int8_t *w, c
 }
 
 hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, int A, int B, int C, int Ap,
-                                  int8_t *out, int *estar_out, hipStream_t st) {
+                                  int8_t *out, int *estar_out, hipStream_t st, const TapOrder &to) {
     if (Ap <= 0 || B <= 0 || C <= 0) return hipSuccess;
     dim3 grid((C + 63) / 64, (Ap + 63) / 64, B);
     const int vec = C % 16 == 0 && Ap % 16 == 0 && ((uintptr_t)w % 16) == 0 && ((uintptr_t)out % 16) == 0;
     prof_begin(st, PROF_ALIGN);
     hipLaunchKernelGGL(align_transpose_kernel, grid, dim3(256), 0, st, w, e, e_row, A, B, C, Ap, out, estar_out,
-                       vec);
+                       vec, to);
     prof_end(st, PROF_ALIGN);
     return hipGetLastError();
 }

@@ -194,11 +194,13 @@ struct Ld<LD_K, ROWS> : KChunks<ROWS> {
     Res res;
     uint32_t off[CH];
     int col;
-    __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid) {
+    __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid, int koff = 0) {
         (void)kb;
         col = B_::col(tid);
         const int vr = min(max(op.rows - i0, 0), ROWS);
-        res = make_res(op.base + (long long)i0 * op.ld, vr * (int)op.ld);
+        // koff: the contraction starts at column koff (a stride phase's taps);
+        // every load stays below column koff + kend <= ld
+        res = make_res(op.base + (long long)i0 * op.ld + koff, vr * (int)op.ld - koff);
 #pragma unroll
         for (int c = 0; c < CH; ++c) off[c] = (uint32_t)(B_::row(c, tid) * (int)op.ld + col);
     }
@@ -272,11 +274,30 @@ struct Ld<LD_IM2COL, ROWS> : KChunks<ROWS> {
     }
 };
 
+// What the input-gradient loader reads of a geometry: the convolution's own,
+// or one of its stride phases (a stride-1 gather over the phase's pixels
+// h = ph + st i, w = pw + st j and taps r = r0 + st a, s = s0 + st b).
+struct DgGeo {
+    int kp, R, S, P, Q, hw, W, padh, padw, stride, st_inv, dc, ds, dr;
+    FastDiv dhw, dw, dst, dk, dsS;
+};
+
+__device__ __forceinline__ DgGeo dg_geo(const ConvGeom &g) {
+    return DgGeo{g.kp, g.r, g.s, g.p, g.q, g.h * g.w, g.w, g.pad, g.pad, g.stride, g.st_inv, g.dg_dc, g.dg_ds,
+                 g.dg_dr, g.dhw, g.dw, g.dst, g.dk, g.ds};
+}
+
+__device__ __forceinline__ DgGeo dg_geo(const ConvGeom &g, const PhaseRec &p) {
+    return DgGeo{g.kp, p.ra, p.sb, g.p, g.q, p.hn * p.wn, p.wn, p.ch, p.cw, 1, 65536, g.dg_dc, p.ds,
+                 p.dr, p.dhw, p.dw, FastDiv{1u << 31, 31}, g.dk, p.dsb};
+}
+
 // Input gradient of a convolution: row m = (n, h, w), k = (r, s, ko) over the
 // padded output-channel count kp; element dY[n, p, q, ko] with
 // p * stride = h + pad - r (zero unless exact).  With h + pad = st a + b, the
 // taps that hit are r = b + st j, at p = a - j = a - floor(r / st).  Window:
-// the output images of the tile's rows.
+// the output images of the tile's rows.  For a stride phase the rows are the
+// phase's pixels and the taps its own, at stride 1.
 template <int ROWS>
 struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
     using B_ = KChunks<ROWS>;
@@ -288,36 +309,39 @@ struct Ld<LD_DGRAD, ROWS> : KChunks<ROWS> {
     int r, s, ko;      // contraction index of the next load
     int kp, S, Q, dc, ds, dr, st_inv;
     __device__ __forceinline__ void init(const Operand &op, int i0, int kb, int tid) {
-        const ConvGeom &g = op.g;
+        init_geo(dg_geo(op.g), op.base, op.rows, i0, kb, tid);
+    }
+    __device__ __forceinline__ void init_geo(const DgGeo &g, const int8_t *base, int nrows, int i0, int kb,
+                                             int tid) {
         kp = g.kp;
-        S = g.s;
-        Q = g.q;
-        dc = g.dg_dc;
-        ds = g.dg_ds;
-        dr = g.dg_dr;
+        S = g.S;
+        Q = g.Q;
+        dc = g.dc;
+        ds = g.ds;
+        dr = g.dr;
         st_inv = g.st_inv;
-        const int last = min(i0 + ROWS, op.rows) - 1;
+        const int last = min(i0 + ROWS, nrows) - 1;
         const int nf = (int)fdiv((uint32_t)i0, g.dhw), nl = (int)fdiv((uint32_t)max(last, i0), g.dhw);
-        const int img = g.p * g.q * g.kp;
-        res = make_res(op.base + (long long)nf * img, (nl - nf + 1) * img);
+        const int img = g.P * g.Q * g.kp;
+        res = make_res(base + (long long)nf * img, (nl - nf + 1) * img);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int m = i0 + B_::row(c, tid);
-            const bool ok = m < op.rows;
+            const bool ok = m < nrows;
             const uint32_t mm = ok ? m : i0;
-            const uint32_t n = fdiv(mm, g.dhw), rem = mm - n * (uint32_t)(g.h * g.w);
-            const uint32_t h = fdiv(rem, g.dw), w = rem - h * g.w;
-            const int hp = (int)h + g.pad, wp = (int)w + g.pad;
+            const uint32_t n = fdiv(mm, g.dhw), rem = mm - n * (uint32_t)g.hw;
+            const uint32_t h = fdiv(rem, g.dw), w = rem - h * g.W;
+            const int hp = (int)h + g.padh, wp = (int)w + g.padw;
             const int ah = (int)fdiv((uint32_t)hp, g.dst), aw = (int)fdiv((uint32_t)wp, g.dst);
-            pix[c] = (((int)(n - nf) * g.p + ah) * g.q + aw) * g.kp;
-            msk[c] = ok ? stride_bits(hp, g.r, g.p, g.stride, g.dst) | stride_bits(wp, g.s, g.q, g.stride, g.dst) << 16
+            pix[c] = (((int)(n - nf) * g.P + ah) * g.Q + aw) * g.kp;
+            msk[c] = ok ? stride_bits(hp, g.R, g.P, g.stride, g.dst) | stride_bits(wp, g.S, g.Q, g.stride, g.dst) << 16
                         : 0u;
         }
         const uint32_t kk = kb + B_::col(tid);
         const uint32_t rs = fdiv(kk, g.dk);
         ko = (int)(kk - rs * g.kp);
-        r = (int)fdiv(rs, g.ds);
-        s = (int)rs - r * g.s;
+        r = (int)fdiv(rs, g.dsS);
+        s = (int)rs - r * g.S;
     }
     __device__ __forceinline__ void load(int k0, int kend, v4i (&reg)[CH]) {
         (void)k0;
@@ -656,6 +680,14 @@ __device__ __forceinline__ void work_of(int bid, int TM, int TN, int S, int &tm,
     tn = __builtin_amdgcn_readfirstlane(t - tm * TN);
 }
 
+// Stride phase of tile row t of a phase-decomposed input gradient: each
+// aligned group of four tile rows holds the four phases, rotated by a hash
+// of the group, so that workgroups walking the tiles at any stride (the
+// persistent first pass) meet every phase, not one.
+__device__ __forceinline__ int phase_of_tile(int t) {
+    return (t + (int)(((uint32_t)(t >> 2) * 2654435761u) >> 30)) & 3;
+}
+
 // Register pipeline depth: 3 for the 2 x 2 tile, which runs two workgroups
 // per CU and would spill at 4, and for the 64 x 64 tile.
 template <int MI, int NI>
@@ -716,8 +748,8 @@ struct TileLds1 {
 // most one step, loaded once, with no pipeline and no second buffer).
 // Returns the tile's group maximum in the first pass of a recomputed
 // whole-tensor product (EPI_MAX), NEED_NONE otherwise.
-template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false>
-__device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int M, int N, int K, int k_chunk,
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false, int MODE = -1>
+__device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int M_, int N, int K, int k_chunk,
                                           int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     constexpr int BMt = 64 * MI, BNt = 64 * NI;
@@ -733,16 +765,43 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
     const int TN = (N + BNt - 1) / BNt;
     int tile_m, tile_n, z;
     work_of(bid, TM, TN, S, tile_m, tile_n, z);
-    const int m0 = tile_m * BMt, n0 = tile_n * BNt;
-    const int kb = z * k_chunk;
-    const int ke = min(K, kb + k_chunk);
-    const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+    int M = M_, m0 = tile_m * BMt;
+    const int n0 = tile_n * BNt;
+    int kb = z * k_chunk;
+    int ke = min(K, kb + k_chunk);
 
     Ld<KA, BMt> la;
     Ld<KB, BNt> lb;
     static_assert(Ld<KA, BMt>::ZK || Ld<KB, BNt>::ZK, "one operand must zero the contraction past its end");
-    la.init(A, m0, kb, tid);
-    lb.init(B, n0, kb, tid);
+    // A stride phase of an input gradient (tile rows are grouped by phase,
+    // the phases in order): the phase's pixels as rows, its taps as the
+    // contraction, its columns of the phase-sorted weight copy.
+    bool phased = false;
+    PhaseRec pr{};
+    if constexpr (KA == LD_DGRAD && KB == LD_K) {
+        if (ep.ph.n) {
+            // the phases interleave: tile row tile_m is row tile_m / 4 of phase
+            // phase_of_tile(tile_m), a rotation within each aligned group of four
+            pr = ep.ph.r[phase_of_tile(tile_m)];
+            phased = true;
+            M = pr.rows;
+            m0 = (tile_m >> 2) * BMt;
+            kb = 0;
+            ke = pr.klen;
+            static_assert(PHASES_MAX == 4, "stride-2 phases");
+            if (m0 >= M) ke = 0;  // past the phase's rows: an empty tile
+            // the first pass finds nothing in a phase without taps or past its rows
+            if constexpr (MODE == EPI_MAX)
+                if (ke == 0) return NEED_NONE;
+            la.init_geo(dg_geo(A.g, pr), A.base, M, m0, 0, tid);
+            lb.init(B, n0, 0, tid, pr.k0);
+        }
+    }
+    if (!phased) {
+        la.init(A, m0, kb, tid);
+        lb.init(B, n0, kb, tid);
+    }
+    const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     constexpr int CA = Ld<KA, BMt>::CH, CB = Ld<KB, BNt>::CH;
 
     // exponents of this tile's rows and columns, for the epilogue
@@ -919,8 +978,17 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
         for (int q0 = 0; q0 < BMt * CPR; q0 += NTHR) {
             const int q = q0 + tid;
             const int row = q / CPR, cb = (q % CPR) * 16;
-            const int grow = m0 + row, gcol = n0 + cb / ES;
+            const int gcol = n0 + cb / ES;
+            int grow = m0 + row;
             if (grow >= M || gcol >= N) continue;
+            if constexpr (KA == LD_DGRAD && KB == LD_K) {
+                // a phase pixel (n, i, j) is input pixel (n, ph + st i, pw + st j)
+                if (phased) {
+                    const uint32_t n = fdiv((uint32_t)grow, pr.dhw), rem = grow - n * (uint32_t)(pr.hn * pr.wn);
+                    const uint32_t i = fdiv(rem, pr.dw), j = rem - i * (uint32_t)pr.wn;
+                    grow = ((int)n * ep.ph.h + pr.ph + ep.ph.st * (int)i) * ep.ph.w + pr.pw + ep.ph.st * (int)j;
+                }
+            }
             v4i v = *(const v4i *)(lds + row * PITCH + cb);
             if constexpr (ES == 1) {
                 if (ep.relu) {
@@ -993,7 +1061,7 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
         const int wq = ep.q;  // results have |C| <= 2^wq - 1
         const int ea0 = seA[0];
         const int eb0 = seB[0];
-        const int mode = ep.mode;
+        const int mode = MODE >= 0 ? MODE : ep.mode;
         const bool direct = mode == EPI_DIRECT || mode == EPI_GIVEN;  // int8 results from this pass
 
         if (!ep.row_group) {
@@ -1370,7 +1438,7 @@ __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::val
     int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, false>::value];
     int run = NEED_NONE;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
+        run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE, EPI_MAX>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
         __syncthreads();  // the next item's stages reuse the LDS
     }
     if (!ep.row_group && threadIdx.x == 0) ep.tneed[blockIdx.x] = run;

@@ -54,6 +54,8 @@ struct Epi {
     int q;            // results have |C| <= 2^q - 1 (mantissa width q + 1 bits)
     int *tneed;       // MAX writes / GIVEN reads: group maxima of the first pass
     int tneed_n;      //   whole tensor: the first pass's grid size (entries)
+    Phases ph;        // input gradient in stride phases (ph.n = 0: not decomposed);
+                      //   rows are then phase pixels, stored at their input pixel
 };
 
 enum LoaderKind {
@@ -144,11 +146,19 @@ hipError_t launch_exp_max2(const int8_t *e0, long long n0, int *out0, const int8
 // Copy rows into a zero-padded pitch, re-expressed at *estar when set.
 hipError_t launch_pad_rows(const int8_t *in, long long rows, long long cols, const int8_t *e, int e_row,
                            const int *estar, long long cols_p, int8_t *out, hipStream_t st);
+// Order of the filter taps b = r s_ + s in a transposed weight copy: as
+// they come (st = 0), or sorted by stride phase (tap (r, s) of phase t =
+// ph st + pw, ph = (r - pad) mod st, goes to tap0[t] + (r / st) sb[t] + s / st).
+struct TapOrder {
+    int st, pad, s;
+    int tap0[PHASES_MAX], sb[PHASES_MAX];
+};
 // w viewed as [A][B][C] with row exponents e[a] (e_row) or e[0]:
-// out[c][b][a] = w[a][b][c] re-expressed at the largest row exponent, zero
-// for A <= a < Ap; that exponent is also written to *estar_out.
+// out[c][b'][a] = w[a][b][c] re-expressed at the largest row exponent, zero
+// for A <= a < Ap, b' the position of b in the tap order; that exponent is
+// also written to *estar_out.
 hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, int A, int B, int C, int Ap,
-                                  int8_t *out, int *estar_out, hipStream_t st);
+                                  int8_t *out, int *estar_out, hipStream_t st, const TapOrder &to = TapOrder{});
 // Second pass of the round-to-odd epilogue: the group exponent is the
 // maximum of the tile needs in p16 (ROW groups: per (row, column tile);
 // whole-tensor groups: per tile, tile_m + TM * tile_n).

@@ -155,6 +155,69 @@ bool conv_fits(const ConvGeom &g) {
 bool weight_window_fits(const ConvGeom &g) { return (long long)g.kp * g.r * g.s * g.c <= WINDOW; }
 
 // ---------------------------------------------------------------------------
+// Stride phases of the input gradient
+// ---------------------------------------------------------------------------
+
+bool phases_apply(const ConvGeom &g) {
+    if (!conv_fits(g) || g.stride != 2 || g.n <= 0) return false;
+    // a phase's tile of at most 256 rows spans at most 256 / (hn wn) + 2
+    // output images (as the whole convolution's does)
+    const long long img_y = (long long)g.p * g.q * g.kp;
+    for (int ph = 0; ph < 2; ++ph)
+        for (int pw = 0; pw < 2; ++pw) {
+            const long long hn = (g.h - ph + 1) / 2, wn = (g.w - pw + 1) / 2;
+            if (hn * wn > 0 && (256 / (hn * wn) + 2) * img_y > WINDOW) return false;
+        }
+    return true;
+}
+
+Phases make_phases(const ConvGeom &g, int bm) {
+    Phases ps;
+    memset(&ps, 0, sizeof ps);
+    if (!phases_apply(g) || bm <= 0) return ps;
+    const int st = g.stride;
+    ps.n = st * st;
+    ps.st = st;
+    ps.h = g.h;
+    ps.w = g.w;
+    int tap = 0, tiles = 0;  // tiles: the most tile rows of one phase
+    for (int t = 0; t < ps.n; ++t) {
+        PhaseRec &p = ps.r[t];
+        p.ph = t / st;
+        p.pw = t % st;
+        p.hn = g.h > p.ph ? (g.h - p.ph + st - 1) / st : 0;
+        p.wn = g.w > p.pw ? (g.w - p.pw + st - 1) / st : 0;
+        const int r0 = (p.ph + g.pad) % st, s0 = (p.pw + g.pad) % st;
+        p.ra = g.r > r0 ? (g.r - r0 + st - 1) / st : 0;
+        p.sb = g.s > s0 ? (g.s - s0 + st - 1) / st : 0;
+        p.ch = (p.ph + g.pad - r0) / st;
+        p.cw = (p.pw + g.pad - s0) / st;
+        const int sb = p.sb > 0 ? p.sb : 1;
+        p.ds = (BK / g.kp) % sb;
+        p.dr = (BK / g.kp) / sb;
+        p.tap0 = tap;
+        p.k0 = tap * g.kp;
+        p.klen = p.ra * p.sb * g.kp;
+        tap += p.ra * p.sb;
+        p.rows = g.n * p.hn * p.wn;
+        if (cdiv(p.rows, bm) > tiles) tiles = cdiv(p.rows, bm);
+        p.dhw = make_fastdiv(p.hn * p.wn > 0 ? (uint32_t)(p.hn * p.wn) : 1u);
+        p.dw = make_fastdiv(p.wn > 0 ? (uint32_t)p.wn : 1u);
+        p.dsb = make_fastdiv((uint32_t)sb);
+        if (p.klen > ps.kmax) ps.kmax = p.klen;
+    }
+    ps.tm = ps.n * tiles;
+    return ps;
+}
+
+int phase_tap(const Phases &ps, const ConvGeom &g, int r, int s) {
+    const int st = ps.st;
+    const int ph = ((r - g.pad) % st + st) % st, pw = ((s - g.pad) % st + st) % st;
+    const PhaseRec &p = ps.r[ph * st + pw];
+    return p.tap0 + (r / st) * p.sb + s / st;
+}
+
+// ---------------------------------------------------------------------------
 // Built tiles
 // ---------------------------------------------------------------------------
 
@@ -261,6 +324,22 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
         }
     }
     return best;
+}
+
+DgradPlan plan_dgrad(const ConvGeom &g, int row_group, const Force &f, bool weight_in_place) {
+    DgradPlan d;
+    memset(&d, 0, sizeof d);
+    d.M = (long long)g.n * g.h * g.w;
+    d.K = (long long)g.r * g.s * g.kp;
+    d.pl = plan_product(d.M, g.c, d.K, row_group, FAM_DGRAD, f);
+    const bool want = f.on ? f.mode == PLAN_RECOMP : d.pl.mode != PLAN_DIRECT && !weight_in_place;
+    if (row_group || !want || d.M == 0 || !phases_apply(g)) return d;
+    d.ps = make_phases(g, d.pl.t.bm());
+    if (d.ps.n == 0) return d;
+    d.M = (long long)d.ps.tm * d.pl.t.bm();
+    d.K = d.ps.kmax;
+    d.pl = Plan{d.pl.t, PLAN_RECOMP, 1, chunk_for(d.K, 1)};
+    return d;
 }
 
 Plan plan_wgrad(long long M, long long N, long long L, int family, const Force &f) {
@@ -389,9 +468,10 @@ bool covers(const Needs &have, const Needs &need) {
            need.partial <= have.partial && need.sums <= have.sums && need.tneed <= have.tneed;
 }
 
-ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f) {
+ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f,
+                        size_t tneed_min) {
     ProductWs w{};
-    Needs n{0, 0, 0, 0, 0, 0};
+    Needs n{0, 0, 0, 0, 0, tneed_min};
     for (int rg = 0; rg < 2; ++rg) {
         const Needs r = product_needs(plan_product(M, N, K, rg, family, f), M, N, K, rg);
         n.gneed = mx(n.gneed, r.gneed);
@@ -473,7 +553,9 @@ ConvBwdWs carve_conv_bwd(Carve &c, const ConvGeom &g, const Force &f, const Forc
     w.wt = c.take<int8_t>((size_t)g.c * g.r * g.s * g.kp);
     if (g.kp != g.k) w.dyp = c.take<int8_t>((size_t)npq * g.kp);
     if (g.cp != g.c) w.xp = c.take<int8_t>((size_t)nhw * g.cp);
-    w.pw = carve_product(c, nhw, g.c, (long long)g.r * g.s * g.kp, FAM_DGRAD, f);
+    const DgradPlan dp = plan_dgrad(g, 0, f);
+    const size_t tn = dp.ps.n ? product_needs(dp.pl, dp.M, g.c, dp.K, 0).tneed : 0;
+    w.pw = carve_product(c, nhw, g.c, (long long)g.r * g.s * g.kp, FAM_DGRAD, f, tn);
     w.w = carve_wgrad(c, g.k, (long long)g.r * g.s * g.cp, npq, FAM_WGRAD_CONV, fw);
     return w;
 }

@@ -68,6 +68,40 @@ struct Tile {
     int bn() const { return 64 * ni; }
 };
 
+// Stride phases of a strided convolution's input gradient.  The input pixels
+// h = ph + st i, w = pw + st j (phase (ph, pw)) are reached only by the
+// filter taps r = r0 + st a, s = s0 + st b with r0 = (ph + pad) % st,
+// s0 = (pw + pad) % st, at output pixel p = i + ch - a, q = j + cw - b
+// (ch = (ph + pad - r0) / st, cw likewise): each phase is a stride-1
+// product over its own pixels and taps, and no tap that misses an output
+// pixel reaches the matrix cores.  The weight copy the phases read holds the
+// taps sorted by phase: phase t's taps (a, b), a < ra, b < sb, are the
+// contraction columns k0 + (a sb + b) kp + ko, k0 = tap0 kp.
+constexpr int PHASES_MAX = 4;  // stride 2
+struct PhaseRec {
+    int ph, pw;        // the phase's first input pixel
+    int hn, wn;        // its pixels per image along h and w
+    int ra, sb;        // its taps along r and s
+    int ch, cw;        // output pixel of its tap (0, 0) relative to pixel (i, j)
+    int ds, dr;        // advance of (a, b) per contraction step (b by ds, a by dr)
+    int tap0;          // its first tap in the sorted weight copy
+    int k0, klen;      // its contraction columns in that copy
+    int rows;          // its GEMM rows (n hn wn)
+    FastDiv dhw, dw, dsb;  // divide by hn wn, wn, sb
+};
+// Tile row t of the product is tile row t / 4 of phase (t + h(t / 4)) % 4,
+// h(x) = (x * 2654435761 mod 2^32) / 2^30: the phases interleaved, rotated
+// per group of four, so that every XCD's contiguous run of tiles and every
+// persistent workgroup's strided walk mixes them; tile rows past a phase's
+// own count are empty.
+struct Phases {
+    int n;             // phases (0: the product is not decomposed)
+    int st, h, w;      // stride and input image size
+    int tm;            // tile rows over all phases: n times the most of one phase
+    int kmax;          // longest contraction of a phase
+    PhaseRec r[PHASES_MAX];
+};
+
 // ---------------------------------------------------------------------------
 // Argument checks
 // ---------------------------------------------------------------------------
@@ -81,6 +115,12 @@ ConvGeom geom(const ie_conv_desc *d);
 bool conv_fits(const ConvGeom &g);
 // The in-place weight read of the input gradient spans the whole weight.
 bool weight_window_fits(const ConvGeom &g);
+// Whether the input gradient of g is decomposed into stride phases (stride
+// 2 only), and the phases for workgroup tiles of bm rows.
+bool phases_apply(const ConvGeom &g);
+Phases make_phases(const ConvGeom &g, int bm);
+// Position of tap (r, s) in the phase-sorted weight copy.
+int phase_tap(const Phases &ps, const ConvGeom &g, int r, int s);
 
 // ---------------------------------------------------------------------------
 // Kernel families and the tiles instantiated for each (one list, used by the
@@ -150,6 +190,22 @@ Force force_from_env(const char *var, bool wgrad);
 // Product A(m, k) B(n, k) over K into an int8 output with one exponent per
 // row (row_group) or one for the whole tensor.
 Plan plan_product(long long M, long long N, long long K, int row_group, int family, const Force &f);
+// Input gradient of a convolution: the product's plan and, for stride 2
+// with one exponent for the whole result, its stride phases (then always
+// the recomputed epilogue, whose second pass stores each phase pixel at its
+// input pixel).  M and K are the row count and contraction the launches
+// take: with phases, tile rows over all phases times the tile height, and
+// the longest phase contraction.  The phases read a weight copy with the
+// taps sorted by phase; when the weight could be read in place instead
+// (weight_in_place), the planner keeps the undecomposed product, whose
+// saved copy outweighs the masked taps at the shapes measured, unless a
+// recomputed plan is forced.
+struct DgradPlan {
+    Plan pl;
+    Phases ps;
+    long long M, K;
+};
+DgradPlan plan_dgrad(const ConvGeom &g, int row_group, const Force &f, bool weight_in_place = false);
 // Weight gradients: always split over the contraction, chunks of at most
 // 65536 rows.
 Plan plan_wgrad(long long M, long long N, long long L, int family, const Force &f);
@@ -206,7 +262,10 @@ struct ProductWs {
     int *tneed;
     Needs n;  // element counts reserved
 };
-ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f);
+// tneed_min: entries the first pass of another plan of the same call needs
+// (a stride-phased input gradient).
+ProductWs carve_product(Carve &c, long long M, long long N, long long K, int family, const Force &f,
+                        size_t tneed_min = 0);
 
 struct WgradWs {
     int *partial;

@@ -343,8 +343,9 @@ static void conv_layouts(const ie_conv_desc &d) {
         touch(w.wt, (size_t)g.c * g.r * g.s * g.kp - 1);
         if (w.dyp) touch(w.dyp, (size_t)npq * g.kp - 1);
         if (w.xp) touch(w.xp, (size_t)nhw * g.cp - 1);
-        const long long rskp = (long long)g.r * g.s * g.kp, rscp = (long long)g.r * g.s * g.cp;
-        product_writes(plan_product(nhw, g.c, rskp, 0, FAM_DGRAD, off), nhw, g.c, rskp, 0, w.pw);
+        const long long rscp = (long long)g.r * g.s * g.cp;
+        const DgradPlan dp = plan_dgrad(g, 0, off);
+        product_writes(dp.pl, dp.M, g.c, dp.K, 0, w.pw);
         const Plan pw = plan_wgrad(g.k, rscp, npq, FAM_WGRAD_CONV, off);
         wgrad_writes(pw, g.k, rscp, (long long)g.r * g.s * g.c, g.c, g.cp, 1, npq, w.w);
     }
@@ -398,6 +399,136 @@ static void check_layouts() {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stride phases of the input gradient
+// ---------------------------------------------------------------------------
+
+// The phases of g: their pixels cover every input pixel once (through the
+// store formula of the second pass), their taps cover every filter tap once
+// (through the weight copy's tap order), each phase's taps and output pixels
+// are exactly those the definition p st = h + pad - r pairs with its
+// pixels, and the first pass's maxima fit the carve.
+static void check_phase_case(const ie_conv_desc &d, int bm, const Force &f) {
+    if (check_conv(&d) != IE_OK) return;
+    const ConvGeom g = geom(&d);
+    if (!phases_apply(g)) return;
+    const Phases ps = make_phases(g, bm);
+    REQUIRE(ps.n == 4 && ps.st == 2, "stride-2 phases: n %d", ps.n);
+    const long long nhw = (long long)g.n * g.h * g.w;
+    // pixels: every phase row stored once, inside dX
+    std::vector<unsigned char> *hits = new std::vector<unsigned char>((size_t)nhw, 0);
+    unsigned char *dx = (unsigned char *)malloc((size_t)nhw);
+    long long rows = 0;
+    int tiles = 0, taps = 0;
+    for (int t = 0; t < ps.n; ++t) {
+        const PhaseRec &p = ps.r[t];
+        REQUIRE(ps.tm % ps.n == 0 && cdiv(p.rows, bm) <= ps.tm / ps.n, "phase %d tile rows beyond its share", t);
+        tiles = cdiv(p.rows, bm) > tiles ? cdiv(p.rows, bm) : tiles;
+        REQUIRE(p.rows == (long long)g.n * p.hn * p.wn, "phase rows");
+        REQUIRE(p.k0 == taps * g.kp && p.tap0 == taps && p.klen == p.ra * p.sb * g.kp, "phase columns");
+        taps += p.ra * p.sb;
+        REQUIRE(p.klen <= ps.kmax, "kmax below a phase");
+        for (long long m = 0; m < p.rows; ++m) {
+            // the kernel's formula (fast divisions) and the plain one
+            const uint32_t hw = (uint32_t)(p.hn * p.wn);
+            const uint32_t n = (uint32_t)(((uint64_t)m * p.dhw.m) >> p.dhw.s), rem = (uint32_t)m - n * hw;
+            const uint32_t i = (uint32_t)(((uint64_t)rem * p.dw.m) >> p.dw.s), j = rem - i * (uint32_t)p.wn;
+            REQUIRE(n == m / hw && i == (m % hw) / p.wn && j == (m % hw) % p.wn, "fast division of a phase row");
+            const long long h = p.ph + 2ll * i, w = p.pw + 2ll * j;
+            REQUIRE(h < g.h && w < g.w, "phase pixel outside the image");
+            const long long phys = ((long long)n * ps.h + h) * ps.w + w;
+            dx[phys] = 1;  // out of bounds aborts under the sanitizer
+            (*hits)[(size_t)phys]++;
+            // taps: the phase's (a, b) reach exactly the output pixels of the definition
+            if (m < 64 || m + 64 > p.rows) {
+                for (int r = 0; r < g.r; ++r)
+                    for (int s_ = 0; s_ < g.s; ++s_) {
+                        const long long ah = h + g.pad - r, aw = w + g.pad - s_;
+                        const bool def = ah >= 0 && aw >= 0 && ah % 2 == 0 && aw % 2 == 0 && ah / 2 < g.p &&
+                                         aw / 2 < g.q;
+                        const bool mine = r % 2 == (p.ph + g.pad) % 2 && s_ % 2 == (p.pw + g.pad) % 2;
+                        bool hit = false;
+                        if (mine) {
+                            const int a = r / 2, b = s_ / 2;
+                            REQUIRE(a < p.ra && b < p.sb, "tap of the phase outside its block");
+                            const long long pp = (long long)i + p.ch - a, qq = (long long)j + p.cw - b;
+                            hit = pp >= 0 && pp < g.p && qq >= 0 && qq < g.q;
+                            if (hit) REQUIRE(pp * 2 == ah && qq * 2 == aw, "phase tap at the wrong output pixel");
+                            REQUIRE(phase_tap(ps, g, r, s_) == p.tap0 + a * p.sb + b, "tap order");
+                        }
+                        REQUIRE(def == hit, "phase taps differ from the definition at (%lld, %lld) tap (%d, %d)",
+                                h, w, r, s_);
+                    }
+            }
+        }
+        rows += p.rows;
+    }
+    REQUIRE(rows == nhw && tiles * ps.n == ps.tm, "phase rows %lld of %lld", rows, nhw);
+    // the kernel's tile order (tile row t: phase (t + h(t / 4)) % 4, rows
+    // from (t / 4) bm) reaches every phase row exactly once
+    std::vector<unsigned char> seen_rows((size_t)nhw, 0);
+    for (int t = 0; t < ps.tm; ++t) {
+        const int ph = (t + (int)(((uint32_t)(t >> 2) * 2654435761u) >> 30)) & 3;
+        const PhaseRec &p = ps.r[ph];
+        for (long long m = (long long)(t / ps.n) * bm; m < (long long)(t / ps.n + 1) * bm && m < p.rows; ++m) {
+            const long long hw = (long long)p.hn * p.wn, nn = m / hw, i = (m % hw) / p.wn, j = (m % hw) % p.wn;
+            seen_rows[(size_t)(((nn * ps.h) + p.ph + 2 * i) * ps.w + p.pw + 2 * j)]++;
+        }
+    }
+    for (long long x = 0; x < nhw; ++x) REQUIRE(seen_rows[(size_t)x] == 1, "tile order stores pixel %lld %d times",
+                                                 x, (int)seen_rows[(size_t)x]);
+    REQUIRE(taps == g.r * g.s, "phase taps %d of %d", taps, g.r * g.s);
+    for (long long x = 0; x < nhw; ++x) REQUIRE((*hits)[(size_t)x] == 1, "input pixel %lld stored %d times", x,
+                                                 (int)(*hits)[(size_t)x]);
+    std::vector<int> seen((size_t)(g.r * g.s), 0);
+    for (int r = 0; r < g.r; ++r)
+        for (int s_ = 0; s_ < g.s; ++s_) seen[(size_t)phase_tap(ps, g, r, s_)]++;
+    for (int v : seen) REQUIRE(v == 1, "tap order not a permutation");
+    free(dx);
+    delete hits;
+    // the plan and its workspace
+    const DgradPlan dp = plan_dgrad(g, 0, f);
+    const bool valid = plan_valid(dp.pl, dp.M, g.c, dp.K, 0, FAM_DGRAD);
+    if (!f.on) REQUIRE(valid, "phased plan invalid");
+    if (dp.ps.n && valid) {
+        REQUIRE(dp.pl.mode == PLAN_RECOMP && dp.M == (long long)dp.ps.tm * dp.pl.t.bm() && dp.K == dp.ps.kmax,
+                "phased plan");
+        Arena a(conv_bwd_ws(g, f, Force{0, 0, 0, 0, 1}));
+        Carve c{a.base, HEADER};
+        const ConvBwdWs w = carve_conv_bwd(c, g, f, Force{0, 0, 0, 0, 1});
+        open_product(a, w.pw);
+        REQUIRE(covers(w.pw.n, product_needs(dp.pl, dp.M, g.c, dp.K, 0)), "carve short of the phased plan");
+        product_writes(dp.pl, dp.M, g.c, dp.K, 0, w.pw);
+        ++g_runs;
+    }
+    REQUIRE(plan_dgrad(g, 1, f).ps.n == 0, "row-grouped input gradient in phases");
+}
+
+static void check_phases() {
+    const ie_conv_desc ds[] = {
+        {2, 9, 9, 24, 40, 3, 3, 2, 1},  {2, 9, 9, 48, 24, 3, 3, 2, 1},  {2, 10, 10, 32, 40, 3, 3, 2, 1},
+        {3, 7, 5, 16, 8, 1, 1, 2, 0},   {2, 8, 8, 16, 16, 1, 1, 2, 1},  {1, 1, 1, 16, 16, 1, 1, 2, 0},
+        {2, 2, 3, 16, 16, 3, 3, 2, 1},  {2, 11, 6, 20, 30, 5, 5, 2, 2}, {2, 6, 11, 16, 16, 2, 2, 2, 0},
+        {2, 12, 12, 16, 48, 4, 4, 2, 1}, {1, 3, 3, 16, 16, 3, 1, 2, 0}, {4, 5, 5, 16, 300, 3, 3, 2, 1},
+        {128, 32, 32, 64, 128, 3, 3, 2, 1}, {128, 56, 56, 128, 128, 3, 3, 2, 1},
+        {128, 56, 56, 256, 512, 1, 1, 2, 0}, {128, 14, 14, 512, 512, 3, 3, 2, 1},
+    };
+    const Force off{0, 0, 0, 0, 1};
+    for (const auto &d : ds)
+        for (int bm : {64, 128, 256}) {
+            check_phase_case(d, bm, off);
+            check_phase_case(d, bm, Force{1, bm / 64, 1, PLAN_RECOMP, 1});
+            check_phase_case(d, bm, Force{1, bm / 64, 2, PLAN_RECOMP, 1});
+        }
+    // other strides and forced non-recomputed plans are not decomposed
+    const ie_conv_desc d1{2, 9, 9, 16, 16, 3, 3, 1, 1}, d3{2, 9, 9, 16, 16, 3, 3, 3, 1};
+    REQUIRE(plan_dgrad(geom(&d1), 0, off).ps.n == 0, "stride 1 in phases");
+    REQUIRE(plan_dgrad(geom(&d3), 0, off).ps.n == 0, "stride 3 in phases");
+    const ie_conv_desc d2{2, 9, 9, 16, 16, 3, 3, 2, 1};
+    REQUIRE(plan_dgrad(geom(&d2), 0, Force{1, 2, 1, PLAN_RTO, 1}).ps.n == 0, "forced round-to-odd in phases");
+    REQUIRE(plan_dgrad(geom(&d2), 0, Force{1, 2, 1, PLAN_RECOMP, 1}).ps.n == 4, "forced recompute not in phases");
+}
+
 // Argument checks and geometry at the ends of their ranges (UB-free under
 // the sanitizer; shapes the kernels cannot take are refused).
 static void check_extremes() {
@@ -431,6 +562,7 @@ int main() {
     check_wgrads();
     check_bmm();
     check_layouts();
+    check_phases();
     printf("plan_check: %lld checks, %lld plans written into their carved workspaces\n", g_checks, g_runs);
     return 0;
 }

@@ -156,6 +156,67 @@ def test_conv_plans(shape, tile, mode, wg, ws, plan):
     assert ws.status() == 0
 
 
+# Stride-2 input gradients, decomposed into stride phases: kernels 1x1 (three
+# phases without taps), 2x2, 3x3, 4x4 and 5x5, odd, unequal and one-pixel
+# images, more output channels than one contraction step; with the
+# planner's tile and every tile forced with the recomputed epilogue, alone
+# and paired with the weight gradient.
+PHASE_CASES = [(2, 9, 9, 16, 24, 1, 1, 2, 0), (3, 7, 5, 32, 40, 1, 1, 2, 0), (2, 8, 8, 16, 16, 1, 1, 2, 1),
+               (1, 1, 1, 16, 16, 1, 1, 2, 0), (2, 2, 3, 16, 16, 3, 3, 2, 1), (2, 11, 6, 20, 30, 5, 5, 2, 2),
+               (2, 6, 11, 16, 16, 2, 2, 2, 0), (2, 12, 12, 16, 48, 4, 4, 2, 1), (4, 5, 5, 16, 300, 3, 3, 2, 1),
+               (2, 20, 20, 64, 64, 3, 3, 2, 1)]
+
+
+@pytest.mark.parametrize("shape", PHASE_CASES, ids=lambda s: "n{}h{}w{}c{}k{}r{}s{}p{}".format(*s[:7], s[8]))
+@pytest.mark.parametrize("tile", [None] + CONV_TILES, ids=lambda t: "planner" if t is None else f"{64 * t[0]}x{64 * t[1]}")
+def test_conv_phases(shape, tile, ws, plan):
+    n, h, w, c, k, r, s, st, pad = shape
+    announce(f"conv phases shape={shape} tile={tile}")
+    d, dd = o.ConvShape(*shape), ie.conv_desc(*shape)
+    rng = np.random.default_rng(sum(shape) * 7 + (tile or (0, 0))[0])
+    X = rand_qt(rng, (n, h, w, c), T, zero_frac=0.2)
+    W = rand_qt(rng, (k, r * s * c), R if k % 2 == 0 else T)
+    dY = rand_qt(rng, (n, d.p, d.q, k), T)
+    Xd, Wd, dYd = qt_to_dev(X, rows=n * h * w), qt_to_dev(W), qt_to_dev(dY, rows=n * d.p * d.q)
+    if tile is not None:
+        plan(tile, 3, 1)
+    want_dx = o.conv_dgrad(d, dY, W, T)
+    dX = ie.Mat.empty(n * h * w, c, T)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, None, ws)
+    assert_same(dX, want_dx, "conv dgrad")
+    dX2 = ie.Mat.empty(n * h * w, c, T)
+    dW = ie.Mat.empty(k, r * s * c, R)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX2, dW, ws)
+    assert_same(dX2, want_dx, "conv dgrad (paired)")
+    assert_same(dW, o.conv_wgrad(d, dY, X, R), "conv wgrad (paired)")
+    assert ws.status() == 0
+
+
+@pytest.mark.parametrize("shape", [(2, 9, 9, 24, 40, 3, 3, 2, 1), (2, 10, 10, 32, 40, 3, 3, 1, 1)],
+                         ids=["st2", "st1"])
+def test_conv_dgrad_row_groups(shape, ws):
+    # one exponent per input pixel: never decomposed, never paired (its
+    # epilogue keeps a row per pixel); alone and with the weight gradient
+    n, h, w, c, k, r, s, st, pad = shape
+    announce(f"conv dgrad row groups shape={shape}")
+    d, dd = o.ConvShape(*shape), ie.conv_desc(*shape)
+    rng = np.random.default_rng(sum(shape) + 99)
+    X = rand_qt(rng, (n, h, w, c), T)
+    W = rand_qt(rng, (k, r * s * c), R)
+    dY = rand_qt(rng, (n, d.p, d.q, k), T)
+    Xd, Wd, dYd = qt_to_dev(X, rows=n * h * w), qt_to_dev(W), qt_to_dev(dY, rows=n * d.p * d.q)
+    want = o.conv_dgrad(d, dY, W, R)
+    dX = ie.Mat.empty(n * h * w, c, R)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX, None, ws)
+    assert_same(dX, want, "row-grouped dgrad")
+    dX2 = ie.Mat.empty(n * h * w, c, R)
+    dW = ie.Mat.empty(k, r * s * c, R)
+    ie.ie_conv_bwd(dd, Xd, Wd, dYd, dX2, dW, ws)
+    assert_same(dX2, want, "row-grouped dgrad with dW")
+    assert_same(dW, o.conv_wgrad(d, dY, X, R), "wgrad with row-grouped dgrad")
+    assert ws.status() == 0
+
+
 @pytest.mark.parametrize("tile", WGRAD_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
 @pytest.mark.parametrize("splits", [1, 3, 7])
 def test_wgrad_plans(tile, splits, ws, plan):
