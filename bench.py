@@ -110,7 +110,7 @@ def kind_symbol(kind: int) -> str:
         return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi >= 6 else 'false'}>"
     if epi == 8:
         return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, false>"
-    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}>"
+    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}, false>"
 
 
 # ---------------------------------------------------------------------------

@@ -50,8 +50,8 @@ def source_digest() -> str:
 
 
 def short_name(name: str) -> str:
-    """'void ie::gemm_i8_kernel<1, 4, 1, 1, true>(ie::Operand, ...)' ->
-    'gemm_i8_kernel<1, 4, 1, 1, true>'."""
+    """'void ie::gemm_i8_kernel<1, 4, 1, 1, true, false>(ie::Operand, ...)' ->
+    'gemm_i8_kernel<1, 4, 1, 1, true, false>'."""
     n = re.sub(r"\(.*$", "", name).replace("void ", "").strip()
     return n.replace("ie::", "")
 

@@ -121,10 +121,12 @@ def test_fused_relu_plans(tile, mode, ws, plan):
 # 24 channels: the input gradient reads a transposed, aligned copy of W;
 # 32 / 48 channels with a whole-tensor W: it reads W in place
 CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1),
-              (2, 10, 10, 32, 40, 3, 3, 1, 1), (2, 9, 9, 48, 24, 3, 3, 2, 1)]
+              (2, 10, 10, 32, 40, 3, 3, 1, 1), (2, 9, 9, 48, 24, 3, 3, 2, 1),
+              # 1x1, stride 1, no padding: the dense product kernels
+              (2, 10, 10, 24, 40, 1, 1, 1, 0), (3, 9, 9, 32, 48, 1, 1, 1, 0)]
 
 
-@pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"c{s[3]}st{s[7]}")
+@pytest.mark.parametrize("shape", CONV_CASES, ids=lambda s: f"c{s[3]}r{s[5]}st{s[7]}")
 @pytest.mark.parametrize("tile", CONV_TILES, ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
 @pytest.mark.parametrize("mode", [(1, 1), (2, 2), (3, 1)], ids=lambda m: f"m{m[0]}s{m[1]}")
 @pytest.mark.parametrize("wg", [T, R], ids=["WT", "WR"])
