@@ -349,12 +349,22 @@ Plan plan_wgrad(long long M, long long N, long long L, int family, const Force &
         p.mode = PLAN_SPLIT;
         return p;
     }
-    const long long t22 = (long long)cdiv(M, 128) * cdiv(N, 128);
-    const Tile t = t22 >= 32 ? Tile{2, 2} : Tile{1, 1};
+    // The 128 x 128 tile whenever both sides fill it (16 matrix instructions
+    // per wave and step, against 4 for the contraction-sliced 64 x 64 one),
+    // and about one workgroup per CU in all (two per CU for more than four
+    // 64 x 64 tiles): measured over ResNet-50's weight gradients, longer
+    // contraction chunks beat a fuller grid, as the split partials (written,
+    // then summed by the finalize) shrink with the split count.
+    const bool big = M >= 128 && N >= 128;
+    const Tile t = big ? Tile{2, 2} : Tile{1, 1};
     const long long nt = (long long)cdiv(M, t.bm()) * cdiv(N, t.bn());
+    const long long target = big || nt <= 4 ? NCU : 2 * NCU;
     const int smin = (int)((L + SPLIT_MAX_ROWS - 1) / SPLIT_MAX_ROWS);
-    int sp = 1;
-    while (sp < 1024 && nt * sp * 2 < WG_TARGET && L / (sp * 2) >= 8 * BK) sp *= 2;
+    long long want = (target + nt / 2) / nt;  // nearest split count to the target
+    const long long smax = L / (8 * BK);      // chunks of at least eight steps
+    if (want > smax) want = smax;
+    if (want > 1024) want = 1024;
+    int sp = want > 1 ? (int)want : 1;
     if (sp < smin) sp = smin;
     const int kc = chunk_for(L, sp);
     const int n = (int)((L + kc - 1) / kc);
