@@ -309,8 +309,11 @@ __device__ __forceinline__ uint32_t umax_wave(uint32_t v) { return wave_umax_dpp
 // by the pass before (tmp[0]: old velocity exponent, tmp[1]: old weight
 // exponent).  All passes run on the same grid of nblk blocks (this block is
 // blk of them).
-template <int D, int WPR, bool WD = false>
-__device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int vec, int blk, int nblk) {
+// RR: velocity and weight both grouped by rows, so that the second pass is
+// the only one (the kernel is then built for it alone).
+template <int D, int WPR, bool WD = false, bool RR = false>
+__device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass_, int vec, int blk, int nblk) {
+    const int pass = RR ? 1 : pass_;
     constexpr int RPB = 4 / WPR;  // rows per block
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -344,7 +347,7 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
         return v;
     };
     auto row_imax = [&](int v) -> int { return (int)(row_umax((uint32_t)(v ^ (int)0x80000000)) ^ 0x80000000u); };
-    const bool v_tensor = a.v_row == 0, w_tensor = a.w_row == 0;
+    const bool v_tensor = !RR && a.v_row == 0, w_tensor = !RR && a.w_row == 0;
     // whole-tensor exponents of this pass (before any write of this pass)
     int ev_t = 0, ew_t = 0, evn_t = 0, ewn_t = 0;
     if (pass == 0) {
@@ -571,9 +574,9 @@ __device__ __forceinline__ void update_rows(const UpdateArgs &a, int pass, int v
     }
 }
 
-template <int D, int WPR, bool WD>
+template <int D, int WPR, bool WD, bool RR = false>
 __global__ __launch_bounds__(256) void sgd_rows_kernel(UpdateArgs a, int pass, int vec) {
-    update_rows<D, WPR, WD>(a, pass, vec, blockIdx.x, gridDim.x);
+    update_rows<D, WPR, WD, RR>(a, pass, vec, blockIdx.x, gridDim.x);
 }
 
 // Several tensors of one (D, WPR) class in one launch: segment i owns blocks
@@ -592,10 +595,11 @@ __device__ __forceinline__ int segment_of(const int *block0, int n) {
     return __builtin_amdgcn_readfirstlane(i);  // block-uniform: keep the segment's arguments scalar
 }
 
-template <int D, int WPR>
+template <int D, int WPR, bool RR = false>
 __global__ __launch_bounds__(256) void sgd_multi_kernel(UpdSegs sg, int pass) {
     const int i = segment_of(sg.block0, sg.n);
-    update_rows<D, WPR>(sg.a[i], pass, sg.vec[i], blockIdx.x - sg.block0[i], sg.block0[i + 1] - sg.block0[i]);
+    update_rows<D, WPR, false, RR>(sg.a[i], pass, sg.vec[i], blockIdx.x - sg.block0[i],
+                                   sg.block0[i + 1] - sg.block0[i]);
 }
 
 // Tensors of the narrow classes (at most 4 dwords of each tensor per lane)
@@ -643,6 +647,13 @@ template <int D, int WPR, bool WD = false>
 static hipError_t run_passes(const UpdateArgs &a, int vec, hipStream_t st) {
     const int blocks = update_blocks(a, WPR);
     hipError_t err;
+    if (a.v_row && a.w_row) {
+        // row groups on both: the one pass, in its own build
+        prof_begin(st, 2001);
+        hipLaunchKernelGGL((sgd_rows_kernel<D, WPR, WD, true>), dim3((int)blocks), dim3(256), 0, st, a, 1, vec);
+        prof_end(st, 2001);
+        return hipGetLastError();
+    }
     for (int pass = 0; pass < 3; ++pass) {
         if (pass == 0 && a.v_row) continue;
         if (pass == 2 && a.w_row) continue;
@@ -670,8 +681,13 @@ static hipError_t run_multi(const UpdateArgs *a, const int *vec, int n, hipStrea
         }
         if (sg.n == 0) continue;
         sg.block0[sg.n] = blocks;
+        bool rr = pass == 1;
+        for (int i = 0; i < sg.n; ++i) rr = rr && sg.a[i].v_row && sg.a[i].w_row;
         prof_begin(st, 2000 + pass);
-        hipLaunchKernelGGL((sgd_multi_kernel<D, WPR>), dim3(blocks), dim3(256), 0, st, sg, pass);
+        if (rr)  // row groups on both for every tensor: the one pass's own build
+            hipLaunchKernelGGL((sgd_multi_kernel<D, WPR, true>), dim3(blocks), dim3(256), 0, st, sg, pass);
+        else
+            hipLaunchKernelGGL((sgd_multi_kernel<D, WPR>), dim3(blocks), dim3(256), 0, st, sg, pass);
         prof_end(st, 2000 + pass);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
