@@ -313,7 +313,15 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
     if (N > 64 && tiles(Tile{2, 2}) >= 4ll * NCU) t = Tile{2, 2};
     else if (tiles(Tile{2, 1}) >= 2ll * NCU) t = Tile{2, 1};
     const bool direct = row_group ? N <= t.bn() : tiles(t) == 1;
-    Plan best{t, direct ? PLAN_DIRECT : K <= RECOMP_KMAX ? PLAN_RECOMP : PLAN_RTO, 1, chunk_for(K, 1)};
+    // Recompute (two passes over the operands) or round to odd (one pass, an
+    // int16 round trip of the output): row groups recompute contractions up
+    // to RECOMP_KMAX; a whole-tensor result recomputes one-step contractions,
+    // and two-step ones whose output is at least twice as wide as the
+    // contraction (measured over ResNet-50's forward and input-gradient
+    // products: elsewhere the second pass's matrix work outweighs the int16
+    // round trip).
+    const bool recomp = row_group ? K <= RECOMP_KMAX : K <= BK || (K <= 2 * BK && N >= 2 * K);
+    Plan best{t, direct ? PLAN_DIRECT : recomp ? PLAN_RECOMP : PLAN_RTO, 1, chunk_for(K, 1)};
     if (!direct && tiles(Tile{1, 1}) < NCU / 2 && K >= 8 * BK) {
         const long long n11 = tiles(Tile{1, 1});
         int sp = 1;

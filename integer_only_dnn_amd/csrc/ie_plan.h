@@ -162,8 +162,9 @@ bool pair_tiles_built(Tile t1, Tile t2);
 //         reads the operands again but saves 4 bytes per output element).
 enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2, PLAN_RECOMP = 3 };
 
-// Contractions of at most this many bytes recompute instead of two-pass
-// rounding (RECOMP instead of RTO).
+// Row-grouped results with contractions of at most this many bytes
+// recompute instead of two-pass rounding (RECOMP instead of RTO);
+// whole-tensor results choose by contraction and width (plan_product).
 constexpr long long RECOMP_KMAX = 512;
 // Workgroups of the first pass of a recomputed whole-tensor product (a
 // persistent grid; each writes one maximum).
