@@ -309,9 +309,15 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
     (void)family;  // every product family has the same tiles for these choices
     if (f.on) return forced(f, K);
     auto tiles = [&](Tile t) { return (long long)cdiv(M, t.bm()) * cdiv(N, t.bn()); };
+    // The 128 x 128 tile for outputs wider than 64 with at least 3/4 of a
+    // tile per CU (its matrix work per LDS byte and per barrier is twice the
+    // 128 x 64 tile's), else 128 x 64 with 1.5 tiles per CU, else 64 x 64: a
+    // sweep of every built tile over the ResNet-50 and ResNet-18 forward and
+    // input-gradient products (the smallest ResNet-18 layers, 2048 rows,
+    // want the 64 x 64 tile's 512 workgroups).
     Tile t{1, 1};
-    if (N > 64 && tiles(Tile{2, 2}) >= 4ll * NCU) t = Tile{2, 2};
-    else if (tiles(Tile{2, 1}) >= 2ll * NCU) t = Tile{2, 1};
+    if (N > 64 && tiles(Tile{2, 2}) >= 3ll * NCU / 4) t = Tile{2, 2};
+    else if (tiles(Tile{2, 1}) >= 3ll * NCU / 2) t = Tile{2, 1};
     const bool direct = row_group ? N <= t.bn() : tiles(t) == 1;
     // Recompute (two passes over the operands) or round to odd (one pass, an
     // int16 round trip of the output): row groups recompute contractions up
