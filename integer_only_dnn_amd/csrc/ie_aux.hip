@@ -861,14 +861,25 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
                 acc[4 * tid + 3] = a3;
             }
             __syncthreads();
-            if (tid < nch) {
-                for (int qq = 1; qq < Q; ++qq) {
-                    const int t = tid + qq * nch;
-                    a0 += acc[4 * t + 0];
-                    a1 += acc[4 * t + 1];
-                    a2 += acc[4 * t + 2];
-                    a3 += acc[4 * t + 3];
+            // the Q partial sums of each chunk, summed as a tree: subset q takes
+            // subset q + h's while q + h < qn (log2 Q steps, all threads busy)
+            for (int qn = Q; qn > 1;) {
+                const int h = (qn + 1) >> 1;
+                if (q + h < qn) {
+                    const int t = tid + h * nch;
+                    acc[4 * tid + 0] += acc[4 * t + 0];
+                    acc[4 * tid + 1] += acc[4 * t + 1];
+                    acc[4 * tid + 2] += acc[4 * t + 2];
+                    acc[4 * tid + 3] += acc[4 * t + 3];
                 }
+                qn = h;
+                __syncthreads();
+            }
+            if (tid < nch) {
+                a0 = acc[4 * tid + 0];
+                a1 = acc[4 * tid + 1];
+                a2 = acc[4 * tid + 2];
+                a3 = acc[4 * tid + 3];
                 v[0][0] = a0;
                 v[0][1] = a1;
                 v[0][2] = a2;
