@@ -44,6 +44,22 @@ import workloads as wl  # noqa: E402
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+# ops per algorithmic byte at which the two roofs meet (625)
+RIDGE_OPS_PER_BYTE = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def roofline(ops, nbytes, ms):
+    """Roofline entry of a kernel that did `ops` int8 operations and moved
+    `nbytes` algorithmic bytes in `ms` milliseconds: a contraction whose ops
+    per byte reach the ridge point is priced against the MFMA peak, anything
+    below it (or with no ops) against HBM bandwidth."""
+    if ops > 0 and nbytes > 0 and ops / nbytes >= RIDGE_OPS_PER_BYTE:
+        achieved = ops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": None}
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
 METRIC = "int8 layer fwd+bwd TOPS & % INT8 MFMA peak; SGD-update GB/s & % HBM"
 
 LOADER = {0: "K", 1: "T", 2: "im2col", 3: "dgrad", 4: "im2colT", 5: "WT"}
@@ -661,14 +677,7 @@ def main():
         # a pointwise workload: algorithmic bytes per second
         value = sum(c.bytes for c in calls) / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-    if is_gemm(dom):
-        achieved = A["ops"] / (A["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": None}
-    else:
-        achieved = A["bytes"] / (A["ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof = roofline(A["ops"] if is_gemm(dom) else 0.0, A["bytes"], A["ms"])
     roof["kernel"] = kind_symbol(dom)
     roof["avg_launch_us"] = round(A["ms"] * 1e3 / A["launches"], 2)
     roof["launches_per_step"] = A["launches"] // args.steps

@@ -34,6 +34,20 @@ def test_kind_names_and_symbols():
     assert not bench.is_gemm(3400) and not bench.is_gemm(2001)
 
 
+def test_roofline_bound_follows_arithmetic_intensity():
+    # 5.0 POP/s over 8 TB/s: the roofs meet at 625 ops per byte
+    assert bench.RIDGE_OPS_PER_BYTE == 625.0
+    # 128x128x128 product at 1000 ops/byte, 1 ms: MFMA roof
+    r = bench.roofline(1e12, 1e9, 1.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TOPS" and r["achieved"] == 1000.0 and r["frac"] == 0.2
+    # a contraction of 64 (attention scores, ~80 ops/byte): HBM roof, bytes / time
+    r = bench.roofline(8e10, 1e9, 0.5)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["achieved"] == 2000.0 and r["frac"] == 0.25
+    # exactly at the ridge: MFMA; no ops (a pointwise pass): HBM
+    assert bench.roofline(625e9, 1e9, 1.0)["bound"] == "mfma"
+    assert bench.roofline(0.0, 4e9, 1.0)["achieved"] == 4000.0
+
+
 def test_attention_inputs():
     a = wl.vit_attention_inputs(2, 3, 197, 64, seed=1)
     assert a.z == 6 and a.Q.mant.shape == (6 * 197, 64) and a.P.mant.shape == (6 * 197, 197)
