@@ -306,9 +306,20 @@ static Plan forced(const Force &f, long long K) {
 }
 
 Plan plan_product(long long M, long long N, long long K, int row_group, int family, const Force &f) {
-    (void)family;  // every product family has the same tiles for these choices
     if (f.on) return forced(f, K);
     auto tiles = [&](Tile t) { return (long long)cdiv(M, t.bm()) * cdiv(N, t.bn()); };
+    // Rows of 129..256 results: the 64 x 256 tile holds a whole row group,
+    // so its epilogue rounds straight to int8 in one pass.  Measured against
+    // the plans below over row-grouped products (bit-identical results): it
+    // wins while its tiles need at most two workgroups per CU (M up to
+    // 32768; 25216 x 192 x 192: 18.9 vs 25.5 us, x 768: 25.7 vs 29.5 us;
+    // 8192 x 192 x 768: 14.6 vs 20.2 us), and loses with more rows (one
+    // workgroup per CU: 50432 x 192 x 576, 46.2 vs 40.6 us).  A few tiles
+    // with a long contraction keep the split plan below.
+    const bool few_long = tiles(Tile{1, 1}) < NCU / 2 && K >= 8 * BK;
+    if (row_group && N > 128 && N <= 256 && !few_long && tile_built(family, Tile{1, 4}, false) &&
+        tiles(Tile{1, 4}) <= 2ll * NCU)
+        return Plan{Tile{1, 4}, PLAN_DIRECT, 1, chunk_for(K, 1)};
     // The 128 x 128 tile for outputs wider than 64 with at least 3/4 of a
     // tile per CU (its matrix work per LDS byte and per barrier is twice the
     // 128 x 64 tile's), else 128 x 64 with 1.5 tiles per CU, else 64 x 64: a
@@ -328,7 +339,7 @@ Plan plan_product(long long M, long long N, long long K, int row_group, int fami
     // round trip).
     const bool recomp = row_group ? K <= RECOMP_KMAX : K <= BK || (K <= 2 * BK && N >= 2 * K);
     Plan best{t, direct ? PLAN_DIRECT : recomp ? PLAN_RECOMP : PLAN_RTO, 1, chunk_for(K, 1)};
-    if (!direct && tiles(Tile{1, 1}) < NCU / 2 && K >= 8 * BK) {
+    if (!direct && few_long) {
         const long long n11 = tiles(Tile{1, 1});
         int sp = 1;
         while (sp < 16 && n11 * sp * 2 <= WG_TARGET && K / (sp * 2) >= 4 * BK) sp *= 2;

@@ -82,6 +82,29 @@ def test_dense_direct(tile, ws, plan):
         assert_same(Y, o.linear_fwd(X, W, gy), f"direct group {gy}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 129, 392), (3000, 197, 64), (3000, 256, 392), (1000, 197, 300),
+                                   (64, 197, 1100)])
+def test_dense_planner_wide_rows(M, N, K, ws, plan):
+    # the planner's own choice for row groups of 129..256 results (a 64 x 256
+    # tile holding whole rows, one pass; the split plan for few long rows)
+    announce(f"dense planner wide rows M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    X = rand_qt(rng, (M, K), R)
+    W = rand_qt(rng, (N, K), R)
+    plan()
+    for gy in (R, T):
+        Y = ie.Mat.empty(M, N, gy)
+        ie.ie_linear_fwd(qt_to_dev(X), qt_to_dev(W), Y, ws)
+        assert_same(Y, o.linear_fwd(X, W, gy), f"fwd group {gy}")
+    # an input gradient with rows of N results: dY2 [M x K] . W2 [K x N]
+    dY2 = rand_qt(rng, (M, K), R)
+    W2 = rand_qt(rng, (K, N), R)
+    dX = ie.Mat.empty(M, N, R)
+    ie.ie_linear_bwd_dx(qt_to_dev(dY2), qt_to_dev(W2), dX, ws)
+    assert_same(dX, o.linear_bwd_dx(dY2, W2, R), "dX group R")
+    assert ws.status() == 0
+
+
 def _relu(t: o.QT) -> o.QT:
     return o.QT(o.relu_fwd(t.mant).astype(np.int8), t.exp, t.group)
 
