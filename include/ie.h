@@ -241,6 +241,26 @@ ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *
                           const ie_mat *Y, int act, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Input gradients passed back through the activation that produced the
+ * layer's input (Table 7, the ReLU backward fused into the product's
+ * output).  With act = IE_ACT_RELU, X is that activation's output and
+ *   dX.C = (the plain input gradient's C) where X.C > 0, else 0,
+ *   dX.exp = the plain input gradient's exponents,
+ * i.e. exactly ie_conv_bwd / ie_linear_bwd_dx followed by ie_relu_bwd(dX, X)
+ * (relu6 = 0), in one pass over dX.  The weight gradient of ie_conv_bwd_act
+ * is that of ie_conv_bwd (it does not depend on the activation).
+ * act = IE_ACT_NONE: the plain entry points; other values return
+ * IE_ERR_UNSUPPORTED.  ie_linear_bwd_dx_act: X [M x K] is read only for the
+ * mask (any group, shape of dX, else IE_ERR_SHAPE).  dX must not be X
+ * (IE_ERR_UNSUPPORTED).  Other arguments, limits and workspace sizes as for
+ * the plain entry points.
+ */
+ie_status ie_linear_bwd_dx_act(const ie_mat *dY, const ie_mat *W, const ie_mat *X, const ie_mat *dX, int act,
+                               void *ws, size_t ws_bytes, void *stream);
+ie_status ie_conv_bwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
+                          const ie_mat *dX, const ie_mat *dW, int act, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * ReLU and ReLU6 of a (C, e) tensor (Table 7, "Clip activations"), on the
  * mantissas; the exponents are copied:
  *   relu:  Y.C = max(X.C, 0)

@@ -85,7 +85,7 @@ ie_status checked_plan(const Plan &pl, long long M, long long N, long long K, in
 // A(m,k) . B(n,k) over K into an int8 output with the planned epilogue.
 ie_status run_product(const Operand &A, const Operand &B, long long M, long long N, long long K, ExpSrc ea,
                       ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, hipStream_t st,
-                      int relu = 0) {
+                      Act act = Act{}) {
     if (M == 0 || N == 0) {
         return hip_status(launch_fill_i8(out->exp, out->group == IE_GROUP_ROW ? M : 1, E_MIN, st));
     }
@@ -107,7 +107,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     ep.out = out->mant;
     ep.out_exp = out->exp;
     ep.flags = flags;
-    ep.relu = relu;
+    ep.act = act;
     ep.q = mat_q(out);
     if (pl.mode == PLAN_DIRECT) {
         ep.mode = EPI_DIRECT;
@@ -119,7 +119,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
         ep.v16 = pw.v16;
         ep.p16 = pw.p16;
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, 1, pl.k_chunk, false, ep, st));
-        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st, relu));
+        IE_TRY(launch_rto_finalize(pw.v16, pw.p16, (int)M, (int)N, pl.t, rg, out->mant, out->exp, flags, st, act));
         return IE_OK;
     }
     if (pl.mode == PLAN_RECOMP) {
@@ -137,7 +137,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     if (rg && split_round_rows_fits((int)N, 1, 1)) {
         IE_TRY(launch_gemm(A, B, (int)M, (int)N, (int)K, pl.t, pl.splits, pl.k_chunk, true, ep, st));
         IE_TRY(launch_split_round_rows(pw.partial, pl.splits, M * N, (int)M, (int)N, (int)N, 1, 1, ea, eb, out->mant,
-                                       out->exp, flags, mat_q(out), st, relu));
+                                       out->exp, flags, mat_q(out), st, act));
         return IE_OK;
     }
     ep.gneed = pw.gneed;
@@ -146,7 +146,7 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
     IE_TRY(launch_partial_reduce(pw.partial, pl.splits, M * N, (int)M, (int)N, ea, eb, rg, pw.sums, pw.gneed,
                                  mat_q(out), st));
     IE_TRY(launch_round_sums(pw.sums, (int)M, (int)N, (int)N, 1, 1, ea, eb, rg, pw.gneed, out->mant, out->exp, flags,
-                             st, relu));
+                             st, act));
     return IE_OK;
 }
 
@@ -154,7 +154,8 @@ ie_status run_product(const Operand &A, const Operand &B, long long M, long long
 // epilogue: group maximum over every phase, then each phase rounded
 // straight to int8 at its input pixels).
 ie_status run_dgrad_phased(const DgradPlan &dp, const Operand &A, const Operand &B, long long N, ExpSrc ea,
-                           ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, hipStream_t st) {
+                           ExpSrc eb, const ie_mat *out, const ProductWs &pw, uint32_t *flags, hipStream_t st,
+                           Act act) {
     IE_CHECK(checked_plan(dp.pl, dp.M, N, dp.K, 0, FAM_DGRAD, pw.n, product_needs(dp.pl, dp.M, N, dp.K, 0)));
     if (dp.pl.mode != PLAN_RECOMP || out->group != IE_GROUP_TENSOR || dp.ps.n == 0) return IE_ERR_UNSUPPORTED;
     log_plan("conv phased", dp.M, N, dp.K, dp.pl);
@@ -166,6 +167,7 @@ ie_status run_dgrad_phased(const DgradPlan &dp, const Operand &A, const Operand 
     ep.out_exp = out->exp;
     ep.flags = flags;
     ep.q = mat_q(out);
+    ep.act = act;
     ep.ph = dp.ps;
     ep.tneed = pw.tneed;
     ep.tneed_n = recomp_grid(dp.M, N, dp.K, dp.pl.t);
@@ -231,7 +233,7 @@ static bool conv_is_dense(const ConvGeom &g) { return g.r == 1 && g.s == 1 && g.
 // finalize.  IE_ERR_UNSUPPORTED, with nothing launched, otherwise.
 ie_status conv_bwd_pair(const ConvGeom &g, const DgradPlan &dp, const ie_mat *X, const Operand &B1, ExpSrc ew,
                         const ie_mat *dY, const ie_mat *dX, const ie_mat *dW, const int8_t *dys, int8_t *xp,
-                        const ConvBwdWs &cw, uint32_t *flags, hipStream_t st) {
+                        const ConvBwdWs &cw, uint32_t *flags, hipStream_t st, Act act1) {
     const long long nhw = (long long)g.n * g.h * g.w, npq = (long long)g.n * g.p * g.q;
     const long long rscp = (long long)g.r * g.s * g.cp;
     const long long rsc = (long long)g.r * g.s * g.c;
@@ -271,6 +273,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const DgradPlan &dp, const ie_mat *X,
     e1.v16 = cw.pw.v16;
     e1.p16 = cw.pw.p16;
     e1.q = mat_q(dX);
+    e1.act = act1;
     e1.ph = dp.ps;
     if (p1.mode == PLAN_RECOMP) {
         e1.tneed = cw.pw.tneed;
@@ -296,7 +299,7 @@ ie_status conv_bwd_pair(const ConvGeom &g, const DgradPlan &dp, const ie_mat *X,
     }
     IE_TRY(launch_finalize_pair(cw.pw.v16, cw.pw.p16, (int)nhw, g.c, p1.t, dX->mant, dX->exp, cw.w.partial,
                                 p2.splits, g.k * rscp, g.k, (int)rsc, (int)rscp, g.c, g.cp, edy, ex, dW->mant, dW->exp,
-                                flags, mat_q(dW), st));
+                                flags, mat_q(dW), st, act1));
     return IE_OK;
 }
 
@@ -528,7 +531,7 @@ static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, v
     Operand B{LD_K, wsrc, Kp, (int)N, {}};
     ExpSrc ea{X->exp, nullptr, X->group == IE_GROUP_ROW};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, M, N, Kp, ea, eb, Y, w.pw, flags, st, relu);
+    return run_product(A, B, M, N, Kp, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr});
 }
 
 ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
@@ -555,8 +558,8 @@ ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, i
     return linear_fwd(X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
-ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
-                           void *stream) {
+static ie_status linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
+                               void *stream, Act act) {
     IE_CHECK(check_mat(dY));
     IE_CHECK(check_mat(W));
     IE_CHECK(check_mat(dX));
@@ -573,7 +576,7 @@ ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, 
     const LinearDxWs w = carve_linear_dx(c, M, N, K, f);
     const long long Np = r16(N);
     if (M == 0 || K == 0)
-        return run_product(Operand{LD_K}, Operand{LD_K}, M, K, Np, ExpSrc{}, ExpSrc{}, dX, w.pw, flags, st);
+        return run_product(Operand{LD_K}, Operand{LD_K}, M, K, Np, ExpSrc{}, ExpSrc{}, dX, w.pw, flags, st, act);
     IE_TRY(launch_align_transpose(W->mant, W->exp, W->group == IE_GROUP_ROW, (int)N, 1, (int)K, (int)Np, w.wt,
                                   w.estar, st));
     const int8_t *dys = dY->mant;
@@ -585,7 +588,23 @@ ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, 
     Operand B{LD_K, w.wt, Np, (int)K, {}};
     ExpSrc ea{dY->exp, nullptr, dY->group == IE_GROUP_ROW};
     ExpSrc eb{nullptr, w.estar, 0};
-    return run_product(A, B, M, K, Np, ea, eb, dX, w.pw, flags, st);
+    return run_product(A, B, M, K, Np, ea, eb, dX, w.pw, flags, st, act);
+}
+
+ie_status ie_linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
+                           void *stream) {
+    return linear_bwd_dx(dY, W, dX, ws, ws_bytes, stream, Act{});
+}
+
+ie_status ie_linear_bwd_dx_act(const ie_mat *dY, const ie_mat *W, const ie_mat *X, const ie_mat *dX, int act,
+                               void *ws, size_t ws_bytes, void *stream) {
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    if (act == IE_ACT_NONE) return linear_bwd_dx(dY, W, dX, ws, ws_bytes, stream, Act{});
+    IE_CHECK(check_mat(X));
+    IE_CHECK(check_mat(dX));
+    if (X->rows != dX->rows || X->cols != dX->cols) return IE_ERR_SHAPE;
+    if (X->mant == dX->mant) return IE_ERR_UNSUPPORTED;
+    return linear_bwd_dx(dY, W, dX, ws, ws_bytes, stream, Act{0, X->mant});
 }
 
 ie_status ie_linear_bwd_dw(const ie_mat *dY, const ie_mat *X, const ie_mat *dW, void *ws, size_t ws_bytes,
@@ -667,7 +686,7 @@ static ie_status conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *
     Operand B{LD_K, wsrc, kg, g.k, {}};
     ExpSrc ea{X->exp, nullptr, 0};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, npq, g.k, kg, ea, eb, Y, w.pw, flags, st, relu);
+    return run_product(A, B, npq, g.k, kg, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr});
 }
 
 ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
@@ -681,8 +700,8 @@ ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *
     return conv_fwd(d, X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
-ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
-                      const ie_mat *dX, const ie_mat *dW, void *ws, size_t ws_bytes, void *stream) {
+static ie_status conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
+                          const ie_mat *dX, const ie_mat *dW, void *ws, size_t ws_bytes, void *stream, int act) {
     IE_CHECK(check_conv(d));
     IE_CHECK(check_mat(X));
     IE_CHECK(check_mat(W));
@@ -701,9 +720,12 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     if (X->group != IE_GROUP_TENSOR || dY->group != IE_GROUP_TENSOR) return IE_ERR_UNSUPPORTED;
     if ((long long)g.k * g.r * g.s > MAX_CONTRACT || nhw > DIM_MAX || !conv_fits(g)) return IE_ERR_UNSUPPORTED;
     if (!aligned(X->mant, 16) || !aligned(dY->mant, 16)) return IE_ERR_UNSUPPORTED;
+    if (dX && act == IE_ACT_RELU && dX->mant == X->mant) return IE_ERR_UNSUPPORTED;
     if (!ws) return IE_ERR_WORKSPACE;
     const Force f = force_product(), fw = force_wgrad();
     if (ws_bytes < conv_bwd_ws(g, f, fw)) return IE_ERR_WORKSPACE;
+    // dX through the ReLU whose output is X: zero where X is not positive
+    const Act act1{0, act == IE_ACT_RELU ? X->mant : nullptr};
     hipStream_t st = (hipStream_t)stream;
     uint32_t *flags = (uint32_t *)ws;
     Carve c{(char *)ws, HEADER};
@@ -744,15 +766,16 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
     if (dX && dW) {
         // the two products are independent: one grid runs both when a paired
         // kernel covers their plans, else they run one after the other
-        const ie_status sp = conv_bwd_pair(g, dp, X, B1, ew, dY, dX, dW, dys, cw.xp, cw, flags, st);
+        const ie_status sp = conv_bwd_pair(g, dp, X, B1, ew, dY, dX, dW, dys, cw.xp, cw, flags, st, act1);
         if (sp != IE_ERR_UNSUPPORTED) return sp;
     }
     if (dX) {
         const Operand A = dense ? Operand{LD_K, dys, g.kp, (int)nhw, {}} : Operand{LD_DGRAD, dys, g.kp, (int)nhw, g};
         if (phased)
-            IE_CHECK(run_dgrad_phased(dp, A, B1, g.c, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st));
+            IE_CHECK(run_dgrad_phased(dp, A, B1, g.c, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st, act1));
         else
-            IE_CHECK(run_product(A, B1, nhw, g.c, rskp, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st));
+            IE_CHECK(
+                run_product(A, B1, nhw, g.c, rskp, ExpSrc{dY->exp, nullptr, 0}, ew, dX, cw.pw, flags, st, act1));
     }
     if (dW) {
         const int8_t *xs = X->mant;
@@ -766,6 +789,17 @@ ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
                            ExpSrc{X->exp, nullptr, 0}, dW, cw.w, flags, st));
     }
     return IE_OK;
+}
+
+ie_status ie_conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
+                      const ie_mat *dX, const ie_mat *dW, void *ws, size_t ws_bytes, void *stream) {
+    return conv_bwd(d, X, W, dY, dX, dW, ws, ws_bytes, stream, IE_ACT_NONE);
+}
+
+ie_status ie_conv_bwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,
+                          const ie_mat *dX, const ie_mat *dW, int act, void *ws, size_t ws_bytes, void *stream) {
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    return conv_bwd(d, X, W, dY, dX, dW, ws, ws_bytes, stream, act);
 }
 
 ie_status ie_sgd_update(const ie_mat *W, const ie_mat *V, const ie_mat *G, ie_scalar lr, ie_scalar momentum,

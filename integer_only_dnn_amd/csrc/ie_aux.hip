@@ -429,7 +429,7 @@ constexpr int FIN_NEEDS = 2048;
 __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int16_t *p16, int M, int N,
                                                            int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
-                                                           FastDiv dper, int relu, int bid, int nblk) {
+                                                           FastDiv dper, Act act, int bid, int nblk) {
     __shared__ int sh[4];
     __shared__ int16_t needs[FIN_NEEDS];
     __shared__ int rowe[256];
@@ -444,10 +444,8 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
             if (j < 2) lo |= b << (16 * j);
             else hi |= b << (16 * (j - 2));
         }
-        if (relu) {
-            lo = relu4(lo);
-            hi = relu4(hi);
-        }
+        lo = act4(lo, act, o);
+        hi = act4(hi, act, o + 4);
         *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
     };
     auto round8 = [&](long long o, int sh_) {
@@ -461,14 +459,11 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
                 if (j < 2) lo |= b << (16 * j);
                 else hi |= b << (16 * (j - 2));
             }
-            if (relu) {
-                lo = relu4(lo);
-                hi = relu4(hi);
-            }
+            lo = act4(lo, act, o);
+            hi = act4(hi, act, o + 4);
             *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
         } else {
-            const int c = rne_shift32(v16[o], sh_);
-            out[o] = (int8_t)(relu && c < 0 ? 0 : c);
+            out[o] = (int8_t)act1(rne_shift32(v16[o], sh_), act, o);
         }
     };
     if (!row_group) {
@@ -566,8 +561,8 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
 __global__ __launch_bounds__(256) void rto_finalize_kernel(const int16_t *v16, const int16_t *p16, int M, int N,
                                                            int lbm, int lbn, int TM, int n_ct, int row_group, int rb,
                                                            int8_t *out, int8_t *out_exp, uint32_t *flags, int vw,
-                                                           FastDiv dper, int relu) {
-    rto_finalize_body(v16, p16, M, N, lbm, lbn, TM, n_ct, row_group, rb, out, out_exp, flags, vw, dper, relu,
+                                                           FastDiv dper, Act act) {
+    rto_finalize_body(v16, p16, M, N, lbm, lbn, TM, n_ct, row_group, rb, out, out_exp, flags, vw, dper, act,
                       blockIdx.x, gridDim.x);
 }
 
@@ -580,17 +575,17 @@ struct RtoFin {
     int vw;
     FastDiv dper;
     int blocks;
-    int relu;
+    Act act;
 };
 
 static RtoFin rto_fin(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group, int8_t *out,
-                      int8_t *out_exp, uint32_t *flags) {
+                      int8_t *out_exp, uint32_t *flags, Act act) {
     RtoFin f;
     f.v16 = v16;
     f.p16 = p16;
     f.M = M;
     f.N = N;
-    f.vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0) ? 8 : 1;
+    f.vw = (N % 8 == 0 && ((uintptr_t)out % 8) == 0 && act_aligned(act, 8)) ? 8 : 1;
     f.TM = (M + t.bm() - 1) / t.bm();
     f.n_ct = (N + t.bn() - 1) / t.bn();
     // row runs of about 8192 elements (at most 256 rows)
@@ -606,17 +601,17 @@ static RtoFin rto_fin(const int16_t *v16, const int16_t *p16, int M, int N, Tile
     f.out_exp = out_exp;
     f.flags = flags;
     f.dper = make_fastdiv((uint32_t)(N / f.vw));
-    f.relu = 0;
+    f.act = act;
     return f;
 }
 
 hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
-                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu) {
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, Act act) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const RtoFin f = rto_fin(v16, p16, M, N, t, row_group, out, out_exp, flags);
+    const RtoFin f = rto_fin(v16, p16, M, N, t, row_group, out, out_exp, flags, act);
     prof_begin(st, PROF_RTO_FINALIZE);
     hipLaunchKernelGGL(rto_finalize_kernel, dim3(f.blocks), dim3(256), 0, st, f.v16, f.p16, f.M, f.N, f.lbm, f.lbn,
-                       f.TM, f.n_ct, f.row_group, f.rb, f.out, f.out_exp, f.flags, f.vw, f.dper, relu);
+                       f.TM, f.n_ct, f.row_group, f.rb, f.out, f.out_exp, f.flags, f.vw, f.dper, f.act);
     prof_end(st, PROF_RTO_FINALIZE);
     return hipGetLastError();
 }
@@ -720,7 +715,7 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
                                                          int mc, int mcp, FastDiv dmc, ExpSrc ea, ExpSrc eb,
                                                          int row_group, const int *gneed, int8_t *out,
                                                          int8_t *out_exp, uint32_t *flags, int vw, FastDiv dper,
-                                                         int relu) {
+                                                         Act act) {
     const uint32_t per_row = N / vw;
     const uint32_t total = (uint32_t)M * per_row;
     const int eT = row_group ? 0 : clamp_exp_flag(max(E_MIN, gneed[0]), flags);
@@ -749,9 +744,8 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
         }
         uint32_t w = 0;
         for (int j = 0; j < vw; ++j) w |= (uint32_t)(uint8_t)rne_shift64(sv[j], e - ev[j]) << (8 * j);
-        if (relu) w = relu4(w);
-        if (vw == 4) *(uint32_t *)(out + o) = w;
-        else out[o] = (int8_t)w;
+        if (vw == 4) *(uint32_t *)(out + o) = act4(w, act, o);
+        else out[o] = (int8_t)act1((int)(int8_t)w, act, o);
         if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
     }
     if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
@@ -820,7 +814,7 @@ template <int THR>
 __device__ __forceinline__ void split_round_body(const int *partial, int splits, long long stride,
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q, int relu,
+                                                                 int8_t *out_exp, uint32_t *flags, int vw, int Q, Act act,
                                                                  int wq, int bid, int nblk) {
     // short rows (THR == SR_THR_SHORT) hold at most one chunk per thread
     constexpr int MAXV = THR == SR_THR_SHORT ? 1 : SR_MAXV;
@@ -941,10 +935,10 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - eps(4 * c + j)) << (8 * j);
-                *(uint32_t *)(orow + 4 * c) = relu ? relu4(w) : w;
+                *(uint32_t *)(orow + 4 * c) = act4(w, act, (long long)row * Nout + 4 * c);
             } else {
                 const int cv = (int)rne_shift64(v[k][0], e - eps(c));
-                orow[c] = (int8_t)(relu && cv < 0 ? 0 : cv);
+                orow[c] = (int8_t)act1(cv, act, (long long)row * Nout + c);
             }
         }
         __syncthreads();
@@ -956,9 +950,9 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void s
                                                                  int M, int Nout, int src_pitch, int mc, int mcp,
                                                                  FastDiv dmc, ExpSrc ea, ExpSrc eb, int8_t *out,
                                                                  int8_t *out_exp, uint32_t *flags, int vw, int Q,
-                                                                 int relu, int wq) {
+                                                                 Act act, int wq) {
     split_round_body<THR>(partial, splits, stride, M, Nout, src_pitch, mc, mcp, dmc, ea, eb, out, out_exp, flags, vw, Q,
-                          relu, wq, blockIdx.x, gridDim.x);
+                          act, wq, blockIdx.x, gridDim.x);
 }
 
 
@@ -974,13 +968,13 @@ struct SplitFin {
     uint32_t *flags;
     int vw, Q, blocks;
     bool shortrow;
-    int relu;
+    Act act;
     int wq;  // results have |C| <= 2^wq - 1
 };
 
 static SplitFin split_fin(const int *partial, int splits, long long split_stride, int M, int Nout, int src_pitch,
                           int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out, int8_t *out_exp, uint32_t *flags,
-                          int wq) {
+                          int wq, Act act) {
     SplitFin f;
     f.partial = partial;
     f.splits = splits;
@@ -995,7 +989,8 @@ static SplitFin split_fin(const int *partial, int splits, long long split_stride
     f.out = out;
     f.out_exp = out_exp;
     f.flags = flags;
-    f.vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
+    f.vw = (mc == mcp && Nout % 4 == 0 && src_pitch % 4 == 0 && ((uintptr_t)out % 4) == 0 && act_aligned(act, 4)) ? 4
+                                                                                                            : 1;
     const int nch = Nout / f.vw;
     f.shortrow = nch <= SR_THR;
     const int thr = f.shortrow ? SR_THR_SHORT : SR_THR;
@@ -1006,26 +1001,26 @@ static SplitFin split_fin(const int *partial, int splits, long long split_stride
     }
     f.blocks = blocks_for(M, 1, 16384);
     f.dmc = make_fastdiv((uint32_t)(mc > 0 ? mc : 1));
-    f.relu = 0;
+    f.act = act;
     f.wq = wq;
     return f;
 }
 
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, int relu) {
+                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, Act act) {
     if (M <= 0 || Nout <= 0) return hipSuccess;
     const SplitFin f = split_fin(partial, splits, split_stride, M, Nout, src_pitch, mc, mcp, ea, eb, out, out_exp,
-                                 flags, q);
+                                 flags, q, act);
     prof_begin(st, PROF_SPLIT_ROUND);
     if (f.shortrow)
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR_SHORT>, dim3(f.blocks), dim3(SR_THR_SHORT), 0, st,
                            f.partial, f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb,
-                           f.out, f.out_exp, f.flags, f.vw, f.Q, relu, f.wq);
+                           f.out, f.out_exp, f.flags, f.vw, f.Q, f.act, f.wq);
     else
         hipLaunchKernelGGL(split_round_rows_kernel<SR_THR>, dim3(f.blocks), dim3(SR_THR), 0, st, f.partial,
                            f.splits, f.stride, f.M, f.Nout, f.src_pitch, f.mc, f.mcp, f.dmc, f.ea, f.eb, f.out,
-                           f.out_exp, f.flags, f.vw, f.Q, relu, f.wq);
+                           f.out_exp, f.flags, f.vw, f.Q, f.act, f.wq);
     prof_end(st, PROF_SPLIT_ROUND);
     return hipGetLastError();
 }
@@ -1040,10 +1035,10 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void f
     if ((int)blockIdx.x < r.blocks) {
         if (threadIdx.x >= 256) return;
         rto_finalize_body(r.v16, r.p16, r.M, r.N, r.lbm, r.lbn, r.TM, r.n_ct, r.row_group, r.rb, r.out, r.out_exp,
-                          r.flags, r.vw, r.dper, r.relu, blockIdx.x, r.blocks);
+                          r.flags, r.vw, r.dper, r.act, blockIdx.x, r.blocks);
     } else {
         split_round_body<THR>(q.partial, q.splits, q.stride, q.M, q.Nout, q.src_pitch, q.mc, q.mcp, q.dmc, q.ea,
-                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, q.relu, q.wq, blockIdx.x - r.blocks,
+                              q.eb, q.out, q.out_exp, q.flags, q.vw, q.Q, q.act, q.wq, blockIdx.x - r.blocks,
                               gridDim.x - r.blocks);
     }
 }
@@ -1051,16 +1046,16 @@ __global__ __launch_bounds__(THR) __attribute__((amdgpu_waves_per_eu(4))) void f
 hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
                                 int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
                                 int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
-                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st) {
+                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st, Act act1) {
     if (M1 <= 0 || N1 <= 0 || M2 <= 0 || Nout <= 0) {
-        hipError_t e = launch_rto_finalize(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags, st);
+        hipError_t e = launch_rto_finalize(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags, st, act1);
         if (e != hipSuccess) return e;
         return launch_split_round_rows(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2,
                                        out2_exp, flags, q2, st);
     }
-    const RtoFin r = rto_fin(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags);
+    const RtoFin r = rto_fin(v16, p16, M1, N1, t1, 0, out1, out1_exp, flags, act1);
     const SplitFin q = split_fin(partial, splits, split_stride, M2, Nout, src_pitch, mc, mcp, ea, eb, out2, out2_exp,
-                                 flags, q2);
+                                 flags, q2, Act{});
     const dim3 grid(r.blocks + q.blocks);
     prof_begin(st, PROF_FIN_PAIR);
     if (q.shortrow)
@@ -1087,14 +1082,14 @@ hipError_t launch_partial_reduce(const int *partial, int splits, long long split
 
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
-                             uint32_t *flags, hipStream_t st, int relu) {
+                             uint32_t *flags, hipStream_t st, Act act) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    const int vw = (N % 4 == 0 && ((uintptr_t)out % 4) == 0) ? 4 : 1;
+    const int vw = (N % 4 == 0 && ((uintptr_t)out % 4) == 0 && act_aligned(act, 4)) ? 4 : 1;
     const long long total = (long long)M * (N / vw);
     prof_begin(st, PROF_ROUND_SUMS);
     hipLaunchKernelGGL(round_sums_kernel, dim3(blocks_for(total, 256, 8192)), dim3(256), 0, st, sums, M, N,
                        src_pitch, mc, mcp, make_fastdiv((uint32_t)(mc > 0 ? mc : 1)), ea, eb, row_group, gneed,
-                       out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)), relu);
+                       out, out_exp, flags, vw, make_fastdiv((uint32_t)(N / vw)), act);
     prof_end(st, PROF_ROUND_SUMS);
     return hipGetLastError();
 }

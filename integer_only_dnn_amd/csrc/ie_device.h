@@ -84,6 +84,41 @@ __device__ __forceinline__ uint32_t relu4(uint32_t w) {
     return w & ~(neg * 0xffu);
 }
 
+// The activation applied to rounded int8 results, their exponents kept
+// (Table 7): ReLU of the results themselves (forward products), or the
+// backward of a ReLU whose output is `mask`, laid out like the results
+// (input gradients: a result stays where the matching mask byte is
+// positive, else it becomes zero).
+struct Act {
+    int relu;
+    const int8_t *mask;
+};
+
+// The bytes of w whose matching byte of x is positive; the others zero.
+__device__ __forceinline__ uint32_t pos_mask4(uint32_t w, uint32_t x) {
+    const uint32_t nz = ((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) & 0x80808080u;  // low seven bits not all zero
+    return w & (((nz & ~x) >> 7) * 0xffu);                                // ... and the sign bit clear
+}
+
+// Four results at out + o (o a multiple of 4 when a.mask is set; the mask
+// 4-byte aligned).
+__device__ __forceinline__ uint32_t act4(uint32_t w, const Act &a, long long o) {
+    if (a.relu) w = relu4(w);
+    if (a.mask) w = pos_mask4(w, *(const uint32_t *)(a.mask + o));
+    return w;
+}
+
+// One result at out + o.
+__device__ __forceinline__ int act1(int c, const Act &a, long long o) {
+    if (a.relu && c < 0) c = 0;
+    if (a.mask && a.mask[o] <= 0) c = 0;
+    return c;
+}
+
+// Whether 4-byte (8-byte) result groups at multiples of 4 (8) may take the
+// vector forms: the mask, if any, aligned like the results.
+__host__ __device__ inline bool act_aligned(const Act &a, int bytes) { return !a.mask || ((uintptr_t)a.mask % bytes) == 0; }
+
 __device__ __forceinline__ int clamp_exp_flag(int e, uint32_t *flags) {
     if (e < E_MIN) e = E_MIN;
     if (e > E_MAX) {

@@ -991,9 +991,26 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
             }
             v4i v = *(const v4i *)(lds + row * PITCH + cb);
             if constexpr (ES == 1) {
-                if (ep.relu) {
+                // the activation on the rounded bytes (mask bytes at the
+                // results' own offsets)
+                const long long o = (long long)grow * ld + gcol;
+                if (vec && gcol + EPC <= N) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = (int)relu4((uint32_t)v[k]);
+                    for (int k = 0; k < 4; ++k) v[k] = (int)act4((uint32_t)v[k], ep.act, o + 4 * k);
+                } else if (ep.act.relu || ep.act.mask) {
+                    const int n = min(16, N - gcol);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint32_t w = (uint32_t)v[k];
+                        if (ep.act.relu) w = relu4(w);
+                        if (ep.act.mask) {
+                            uint32_t x = 0;
+                            for (int j = 0; j < 4; ++j)
+                                if (4 * k + j < n) x |= (uint32_t)(uint8_t)ep.act.mask[o + 4 * k + j] << (8 * j);
+                            w = pos_mask4(w, x);
+                        }
+                        v[k] = (int)w;
+                    }
                 }
             }
             int8_t *g = (int8_t *)dst + ((long long)grow * ld + gcol) * ES;
@@ -1404,7 +1421,8 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
             }
         }
         __syncthreads();
-        if (direct) flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0);
+        if (direct)
+            flush(ES1{}, ep.out, N, (N & 15) == 0 && ((uintptr_t)ep.out & 15) == 0 && act_aligned(ep.act, 16));
         else flush(ES2{}, ep.v16, N, (N & 7) == 0);
         return NEED_NONE;
     }

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ie_device.h"
 #include "ie_plan.h"
 
 namespace ie {
@@ -50,7 +51,7 @@ struct Epi {
     int *partial;     // PARTIAL: int32 [splits][M][N]
     long long split_stride;
     uint32_t *flags;
-    int relu;         // int8 results pass through ReLU (forward products)
+    Act act;          // applied to the int8 results (fused ReLU or ReLU backward)
     int q;            // results have |C| <= 2^q - 1 (mantissa width q + 1 bits)
     int *tneed;       // MAX writes / GIVEN reads: group maxima of the first pass
     int tneed_n;      //   whole tensor: the first pass's grid size (entries)
@@ -163,7 +164,7 @@ hipError_t launch_align_transpose(const int8_t *w, const int8_t *e, int e_row, i
 // maximum of the tile needs in p16 (ROW groups: per (row, column tile);
 // whole-tensor groups: per tile, tile_m + TM * tile_n).
 hipError_t launch_rto_finalize(const int16_t *v16, const int16_t *p16, int M, int N, Tile t, int row_group,
-                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, int relu = 0);
+                               int8_t *out, int8_t *out_exp, uint32_t *flags, hipStream_t st, Act act = Act{});
 // Split-contraction finalize: sum int32 partials into int64 and raise the
 // group maxima (set empty by the split kernel, or by launch_fill_i32 when no
 // split kernel ran); then round the sums into int8.
@@ -172,20 +173,20 @@ hipError_t launch_partial_reduce(const int *partial, int splits, long long split
                                  hipStream_t st);
 hipError_t launch_round_sums(const long long *sums, int M, int N, int src_pitch, int mc, int mcp, ExpSrc ea,
                              ExpSrc eb, int row_group, const int *gneed, int8_t *out, int8_t *out_exp,
-                             uint32_t *flags, hipStream_t st, int relu = 0);
+                             uint32_t *flags, hipStream_t st, Act act = Act{});
 // Split finalize of row groups in one pass (sums never stored): output
 // [M x Nout] from partials [splits][M][src_pitch] with the column map of
 // launch_round_sums.  Requires split_round_rows_fits(Nout, mc, mcp).
 hipError_t launch_split_round_rows(const int *partial, int splits, long long split_stride, int M, int Nout,
                                    int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out,
-                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, int relu = 0);
+                                   int8_t *out_exp, uint32_t *flags, int q, hipStream_t st, Act act = Act{});
 // A round-to-odd finalize (whole-tensor group, M1 x N1 from tile t1) and a
 // split finalize by rows (the arguments of launch_split_round_rows) in one
 // launch.
 hipError_t launch_finalize_pair(const int16_t *v16, const int16_t *p16, int M1, int N1, Tile t1, int8_t *out1,
                                 int8_t *out1_exp, const int *partial, int splits, long long split_stride, int M2,
                                 int Nout, int src_pitch, int mc, int mcp, ExpSrc ea, ExpSrc eb, int8_t *out2,
-                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st);
+                                int8_t *out2_exp, uint32_t *flags, int q2, hipStream_t st, Act act1 = Act{});
 hipError_t launch_zero_flags(void *ws, hipStream_t st);
 
 // Integer SGD update (ie_update.hip).

@@ -68,6 +68,8 @@ EXPORTS = [
     ("ie_sgd_update_multi", c_int, [c_int32] + [POINTER(ie_mat)] * 3 + [ie_scalar] * 3 + [c_void_p, c_size_t, c_void_p]),
     ("ie_linear_fwd_act", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
     ("ie_conv_fwd_act", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 3 + [c_int, c_void_p, c_size_t, c_void_p]),
+    ("ie_linear_bwd_dx_act", c_int, [POINTER(ie_mat)] * 4 + [c_int, c_void_p, c_size_t, c_void_p]),
+    ("ie_conv_bwd_act", c_int, [POINTER(ie_conv_desc)] + [POINTER(ie_mat)] * 5 + [c_int, c_void_p, c_size_t, c_void_p]),
     ("ie_relu_fwd", c_int, [POINTER(ie_mat)] * 2 + [c_int, c_void_p]),
     ("ie_relu_bwd", c_int, [POINTER(ie_mat)] * 3 + [c_int, c_void_p]),
     ("ie_add_workspace", c_size_t, [c_int64, c_int64]),
@@ -241,6 +243,31 @@ def ie_conv_bwd(d: ie_conv_desc, X: Mat, W: Mat, dY: Mat, dX: Mat | None, dW: Ma
     _check(lib().ie_conv_bwd(byref(d), byref(x), byref(w), byref(dy),
                              byref(dx) if dx is not None else None,
                              byref(dw) if dw is not None else None, p, b, _stream(ws.device)), "ie_conv_bwd")
+
+
+def ie_conv_bwd_act(d: ie_conv_desc, X: Mat, W: Mat, dY: Mat, dX: Mat | None, dW: Mat | None, act: int,
+                    ws: Workspace) -> None:
+    """ie_conv_bwd with dX passed back through the activation whose output is X."""
+    P = (d.h + 2 * d.pad - d.r) // d.stride + 1
+    Q = (d.w + 2 * d.pad - d.s) // d.stride + 1
+    x = X.c(d.n * d.h * d.w, d.c)
+    w = W.c(d.k, d.r * d.s * d.c)
+    dy = dY.c(d.n * P * Q, d.k)
+    dx = dX.c(d.n * d.h * d.w, d.c) if dX is not None else None
+    dw = dW.c(d.k, d.r * d.s * d.c) if dW is not None else None
+    p, b = ws.get(_ws_size("ie_conv_bwd_workspace", d))
+    _check(lib().ie_conv_bwd_act(byref(d), byref(x), byref(w), byref(dy),
+                                 byref(dx) if dx is not None else None,
+                                 byref(dw) if dw is not None else None, int(act), p, b, _stream(ws.device)),
+           "ie_conv_bwd_act")
+
+
+def ie_linear_bwd_dx_act(dY: Mat, W: Mat, X: Mat, dX: Mat, act: int, ws: Workspace) -> None:
+    """ie_linear_bwd_dx with dX passed back through the activation whose output is X."""
+    dy, w, x, dx = dY.c(), W.c(), X.c(), dX.c()
+    p, b = ws.get(_ws_size("ie_linear_bwd_dx_workspace", dy.rows, dy.cols, w.cols))
+    _check(lib().ie_linear_bwd_dx_act(byref(dy), byref(w), byref(x), byref(dx), int(act), p, b, _stream(ws.device)),
+           "ie_linear_bwd_dx_act")
 
 
 def ie_sgd_update(W: Mat, V: Mat, G: Mat, lr, momentum, weight_decay=(0, 0), ws: Workspace = None) -> None:
