@@ -30,6 +30,15 @@
 #ifndef IE_UNROLL
 #define IE_UNROLL 4
 #endif
+#ifndef IE_PIPE
+#define IE_PIPE 1
+#endif
+#ifndef IE_STAGES22
+#define IE_STAGES22 3
+#endif
+#ifndef IE_OCC22
+#define IE_OCC22 2
+#endif
 
 #include <type_traits>
 
@@ -692,7 +701,7 @@ __device__ __forceinline__ int phase_of_tile(int t) {
 // per CU and would spill at 4, and for the 64 x 64 tile.
 template <int MI, int NI>
 struct Stages {
-    static constexpr int value = MI * NI >= 8 ? 2 : (MI == 2 && NI == 2) || MI * NI == 1 ? 3 : IE_STAGES;
+    static constexpr int value = MI * NI >= 8 ? 2 : (MI == 2 && NI == 2) ? IE_STAGES22 : MI * NI == 1 ? 3 : IE_STAGES;
 };
 
 // Contraction slicing of the 64 x 64 tile: wave w takes the w-th 32-byte
@@ -711,7 +720,7 @@ struct KSlice {
 // Workgroups per CU that a tile's register budget is sized for.
 template <int MI, int NI>
 struct Occ {
-    static constexpr int value = MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI <= 4 ? 2 : 1;
+    static constexpr int value = MI * NI == 1 ? (KSlice<MI, NI>::value ? 3 : 4) : MI * NI < 4 ? 2 : MI * NI == 4 ? IE_OCC22 : 1;
 };
 // The same for the one-step form of a tile (one LDS stage, no register
 // pipeline): up to four workgroups per CU.
@@ -880,12 +889,88 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
         }
     };
 
+    // Fragments of one 32-byte sub-step, read ahead of the MFMAs that take
+    // them: sub-step ks + 1 is read while sub-step ks multiplies, and the
+    // first sub-step of the next LDS buffer right after the barrier, while
+    // the last sub-step of the current one multiplies.  The scheduling
+    // groups interleave one fragment read with each MFMA, so that the LDS
+    // latency hides under matrix work within the wave.
+    constexpr int RD = (IsT<KA>::value ? 2 : 1) * MI + (IsT<KB>::value ? 2 : 1) * NI;  // LDS reads per sub-step
+    constexpr int NMF = MI * NI;
+    v4i fa[2][MI], fb[2][NI];
+    auto rdfrag = [&](const int8_t *sA, const int ks, v4i (&af)[MI], v4i (&bf)[NI]) {
+        const int8_t *sB = sA + LA::BYTES;
+#pragma unroll
+        for (int a = 0; a < MI; ++a) af[a] = frag<KA, BMt>(sA, wm * 32 * MI + a * 32, ks, lane);
+#pragma unroll
+        for (int b = 0; b < NI; ++b) bf[b] = frag<KB, BNt>(sB, wn * 32 * NI + b * 32, ks, lane);
+    };
+    auto mma = [&](const v4i (&af)[MI], const v4i (&bf)[NI]) {
+#pragma unroll
+        for (int a = 0; a < MI; ++a)
+#pragma unroll
+            for (int b = 0; b < NI; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+    };
+    // the next sub-step's reads first, then this sub-step's MFMAs: a read
+    // has a whole sub-step of matrix work to land
+    auto interleave = [&]() {
+#if IE_PIPE == 2
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            constexpr int per = (RD + NMF - 1) / NMF;
+            __builtin_amdgcn_sched_group_barrier(0x100, per, 0);  // LDS read
+        }
+#else
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);  // MFMAs
+#endif
+    };
+
     // Trips of NU steps with no exit inside: the loads of the next stages stay
     // in flight across the back edge (an exit inside the trip would make the
     // loop head wait for all of them).  The last nk % NU steps follow the loop.
     if constexpr (ONE) {
         // nk <= 1: the stage loaded above is the whole contraction
         if (nk > 0) compute(lds);
+    } else if constexpr (IE_PIPE && !KS) {
+        static_assert(BK / 32 % 2 == 0, "sub-step parity picks the fragment set");
+        rdfrag(lds, 0, fa[0], fb[0]);
+        auto step = [&](const int uu, const int s) {
+            const int u = uu % NS;
+            la.load(kb + (s + NS) * BK, ke, ra[u]);
+            lb.load(kb + (s + NS) * BK, ke, rb[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            const int8_t *cur = lds + (uu & 1) * STAGE;
+#pragma unroll
+            for (int ks = 0; ks + 1 < BK / 32; ++ks) {
+                rdfrag(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                mma(fa[ks & 1], fb[ks & 1]);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // stage s + 1 into the other buffer, whose readers all passed
+            // the previous barrier (past the end: zeros nobody reads)
+            la.store(lds + ((uu + 1) & 1) * STAGE, tid, ra[(u + 1) % NS]);
+            lb.store(lds + ((uu + 1) & 1) * STAGE + LA::BYTES, tid, rb[(u + 1) % NS]);
+            __syncthreads();
+            rdfrag(lds + ((uu + 1) & 1) * STAGE, 0, fa[0], fb[0]);
+            mma(fa[1], fb[1]);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        constexpr int NU = NS % 2 ? 4 * NS : IE_UNROLL * NS;  // even: step parity picks the LDS buffer
+        const int full = nk - nk % NU;
+        for (int it = 0; it < full; it += NU) {
+#pragma unroll
+            for (int uu = 0; uu < NU; ++uu) step(uu, it + uu);
+        }
+#pragma unroll
+        for (int uu = 0; uu < NU - 1; ++uu) {
+            if (full + uu >= nk) break;
+            step(uu, full + uu);
+        }
     } else {
         auto step = [&](const int uu, const int s) {
             const int u = uu % NS;
