@@ -162,10 +162,14 @@ bool pair_tiles_built(Tile t1, Tile t2);
 //         reads the operands again but saves 4 bytes per output element).
 enum PlanMode { PLAN_DIRECT = 0, PLAN_RTO = 1, PLAN_SPLIT = 2, PLAN_RECOMP = 3 };
 
-// Row-grouped results with contractions of at most this many bytes
-// recompute instead of two-pass rounding (RECOMP instead of RTO);
+// Row-grouped results with contractions of at most this many bytes (one
+// step) recompute instead of two-pass rounding (RECOMP instead of RTO);
 // whole-tensor results choose by contraction and width (plan_product).
-constexpr long long RECOMP_KMAX = 512;
+// Measured on row-grouped products whose rows span several 128-wide tiles,
+// round to odd against recompute: 50432 x 576 x 192 59.0 vs 64.6 us,
+// 50432 x 768 x 192 71.9 vs 78.6, 25216 x 3072 x 256 133.7 vs 160.9,
+// 25216 x 3072 x 512 159.0 vs 205.5.
+constexpr long long RECOMP_KMAX = 128;
 // Workgroups of the first pass of a recomputed whole-tensor product (a
 // persistent grid; each writes one maximum).
 int recomp_grid(long long M, long long N, long long K, Tile t);
