@@ -229,16 +229,12 @@ ie_status ie_sgd_update_multi(int32_t n, const ie_mat *W, const ie_mat *V, const
 /*
  * Forward products with the activation fused into their output (Table 7:
  * the clip acts on the rounded mantissas, the exponents are those of the
- * plain product).  act: IE_ACT_NONE (same as ie_linear_fwd / ie_conv_fwd),
- * IE_ACT_RELU (C -> max(C, 0)) or IE_ACT_RELU6 (C -> min(max(C, 0), c),
- * c = floor(6 * 2^-e) and at most Y's largest mantissa 2^(bits-1) - 1, e the
- * result's group exponent: exactly ie_relu_fwd with relu6 = 1 applied to the
- * plain product); other values return IE_ERR_UNSUPPORTED.  Arguments,
- * limits and workspace sizes as for the plain entry points.
+ * plain product).  act: IE_ACT_NONE (same as ie_linear_fwd / ie_conv_fwd) or
+ * IE_ACT_RELU; other values return IE_ERR_UNSUPPORTED.  Arguments, limits
+ * and workspace sizes as for the plain entry points.
  */
 #define IE_ACT_NONE 0
 #define IE_ACT_RELU 1
-#define IE_ACT_RELU6 2
 ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act,
                             void *ws, size_t ws_bytes, void *stream);
 ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W,

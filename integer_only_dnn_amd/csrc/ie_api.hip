@@ -531,7 +531,7 @@ static ie_status linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, v
     Operand B{LD_K, wsrc, Kp, (int)N, {}};
     ExpSrc ea{X->exp, nullptr, X->group == IE_GROUP_ROW};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, M, N, Kp, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr, mat_q(Y)});
+    return run_product(A, B, M, N, Kp, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr});
 }
 
 ie_status ie_linear_fwd(const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws, size_t ws_bytes,
@@ -554,8 +554,8 @@ ie_status ie_linear_fwd_noalloc(const ie_mat *X, const ie_mat *W, const ie_mat *
 
 ie_status ie_linear_fwd_act(const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act, void *ws, size_t ws_bytes,
                             void *stream) {
-    if (act != IE_ACT_NONE && act != IE_ACT_RELU && act != IE_ACT_RELU6) return IE_ERR_UNSUPPORTED;
-    return linear_fwd(X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU6 ? 2 : act == IE_ACT_RELU ? 1 : 0);
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    return linear_fwd(X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
 static ie_status linear_bwd_dx(const ie_mat *dY, const ie_mat *W, const ie_mat *dX, void *ws, size_t ws_bytes,
@@ -686,7 +686,7 @@ static ie_status conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *
     Operand B{LD_K, wsrc, kg, g.k, {}};
     ExpSrc ea{X->exp, nullptr, 0};
     ExpSrc eb{W->exp, nullptr, W->group == IE_GROUP_ROW};
-    return run_product(A, B, npq, g.k, kg, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr, mat_q(Y)});
+    return run_product(A, B, npq, g.k, kg, ea, eb, Y, w.pw, flags, st, Act{relu, nullptr});
 }
 
 ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, void *ws,
@@ -696,8 +696,8 @@ ie_status ie_conv_fwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, c
 
 ie_status ie_conv_fwd_act(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *Y, int act,
                           void *ws, size_t ws_bytes, void *stream) {
-    if (act != IE_ACT_NONE && act != IE_ACT_RELU && act != IE_ACT_RELU6) return IE_ERR_UNSUPPORTED;
-    return conv_fwd(d, X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU6 ? 2 : act == IE_ACT_RELU ? 1 : 0);
+    if (act != IE_ACT_NONE && act != IE_ACT_RELU) return IE_ERR_UNSUPPORTED;
+    return conv_fwd(d, X, W, Y, ws, ws_bytes, stream, act == IE_ACT_RELU);
 }
 
 static ie_status conv_bwd(const ie_conv_desc *d, const ie_mat *X, const ie_mat *W, const ie_mat *dY,

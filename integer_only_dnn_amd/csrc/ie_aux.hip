@@ -435,7 +435,7 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
     __shared__ int rowe[256];
     const uint32_t per_row = N / vw;
     // eight values held in registers -> eight bytes at out + o
-    auto store8 = [&](long long o, const v4i &v, int sh_, int e_) {
+    auto store8 = [&](long long o, const v4i &v, int sh_) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -444,11 +444,11 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
             if (j < 2) lo |= b << (16 * j);
             else hi |= b << (16 * (j - 2));
         }
-        lo = act4(lo, act, o, e_);
-        hi = act4(hi, act, o + 4, e_);
+        lo = act4(lo, act, o);
+        hi = act4(hi, act, o + 4);
         *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
     };
-    auto round8 = [&](long long o, int sh_, int e_) {
+    auto round8 = [&](long long o, int sh_) {
         if (vw == 8) {
             v4i v = *(const v4i *)(v16 + o);
             uint32_t lo = 0, hi = 0;
@@ -459,11 +459,11 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
                 if (j < 2) lo |= b << (16 * j);
                 else hi |= b << (16 * (j - 2));
             }
-            lo = act4(lo, act, o, e_);
-            hi = act4(hi, act, o + 4, e_);
+            lo = act4(lo, act, o);
+            hi = act4(hi, act, o + 4);
             *(v2i *)(out + o) = v2i{(int)lo, (int)hi};
         } else {
-            out[o] = (int8_t)act1(rne_shift32(v16[o], sh_), act, o, e_);
+            out[o] = (int8_t)act1(rne_shift32(v16[o], sh_), act, o);
         }
     };
     if (!row_group) {
@@ -508,8 +508,8 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
             for (int u = 0; u < U; ++u) {
                 if (i0 + 256 * u >= total) break;
                 const int sh_ = eT - (t[u] == P_NONE ? P_NONE : t[u] - 2);
-                if (vw == 8) store8(o[u], v[u], sh_, eT);
-                else round8(o[u], sh_, eT);
+                if (vw == 8) store8(o[u], v[u], sh_);
+                else round8(o[u], sh_);
             }
         }
         if (bid == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
@@ -552,7 +552,7 @@ __device__ __forceinline__ void rto_finalize_body(const int16_t *v16, const int1
             const uint32_t lr = fdiv32(i, dper);
             const int c0 = (int)(i - lr * per_row) * vw;
             const int t = staged ? needs[lr * n_ct + (c0 >> lbn)] : pr[c0 >> lbn];
-            round8((r0 + lr) * N + c0, rowe[lr] - (t == P_NONE ? P_NONE : t - 2), rowe[lr]);
+            round8((r0 + lr) * N + c0, rowe[lr] - (t == P_NONE ? P_NONE : t - 2));
         }
         __syncthreads();
     }
@@ -744,8 +744,8 @@ __global__ __launch_bounds__(256) void round_sums_kernel(const long long *sums, 
         }
         uint32_t w = 0;
         for (int j = 0; j < vw; ++j) w |= (uint32_t)(uint8_t)rne_shift64(sv[j], e - ev[j]) << (8 * j);
-        if (vw == 4) *(uint32_t *)(out + o) = act4(w, act, o, e);
-        else out[o] = (int8_t)act1((int)(int8_t)w, act, o, e);
+        if (vw == 4) *(uint32_t *)(out + o) = act4(w, act, o);
+        else out[o] = (int8_t)act1((int)(int8_t)w, act, o);
         if (row_group && c0 == 0) out_exp[row] = (int8_t)e;
     }
     if (!row_group && blockIdx.x == 0 && threadIdx.x == 0) out_exp[0] = (int8_t)eT;
@@ -935,10 +935,10 @@ __device__ __forceinline__ void split_round_body(const int *partial, int splits,
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     w |= (uint32_t)(uint8_t)rne_shift64(v[k][j], e - eps(4 * c + j)) << (8 * j);
-                *(uint32_t *)(orow + 4 * c) = act4(w, act, (long long)row * Nout + 4 * c, e);
+                *(uint32_t *)(orow + 4 * c) = act4(w, act, (long long)row * Nout + 4 * c);
             } else {
                 const int cv = (int)rne_shift64(v[k][0], e - eps(c));
-                orow[c] = (int8_t)act1(cv, act, (long long)row * Nout + c, e);
+                orow[c] = (int8_t)act1(cv, act, (long long)row * Nout + c);
             }
         }
         __syncthreads();

@@ -90,27 +90,9 @@ __device__ __forceinline__ uint32_t relu4(uint32_t w) {
 // (input gradients: a result stays where the matching mask byte is
 // positive, else it becomes zero).
 struct Act {
-    int relu;            // 1: ReLU of the results; 2: ReLU6 (also capped, below)
-    const int8_t *mask;  // results kept where this byte is positive (ReLU backward)
-    int q;               // ReLU6: the results' width, |C| <= 2^q - 1
+    int relu;
+    const int8_t *mask;
 };
-
-// ReLU6's cap on mantissas at exponent e: floor(6 * 2^-e), at most 2^q - 1
-// (q <= 7; Table 7).
-__device__ __forceinline__ int relu6_cap(int e, int q) {
-    if (e >= 3) return 0;
-    const int c = e >= 0 ? 6 >> e : (-e >= 5 ? 192 : 6 << -e);
-    return min(c, (1 << q) - 1);
-}
-
-// Each byte of w (all in [0, 127]) capped at c (0 <= c <= 127): a byte at or
-// above c is replaced by c.
-__device__ __forceinline__ uint32_t cap4(uint32_t w, int c) {
-    const uint32_t c4 = (uint32_t)c * 0x01010101u;
-    const uint32_t ge = (((w | 0x80808080u) - c4) & 0x80808080u) >> 7;  // no borrow between bytes
-    const uint32_t m = ge * 0xffu;
-    return (w & ~m) | (c4 & m);
-}
 
 // The bytes of w whose matching byte of x is positive; the others zero.
 __device__ __forceinline__ uint32_t pos_mask4(uint32_t w, uint32_t x) {
@@ -118,19 +100,17 @@ __device__ __forceinline__ uint32_t pos_mask4(uint32_t w, uint32_t x) {
     return w & (((nz & ~x) >> 7) * 0xffu);                                // ... and the sign bit clear
 }
 
-// Four results at out + o, all of one group with exponent e (o a multiple
-// of 4 when a.mask is set; the mask 4-byte aligned).
-__device__ __forceinline__ uint32_t act4(uint32_t w, const Act &a, long long o, int e) {
+// Four results at out + o (o a multiple of 4 when a.mask is set; the mask
+// 4-byte aligned).
+__device__ __forceinline__ uint32_t act4(uint32_t w, const Act &a, long long o) {
     if (a.relu) w = relu4(w);
-    if (a.relu == 2) w = cap4(w, relu6_cap(e, a.q));
     if (a.mask) w = pos_mask4(w, *(const uint32_t *)(a.mask + o));
     return w;
 }
 
-// One result at out + o, of a group with exponent e.
-__device__ __forceinline__ int act1(int c, const Act &a, long long o, int e) {
+// One result at out + o.
+__device__ __forceinline__ int act1(int c, const Act &a, long long o) {
     if (a.relu && c < 0) c = 0;
-    if (a.relu == 2) c = min(c, relu6_cap(e, a.q));
     if (a.mask && a.mask[o] <= 0) c = 0;
     return c;
 }

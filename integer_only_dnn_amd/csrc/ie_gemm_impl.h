@@ -1047,12 +1047,6 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
     auto TR = [&](int a, int r) { return tr0 + a * 32 + 8 * (r >> 2) + (r & 3); };
     auto TC = [&](int b) { return tc0 + b * 32; };
 
-    // The int8 results' exponent, for the activation (ReLU6's cap): one for
-    // the tile, or with row groups that of each tile row, fe_off[row] +
-    // seA[row] (fe_off set by the row-group epilogue, in LDS).
-    int fe = 0;
-    const int *fe_off = nullptr;
-
     // Results leave through LDS: every lane writes its values into a
     // row-major staging tile (element size ES bytes, row pitch padded so that
     // the two half-waves, four rows apart, hit different banks), then the
@@ -1082,17 +1076,15 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
                 // the activation on the rounded bytes (mask bytes at the
                 // results' own offsets)
                 const long long o = (long long)grow * ld + gcol;
-                const int ee = fe_off ? fe_off[row] + seA[row] : fe;
                 if (vec && gcol + EPC <= N) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = (int)act4((uint32_t)v[k], ep.act, o + 4 * k, ee);
+                    for (int k = 0; k < 4; ++k) v[k] = (int)act4((uint32_t)v[k], ep.act, o + 4 * k);
                 } else if (ep.act.relu || ep.act.mask) {
                     const int n = min(16, N - gcol);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         uint32_t w = (uint32_t)v[k];
                         if (ep.act.relu) w = relu4(w);
-                        if (ep.act.relu == 2) w = cap4(w, relu6_cap(ee, ep.act.q));
                         if (ep.act.mask) {
                             uint32_t x = 0;
                             for (int j = 0; j < 4; ++j)
@@ -1239,7 +1231,6 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
             int e = 0, p = 0;
             if (direct) {
                 e = clamp_exp_flag(max(E_MIN, gmax), ep.flags);
-                fe = e;
                 if (tid == 0 && bid == 0) ep.out_exp[0] = (int8_t)e;
             } else {
                 // round to odd two bits below the tile's own need; the tile's
@@ -1352,7 +1343,6 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
             // every element's need and shift are computed in integers.
             int *rowi = scr - 2 * BMt;              // per tile row: integer offset
             float *rowf = (float *)(scr - BMt);     //   or fp32 scale
-            fe_off = rowi;                          // direct: the row's exponent - seA
             int lo = ebv[0], hi = ebv[0];
 #pragma unroll
             for (int b = 1; b < NI; ++b) {

@@ -15,6 +15,13 @@
 
 namespace ie {
 
+// floor(6 * 2^-e), at most 2^q - 1 (q <= 7)
+__device__ __forceinline__ int relu6_cap(int e, int q) {
+    if (e >= 3) return 0;
+    const int c = e >= 0 ? 6 >> e : (-e >= 5 ? 192 : 6 << -e);
+    return min(c, (1 << q) - 1);
+}
+
 // Walks the bytes of one 16-byte chunk of a row-major [rows x cols] buffer
 // (flat byte offset f0) with the row of each byte; `row`/`next` track the
 // current row and the flat offset where the next row begins.

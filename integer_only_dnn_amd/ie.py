@@ -318,7 +318,7 @@ def ie_bmm_tn(batch: int, A: Mat, B: Mat, C: Mat, ws: Workspace) -> None:
     _bmm("ie_bmm_tn", batch, A, B, C, ws)
 
 
-ACT_NONE, ACT_RELU, ACT_RELU6 = 0, 1, 2
+ACT_NONE, ACT_RELU = 0, 1
 
 
 def ie_linear_fwd_act(X: Mat, W: Mat, Y: Mat, act: int, ws: Workspace) -> None:

@@ -150,14 +150,12 @@ def test_pointwise_argument_errors():
     assert L.ie_add(by(A), by(B), by(_mat(4, 8)), 1, 16, None) == 4
     assert L.ie_add(by(A), by(_mat(4, 7)), by(_mat(4, 8)), 1, 1 << 20, None) == 2
     assert L.ie_add_workspace(4, 8) >= 256
-    # fused activations: none, ReLU and ReLU6 forward; none and ReLU backward
+    # fused activations: only none and ReLU
     X, W, Y = _mat(4, 8), _mat(3, 8), _mat(4, 3)
-    assert L.ie_linear_fwd_act(by(X), by(W), by(Y), 3, 1, 1 << 20, None) == 6
+    assert L.ie_linear_fwd_act(by(X), by(W), by(Y), 2, 1, 1 << 20, None) == 6
     d = ie.conv_desc(2, 8, 8, 16, 32, 3, 3, 1, 1)
     assert L.ie_conv_fwd_act(by(d), by(_mat(128, 16)), by(_mat(32, 144)), by(_mat(128, 32)), 5, 1, 1 << 30,
                              None) == 6
-    assert L.ie_linear_bwd_dx_act(by(_mat(4, 3)), by(_mat(3, 8)), by(X), by(_mat(4, 8)), ie.ACT_RELU6, 1, 1 << 20,
-                                  None) == 6
 
 
 @pytest.mark.parametrize("force", ["1,1,0,1", "2,2,0", "0,1", "1,0,1", "3,1,1", "4,4,1", "8,8,1", "1,1,7"])

@@ -141,61 +141,6 @@ def test_fused_relu_plans(tile, mode, ws, plan):
     assert ws.status() == 0
 
 
-def _relu6(t: o.QT, bits: int = 8) -> o.QT:
-    """The oracle's ReLU6 of every result group at its own exponent."""
-    m = np.asarray(t.mant)
-    if t.group == T:
-        c = o.relu6_fwd(m, int(t.exp[0]), bits)
-    else:
-        m2 = m.reshape(m.shape[0], -1)
-        c = np.stack([o.relu6_fwd(m2[i], int(t.exp[i]), bits) for i in range(m2.shape[0])]).reshape(m.shape)
-    return o.QT(c.astype(np.int8), t.exp, t.group)
-
-
-@pytest.mark.parametrize("tile", [(2, 2), (1, 1), (2, 1)], ids=lambda t: f"{64 * t[0]}x{64 * t[1]}")
-@pytest.mark.parametrize("mode", [(0, 1)] + MODES, ids=lambda m: f"m{m[0]}s{m[1]}")
-def test_fused_relu6_plans(tile, mode, ws, plan):
-    """ReLU6 fused into the forward products' output equals the oracle's
-    ReLU6 of the plain product, the cap taken at each result group's own
-    exponent, through every epilogue, with rows of 16-byte multiples and
-    ragged ones.  The activation's row exponents step through ten values, so
-    that the results' exponents, and with them the caps (127 down to 0),
-    change from row to row; whole-tensor results take caps 24, 3 and 0; a
-    5-bit output caps at its largest mantissa 15."""
-    direct = mode[0] == 0
-    shapes = ([(64 * tile[0] - 3, 64 * tile[1] - 5, 200), (64 * tile[0], 64 * tile[1], 200)] if direct
-              else [(200, 150, 392), (200, 160, 392)])
-    rng = np.random.default_rng(5 * tile[0] + tile[1] + 19 * mode[0] + mode[1])
-    plan(tile, *mode)
-    for M, N, K in shapes:
-        announce(f"fused relu6 tile={tile} mode={mode} M={M} N={N} K={K}")
-        Xm = rand_qt(rng, (M, K), R).mant
-        X = o.QT(Xm, (-18 + np.arange(M) % 10).astype(np.int8), R)
-        W = rand_qt(rng, (N, K), R, elo=0, ehi=0)
-        Xd, Wd = qt_to_dev(X), qt_to_dev(W)
-        for gy in (T, R):
-            Y = ie.Mat.empty(M, N, gy)
-            ie.ie_linear_fwd_act(Xd, Wd, Y, ie.ACT_RELU6, ws)
-            assert_same(Y, _relu6(o.linear_fwd(X, W, gy)), f"linear relu6 group {gy}")
-        Y5 = ie.Mat.empty(M, N, R, bits=5)
-        ie.ie_linear_fwd_act(Xd, Wd, Y5, ie.ACT_RELU6, ws)
-        assert_same(Y5, _relu6(o.linear_fwd(X, W, R, 5), 5), "linear relu6 5 bits")
-        for ex in (-14, -11, -8):
-            Xt = o.QT(Xm, np.array([ex], np.int8), T)
-            Y = ie.Mat.empty(M, N, T)
-            ie.ie_linear_fwd_act(qt_to_dev(Xt), Wd, Y, ie.ACT_RELU6, ws)
-            assert_same(Y, _relu6(o.linear_fwd(Xt, W, T)), f"linear relu6 tensor x_exp {ex}")
-    if not direct:
-        shape = (2, 10, 10, 32, 40, 3, 3, 1, 1)
-        d, dd = o.ConvShape(*shape), ie.conv_desc(*shape)
-        Xc = rand_qt(rng, (2, 10, 10, 32), T, elo=-12, ehi=-12, zero_frac=0.2)
-        Wc = rand_qt(rng, (40, 288), R, elo=-1, ehi=1)
-        Y = ie.Mat.empty(2 * d.p * d.q, 40, T)
-        ie.ie_conv_fwd_act(dd, qt_to_dev(Xc, rows=200), qt_to_dev(Wc), Y, ie.ACT_RELU6, ws)
-        assert_same(Y, _relu6(o.conv_fwd(d, Xc, Wc, T)), "conv relu6")
-    assert ws.status() == 0
-
-
 # 24 channels: the input gradient reads a transposed, aligned copy of W;
 # 32 / 48 channels with a whole-tensor W: it reads W in place
 CONV_CASES = [(2, 10, 10, 24, 40, 3, 3, 1, 1), (2, 9, 9, 24, 40, 3, 3, 2, 1),
