@@ -763,7 +763,10 @@ struct TileLds1 {
 // most one step, loaded once, with no pipeline and no second buffer).
 // Returns the tile's group maximum in the first pass of a recomputed
 // whole-tensor product (EPI_MAX), NEED_NONE otherwise.
-template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false, int MODE = -1>
+// RG: the result groups when fixed at compile time (0: one for the whole
+// tensor, 1: one per row; -1: ep.row_group decides), so that a kernel that
+// only ever takes one of them carries no code for the other.
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false, int MODE = -1, int RG = -1>
 __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int M_, int N, int K, int k_chunk,
                                           int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
@@ -832,7 +835,7 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
     // maxima, loaded now so that they land during the main loop
     int given = NEED_NONE;
     if constexpr (!PARTIAL) {
-        if (ep.mode == EPI_GIVEN && !ep.row_group)
+        if (ep.mode == EPI_GIVEN && !(RG >= 0 ? RG == 1 : ep.row_group))
             for (int i = tid; i < ep.tneed_n; i += NTHR) given = max(given, ep.tneed[i]);
     }
 
@@ -1163,7 +1166,7 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
         const int mode = MODE >= 0 ? MODE : ep.mode;
         const bool direct = mode == EPI_DIRECT || mode == EPI_GIVEN;  // int8 results from this pass
 
-        if (!ep.row_group) {
+        if (!(RG >= 0 ? RG == 1 : ep.row_group)) {
             // whole-tensor group: one maximum for the tile (or, in the second
             // pass of a recomputed product, the first pass's maxima)
             int tmax;
@@ -1584,8 +1587,8 @@ void gemm_pair_kernel(PairPart p1, PairPart p2, int g1) {
     const int b = blockIdx.x;
     if (b < g1) {
         if (b < p1.nblk)
-            gemm_tile<KA1, KB1, MI1, NI1, false>(p1.A, p1.B, p1.M, p1.N, p1.K, p1.k_chunk, p1.TM, p1.S, p1.ep, b,
-                                                 p1.nblk, lds);
+            gemm_tile<KA1, KB1, MI1, NI1, false, false, -1, 0>(p1.A, p1.B, p1.M, p1.N, p1.K, p1.k_chunk, p1.TM,
+                                                                 p1.S, p1.ep, b, p1.nblk, lds);
     } else {
         gemm_tile<KA2, KB2, MI2, NI2, true>(p2.A, p2.B, p2.M, p2.N, p2.K, p2.k_chunk, p2.TM, p2.S, p2.ep, b - g1,
                                             p2.nblk, lds);
@@ -1611,6 +1614,8 @@ inline PairPart pair_part(const Operand &A, const Operand &B, int M, int N, int 
 
 template <int KA1, int KB1, int MI1, int NI1, int KA2, int KB2, int MI2, int NI2>
 hipError_t launch_pair(const PairPart &p1, const PairPart &p2, hipStream_t st) {
+    // the input-gradient part is built for one whole-tensor group only
+    if (p1.ep.row_group) return hipErrorInvalidValue;
     const int g1 = (p1.nblk + 7) / 8 * 8;
     const int kind = 1000000 * (10 * MI2 + NI2) + 10000 * (10 * MI1 + NI1) + 1000 + 100 * 3 + 10 * KA1 + KB1;
     prof_begin(st, kind);
@@ -1660,13 +1665,15 @@ __global__ __launch_bounds__(NTHR, (Occ<MI, NI>::value)) void gemm_batched_kerne
     if (ep.v16) ep.v16 += z * ba.out;
     if (ep.out_exp) ep.out_exp += z * ba.out_exp;
     if (ep.p16) ep.p16 += z * ba.p16;
-    gemm_tile<KA, KB, MI, NI, false, ONE>(A, B, M, N, K, K, TM, 1, ep, block_of_tile(tm * TN + tn, T), T, lds);
+    gemm_tile<KA, KB, MI, NI, false, ONE, -1, 1>(A, B, M, N, K, K, TM, 1, ep, block_of_tile(tm * TN + tn, T), T,
+                                                 lds);
 }
 
 template <int KA, int KB, int MI, int NI, bool ONE = false>
 hipError_t launch_batched_one(const Operand &A, const Operand &B, int M, int N, int K, const Epi &ep,
                               const BatchArgs &ba, hipStream_t st) {
     if (ONE && K > BK) return hipErrorInvalidValue;
+    if (!ep.row_group) return hipErrorInvalidValue;  // the kernel is built for row groups only
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     const long long blocks = (long long)TM * TN * ba.Z;
     if (blocks <= 0) return hipSuccess;
