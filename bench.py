@@ -78,14 +78,23 @@ OTHER = {2000: ("sgd_pass0", "sgd_rows_kernel"), 2001: ("sgd_pass1", "sgd_rows_k
 
 
 ONE_KIND = 99000000  # added to the code of a one-step (K <= 128) contraction kernel
+ROW_KIND = 200000000  # added to the code of a kernel built for row-grouped results
 
 
 def is_gemm(kind: int) -> bool:
     return kind >= 10000 and 1000 <= kind % 10000 < 2000
 
 
+def is_row(kind: int) -> bool:
+    return is_gemm(kind) and kind >= ROW_KIND
+
+
+def _base(kind: int) -> int:
+    return kind - ROW_KIND if is_row(kind) else kind
+
+
 def is_one(kind: int) -> bool:
-    return kind >= ONE_KIND
+    return _base(kind) >= ONE_KIND
 
 
 def is_pair(kind: int) -> bool:
@@ -102,6 +111,8 @@ def _decode(kind: int):
 def kind_name(kind: int) -> str:
     if not is_gemm(kind):
         return OTHER.get(kind, (str(kind), ""))[0]
+    if is_row(kind):
+        return kind_name(_base(kind)) + "_rows"
     if is_one(kind):
         return kind_name(kind - ONE_KIND) + "_1step"
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
@@ -114,19 +125,21 @@ def kind_symbol(kind: int) -> str:
     """The kernel's name as rocprofv3 reports it."""
     if not is_gemm(kind):
         return OTHER.get(kind, ("", str(kind)))[1]
+    rg = 1 if is_row(kind) else 0
+    kind = _base(kind)
     if is_one(kind):
         mi, ni, _, _, ka, kb, epi = _decode(kind - ONE_KIND)
         if epi == 8:
-            return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, true>"
-        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, true>"
+            return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, true, {rg}>"
+        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, true, {rg}>"
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
     if epi in (4, 5, 6, 7):
         return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi >= 6 else 'false'}>"
     if epi == 8:
-        return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, false>"
-    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}, false>"
+        return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, false, {rg}>"
+    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}, false, {rg}>"
 
 
 # ---------------------------------------------------------------------------

@@ -1516,14 +1516,20 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
 // ONE: the contraction is at most one step (K <= BK; not for split
 // contractions), so the tile loads it once into a single LDS stage and more
 // workgroups fit a CU.
-template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false>
+// RG: the result groups it is built for (0 whole tensor, 1 rows; split
+// products, whose int32 partials have no groups yet, take 0).
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE, int RG>
 __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_i8_kernel(
     Operand A, Operand B, int M, int N, int K, int k_chunk, int TM, int S, Epi ep) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     __shared__ __attribute__((aligned(16)))
     int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, PARTIAL>::value];
-    gemm_tile<KA, KB, MI, NI, PARTIAL, ONE>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
+    gemm_tile<KA, KB, MI, NI, PARTIAL, ONE, -1, RG>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
 }
+
+// Kind codes of kernels built for row groups: the code of the whole-tensor
+// kernel plus ROW_KIND.
+constexpr int ROW_KIND = 200000000;
 
 // Kind codes of one-step kernels for the timing records: the code of the
 // plain kernel plus ONE_KIND.
@@ -1534,17 +1540,18 @@ constexpr int ONE_KIND = 99000000;
 // item % 8 on the workgroup's XCD), finding group maxima without storing
 // values.  Whole-tensor groups: each workgroup writes its running maximum to
 // tneed[blockIdx.x]; row groups: the tiles write tneed[row][column tile].
-template <int KA, int KB, int MI, int NI, bool ONE>
+template <int KA, int KB, int MI, int NI, bool ONE, int RG>
 __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_max_kernel(
     Operand A, Operand B, int M, int N, int K, int TM, int items, Epi ep) {
     __shared__ __attribute__((aligned(16)))
     int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, false>::value];
     int run = NEED_NONE;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE, EPI_MAX>(A, B, M, N, K, K, TM, 1, ep, item, items, lds));
+        run = max(run, gemm_tile<KA, KB, MI, NI, false, ONE, EPI_MAX, RG>(A, B, M, N, K, K, TM, 1, ep, item, items,
+                                                                          lds));
         __syncthreads();  // the next item's stages reuse the LDS
     }
-    if (!ep.row_group && threadIdx.x == 0) ep.tneed[blockIdx.x] = run;
+    if (RG == 0 && threadIdx.x == 0) ep.tneed[blockIdx.x] = run;
 }
 
 template <int KA, int KB, int MI, int NI>
@@ -1555,14 +1562,26 @@ hipError_t launch_max(const Operand &A, const Operand &B, int M, int N, int K, c
     if (grid <= 0) return hipSuccess;
     if (!ep.row_group && ep.tneed_n != grid) return hipErrorInvalidValue;
     const bool one = K <= BK;
-    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * EPI_MAX + 10 * KA + KB + (one ? ONE_KIND : 0);
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * EPI_MAX + 10 * KA + KB + (one ? ONE_KIND : 0) +
+                     (ep.row_group ? ROW_KIND : 0);
     prof_begin(st, kind);
-    if (one)
-        hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI, true>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K,
+    auto go = [&](auto one_tag, auto rg_tag) {
+        constexpr bool O = decltype(one_tag)::value;
+        constexpr int R = decltype(rg_tag)::value;
+        hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI, O, R>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K,
                            TM, items, ep);
-    else
-        hipLaunchKernelGGL((gemm_max_kernel<KA, KB, MI, NI, false>), dim3(grid), dim3(NTHR), 0, st, A, B, M, N, K,
-                           TM, items, ep);
+    };
+    using T1 = std::true_type;
+    using F1 = std::false_type;
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    if (one) {
+        if (ep.row_group) go(T1{}, R1{});
+        else go(T1{}, R0{});
+    } else {
+        if (ep.row_group) go(F1{}, R1{});
+        else go(F1{}, R0{});
+    }
     prof_end(st, kind);
     return hipGetLastError();
 }
@@ -1692,18 +1711,30 @@ hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, i
     const int TM = (M + 64 * MI - 1) / (64 * MI), TN = (N + 64 * NI - 1) / (64 * NI);
     dim3 grid(TM * TN * splits, 1, 1);
     const bool one = !PARTIAL && K <= BK;
-    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB + (one ? ONE_KIND : 0);
+    const bool rows = !PARTIAL && ep.row_group;
+    const int kind = 10000 * (10 * MI + NI) + 1000 + 100 * (PARTIAL ? 2 : ep.mode) + 10 * KA + KB +
+                     (one ? ONE_KIND : 0) + (rows ? ROW_KIND : 0);
     prof_begin(st, kind);
     if constexpr (!PARTIAL) {
+        auto go = [&](auto one_tag, auto rg_tag) {
+            constexpr bool O = decltype(one_tag)::value;
+            constexpr int R = decltype(rg_tag)::value;
+            hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, false, O, R>), grid, dim3(NTHR), 0, st, A, B, M, N,
+                               K, k_chunk, TM, splits, ep);
+        };
+        using R0 = std::integral_constant<int, 0>;
+        using R1 = std::integral_constant<int, 1>;
         if (one) {
-            hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, false, true>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
-                               k_chunk, TM, splits, ep);
-            prof_end(st, kind);
-            return hipGetLastError();
+            if (rows) go(std::true_type{}, R1{});
+            else go(std::true_type{}, R0{});
+        } else {
+            if (rows) go(std::false_type{}, R1{});
+            else go(std::false_type{}, R0{});
         }
+    } else {
+        hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, true, false, 0>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
+                           k_chunk, TM, splits, ep);
     }
-    hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, PARTIAL>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
-                       k_chunk, TM, splits, ep);
     prof_end(st, kind);
     return hipGetLastError();
 }
