@@ -131,7 +131,7 @@ def kind_symbol(kind: int) -> str:
         mi, ni, _, _, ka, kb, epi = _decode(kind - ONE_KIND)
         if epi == 8:
             return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, true, {rg}>"
-        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, true, {rg}>"
+        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, true, {rg}, {0 if epi == 1 else 1}>"
     mi, ni, mi2, ni2, ka, kb, epi = _decode(kind)
     if is_pair(kind):
         return f"gemm_pair_kernel<{ka}, {kb}, {mi}, {ni}, 1, 4, {mi2}, {ni2}>"
@@ -139,7 +139,9 @@ def kind_symbol(kind: int) -> str:
         return f"gemm_batched_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi >= 6 else 'false'}>"
     if epi == 8:
         return f"gemm_max_kernel<{ka}, {kb}, {mi}, {ni}, false, {rg}>"
-    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, {'true' if epi == 2 else 'false'}, false, {rg}>"
+    if epi == 2:
+        return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, true, false, 0, 0>"
+    return f"gemm_i8_kernel<{ka}, {kb}, {mi}, {ni}, false, false, {rg}, {0 if epi == 1 else 1}>"
 
 
 # ---------------------------------------------------------------------------

@@ -765,8 +765,10 @@ struct TileLds1 {
 // whole-tensor product (EPI_MAX), NEED_NONE otherwise.
 // RG: the result groups when fixed at compile time (0: one for the whole
 // tensor, 1: one per row; -1: ep.row_group decides), so that a kernel that
-// only ever takes one of them carries no code for the other.
-template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false, int MODE = -1, int RG = -1>
+// only ever takes one of them carries no code for the other.  DI likewise
+// for the epilogue: 1 rounds to int8 in this pass (direct, or the second
+// pass of a recomputed product), 0 rounds to odd; -1: ep.mode decides.
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE = false, int MODE = -1, int RG = -1, int DI = -1>
 __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int M_, int N, int K, int k_chunk,
                                           int TM, int S, const Epi &ep, int bid, int nblk, int8_t *lds) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
@@ -1164,7 +1166,8 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
         const int ea0 = seA[0];
         const int eb0 = seB[0];
         const int mode = MODE >= 0 ? MODE : ep.mode;
-        const bool direct = mode == EPI_DIRECT || mode == EPI_GIVEN;  // int8 results from this pass
+        // int8 results from this pass
+        const bool direct = DI >= 0 ? DI == 1 : (mode == EPI_DIRECT || mode == EPI_GIVEN);
 
         if (!(RG >= 0 ? RG == 1 : ep.row_group)) {
             // whole-tensor group: one maximum for the tile (or, in the second
@@ -1516,15 +1519,17 @@ __device__ __forceinline__ int gemm_tile(const Operand &A, const Operand &B, int
 // ONE: the contraction is at most one step (K <= BK; not for split
 // contractions), so the tile loads it once into a single LDS stage and more
 // workgroups fit a CU.
-// RG: the result groups it is built for (0 whole tensor, 1 rows; split
-// products, whose int32 partials have no groups yet, take 0).
-template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE, int RG>
+// RG: the result groups it is built for (0 whole tensor, 1 rows); DI: its
+// epilogue (1 int8 in this pass, 0 round to odd).  Split products, whose
+// int32 partials have neither yet, take 0 and 0.
+template <int KA, int KB, int MI, int NI, bool PARTIAL, bool ONE, int RG, int DI>
 __global__ __launch_bounds__(NTHR, (ONE ? Occ1<MI, NI>::value : Occ<MI, NI>::value)) void gemm_i8_kernel(
     Operand A, Operand B, int M, int N, int K, int k_chunk, int TM, int S, Epi ep) {
     static_assert(!(ONE && PARTIAL), "one-step tiles have no split form");
     __shared__ __attribute__((aligned(16)))
     int8_t lds[ONE ? TileLds1<KA, KB, MI, NI>::value : TileLds<KA, KB, MI, NI, PARTIAL>::value];
-    gemm_tile<KA, KB, MI, NI, PARTIAL, ONE, -1, RG>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x, lds);
+    gemm_tile<KA, KB, MI, NI, PARTIAL, ONE, -1, RG, DI>(A, B, M, N, K, k_chunk, TM, S, ep, blockIdx.x, gridDim.x,
+                                                        lds);
 }
 
 // Kind codes of kernels built for row groups: the code of the whole-tensor
@@ -1716,24 +1721,28 @@ hipError_t launch_one(const Operand &A, const Operand &B, int M, int N, int K, i
                      (one ? ONE_KIND : 0) + (rows ? ROW_KIND : 0);
     prof_begin(st, kind);
     if constexpr (!PARTIAL) {
-        auto go = [&](auto one_tag, auto rg_tag) {
+        auto go = [&](auto one_tag, auto rg_tag, auto dir_tag) {
             constexpr bool O = decltype(one_tag)::value;
-            constexpr int R = decltype(rg_tag)::value;
-            hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, false, O, R>), grid, dim3(NTHR), 0, st, A, B, M, N,
-                               K, k_chunk, TM, splits, ep);
+            constexpr int R = decltype(rg_tag)::value, D = decltype(dir_tag)::value;
+            hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, false, O, R, D>), grid, dim3(NTHR), 0, st, A, B, M,
+                               N, K, k_chunk, TM, splits, ep);
         };
-        using R0 = std::integral_constant<int, 0>;
-        using R1 = std::integral_constant<int, 1>;
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        auto go2 = [&](auto one_tag, auto rg_tag) {
+            if (ep.mode == EPI_RTO) go(one_tag, rg_tag, I0{});
+            else go(one_tag, rg_tag, I1{});
+        };
         if (one) {
-            if (rows) go(std::true_type{}, R1{});
-            else go(std::true_type{}, R0{});
+            if (rows) go2(std::true_type{}, I1{});
+            else go2(std::true_type{}, I0{});
         } else {
-            if (rows) go(std::false_type{}, R1{});
-            else go(std::false_type{}, R0{});
+            if (rows) go2(std::false_type{}, I1{});
+            else go2(std::false_type{}, I0{});
         }
     } else {
-        hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, true, false, 0>), grid, dim3(NTHR), 0, st, A, B, M, N, K,
-                           k_chunk, TM, splits, ep);
+        hipLaunchKernelGGL((gemm_i8_kernel<KA, KB, MI, NI, true, false, 0, 0>), grid, dim3(NTHR), 0, st, A, B, M, N,
+                           K, k_chunk, TM, splits, ep);
     }
     prof_end(st, kind);
     return hipGetLastError();

@@ -23,13 +23,14 @@ def test_more_than_one_gpu_is_refused():
 
 def test_kind_names_and_symbols():
     # 10000*(10*mi + ni) + 1000 + 100*epilogue + 10*loader_A + loader_B
-    assert bench.kind_symbol(220000 + 1000 + 100 * 1 + 0) == "gemm_i8_kernel<0, 0, 2, 2, false, false, 0>"
-    assert bench.kind_symbol(bench.ROW_KIND + 220000 + 1000 + 100 * 1 + 0) == "gemm_i8_kernel<0, 0, 2, 2, false, false, 1>"
-    assert bench.kind_symbol(110000 + 1000 + 100 * 2 + 10 * 1 + 4) == "gemm_i8_kernel<1, 4, 1, 1, true, false, 0>"
+    assert bench.kind_symbol(220000 + 1000 + 100 * 1 + 0) == "gemm_i8_kernel<0, 0, 2, 2, false, false, 0, 0>"
+    assert bench.kind_symbol(bench.ROW_KIND + 220000 + 1000 + 100 * 1 + 0) == "gemm_i8_kernel<0, 0, 2, 2, false, false, 1, 0>"
+    assert bench.kind_symbol(110000 + 1000 + 100 * 2 + 10 * 1 + 4) == "gemm_i8_kernel<1, 4, 1, 1, true, false, 0, 0>"
     one_row = bench.ROW_KIND + bench.ONE_KIND + 220000 + 1000 + 100 * 8
     assert bench.is_one(one_row) and bench.is_row(one_row)
     assert bench.kind_symbol(one_row) == "gemm_max_kernel<0, 0, 2, 2, true, 1>"
-    assert bench.kind_symbol(bench.ONE_KIND + 220000 + 1000 + 100 * 3) == "gemm_i8_kernel<0, 0, 2, 2, false, true, 0>"
+    assert bench.kind_symbol(bench.ONE_KIND + 220000 + 1000 + 100 * 9) == "gemm_i8_kernel<0, 0, 2, 2, false, true, 0, 1>"
+    assert bench.kind_symbol(220000 + 1000 + 100 * 0) == "gemm_i8_kernel<0, 0, 2, 2, false, false, 0, 1>"
     assert bench.kind_name(one_row) == bench.kind_name(one_row - bench.ROW_KIND) + "_rows"
     assert bench.kind_symbol(140000 + 1000 + 100 * 6) == "gemm_batched_kernel<0, 0, 1, 4, true>"
     assert bench.kind_symbol(210000 + 1000 + 100 * 4 + 1) == "gemm_batched_kernel<0, 1, 2, 1, false>"
